@@ -1,0 +1,422 @@
+"""Pins of the CPU oracle to things other than itself.
+
+Each pin is a plain function of an ``oracle.Oracle`` that raises AssertionError when
+the oracle disagrees with what the pages or the mathematics fix: printed values
+(``tests/golden``), closed forms, invariants, exact rational arithmetic, brute force
+on tiny inputs, and special cases that reduce to a numpy routine. The same pins run
+against deliberately broken copies of the oracle (``test_oracle_mutants.py``), each
+of which must fail at least one of them.
+"""
+from __future__ import annotations
+
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import workloads
+from exact import rne_int, round_to_f16, round_to_f32
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+F32_1EM10 = float(np.float32(1e-10))
+# Half a quantization step plus the fp32 roundings of x / s and of s itself, in units
+# of s: below 128 * 2^-24 + 2^-18 < 2^-15.
+SLOP = 2.0 ** -15
+
+
+def _rows(path):
+    out = []
+    for line in open(os.path.join(GOLDEN, path)):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            out.append([p.strip() for p in line.split(";")])
+    return out
+
+
+def _finite_halves():
+    bits = np.arange(65536, dtype=np.uint16)
+    h = bits.view(np.float16)
+    return bits[np.isfinite(h)]
+
+
+# ------------------------------------------------------------------ binary16
+
+def pin_f16_decode_all(orc):
+    """Every binary16 bit pattern decodes to numpy's float16 value."""
+    bits = np.arange(65536, dtype=np.uint16)
+    got = orc.f16_bits_to_f32(bits)
+    ref = bits.view(np.float16).astype(np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def pin_f16_encode_ties_and_roundtrip(orc):
+    """Exact halves encode to themselves; midpoints between neighbours go to the even
+    neighbour (computed exactly from the binary16 definition); random floats match the
+    exact rational rounding."""
+    bits = _finite_halves()
+    vals = bits.view(np.float16).astype(np.float32)
+    got = orc.f32_to_f16_bits(vals)
+    # -0.0 and +0.0 both round-trip bit-exactly
+    assert np.array_equal(got, bits)
+    pos = np.sort(vals[(vals > 0)].astype(np.float64))
+    mids = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)     # exact: 12 significant bits
+    gm = orc.f32_to_f16_bits(mids).view(np.float16).astype(np.float64)
+    rng = np.random.default_rng(7)
+    pick = rng.choice(mids.size, 400, replace=False)
+    for i in pick:
+        assert gm[i] == round_to_f16(Fraction(float(mids[i]))), float(mids[i])
+    # above the largest finite half by at least half an ulp -> inf
+    assert orc.f32_to_f16_bits(np.array([65520.0], np.float32))[0] == 0x7C00
+    assert orc.f32_to_f16_bits(np.array([65519.0], np.float32))[0] == 0x7BFF
+    r = (rng.standard_normal(300) * np.exp2(rng.uniform(-26, 15, 300))).astype(np.float32)
+    gr = orc.f32_to_f16_bits(r).view(np.float16).astype(np.float64)
+    for v, g in zip(r, gr):
+        assert g == round_to_f16(Fraction(float(v))), float(v)
+
+
+# ---------------------------------------------------------- int8 quantizer
+
+def pin_quant_golden_ties(orc):
+    """Hand-derived tie cases (tests/golden/quant_ties.txt)."""
+    for s_txt, x_txt, q_txt in _rows("quant_ties.txt"):
+        x = np.array([float(v) for v in x_txt.split()], np.float32)[None, :]
+        q_ref = np.array([int(v) for v in q_txt.split()], np.int8)
+        q, s = orc.quant_rows_i8(x)
+        assert float(s[0]) == float(s_txt), (s, s_txt)
+        assert np.array_equal(q[0], q_ref), (q[0], q_ref)
+
+
+def pin_quant_exact_rational(orc):
+    """scale = round_f32(max(absmax, 1e-10) / 127) and q = rne(round_f32(x / scale)),
+    clamped to [-127, 127], checked in exact rational arithmetic on sampled elements."""
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal((6, 300)) * np.exp2(rng.integers(-20, 20, (6, 1)))).astype(np.float32)
+    x[2, :] = 0.0
+    x[3, 5] = 7.0e-12          # tiny row absmax below the floor
+    x[3, :5] = 0.0
+    x[3, 6:] = 0.0
+    q, s = orc.quant_rows_i8(x)
+    for r in range(x.shape[0]):
+        a = max(abs(float(v)) for v in x[r])
+        s_ref = round_to_f32(Fraction(max(a, F32_1EM10)) / 127)
+        assert float(s[r]) == s_ref, (r, float(s[r]), s_ref)
+        for c in rng.choice(x.shape[1], 60, replace=False):
+            qt = rne_int(round_to_f32(Fraction(float(x[r, c])) / Fraction(s_ref)))
+            qt = max(-127, min(127, qt))
+            assert int(q[r, c]) == qt, (r, c)
+
+
+def pin_quant_invariants(orc):
+    """|q| <= 127; |x - q s| <= s/2 (+ the division's rounding); each row's absmax
+    element maps to +-127; rows are quantized independently (per-row axis)."""
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((32, 512)).astype(np.float32)
+    x *= np.exp2(rng.integers(-12, 12, (32, 1))).astype(np.float32)   # very different row ranges
+    x[:, 17] *= 20.0
+    q, s = orc.quant_rows_i8(x)
+    assert q.min() >= -127 and q.max() <= 127
+    err = np.abs(x.astype(np.float64) - q.astype(np.float64) * s[:, None].astype(np.float64))
+    assert np.all(err <= s[:, None].astype(np.float64) * (0.5 + SLOP))
+    am = np.argmax(np.abs(x), axis=1)
+    assert np.array_equal(np.abs(q[np.arange(32), am]).astype(int), np.full(32, 127))
+    assert np.all(np.max(np.abs(q.astype(int)), axis=1) == 127)
+
+
+def pin_quant_zero_row_floor(orc):
+    """An all-zero row has absmax floored at 1e-10: scale = 1e-10/127, codes 0."""
+    x = np.zeros((2, 64), np.float32)
+    x[1, 3] = -1.0
+    q, s = orc.quant_rows_i8(x)
+    assert float(s[0]) == round_to_f32(Fraction(F32_1EM10) / 127)
+    assert not q[0].any()
+    assert q[1, 3] == -127
+
+
+def pin_quant_power_of_two_invariance(orc):
+    """Scaling a row by 2^j scales its scale by 2^j exactly and leaves the codes alone."""
+    rng = np.random.default_rng(13)
+    x = rng.standard_normal((8, 256)).astype(np.float32)
+    q0, s0 = orc.quant_rows_i8(x)
+    for j in (-7, -1, 3, 9):
+        q1, s1 = orc.quant_rows_i8(x * np.float32(2.0 ** j))
+        assert np.array_equal(q0, q1)
+        assert np.array_equal(s1, s0 * np.float32(2.0 ** j))
+
+
+def pin_quant_fp16_domain(orc):
+    """Every finite fp16 value as an activation under several row absmax values:
+    codes stay within [-127, 127] and within half a step of x / s (exact arithmetic
+    on a sample, bound on all); fp16 rows decode exactly before quantizing."""
+    vals = _finite_halves().view(np.float16)
+    for amax in (np.float16(65504.0), np.float16(127.0), np.float16(1.0), np.float16(0.0078125)):
+        row = vals[np.abs(vals.astype(np.float32)) <= np.float32(amax)]
+        row = np.concatenate([[amax], row]).astype(np.float16)[None, :]
+        q, s = orc.quant_rows_i8(row)
+        xf = row.astype(np.float64)[0]
+        sv = float(s[0])
+        assert sv == round_to_f32(Fraction(float(amax)) / 127)
+        assert q.min() >= -127 and q.max() <= 127
+        assert np.all(np.abs(xf / sv - q[0]) <= 0.5 + SLOP)
+        idx = np.random.default_rng(int(float(amax) * 8)).choice(row.shape[1], 200, replace=False)
+        for c in idx:
+            qt = rne_int(round_to_f32(Fraction(float(xf[c])) / Fraction(sv)))
+            assert int(q[0, c]) == max(-127, min(127, qt))
+
+
+def pin_quant_fp16_domain_exhaustive(orc):
+    """Every finite fp16 activation under each of six row absmax values, every code
+    checked: q = rne(fl32(x / s)). fl32 of a quotient is computed as the fp64 quotient
+    rounded to fp32, which equals the directly rounded fp32 quotient because double
+    rounding through 53 bits is innocuous for division at 24 bits (53 >= 2*24 + 2)."""
+    vals = _finite_halves().view(np.float16)
+    # the last four absmax values are ones where x * (127 / a) would round differently
+    for amax in (65504.0, 1000.0, 127.0, 3.0, 1.0, 0.0078125,
+                 0.947265625, 2.32421875, 1.4931640625, 0.1285400390625):
+        amax16 = np.float16(amax)
+        row = vals[np.abs(vals.astype(np.float32)) <= np.float32(amax16)]
+        row = np.concatenate([[amax16], row]).astype(np.float16)[None, :]
+        q, s = orc.quant_rows_i8(row)
+        sv = round_to_f32(Fraction(float(amax16)) / 127)
+        assert float(s[0]) == sv
+        quot = (row[0].astype(np.float64) / sv).astype(np.float32).astype(np.float64)
+        ref = np.clip(np.rint(quot), -127, 127).astype(np.int8)
+        assert np.array_equal(q[0], ref), amax
+
+
+def pin_int4_golden_ties(orc):
+    """Hand-derived int4 tie cases (tests/golden/int4_ties.txt); one group of 8 padded
+    with zeros to the group size 128 is still the same group absmax."""
+    for s_txt, w_txt, q_txt in _rows("int4_ties.txt"):
+        wv = [float(v) for v in w_txt.split()]
+        w = np.zeros((1, 128), np.float32)
+        w[0, :len(wv)] = wv
+        packed, s16 = orc.quant_int4_group(w, 128)
+        assert float(s16[0, 0]) == float(s_txt)
+        q = orc.unpack_int4(packed, 128)[0, :len(wv)]
+        assert q.tolist() == [int(v) for v in q_txt.split()], (q, q_txt)
+
+
+def pin_per_channel_beats_per_tensor(orc):
+    """On weights whose column ranges vary (log-uniform sigma in [0.005, 0.5], the small
+    W8A8 workload's law), per-output-channel scales give a weight MSE at least 5x below
+    one per-tensor scale, and a smaller output error (2048ai.net §4, §6.2, qualitative)."""
+    inp = workloads.draw(workloads.W8A8_SMALL)
+    w = inp.w_nk
+    qc, sc = orc.quant_weight_per_channel(w)
+    qt, st = orc.quant_tensor_i8(w)
+    wc = qc.astype(np.float64) * sc[:, None]
+    wt = qt.astype(np.float64) * st
+    mse_c = np.mean((wc - w) ** 2)
+    mse_t = np.mean((wt - w) ** 2)
+    assert mse_t >= 5.0 * mse_c, (mse_c, mse_t)
+    x = inp.x.astype(np.float64)
+    y = x @ w.T
+    assert np.mean((x @ wc.T - y) ** 2) < np.mean((x @ wt.T - y) ** 2)
+
+
+# ------------------------------------------------------------ integer GEMM
+
+def pin_gemm_brute_force(orc):
+    """int32 GEMM equals a Python-int triple loop on tiny non-square shapes."""
+    rng = np.random.default_rng(21)
+    for M, N, K in ((1, 1, 64), (3, 17, 64), (17, 3, 128), (5, 7, 192)):
+        a = rng.integers(-127, 128, (M, K), dtype=np.int8)
+        b = rng.integers(-127, 128, (N, K), dtype=np.int8)
+        acc = orc.gemm_i32(a, b)
+        al, bl = a.tolist(), b.tolist()
+        for m in range(M):
+            for n in range(N):
+                assert acc[m, n] == sum(al[m][k] * bl[n][k] for k in range(K))
+
+
+def pin_gemm_numpy_and_extremes(orc):
+    """Equals numpy's int64 matmul of X and W (W given column-major); all +127 against all
+    -127 gives -K * 127^2."""
+    rng = np.random.default_rng(22)
+    a = rng.integers(-127, 128, (37, 320), dtype=np.int8)
+    b = rng.integers(-127, 128, (29, 320), dtype=np.int8)
+    assert np.array_equal(orc.gemm_i32(a, b), a.astype(np.int64) @ b.astype(np.int64).T)
+    K = 4096
+    acc = orc.gemm_i32(np.full((2, K), 127, np.int8), np.full((3, K), -127, np.int8))
+    assert np.all(acc == -K * 127 * 127)
+
+
+# ---------------------------------------------------------------- epilogue
+
+def pin_epilogue_special_and_bound(orc):
+    """Unit scales and no bias give the accumulator itself; power-of-two scales and a
+    dyadic bias are exact; in general the fp32 result lies within 4u of the exact value
+    (relative to |acc xs ws| + |bias|), and the fp64 result within 4 * 2^-53."""
+    rng = np.random.default_rng(31)
+    acc = rng.integers(-(1 << 23), 1 << 23, (4, 6)).astype(np.int32)
+    y32, y64 = orc.epilogue_w8a8(acc, np.ones(4, np.float32), np.ones(6, np.float32))
+    assert np.array_equal(y32, acc.astype(np.float32)) and np.array_equal(y64, acc.astype(np.float64))
+    # |acc| < 2^11, scales 2^-6..2^0 and bias a multiple of 2^-12 in [-1, 1]: every
+    # intermediate is a multiple of 2^-12 below 2^12, i.e. exact in 24 bits
+    acc = rng.integers(-(1 << 11), 1 << 11, (4, 6)).astype(np.int32)
+    xs = np.exp2(rng.integers(-6, 1, 4)).astype(np.float32)
+    ws = np.exp2(rng.integers(-6, 1, 6)).astype(np.float32)
+    b = (rng.integers(-4096, 4097, 6) / 4096.0).astype(np.float32)
+    y32, _ = orc.epilogue_w8a8(acc, xs, ws, b)
+    for m in range(4):
+        for n in range(6):
+            assert Fraction(float(y32[m, n])) == (Fraction(int(acc[m, n])) * Fraction(float(xs[m]))
+                                                   * Fraction(float(ws[n])) + Fraction(float(b[n])))
+    acc = rng.integers(-66064384, 66064384, (5, 7)).astype(np.int32)
+    xs = rng.uniform(1e-3, 1e-1, 5).astype(np.float32)
+    ws = rng.uniform(1e-4, 1e-2, 7).astype(np.float32)
+    b = rng.standard_normal(7).astype(np.float32)
+    y32, y64 = orc.epilogue_w8a8(acc, xs, ws, b)
+    for m in range(5):
+        for n in range(7):
+            prod = Fraction(int(acc[m, n])) * Fraction(float(xs[m])) * Fraction(float(ws[n]))
+            exact = prod + Fraction(float(b[n]))
+            mag = abs(prod) + abs(Fraction(float(b[n])))
+            assert abs(Fraction(float(y32[m, n])) - exact) <= Fraction(4, 2 ** 24) * mag
+            assert abs(Fraction(float(y64[m, n])) - exact) <= Fraction(4, 2 ** 53) * mag
+
+
+def pin_w8a8_one_hot(orc):
+    """X = e_k rows: x_scale = fl(1/127), xq = 127 e_k, acc[m, n] = 127 wq[k_m, n], and the
+    layer output is within one quantization step of W[k_m, n] (+ bias)."""
+    rng = np.random.default_rng(32)
+    K, N = 128, 24
+    w = (rng.standard_normal((N, K)) * rng.uniform(0.01, 1, (N, 1))).astype(np.float32)
+    wq, ws = orc.quant_weight_per_channel(w)
+    ks = np.array([0, 5, 77, 127])
+    x = np.zeros((4, K), np.float32)
+    x[np.arange(4), ks] = 1.0
+    bias = rng.standard_normal(N).astype(np.float32)
+    r = orc.linear_w8a8(x, wq, ws, bias)
+    assert np.all(r["x_scale"] == np.float32(1.0) / np.float32(127.0))
+    assert np.array_equal(r["xq"], (127 * x).astype(np.int8))
+    assert np.array_equal(r["acc"], 127 * wq[:, ks].T.astype(np.int32))
+    err = np.abs(r["y64"] - (w[:, ks].T.astype(np.float64) + bias))
+    assert np.all(err <= 0.5 * ws[None, :] * 1.001)
+
+
+# -------------------------------------------------------------- weight-only
+
+def pin_w8a16_integer_special_case(orc):
+    """Unit scales and no zero point: an fp GEMM with integer weights, equal to numpy's
+    float64 matmul."""
+    rng = np.random.default_rng(41)
+    x = rng.standard_normal((3, 256)).astype(np.float16)
+    q = rng.integers(-127, 128, (40, 256), dtype=np.int8)
+    y = orc.w8a16_f64(x, q, np.ones(40, np.float32))
+    ref = x.astype(np.float64) @ q.astype(np.float64).T
+    assert np.allclose(y, ref, rtol=1e-13, atol=1e-12)
+
+
+def pin_w8a16_one_hot(orc):
+    """x = e_k: y[n] = (q[k, n] - z[b(k), n]) * s[b(k), n] exactly, for per-channel and
+    block-64 zero-point layouts (pins the scale/zero indexing and the sign of z)."""
+    rng = np.random.default_rng(42)
+    N, K = 10, 256
+    q = rng.integers(-127, 128, (N, K), dtype=np.int8)
+    s = rng.uniform(1e-3, 1e-1, N).astype(np.float32)
+    bias = rng.standard_normal(N).astype(np.float32)
+    ks = [0, 63, 64, 200]
+    x = np.zeros((len(ks), K), np.float16)
+    x[np.arange(len(ks)), ks] = 1.0
+    y = orc.w8a16_f64(x, q, s, bias=bias)
+    for i, k in enumerate(ks):
+        for n in range(N):
+            assert y[i, n] == float(Fraction(int(q[n, k])) * Fraction(float(s[n])) + Fraction(float(bias[n])))
+    u = rng.integers(0, 256, (N, K), dtype=np.uint8)
+    sb = rng.uniform(1e-3, 1e-1, (N, K // 64)).astype(np.float32)
+    zb = rng.integers(0, 256, (N, K // 64), dtype=np.uint8)
+    y = orc.w8a16_f64(x, u, sb, zero_point=zb, group_size=64)
+    for i, k in enumerate(ks):
+        for n in range(N):
+            assert y[i, n] == float((int(u[n, k]) - int(zb[n, k // 64])) * Fraction(float(sb[n, k // 64])))
+
+
+def pin_block_asym_quantizer(orc):
+    """Block-64 asymmetric uint8 (zingnex.cn steps 1-2): scale = (max-min)/255 (fp32),
+    the block minimum codes to 0 exactly, the maximum to 254 or 255, and every weight
+    comes back within half a step: |w - (q - zp) s| <= s/2 (+ rounding)."""
+    inp = workloads.draw(workloads.with_shape(workloads.W8A16_BLOCK, 1, 512, 48))
+    w = inp.w_nk
+    q, s, z = orc.quant_block_asym_u8(w, 64)
+    blocks = w.reshape(48, 8, 64)
+    qb = q.reshape(48, 8, 64).astype(np.int64)
+    mn, mx = blocks.min(-1), blocks.max(-1)
+    for n in range(0, 48, 5):
+        for b in range(8):
+            assert float(s[n, b]) == round_to_f32(Fraction(round_to_f32(Fraction(float(mx[n, b])) - Fraction(float(mn[n, b])))) / 255)
+    assert np.all(qb[np.arange(48)[:, None], np.arange(8)[None, :], blocks.argmin(-1)] == 0)
+    assert np.all(np.isin(qb[np.arange(48)[:, None], np.arange(8)[None, :], blocks.argmax(-1)], (254, 255)))
+    deq = (qb - z[:, :, None].astype(np.int64)) * s[:, :, None].astype(np.float64)
+    assert np.all(np.abs(deq - blocks) <= s[:, :, None] * (0.5 + 2.0 ** -16))
+
+
+def pin_int4_pack_layout(orc):
+    """Eight two's-complement nibbles per int32 along K, element k%8 = j in bits
+    [4j, 4j+3]: the oracle's unpack inverts an independent numpy pack, over all 16 values
+    at all 8 positions."""
+    N, K = 16, 128
+    q = np.empty((N, K), np.int64)
+    for n in range(N):
+        q[n] = (np.arange(K) + n) % 16 - 8
+    nib = (q & 0xF).astype(np.uint64).reshape(N, K // 8, 8)
+    words = np.zeros((N, K // 8), np.uint64)
+    for j in range(8):
+        words |= nib[:, :, j] << np.uint64(4 * j)
+    packed = words.astype(np.uint32).view(np.int32)
+    assert np.array_equal(orc.unpack_int4(packed, K).astype(np.int64), q)
+
+
+def pin_int4_quantizer(orc):
+    """int4 group quantizer (xdnf.cn §5.1, scale = absmax/7, stored fp16): the scale is
+    the fp16 rounding of the fp32 quotient, each group's absmax element codes to +-7,
+    codes stay in [-8, 7] and every weight is within half a step of q * s16."""
+    inp = workloads.draw(workloads.with_shape(workloads.W4A16_GROUP, 1, 512, 40))
+    w = inp.w_nk
+    packed, s16 = orc.quant_int4_group(w, 128)
+    q = orc.unpack_int4(packed, 512).astype(np.int64).reshape(40, 4, 128)
+    g = w.reshape(40, 4, 128)
+    a = np.abs(g).max(-1)
+    for n in range(0, 40, 3):
+        for b in range(4):
+            s32 = round_to_f32(Fraction(float(a[n, b])) / 7)
+            assert float(s16[n, b]) == round_to_f16(Fraction(s32))
+    sv = s16.astype(np.float64)[:, :, None]
+    am = np.abs(g).argmax(-1)
+    assert np.all(np.abs(q[np.arange(40)[:, None], np.arange(4)[None, :], am]) == 7)
+    assert q.min() >= -8 and q.max() <= 7
+    assert np.all(np.abs(g - q * sv) <= sv * (0.5 + 2.0 ** -16))
+
+
+def pin_w4a16_one_hot(orc):
+    """x = e_k: y[n] = q[k, n] * s16[k // group, n] exactly (pins nibble order, sign
+    extension and group indexing)."""
+    rng = np.random.default_rng(51)
+    N, K, G = 12, 512, 128
+    w = rng.standard_normal((N, K)).astype(np.float32)
+    packed, s16 = orc.quant_int4_group(w, G)
+    q = orc.unpack_int4(packed, K)
+    ks = [0, 1, 7, 8, 127, 128, 300, 511]
+    x = np.zeros((len(ks), K), np.float16)
+    x[np.arange(len(ks)), ks] = 1.0
+    y = orc.w4a16_f64(x, packed, s16, G)
+    for i, k in enumerate(ks):
+        assert np.array_equal(y[i], q[:, k].astype(np.float64) * s16[:, k // G].astype(np.float64))
+
+
+def pin_footprint_golden(orc):
+    """The pages' printed footprints (tests/golden/footprint.txt) follow from the code
+    formats' storage: 1 byte per int8 code, 4 bytes per 8 int4 codes."""
+    w = np.random.default_rng(61).standard_normal((8, 256)).astype(np.float32)
+    q8, _ = orc.quant_weight_per_channel(w)
+    p4, _ = orc.quant_int4_group(w, 128)
+    bytes_per = {16: 2.0, 8: q8.nbytes / w.size, 4: p4.nbytes / w.size}
+    for params, bits, printed, unit in _rows("footprint.txt"):
+        size = float(params) * bytes_per[int(bits)] / (2 ** 30 if unit == "GiB" else 1e9)
+        nd = len(printed.split(".")[1]) if "." in printed else 0
+        assert abs(size - float(printed)) <= 0.5 * 10 ** -nd + 1e-9, (params, bits, size, printed)
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

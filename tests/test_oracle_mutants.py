@@ -1,0 +1,66 @@
+"""The pins have teeth: copies of the oracle with one plausible mistake planted
+(a dropped term, a wrong sign or index, a transposed operand, the other rounding
+rule) are compiled on the CPU and each must fail at least one pin."""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import oracle_pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "ql_oracle.c")
+
+# (name, text in ql_oracle.c, replacement)
+MUTANTS = [
+    ("round_half_away", "float r = nearbyintf(v[i] / s);\n        if (r > 127.0f)",
+     "float r = roundf(v[i] / s);\n        if (r > 127.0f)"),
+    ("reciprocal_multiply", "float r = nearbyintf(v[i] / s);\n        if (r > 127.0f)",
+     "float r = nearbyintf(v[i] * (127.0f / (a > floor_a ? a : floor_a)));\n        if (r > 127.0f)"),
+    ("int4_round_half_away", "float r = nearbyintf(v[i] / s);\n                if (r > 7.0f)",
+     "float r = roundf(v[i] / s);\n                if (r > 7.0f)"),
+    ("signed_absmax", "        float t = fabsf(v[i]);\n        if (t > a)\n            a = t;\n    }\n    const float floor_a = 1e-10f;",
+     "        float t = v[i];\n        if (t > a)\n            a = t;\n    }\n    const float floor_a = 1e-10f;"),
+    ("no_absmax_floor", "float s = (a > floor_a ? a : floor_a) / 127.0f;", "float s = a / 127.0f;"),
+    ("scale_over_128", "float s = (a > floor_a ? a : floor_a) / 127.0f;", "float s = (a > floor_a ? a : floor_a) / 128.0f;"),
+    ("gemm_transposed_w", "t += (int32_t)xq[m * K + k] * (int32_t)wq[n * K + k];",
+     "t += (int32_t)xq[m * K + k] * (int32_t)wq[(k % N) * K + (n % K)];"),
+    ("gemm_int16_accumulate", "t += (int32_t)xq[m * K + k] * (int32_t)wq[n * K + k];",
+     "t = (int16_t)(t + (int32_t)xq[m * K + k] * (int32_t)wq[n * K + k]);"),
+    ("epilogue_drops_bias", "                    y = y + bias[n];", "                    y = y;"),
+    ("epilogue_wrong_scale_axis", "float y = t * x_scale[m];", "float y = t * x_scale[n % M];"),
+    ("wonly_scale_row_major", "double s = group > 0 ? (double)scale[n * G + g] : (double)scale[n];",
+     "double s = group > 0 ? (double)scale[g * N + n] : (double)scale[n];"),
+    ("wonly_zero_sign", "acc += (double)x[m * K + k] * ((q - z) * s);", "acc += (double)x[m * K + k] * ((q + z) * s);"),
+    ("int4_no_sign_extend", "return nib >= 8 ? nib - 16 : nib;", "return nib;"),
+    ("int4_nibble_order", "int nib = (int)((word >> (4 * (k % 8))) & 0xFu);",
+     "int nib = (int)((word >> (4 * (7 - k % 8))) & 0xFu);"),
+    ("w4a16_group_index", "scale16[n * G + k / group]", "scale16[n * G + (k % G)]"),
+    ("int4_fp32_scale", "float s = oracle_f16_to_f32(h);", "float s = (a > floor_a ? a : floor_a) / 7.0f;"),
+    ("int4_scale_over_8", "uint16_t h = oracle_f32_to_f16((a > floor_a ? a : floor_a) / 7.0f);",
+     "uint16_t h = oracle_f32_to_f16((a > floor_a ? a : floor_a) / 8.0f);"),
+    ("block_zero_sign", "float zf = nearbyintf(-mn / s);", "float zf = nearbyintf(mn / s);"),
+    ("block_range_254", "float s = (mx - mn) / 255.0f;", "float s = (mx - mn) / 254.0f;"),
+    ("f16_ties_away", "double r = nearbyint(ldexp(a, 10 - E));", "double r = round(ldexp(a, 10 - E));"),
+    ("f16_subnormal_scale", "v = ldexp((double)f, -24);", "v = ldexp((double)f, -25);"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(name, old, new, tmp_path):
+    text = open(SRC).read()
+    assert text.count(old) == 1, "mutation site not found exactly once: " + name
+    src = tmp_path / "ql_oracle.c"
+    src.write_text(text.replace(old, new))
+    hdr = os.path.join(os.path.dirname(SRC), "ql_oracle.h")
+    (tmp_path / "ql_oracle.h").write_text(open(hdr).read())
+    so = tmp_path / "libmutant.so"
+    subprocess.check_call(["gcc", *oracle.CFLAGS, str(src), "-o", str(so), "-lm"])
+    orc = oracle.Oracle(str(so))
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(orc)
+        except (AssertionError, OverflowError, ValueError):
+            failed.append(pin.__name__)
+    assert failed, "no pin catches the planted mistake " + name
