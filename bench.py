@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized linear layer's hot path on one MI355X (gfx950).
+
+One step is one pass of every step of the path over one batch of synthetic input, with
+all inputs resident in HBM:
+  1. per-row int8 quantization of X [2048, 4096] fp16            (W8A8 prefill layer)
+  2. W8A8 GEMM M=2048 K=4096 N=11008 + fused dequant/bias, fp16 out
+  3. W8A16 decode GEMV M=1 K=4096 N=4096 (per-channel int8 weights)
+  4. block-asymmetric W8A16 M=8 K=4096 N=4096 (uint8, blocks of 64)
+  5. W4A16 M=32 K=4096 N=14336 (int4, groups of 128)
+Weight quantization is offline (done once, untimed). The decode weights are replicated
+in enough distinct buffers (over 512 MiB per workload) that each step streams its
+weights from HBM rather than from the 256 MB Infinity Cache.
+
+Printed: one JSON line. ``value`` is the W8A8 prefill layer's throughput in TOPS
+(2*M*N*K integer ops over the average time of steps 1 + 2); the decode workloads'
+GB/s are reported alongside. Kernel times come from HIP events recorded around each
+launch on the stream the kernels run on, inside the timed region.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "W8A8 per-channel GEMM TOPS at Llama-7B shapes; W8A16 decode GEMV GB/s"
+PEAK_INT8_TOPS = 5000.0        # MI355X dense int8 MFMA, 5.0 POP/s
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+ROTATE_BYTES = 512 << 20
+
+
+def _algorithmic_bytes():
+    import workloads as wl
+    w2, w4, w5, w3 = wl.W8A16_DECODE, wl.W8A16_BLOCK, wl.W4A16_GROUP, wl.W8A8_PREFILL
+    return {
+        # weights + scales (+ zero points) + X + Y
+        "w8a16": w2.N * w2.K + 4 * w2.N + 2 * w2.M * w2.K + 2 * w2.M * w2.N,
+        "w8a16_block": (w4.N * w4.K + 4 * w4.N * (w4.K // 64) + w4.N * (w4.K // 64)
+                        + 2 * w4.M * w4.K + 2 * w4.M * w4.N),
+        "w4a16": (w5.N * w5.K // 2 + 2 * w5.N * (w5.K // 128) + 2 * w5.M * w5.K
+                  + 2 * w5.M * w5.N),
+        # fp16 X in, int8 codes and fp32 scales out
+        "quant": 2 * w3.M * w3.K + w3.M * w3.K + 4 * w3.M,
+    }
+
+
+def _kernel_hash():
+    src = os.path.join(ROOT, "int8_quantized_linear_amd", "csrc", "gemm_w8a8.hip")
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+
+
+def _traffic_for_gemm():
+    """HBM bytes per launch of the W8A8 GEMM from committed rocprofv3 counter runs, or None
+    if absent or taken on a different version of the kernel source."""
+    path = os.path.join(ROOT, "profiles", "gemm_w8a8_m2048_k4096_n11008_traffic.json")
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != _kernel_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(target_s: float):
+    """The oracle timed on this host on a bounded sample of the W8A8 prefill layer: the first
+    R rows of X through per-row quantization, the exact int32 GEMM against all of W, and the
+    epilogue. R is chosen so the timed work takes about target_s seconds."""
+    import numpy as np
+
+    import oracle
+    import workloads as wl
+
+    w = wl.W8A8_PREFILL
+    inp = wl.draw(w)
+    wq, ws = oracle.quant_weight_per_channel(inp.w_nk)   # offline, untimed
+
+    def run(r):
+        t0 = time.perf_counter()
+        res = oracle.linear_w8a8(inp.x[:r], wq, ws, inp.bias)
+        _ = res["y32"].astype(np.float16)
+        return time.perf_counter() - t0
+
+    # rows are spread over the oracle's OpenMP threads: calibrate on one row per thread
+    nt = max(1, min(64, oracle.num_threads()))
+    per_row = run(nt) / nt
+    rows = int(max(nt, min(w.M, nt * round(target_s / per_row / nt))))
+    dt = run(rows)
+    ops = 2.0 * rows * w.N * w.K
+    return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "rows 0..%d of X [2048,4096] through the W8A8 layer (per-row quantize, exact "
+                      "int32 GEMM with W [4096,11008], fp32 epilogue, fp16 output): %.1f s" % (rows - 1, dt),
+            "seconds": dt, "host": platform.processor() or platform.machine()}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", dest="cpu", action="store_false")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calib-copy-mib", type=int, default=256,
+                    help="size of the plain device copy run once before the timed region "
+                         "(reference point for hardware byte counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(got --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import int8_quantized_linear_amd as ql
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def progress(msg):
+        print("[bench] " + msg, file=sys.stderr, flush=True)
+
+    # ---------------------------------------------------------------- inputs
+    progress("drawing inputs")
+    w3 = wl.W8A8_PREFILL
+    i3 = wl.draw(w3)
+    wq3, ws3 = ql.quantize_weight_per_channel(up(i3.w_nk))
+    x3, b3 = up(i3.x), up(i3.bias)
+    xq3 = torch.empty((w3.M, w3.K), dtype=torch.int8, device=dev)
+    xs3 = torch.empty((w3.M,), dtype=torch.float32, device=dev)
+    y3 = torch.empty((w3.M, w3.N), dtype=torch.float16, device=dev)
+    del i3
+
+    def rotations(nbytes):
+        return max(2, math.ceil(ROTATE_BYTES / nbytes))
+
+    ab = _algorithmic_bytes()
+    w2 = wl.W8A16_DECODE
+    i2 = wl.draw(w2)
+    q2, s2 = ql.quantize_weight_per_channel(up(i2.w_nk))
+    r2 = rotations(ab["w8a16"])
+    set2 = [(q2.clone(), s2.clone()) for _ in range(r2)]
+    x2 = up(i2.x)
+    y2 = torch.empty((w2.M, w2.N), dtype=torch.float16, device=dev)
+
+    w4 = wl.W8A16_BLOCK
+    i4 = wl.draw(w4)
+    q4, s4, z4 = ql.quantize_weight_block_asym_u8(up(i4.w_nk), 64)
+    r4 = rotations(ab["w8a16_block"])
+    set4 = [(q4.clone(), s4.clone(), z4.clone()) for _ in range(r4)]
+    x4 = up(i4.x)
+    y4 = torch.empty((w4.M, w4.N), dtype=torch.float16, device=dev)
+
+    w5 = wl.W4A16_GROUP
+    i5 = wl.draw(w5)
+    p5, s5 = ql.quantize_weight_int4_grouped(up(i5.w_nk), 128)
+    r5 = rotations(ab["w4a16"])
+    set5 = [(p5.clone(), s5.clone()) for _ in range(r5)]
+    x5 = up(i5.x)
+    y5 = torch.empty((w5.M, w5.N), dtype=torch.float16, device=dev)
+    del i2, i4, i5
+    torch.cuda.synchronize()
+
+    # ------------------------------------------------- prepared launches
+    F16 = 1
+    quant = ql.prepare("quantize_per_row_int8", x3, F16, w3.M, w3.K, xq3, xs3)
+    gemm = ql.prepare("gemm_w8a8_per_channel", xq3, xs3, wq3, ws3, b3, y3, F16, w3.M, w3.N, w3.K)
+    dec2 = [ql.prepare("gemm_w8a16", x2, q, s, None, 0, None, y2, w2.M, w2.N, w2.K) for q, s in set2]
+    dec4 = [ql.prepare("gemm_w8a16", x4, q, s, z, 64, None, y4, w4.M, w4.N, w4.K) for q, s, z in set4]
+    dec5 = [ql.prepare("gemm_w4a16_grouped", x5, p, s, 128, None, y5, w5.M, w5.N, w5.K) for p, s in set5]
+    names = ["quant", "gemm", "w8a16", "w8a16_block", "w4a16"]
+
+    def step(i, ev=None):
+        launches = [quant, gemm, dec2[i % r2], dec4[i % r4], dec5[i % r5]]
+        for j, fn in enumerate(launches):
+            if ev is not None:
+                ev[j][0].record()
+            fn()
+            if ev is not None:
+                ev[j][1].record()
+
+    # Plain device copy of known size (reference for hardware byte counters), untimed.
+    if args.calib_copy_mib > 0:
+        nb = args.calib_copy_mib << 20
+        src = torch.empty(nb, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    progress("warmup %d steps" % args.warmup)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    events = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+               for _ in names] for _ in range(K)]
+    progress("timing %d steps" % K)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(args.warmup + i, events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+    avg_ms = {n: sum(events[i][j][0].elapsed_time(events[i][j][1]) for i in range(K)) / K
+              for j, n in enumerate(names)}
+
+    ops = 2.0 * w3.M * w3.N * w3.K
+    layer_s = (avg_ms["quant"] + avg_ms["gemm"]) * 1e-3
+    gemm_s = avg_ms["gemm"] * 1e-3
+    value = ops / layer_s / 1e12
+    gemm_tops = ops / gemm_s / 1e12
+
+    def gbs(name):
+        return ab[name] / (avg_ms[name] * 1e-3) / 1e9
+
+    decode = {}
+    for name, w, rot in (("w8a16", w2, r2), ("w8a16_block", w4, r4), ("w4a16", w5, r5)):
+        decode[name] = {"workload": w.name, "us": avg_ms[name] * 1e3, "GB_per_s": gbs(name),
+                        "frac_hbm_peak": gbs(name) / PEAK_HBM_GBS, "bytes": ab[name],
+                        "weight_sets_rotated": rot}
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": w3.name, "M": w3.M, "K": w3.K, "N": w3.N, "x": "fp16", "y": "fp16",
+                   "bias": True, "value_covers": "per-row quantization + W8A8 GEMM",
+                   "decode_workloads": [w2.name, w4.name, w5.name]},
+        "roofline": {"bound": "mfma", "kernel": "gemm_w8a8_per_channel", "achieved": gemm_tops,
+                     "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s", "frac": gemm_tops / PEAK_INT8_TOPS,
+                     "traffic": _traffic_for_gemm(), "avg_us": avg_ms["gemm"] * 1e3,
+                     "note": "int8 operations (2*M*N*K per launch) against the dense int8 MFMA peak"},
+        "w8a16_decode_GB_per_s": decode["w8a16"]["GB_per_s"],
+        "quantizer": {"us": avg_ms["quant"] * 1e3, "GB_per_s": gbs("quant"),
+                      "frac_hbm_peak": gbs("quant") / PEAK_HBM_GBS},
+        "decode": decode,
+        "device": torch.cuda.get_device_name(0),
+    }
+    if args.cpu:
+        progress("cpu baseline (oracle) ~%.0f s" % args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,207 @@
+/*
+ * ql.h -- C ABI of libql.so, a quantized linear layer for AMD Instinct MI355X (gfx950)
+ *
+ *     Y = (x_scale (.) Xq) @ (w_scale (.) Wq) + bias
+ *
+ * Sources of the operation (web pages; cited by title and section):
+ *   [hotelren]  hotelren.com, "量化算法的本质" -- the statement of Y = XW with X [M,K]
+ *               row-major and W [K,N] column-major (opening section); the
+ *               per_tensor_quant_int8 and per_channel_quant_int8 quantizers; the list
+ *               of a quantized GEMM's parameters (X, W, scale, optional zero, optional
+ *               bias) in "量化模型的矩阵乘法"; and Y = (x_scale*X)@(w_scale*W)+bias in
+ *               "W8A8矩阵乘法".
+ *   [quant67]   quant67.com GPU-kernel series ch.17, "量化与多精度算子：INT8 / FP8、反量化
+ *               与 per-channel" -- §二 q = round(x/s) + z and the integer-GEMM expansion;
+ *               §三 granularity; §四 int32 accumulation and dequantization in the
+ *               epilogue, weight-only dequantization inside the kernel; §六 pitfalls.
+ *   [2048ai]    2048ai.net, INT8 Llama-2-7B on Ascend write-up -- §2.2 scale = max/127;
+ *               §4 per-output-channel weight scales; §5.2-§5.4 the per-channel INT8 GEMM
+ *               C = (A_int8 B_int8) (.) scales[N] with int32 accumulation and dequant at
+ *               write-back.
+ *   [zingnex]   zingnex.cn, "从零实现大语言模型 INT8 量化" -- 核心量化流程 steps 1-2:
+ *               blocks of 64, scale = (max-min)/255, zero_point = round(-min/scale).
+ *   [xdnf]      xdnf.cn, INT4/FP16 mixed-precision GEMM as a CANN TBE operator -- §3.2
+ *               unpack then dequantize with fp32 accumulation; §4.1 the operator's
+ *               (M,K) fp16 x packed int4 -> (M,N) fp16 contract; §5.1 scale = absmax/7.
+ *
+ * Conventions for every entry point:
+ *   - Every array is a DEVICE pointer owned by the caller. The library never
+ *     allocates, frees, retains or synchronizes, and keeps no state.
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL is the null stream) and the
+ *     call returns without waiting. Device faults surface at the caller's next
+ *     synchronization on that stream.
+ *   - Layouts: X and Y are row-major and contiguous. W [K,N] is column-major, i.e. an
+ *     [N][K] array with K contiguous ([hotelren] opening section). Per-group scales
+ *     and zero points are column-major [K/group, N], i.e. [N][K/group].
+ *   - Outputs must not overlap inputs or each other.
+ *   - Shapes: M == 0 or N == 0 is an empty problem: QL_OK, nothing is launched.
+ *   - All arguments are validated before anything is enqueued; on any error nothing is
+ *     written. Validation touches no GPU, so it can be exercised without one.
+ *     QL_ERR_NULL  a required pointer is NULL
+ *     QL_ERR_SHAPE a size is negative or breaks the divisibility stated per call
+ *     QL_ERR_ALIGN a large operand (X, W, Y, codes) is not 16-byte aligned, or a
+ *                  scale/bias/zero array is not aligned to its element size
+ *     QL_ERR_DTYPE an unknown dtype code
+ *     QL_ERR_DEVICE the HIP launch reported an error (hipGetLastError)
+ *   - Inputs are assumed finite (no NaN or Inf).
+ *   - Quantization rounds half to even, divides in correctly rounded fp32 (x / s with
+ *     s = absmax / 127, never x * (127 / absmax)) and clamps symmetric codes to
+ *     [-127, 127]; an all-zero row or column gets absmax floored at 1e-10.
+ */
+#ifndef QL_H
+#define QL_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QL_OK = 0,
+    QL_ERR_NULL = 1,
+    QL_ERR_SHAPE = 2,
+    QL_ERR_ALIGN = 3,
+    QL_ERR_DTYPE = 4,
+    QL_ERR_DEVICE = 5
+} ql_status;
+
+typedef enum { QL_F32 = 0, QL_F16 = 1 } ql_dtype;
+
+/* Human-readable name of a status code (a static string). */
+const char* ql_status_str(ql_status s);
+
+/*
+ * Per-row (per-token) dynamic symmetric int8 quantization of activations.
+ * [hotelren] per_channel_quant_int8 (symmetric branch, absmax along the last
+ * dimension, clamp_min 1e-10, scale = absmax/127, torch.round); [2048ai] §2.2.
+ *
+ *   a[m] = max_k |x[m,k]|,  x_scale[m] = max(a[m], 1e-10) / 127   (fp32)
+ *   xq[m,k] = clamp(round_half_even(x[m,k] / x_scale[m]), -127, 127)
+ *
+ * x       [M,K] row-major, fp32 (x_dtype QL_F32) or fp16 (QL_F16)
+ * xq      [M,K] int8 row-major (out)
+ * x_scale [M] fp32 (out)
+ * Requires K > 0 and K % 16 == 0.
+ */
+ql_status quantize_per_row_int8(const void* x, ql_dtype x_dtype, int64_t M, int64_t K,
+                                int8_t* xq, float* x_scale, void* stream);
+
+/*
+ * Per-output-channel symmetric int8 quantization of weights (offline, before serving).
+ * [2048ai] §4.2 and §6.1 (one scale per output channel n); [hotelren]
+ * per_channel_quant_int8. Same arithmetic as quantize_per_row_int8, per column n.
+ *
+ * w       W [K,N] fp32, column-major ([N][K])
+ * wq      W [K,N] int8, column-major ([N][K]) (out)
+ * w_scale [N] fp32 (out)
+ * Requires K > 0 and K % 16 == 0.
+ */
+ql_status quantize_weight_per_channel(const float* w, int64_t K, int64_t N, int8_t* wq,
+                                      float* w_scale, void* stream);
+
+/*
+ * W8A8 GEMM with int32 accumulation and a fused dequantization + bias epilogue.
+ * [hotelren] "W8A8矩阵乘法": Y = (x_scale*X) @ (w_scale*W) + bias; [quant67] §四
+ * (int32 accumulate, scales and bias applied in the epilogue while in registers);
+ * [2048ai] §5.2-§5.4.
+ *
+ *   acc[m,n] = sum_k xq[m,k] * wq[k,n]          (int32, exact)
+ *   y[m,n]   = float(acc) * x_scale[m] * w_scale[n] + bias[n]
+ *
+ * xq      [M,K] int8 row-major;  x_scale [M] fp32
+ * wq      W [K,N] int8 column-major ([N][K]);  w_scale [N] fp32
+ * bias    [N] fp32, or NULL for none
+ * y       [M,N] row-major, fp32 (y_dtype QL_F32) or fp16 (QL_F16, rounded to nearest even)
+ * Requires K > 0, K % 64 == 0 and K <= 131008 (so that |acc| < 2^31 for any codes).
+ */
+ql_status gemm_w8a8_per_channel(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                                const float* w_scale, const float* bias, void* y,
+                                ql_dtype y_dtype, int64_t M, int64_t N, int64_t K,
+                                void* stream);
+
+/*
+ * The W8A8 integer accumulators alone, acc[m,n] = sum_k xq[m,k] * wq[k,n] as int32
+ * [M,N] row-major. A checking aid for the exact integer stage of
+ * gemm_w8a8_per_channel (same main loop); [hotelren] "W8A8矩阵乘法" scheme 1 names
+ * this int32 intermediate. Same requirements as gemm_w8a8_per_channel.
+ */
+ql_status gemm_w8a8_int32(const int8_t* xq, const int8_t* wq, int32_t* acc, int64_t M,
+                          int64_t N, int64_t K, void* stream);
+
+/*
+ * Weight-only W8A16 GEMM / decode GEMV: fp16 activations, 8-bit weight codes
+ * dequantized inside the kernel, fp32 accumulation, fp16 output. [quant67] §四
+ * (weight-only: store low-bit weights, dequantize on chip); [hotelren] "量化模型的矩阵
+ * 乘法" (optional zero => asymmetric); [zingnex] 核心量化流程 (block-64 uint8).
+ *
+ *   y[m,n] = sum_k x[m,k] * (q[k,n] - z[g(k),n]) * s[g(k),n] + bias[n]
+ *
+ * x          [M,K] fp16 row-major
+ * wq         W [K,N] column-major ([N][K]): int8 codes if zero_point is NULL, else
+ *            uint8 codes
+ * w_scale    fp32: [N] if group_size == 0, else [K/group_size, N] column-major
+ * zero_point NULL (symmetric), or uint8 with the same shape as w_scale
+ * group_size 0 (one scale per output column) or a multiple of 64 dividing K
+ * bias       [N] fp32, or NULL
+ * y          [M,N] fp16 row-major (out)
+ * Requires K > 0, K % 64 == 0.
+ */
+ql_status gemm_w8a16(const void* x, const void* wq, const float* w_scale,
+                     const uint8_t* zero_point, int64_t group_size, const float* bias, void* y,
+                     int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * Weight-only W4A16 GEMM with per-group symmetric int4 weights. [xdnf] §3.2, §4.1-§4.3
+ * (unpack by shift and mask, dequantize, fp16 products with fp32 accumulation, fp16
+ * output), §5.1 (scale = absmax/7); [quant67] §三 (per-group scales along K).
+ *
+ *   y[m,n] = sum_g s[g,n] * sum_{k in g} x[m,k] * q[k,n] + bias[n]
+ *
+ * x          [M,K] fp16 row-major
+ * wq_packed  int32 [N][K/8]: word w of column n holds k = 8w + j in bits [4j, 4j+3],
+ *            two's complement (values -8..7)
+ * scales     fp16 [K/group_size, N] column-major ([N][K/group_size])
+ * group_size a multiple of 64 dividing K
+ * bias       [N] fp32, or NULL
+ * y          [M,N] fp16 row-major (out)
+ * Requires K > 0, K % 64 == 0.
+ */
+ql_status gemm_w4a16_grouped(const void* x, const int32_t* wq_packed, const void* scales,
+                             int64_t group_size, const float* bias, void* y, int64_t M,
+                             int64_t N, int64_t K, void* stream);
+
+/*
+ * Producer of the block-asymmetric uint8 weight format consumed by gemm_w8a16.
+ * [zingnex] 核心量化流程 steps 1-2, per block b of `block` weights along K and column n:
+ *   s = max((max - min) / 255, 1e-8) (fp32);  zp = clamp(round(-min / s), 0, 255)
+ *   q = clamp(round(w / s) + zp, 0, 255)                       (round half to even)
+ *
+ * w          W [K,N] fp32 column-major ([N][K])
+ * wq         uint8 [N][K] (out);  scale fp32 [N][K/block] (out);  zero_point uint8
+ *            [N][K/block] (out)
+ * Requires K > 0, block % 16 == 0, K % block == 0.
+ */
+ql_status quantize_weight_block_asym_u8(const float* w, int64_t K, int64_t N, int64_t block,
+                                        uint8_t* wq, float* scale, uint8_t* zero_point,
+                                        void* stream);
+
+/*
+ * Producer of the per-group int4 weight format consumed by gemm_w4a16_grouped.
+ * [xdnf] §5.1, per group g of `group` weights along K and column n:
+ *   s16 = fp16(max(absmax, 7 * 2^-24) / 7);  q = clamp(round(w / s16), -8, 7)
+ * (codes are taken with the stored fp16 scale; the floor keeps s16 > 0).
+ *
+ * w          W [K,N] fp32 column-major ([N][K])
+ * wq_packed  int32 [N][K/8] (out), layout as in gemm_w4a16_grouped
+ * scales     fp16 [N][K/group] (out)
+ * Requires K > 0, group % 16 == 0, K % group == 0.
+ */
+ql_status quantize_weight_int4_grouped(const float* w, int64_t K, int64_t N, int64_t group,
+                                       int32_t* wq_packed, void* scales, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QL_H */

@@ -1,0 +1,260 @@
+"""Python binding of libql.so, the MI355X quantized linear layer.
+
+Every function here has the name of a C entry point in ``include/ql.h`` and does
+argument marshalling only: it checks torch tensors (device, dtype, contiguity,
+shape), allocates outputs the caller did not pass, and hands raw device pointers and
+the current HIP stream to the library. Every step of the computation runs in the
+library's HIP kernels; there is no other code path. If the library has not been built
+the import fails with an ImportError.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "QLError", "lib", "library_path", "quantize_per_row_int8", "quantize_weight_per_channel",
+    "gemm_w8a8_per_channel", "gemm_w8a8_int32", "gemm_w8a16", "gemm_w4a16_grouped",
+    "quantize_weight_block_asym_u8", "quantize_weight_int4_grouped", "linear_w8a8", "prepare",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libql.so")
+
+if not os.path.exists(library_path):
+    raise ImportError(
+        "libql.so is not built at %s; build it with `python -m int8_quantized_linear_amd.build`"
+        % library_path)
+
+lib = ctypes.CDLL(library_path)
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I = ctypes.c_int
+
+QL_F32, QL_F16 = 0, 1
+STATUS = {0: "QL_OK", 1: "QL_ERR_NULL", 2: "QL_ERR_SHAPE", 3: "QL_ERR_ALIGN", 4: "QL_ERR_DTYPE",
+          5: "QL_ERR_DEVICE"}
+
+_SIGS = {
+    "quantize_per_row_int8": [_P, _I, _I64, _I64, _P, _P, _P],
+    "quantize_weight_per_channel": [_P, _I64, _I64, _P, _P, _P],
+    "gemm_w8a8_per_channel": [_P, _P, _P, _P, _P, _P, _I, _I64, _I64, _I64, _P],
+    "gemm_w8a8_int32": [_P, _P, _P, _I64, _I64, _I64, _P],
+    "gemm_w8a16": [_P, _P, _P, _P, _I64, _P, _P, _I64, _I64, _I64, _P],
+    "gemm_w4a16_grouped": [_P, _P, _P, _I64, _P, _P, _I64, _I64, _I64, _P],
+    "quantize_weight_block_asym_u8": [_P, _I64, _I64, _I64, _P, _P, _P, _P],
+    "quantize_weight_int4_grouped": [_P, _I64, _I64, _I64, _P, _P, _P],
+}
+for _name, _args in _SIGS.items():
+    _f = getattr(lib, _name)
+    _f.argtypes = _args
+    _f.restype = _I
+lib.ql_status_str.argtypes = [_I]
+lib.ql_status_str.restype = ctypes.c_char_p
+
+
+class QLError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__("%s: %s" % (fn, lib.ql_status_str(status).decode()))
+
+
+def _call(fn: str, *args):
+    st = getattr(lib, fn)(*args)
+    if st != 0:
+        raise QLError(fn, st)
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t: torch.Tensor, name: str, dtypes, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a GPU tensor, got %s" % (name, t.device))
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if t.dtype not in dtypes:
+        raise TypeError("%s has dtype %s, expected one of %s" % (name, t.dtype, dtypes))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous (row-major)" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    return t
+
+
+def _out(t, name, shape, dtype, device):
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    return _check(t, name, (dtype,), shape, device)
+
+
+# ---------------------------------------------------------------- quantizers
+
+def quantize_per_row_int8(x: torch.Tensor, xq: Optional[torch.Tensor] = None,
+                          x_scale: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Per-row symmetric int8 of x [M, K] (fp16 or fp32): returns (xq int8 [M, K], x_scale fp32 [M])."""
+    _check(x, "x", (torch.float16, torch.float32))
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, K]")
+    M, K = x.shape
+    xq = _out(xq, "xq", (M, K), torch.int8, x.device)
+    x_scale = _out(x_scale, "x_scale", (M,), torch.float32, x.device)
+    _call("quantize_per_row_int8", _ptr(x), QL_F16 if x.dtype == torch.float16 else QL_F32, M, K,
+          _ptr(xq), _ptr(x_scale), _stream(x))
+    return xq, x_scale
+
+
+def quantize_weight_per_channel(w_nk: torch.Tensor, wq: Optional[torch.Tensor] = None,
+                                w_scale: Optional[torch.Tensor] = None):
+    """Per-output-channel symmetric int8 of W [K, N] column-major, given as its [N, K]
+    row-major storage (e.g. ``linear.weight``). Returns (wq int8 [N, K], w_scale fp32 [N])."""
+    _check(w_nk, "w", (torch.float32,))
+    N, K = w_nk.shape
+    wq = _out(wq, "wq", (N, K), torch.int8, w_nk.device)
+    w_scale = _out(w_scale, "w_scale", (N,), torch.float32, w_nk.device)
+    _call("quantize_weight_per_channel", _ptr(w_nk), K, N, _ptr(wq), _ptr(w_scale), _stream(w_nk))
+    return wq, w_scale
+
+
+def quantize_weight_block_asym_u8(w_nk: torch.Tensor, block: int = 64):
+    """Block-asymmetric uint8 of W ([N, K] storage): (q uint8 [N, K], scale fp32 [N, K/block],
+    zero_point uint8 [N, K/block])."""
+    _check(w_nk, "w", (torch.float32,))
+    N, K = w_nk.shape
+    if block <= 0 or K % block:
+        raise ValueError("block must divide K")
+    dev = w_nk.device
+    q = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    s = torch.empty((N, K // block), dtype=torch.float32, device=dev)
+    z = torch.empty((N, K // block), dtype=torch.uint8, device=dev)
+    _call("quantize_weight_block_asym_u8", _ptr(w_nk), K, N, block, _ptr(q), _ptr(s), _ptr(z),
+          _stream(w_nk))
+    return q, s, z
+
+
+def quantize_weight_int4_grouped(w_nk: torch.Tensor, group: int = 128):
+    """Per-group int4 of W ([N, K] storage): (packed int32 [N, K/8], scales fp16 [N, K/group])."""
+    _check(w_nk, "w", (torch.float32,))
+    N, K = w_nk.shape
+    if group <= 0 or K % group:
+        raise ValueError("group must divide K")
+    dev = w_nk.device
+    p = torch.empty((N, K // 8), dtype=torch.int32, device=dev)
+    s = torch.empty((N, K // group), dtype=torch.float16, device=dev)
+    _call("quantize_weight_int4_grouped", _ptr(w_nk), K, N, group, _ptr(p), _ptr(s), _stream(w_nk))
+    return p, s
+
+
+# --------------------------------------------------------------------- GEMMs
+
+def gemm_w8a8_per_channel(xq, x_scale, wq, w_scale, bias=None, out_dtype=torch.float16, y=None):
+    """y [M, N] = float(xq @ wq^T) * x_scale[:, None] * w_scale[None, :] + bias."""
+    _check(xq, "xq", (torch.int8,))
+    M, K = xq.shape
+    dev = xq.device
+    _check(wq, "wq", (torch.int8,), None, dev)
+    N = wq.shape[0]
+    _check(wq, "wq", (torch.int8,), (N, K), dev)
+    _check(x_scale, "x_scale", (torch.float32,), (M,), dev)
+    _check(w_scale, "w_scale", (torch.float32,), (N,), dev)
+    if bias is not None:
+        _check(bias, "bias", (torch.float32,), (N,), dev)
+    if out_dtype not in (torch.float16, torch.float32):
+        raise TypeError("out_dtype must be float16 or float32")
+    y = _out(y, "y", (M, N), out_dtype, dev)
+    _call("gemm_w8a8_per_channel", _ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale), _ptr(bias),
+          _ptr(y), QL_F16 if out_dtype == torch.float16 else QL_F32, M, N, K, _stream(xq))
+    return y
+
+
+def gemm_w8a8_int32(xq, wq, acc=None):
+    """int32 accumulators xq @ wq^T, [M, N]."""
+    _check(xq, "xq", (torch.int8,))
+    M, K = xq.shape
+    N = wq.shape[0]
+    _check(wq, "wq", (torch.int8,), (N, K), xq.device)
+    acc = _out(acc, "acc", (M, N), torch.int32, xq.device)
+    _call("gemm_w8a8_int32", _ptr(xq), _ptr(wq), _ptr(acc), M, N, K, _stream(xq))
+    return acc
+
+
+def gemm_w8a16(x, wq, w_scale, zero_point=None, group_size: int = 0, bias=None, y=None):
+    """Weight-only 8-bit GEMM: x fp16 [M, K]; wq [N, K] int8 (symmetric) or uint8 (with
+    zero_point); w_scale fp32 [N] (group_size 0) or [N, K/group_size]."""
+    _check(x, "x", (torch.float16,))
+    M, K = x.shape
+    dev = x.device
+    N = wq.shape[0]
+    _check(wq, "wq", (torch.uint8,) if zero_point is not None else (torch.int8,), (N, K), dev)
+    sshape = (N,) if group_size == 0 else (N, K // group_size)
+    _check(w_scale, "w_scale", (torch.float32,), sshape, dev)
+    if zero_point is not None:
+        _check(zero_point, "zero_point", (torch.uint8,), sshape, dev)
+    if bias is not None:
+        _check(bias, "bias", (torch.float32,), (N,), dev)
+    y = _out(y, "y", (M, N), torch.float16, dev)
+    _call("gemm_w8a16", _ptr(x), _ptr(wq), _ptr(w_scale), _ptr(zero_point), group_size, _ptr(bias),
+          _ptr(y), M, N, K, _stream(x))
+    return y
+
+
+def gemm_w4a16_grouped(x, wq_packed, scales, group_size: int, bias=None, y=None):
+    """W4A16: x fp16 [M, K]; wq_packed int32 [N, K/8]; scales fp16 [N, K/group_size]."""
+    _check(x, "x", (torch.float16,))
+    M, K = x.shape
+    dev = x.device
+    N = wq_packed.shape[0]
+    _check(wq_packed, "wq_packed", (torch.int32,), (N, K // 8), dev)
+    _check(scales, "scales", (torch.float16,), (N, K // group_size) if group_size > 0 else None, dev)
+    if bias is not None:
+        _check(bias, "bias", (torch.float32,), (N,), dev)
+    y = _out(y, "y", (M, N), torch.float16, dev)
+    _call("gemm_w4a16_grouped", _ptr(x), _ptr(wq_packed), _ptr(scales), group_size, _ptr(bias),
+          _ptr(y), M, N, K, _stream(x))
+    return y
+
+
+def linear_w8a8(x, wq, w_scale, bias=None, out_dtype=None):
+    """The whole W8A8 layer: per-row quantization of x, then the fused GEMM."""
+    xq, xs = quantize_per_row_int8(x)
+    od = out_dtype or (torch.float32 if x.dtype == torch.float32 else torch.float16)
+    return gemm_w8a8_per_channel(xq, xs, wq, w_scale, bias, od)
+
+
+def prepare(fn: str, *args):
+    """Pre-marshals one library call for repeated launches (benchmark loops): tensors
+    become raw device pointers, Python ints stay sizes, and the current stream of the
+    first tensor's device is captured. Returns a zero-argument callable that launches
+    and raises QLError on a non-OK status. The caller keeps the tensors alive."""
+    f = getattr(lib, fn)
+    conv = []
+    device = None
+    for a in args:
+        if isinstance(a, torch.Tensor):
+            if a.device.type != "cuda":
+                raise ValueError("prepare: tensors must be on the GPU")
+            device = device or a.device
+            conv.append(ctypes.c_void_p(a.data_ptr()))
+        elif a is None:
+            conv.append(None)
+        else:
+            conv.append(a)
+    conv.append(ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream))
+
+    def launch():
+        st = f(*conv)
+        if st != 0:
+            raise QLError(fn, st)
+
+    return launch

@@ -1,0 +1,255 @@
+// quant.hip -- quantizer kernels for gfx950.
+//
+// Per-row symmetric int8 (activations per token, weights per output channel), and the
+// producers of the block-asymmetric uint8 and per-group int4 weight formats.
+//
+// All are HBM-bound streaming kernels: each element is read once from HBM and its code
+// written once. Codes are decided in fp32 with correctly rounded division (this file is
+// compiled without fast-math, so `a / b` is the IEEE quotient) and v_rndne (rintf,
+// round half to even), the precision and rounding of the definitions:
+//   scale = max|x| / 127, q = round(x / scale), codes in [-127, 127]
+//       2048ai.net INT8 Llama-2-7B write-up §2.2; quant67.com ch.17 §二
+//   absmax along the row, clamp_min(1e-10), torch.round (half to even)
+//       hotelren.com "量化算法的本质", per_channel_quant_int8
+#include "ql_internal.h"
+
+namespace ql {
+namespace {
+
+constexpr int QT = 256;       // threads per row-quantizer workgroup
+constexpr int QMAXC = 4;      // 16-byte chunks per thread kept in registers
+
+__device__ inline float block_max(float v, float* red) {
+#pragma unroll
+    for (int o = WAVE / 2; o > 0; o >>= 1)
+        v = fmaxf(v, __shfl_xor(v, o, WAVE));
+    const int w = threadIdx.x / WAVE;
+    if ((threadIdx.x & (WAVE - 1)) == 0)
+        red[w] = v;
+    __syncthreads();
+    float r = red[0];
+#pragma unroll
+    for (int i = 1; i < QT / WAVE; ++i)
+        r = fmaxf(r, red[i]);
+    return r;
+}
+
+__device__ inline int8_t code_i8(float x, float s) {
+    float r = rintf(x / s);
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return (int8_t)(int)r;
+}
+
+// One 16-byte chunk of input as fp32 values: 8 fp16 or 4 fp32 elements.
+template <bool F16>
+struct Chunk {
+    static constexpr int E = F16 ? 8 : 4;
+    float v[E];
+    __device__ inline void load(const void* p) {
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(p);
+        if constexpr (F16) {
+            f16x8 h = __builtin_bit_cast(f16x8, raw);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                v[i] = (float)h[i];
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                v[i] = __builtin_bit_cast(float, raw[i]);
+        }
+    }
+    __device__ inline float absmax() const {
+        float a = 0.0f;
+#pragma unroll
+        for (int i = 0; i < E; ++i)
+            a = fmaxf(a, fabsf(v[i]));
+        return a;
+    }
+    __device__ inline void store_codes(int8_t* q, float s) const {
+        uint32_t w[E / 4];
+#pragma unroll
+        for (int j = 0; j < E / 4; ++j) {
+            uint32_t b = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                b |= (uint32_t)(uint8_t)code_i8(v[4 * j + i], s) << (8 * i);
+            w[j] = b;
+        }
+        if constexpr (E == 8)
+            *reinterpret_cast<u32x2*>(q) = u32x2{w[0], w[1]};
+        else
+            *reinterpret_cast<uint32_t*>(q) = w[0];
+    }
+};
+
+// One workgroup per row. Rows of up to QT * QMAXC chunks stay in registers (one HBM
+// read); longer rows are read a second time for the codes (the re-read hits L2).
+template <bool F16>
+__global__ __launch_bounds__(QT) void quant_rows_i8_kernel(const void* __restrict__ x, int64_t K,
+                                                          int8_t* __restrict__ q,
+                                                          float* __restrict__ scale) {
+    using C = Chunk<F16>;
+    __shared__ float red[QT / WAVE];
+    const int64_t row = blockIdx.x;
+    const char* xr = reinterpret_cast<const char*>(x) + row * K * (F16 ? 2 : 4);
+    int8_t* qr = q + row * K;
+    const int nch = (int)(K / C::E);
+
+    float amax = 0.0f;
+    if (nch <= QT * QMAXC) {
+        C c[QMAXC];
+#pragma unroll
+        for (int i = 0; i < QMAXC; ++i) {
+            const int ch = threadIdx.x + i * QT;
+            if (ch < nch) {
+                c[i].load(xr + (int64_t)ch * 16);
+                amax = fmaxf(amax, c[i].absmax());
+            }
+        }
+        amax = block_max(amax, red);
+        const float s = fmaxf(amax, 1e-10f) / 127.0f;
+        if (threadIdx.x == 0)
+            scale[row] = s;
+#pragma unroll
+        for (int i = 0; i < QMAXC; ++i) {
+            const int ch = threadIdx.x + i * QT;
+            if (ch < nch)
+                c[i].store_codes(qr + (int64_t)ch * C::E, s);
+        }
+    } else {
+        for (int ch = threadIdx.x; ch < nch; ch += QT) {
+            C c;
+            c.load(xr + (int64_t)ch * 16);
+            amax = fmaxf(amax, c.absmax());
+        }
+        amax = block_max(amax, red);
+        const float s = fmaxf(amax, 1e-10f) / 127.0f;
+        if (threadIdx.x == 0)
+            scale[row] = s;
+        for (int ch = threadIdx.x; ch < nch; ch += QT) {
+            C c;
+            c.load(xr + (int64_t)ch * 16);
+            c.store_codes(qr + (int64_t)ch * C::E, s);
+        }
+    }
+}
+
+// Block-wise asymmetric uint8 (zingnex.cn "从零实现大语言模型 INT8 量化", 核心量化流程
+// steps 1-2): per block of `block` weights along K in column n,
+//   s = max((max - min) / 255, 1e-8); zp = clamp(round(-min / s), 0, 255);
+//   q = clamp(round(w / s) + zp, 0, 255).
+// One thread per (column, block); an offline producer, not on the serving path.
+__global__ __launch_bounds__(256) void quant_block_asym_u8_kernel(
+    const float* __restrict__ w, int64_t K, int64_t N, int64_t block, uint8_t* __restrict__ q,
+    float* __restrict__ scale, uint8_t* __restrict__ zp) {
+    const int64_t G = K / block;
+    const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (id >= N * G)
+        return;
+    const int64_t n = id / G, g = id % G;
+    const float* v = w + n * K + g * block;
+    float mn = v[0], mx = v[0];
+    for (int64_t i = 0; i < block; i += 4) {
+        const f32x4 t = *reinterpret_cast<const f32x4*>(v + i);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            mn = fminf(mn, t[j]);
+            mx = fmaxf(mx, t[j]);
+        }
+    }
+    float s = (mx - mn) / 255.0f;
+    s = fmaxf(s, 1e-8f);
+    const float zf = fminf(fmaxf(rintf(-mn / s), 0.0f), 255.0f);
+    const int z = (int)zf;
+    uint8_t* qo = q + n * K + g * block;
+    for (int64_t i = 0; i < block; i += 4) {
+        const f32x4 t = *reinterpret_cast<const f32x4*>(v + i);
+        uint32_t b = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            int c = (int)rintf(t[j] / s) + z;
+            c = c < 0 ? 0 : (c > 255 ? 255 : c);
+            b |= (uint32_t)c << (8 * j);
+        }
+        *reinterpret_cast<uint32_t*>(qo + i) = b;
+    }
+    scale[id] = s;
+    zp[id] = (uint8_t)z;
+}
+
+// Per-group symmetric int4 (xdnf.cn INT4/FP16 mixed GEMM on CANN TBE, §5.1: scale =
+// absmax / 7, stored fp16 per §3.1): s16 = fp16(max(absmax, 7 * 2^-24) / 7) (round to
+// nearest even); q = clamp(round(w / s16), -8, 7), packed eight per int32 along K with
+// element k % 8 = j in bits [4j, 4j+3]. One thread per (column, group).
+__global__ __launch_bounds__(256) void quant_int4_group_kernel(
+    const float* __restrict__ w, int64_t K, int64_t N, int64_t group, int32_t* __restrict__ packed,
+    _Float16* __restrict__ scales) {
+    const int64_t G = K / group;
+    const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (id >= N * G)
+        return;
+    const int64_t n = id / G, g = id % G;
+    const float* v = w + n * K + g * group;
+    float a = 0.0f;
+    for (int64_t i = 0; i < group; i += 4) {
+        const f32x4 t = *reinterpret_cast<const f32x4*>(v + i);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            a = fmaxf(a, fabsf(t[j]));
+    }
+    const float floor_a = 7.0f * 0x1p-24f;
+    const _Float16 h = (_Float16)(fmaxf(a, floor_a) / 7.0f);
+    const float s = (float)h;
+    int32_t* po = packed + n * (K / 8) + g * (group / 8);
+    for (int64_t i = 0; i < group; i += 8) {
+        const f32x4 t0 = *reinterpret_cast<const f32x4*>(v + i);
+        const f32x4 t1 = *reinterpret_cast<const f32x4*>(v + i + 4);
+        uint32_t word = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float x = j < 4 ? t0[j] : t1[j - 4];
+            const float r = fminf(fmaxf(rintf(x / s), -8.0f), 7.0f);
+            word |= ((uint32_t)(int)r & 0xFu) << (4 * j);
+        }
+        po[i / 8] = (int32_t)word;
+    }
+    scales[id] = h;
+}
+
+}  // namespace
+
+ql_status launch_quant_rows_i8(const void* x, int x_is_f16, int64_t rows, int64_t K, int8_t* q,
+                               float* scale, hipStream_t stream) {
+    if (rows == 0)
+        return QL_OK;
+    const dim3 grid((unsigned)rows), block(QT);
+    if (x_is_f16)
+        hipLaunchKernelGGL(quant_rows_i8_kernel<true>, grid, block, 0, stream, x, K, q, scale);
+    else
+        hipLaunchKernelGGL(quant_rows_i8_kernel<false>, grid, block, 0, stream, x, K, q, scale);
+    return launch_status();
+}
+
+ql_status launch_quant_block_asym_u8(const float* w, int64_t K, int64_t N, int64_t block,
+                                     uint8_t* q, float* scale, uint8_t* zp, hipStream_t stream) {
+    const int64_t total = N * (K / block);
+    if (total == 0)
+        return QL_OK;
+    const dim3 grid((unsigned)((total + 255) / 256)), blk(256);
+    hipLaunchKernelGGL(quant_block_asym_u8_kernel, grid, blk, 0, stream, w, K, N, block, q, scale,
+                       zp);
+    return launch_status();
+}
+
+ql_status launch_quant_int4_group(const float* w, int64_t K, int64_t N, int64_t group,
+                                  int32_t* packed, void* scales, hipStream_t stream) {
+    const int64_t total = N * (K / group);
+    if (total == 0)
+        return QL_OK;
+    const dim3 grid((unsigned)((total + 255) / 256)), blk(256);
+    hipLaunchKernelGGL(quant_int4_group_kernel, grid, blk, 0, stream, w, K, N, group, packed,
+                       reinterpret_cast<_Float16*>(scales));
+    return launch_status();
+}
+
+}  // namespace ql

@@ -1,0 +1,162 @@
+"""The C-ABI library on a machine without a GPU: it loads, exports every function that
+include/ql.h declares, and rejects bad arguments with the documented status codes
+before making any HIP call (no compute call is made here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ql.h")
+LIB = os.path.join(ROOT, "int8_quantized_linear_amd", "libql.so")
+
+OK, NULL, SHAPE, ALIGN, DTYPE = 0, 1, 2, 3, 4
+F32, F16 = 0, 1
+A = 0x10000            # a fake, 16-byte aligned address: never dereferenced on error paths
+MIS = 0x10001          # a misaligned one
+
+
+def declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\*?\s+\**([a-z_0-9]+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.skip("libql.so not built")
+    L = ctypes.CDLL(LIB)
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    sig = {
+        "quantize_per_row_int8": [P, I, I64, I64, P, P, P],
+        "quantize_weight_per_channel": [P, I64, I64, P, P, P],
+        "gemm_w8a8_per_channel": [P, P, P, P, P, P, I, I64, I64, I64, P],
+        "gemm_w8a8_int32": [P, P, P, I64, I64, I64, P],
+        "gemm_w8a16": [P, P, P, P, I64, P, P, I64, I64, I64, P],
+        "gemm_w4a16_grouped": [P, P, P, I64, P, P, I64, I64, I64, P],
+        "quantize_weight_block_asym_u8": [P, I64, I64, I64, P, P, P, P],
+        "quantize_weight_int4_grouped": [P, I64, I64, I64, P, P, P],
+    }
+    for name, args in sig.items():
+        getattr(L, name).argtypes = args
+        getattr(L, name).restype = I
+    L.ql_status_str.argtypes = [I]
+    L.ql_status_str.restype = ctypes.c_char_p
+    return L
+
+
+def test_header_declares_the_entry_points():
+    names = declared()
+    for n in ("quantize_per_row_int8", "quantize_weight_per_channel", "gemm_w8a8_per_channel",
+              "gemm_w8a16", "gemm_w4a16_grouped", "gemm_w8a8_int32", "ql_status_str",
+              "quantize_weight_block_asym_u8", "quantize_weight_int4_grouped"):
+        assert n in names
+
+
+def test_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared():
+        assert name in exported, name
+        getattr(lib, name)
+
+
+def test_library_is_gfx950_only():
+    """The embedded device code objects target gfx950 and nothing else."""
+    if not os.path.exists(LIB):
+        pytest.skip("libql.so not built")
+    blob = open(LIB, "rb").read()
+    targets = set(re.findall(rb"amdgcn-amd-amdhsa--(gfx[0-9a-z]+)", blob))
+    assert targets == {b"gfx950"}, targets
+
+
+def test_status_strings(lib):
+    for s in range(6):
+        assert lib.ql_status_str(s)
+    assert b"NULL" in lib.ql_status_str(NULL)
+
+
+def test_quantize_per_row_validation(lib):
+    f = lib.quantize_per_row_int8
+    assert f(None, F16, 4, 64, A, A, None) == NULL
+    assert f(A, F16, 4, 64, None, A, None) == NULL
+    assert f(A, F16, 4, 64, A, None, None) == NULL
+    assert f(A, 7, 4, 64, A, A, None) == DTYPE
+    assert f(A, F16, -1, 64, A, A, None) == SHAPE
+    assert f(A, F16, 4, 0, A, A, None) == SHAPE
+    assert f(A, F16, 4, 24, A, A, None) == SHAPE
+    assert f(MIS, F16, 4, 64, A, A, None) == ALIGN
+    assert f(A, F16, 4, 64, MIS, A, None) == ALIGN
+    assert f(A, F32, 4, 64, A, MIS, None) == ALIGN
+    # an empty batch is a no-op, whatever the pointers
+    assert f(None, F16, 0, 64, None, None, None) == OK
+
+
+def test_quantize_weight_validation(lib):
+    f = lib.quantize_weight_per_channel
+    assert f(None, 64, 8, A, A, None) == NULL
+    assert f(A, 63, 8, A, A, None) == SHAPE
+    assert f(A, 64, -8, A, A, None) == SHAPE
+    assert f(A, 64, 8, MIS, A, None) == ALIGN
+    assert f(None, 64, 0, None, None, None) == OK
+
+
+def test_gemm_w8a8_validation(lib):
+    f = lib.gemm_w8a8_per_channel
+    assert f(None, A, A, A, None, A, F16, 8, 8, 64, None) == NULL
+    assert f(A, None, A, A, None, A, F16, 8, 8, 64, None) == NULL
+    assert f(A, A, A, None, None, A, F16, 8, 8, 64, None) == NULL
+    assert f(A, A, A, A, None, None, F16, 8, 8, 64, None) == NULL
+    assert f(A, A, A, A, None, A, 3, 8, 8, 64, None) == DTYPE
+    assert f(A, A, A, A, None, A, F16, 8, 8, 96, None) == SHAPE
+    assert f(A, A, A, A, None, A, F16, 8, 8, 131072, None) == SHAPE
+    assert f(A, A, A, A, None, A, F16, -1, 8, 64, None) == SHAPE
+    assert f(A, A, A, A, None, A, F16, 8, 8, 0, None) == SHAPE
+    assert f(A, A, MIS, A, None, A, F16, 8, 8, 64, None) == ALIGN
+    assert f(A, A, A, A, MIS, A, F16, 8, 8, 64, None) == ALIGN
+    assert f(None, None, None, None, None, None, F16, 0, 8, 64, None) == OK
+    g = lib.gemm_w8a8_int32
+    assert g(None, A, A, 8, 8, 64, None) == NULL
+    assert g(A, A, A, 8, 8, 65, None) == SHAPE
+    assert g(A, A, MIS, 8, 8, 64, None) == ALIGN
+    assert g(None, None, None, 8, 0, 64, None) == OK
+
+
+def test_gemm_w8a16_validation(lib):
+    f = lib.gemm_w8a16
+    assert f(None, A, A, None, 0, None, A, 1, 64, 128, None) == NULL
+    assert f(A, A, None, None, 0, None, A, 1, 64, 128, None) == NULL
+    assert f(A, A, A, None, 0, None, A, 1, 64, 100, None) == SHAPE
+    assert f(A, A, A, A, 96, None, A, 1, 64, 192, None) == SHAPE     # group not a multiple of 64
+    assert f(A, A, A, A, 128, None, A, 1, 64, 192, None) == SHAPE    # group does not divide K
+    assert f(A, A, A, None, -64, None, A, 1, 64, 128, None) == SHAPE
+    assert f(A, MIS, A, None, 0, None, A, 1, 64, 128, None) == ALIGN
+    assert f(A, A, A, None, 0, None, MIS, 1, 64, 128, None) == ALIGN
+    assert f(None, None, None, None, 0, None, None, 0, 64, 128, None) == OK
+
+
+def test_gemm_w4a16_validation(lib):
+    f = lib.gemm_w4a16_grouped
+    assert f(None, A, A, 128, None, A, 32, 64, 256, None) == NULL
+    assert f(A, A, None, 128, None, A, 32, 64, 256, None) == NULL
+    assert f(A, A, A, 0, None, A, 32, 64, 256, None) == SHAPE
+    assert f(A, A, A, 96, None, A, 32, 64, 384, None) == SHAPE
+    assert f(A, A, A, 128, None, A, 32, 64, 320, None) == SHAPE
+    assert f(A, MIS, A, 128, None, A, 32, 64, 256, None) == ALIGN
+    assert f(A, A, MIS, 128, None, A, 32, 64, 256, None) == ALIGN
+    assert f(None, None, None, 128, None, None, 32, 0, 256, None) == OK
+
+
+def test_producer_validation(lib):
+    f = lib.quantize_weight_block_asym_u8
+    assert f(None, 128, 8, 64, A, A, A, None) == NULL
+    assert f(A, 128, 8, 48, A, A, A, None) == SHAPE
+    assert f(A, 128, 8, 0, A, A, A, None) == SHAPE
+    assert f(A, 128, 8, 64, MIS, A, A, None) == ALIGN
+    g = lib.quantize_weight_int4_grouped
+    assert g(None, 256, 8, 128, A, A, None) == NULL
+    assert g(A, 256, 8, 96, A, A, None) == SHAPE
+    assert g(A, 256, 8, 128, MIS, A, None) == ALIGN

@@ -1,0 +1,134 @@
+"""GPU parity of the W8A8 path: int32 accumulators bit-exact, outputs within tolerance.
+
+Tolerances (derived from the arithmetic, since the accumulators are exact):
+  fp32 output: |y - y64| <= 1e-5 * (|acc * xs * ws| + |bias|); the only error is the
+               few fp32 roundings of the epilogue (about 4 * 2^-24 of that magnitude).
+  fp16 output: |y - fp16(y32)| <= one fp16 ulp at the oracle's value, where y32 is the
+               oracle's fp32 epilogue; fp32 reordering can move a value across an fp16
+               rounding boundary but by no more than one step.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import DEV, Guarded, dev, f16_ulp, host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ql():
+    import int8_quantized_linear_amd as ql
+    return ql
+
+
+def _rand_codes(rng, shape, lo=-127):
+    return rng.integers(lo, 128, shape, dtype=np.int8)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 64), (16, 256, 256), (300, 520, 384), (257, 129, 192),
+                                   (512, 768, 1024), (33, 1000, 192), (256, 256, 64)])
+def test_int32_bit_exact(ql, M, N, K):
+    """Several tiles in M and N, ragged tails, K with a half k-tile tail, codes including -128."""
+    rng = np.random.default_rng(M * 1000 + N + K)
+    a = _rand_codes(rng, (M, K), -128)
+    b = _rand_codes(rng, (N, K), -128)
+    acc = ql.gemm_w8a8_int32(dev(a), dev(b))
+    assert np.array_equal(host(acc), oracle.gemm_i32(a, b))
+
+
+def test_int32_extremes(ql):
+    """The largest K the boundary accepts with the most negative products."""
+    K = 131008
+    a = np.full((20, K), 127, np.int8)
+    b = np.full((17, K), -128, np.int8)
+    acc = host(ql.gemm_w8a8_int32(dev(a), dev(b)))
+    assert np.all(acc == np.int64(127) * -128 * K)
+
+
+def _layer(ql, w: workloads.Workload, rows=None):
+    inp = workloads.draw(w, x_rows=rows)
+    wq_ref, ws_ref = oracle.quant_weight_per_channel(inp.w_nk)
+    xq_ref, xs_ref = oracle.quant_rows_i8(inp.x)
+    wq, ws = ql.quantize_weight_per_channel(dev(inp.w_nk))
+    xq, xs = ql.quantize_per_row_int8(dev(inp.x))
+    assert np.array_equal(host(wq), wq_ref) and np.array_equal(host(ws), ws_ref)
+    assert np.array_equal(host(xq), xq_ref) and np.array_equal(host(xs), xs_ref)
+    return inp, (xq, xs, wq, ws), (xq_ref, xs_ref, wq_ref, ws_ref)
+
+
+def test_small_layer_fp32(ql):
+    """M=16 K=256 N=256 with fp32 output: the whole layer against the oracle."""
+    inp, (xq, xs, wq, ws), (xq_r, xs_r, wq_r, ws_r) = _layer(ql, workloads.W8A8_SMALL)
+    acc_ref = oracle.gemm_i32(xq_r, wq_r)
+    assert np.array_equal(host(ql.gemm_w8a8_int32(xq, wq)), acc_ref)
+    y32, y64 = oracle.epilogue_w8a8(acc_ref, xs_r, ws_r, inp.bias)
+    y = host(ql.gemm_w8a8_per_channel(xq, xs, wq, ws, dev(inp.bias), torch.float32)).astype(np.float64)
+    mag = np.abs(acc_ref.astype(np.float64) * xs_r[:, None] * ws_r[None, :]) + np.abs(inp.bias)[None, :]
+    assert np.all(np.abs(y - y64) <= 1e-5 * mag)
+    # and the one-call layer
+    y2 = host(ql.linear_w8a8(dev(inp.x), wq, ws, dev(inp.bias))).astype(np.float64)
+    assert np.array_equal(y2, y)
+
+
+def test_prefill_full_size(ql):
+    """M=2048 K=4096 N=11008 in the benchmark's launch configuration: quantized tensors
+    bit-exact everywhere; accumulators and fp16 outputs on rows sampled from every M tile."""
+    inp, (xq, xs, wq, ws), (xq_r, xs_r, wq_r, ws_r) = _layer(ql, workloads.W8A8_PREFILL)
+    y = ql.gemm_w8a8_per_channel(xq, xs, wq, ws, dev(inp.bias), torch.float16)
+    acc = ql.gemm_w8a8_int32(xq, wq)
+    rows = np.unique(np.concatenate([np.arange(0, 2048, 97), [255, 256, 2047]]))
+    acc_ref = oracle.gemm_i32(xq_r[rows], wq_r)
+    assert np.array_equal(host(acc)[rows], acc_ref)
+    y32, y64 = oracle.epilogue_w8a8(acc_ref, xs_r[rows], ws_r, inp.bias)
+    yg = host(y)
+    assert np.all(np.isfinite(yg))
+    ref16 = y32.astype(np.float16).astype(np.float64)
+    assert np.all(np.abs(yg[rows].astype(np.float64) - ref16) <= f16_ulp(ref16))
+    same = np.mean(yg[rows] == y32.astype(np.float16))
+    assert same > 0.99, same
+
+
+@pytest.mark.parametrize("M,N,K,with_bias,out", [(300, 520, 384, True, torch.float16),
+                                                 (300, 520, 384, False, torch.float16),
+                                                 (1, 77, 64, True, torch.float32),
+                                                 (513, 300, 640, True, torch.float32)])
+def test_ragged_layer(ql, M, N, K, with_bias, out):
+    w = workloads.with_shape(workloads.W8A8_PREFILL, M, K, N)
+    inp, (xq, xs, wq, ws), (xq_r, xs_r, wq_r, ws_r) = _layer(ql, w)
+    bias = inp.bias if with_bias else None
+    g = Guarded((M, N), out)
+    ql.gemm_w8a8_per_channel(xq, xs, wq, ws, dev(bias) if with_bias else None, out, y=g.view)
+    g.check()
+    acc_ref = oracle.gemm_i32(xq_r, wq_r)
+    y32, y64 = oracle.epilogue_w8a8(acc_ref, xs_r, ws_r, bias)
+    y = host(g.view).astype(np.float64)
+    if out == torch.float32:
+        mag = np.abs(acc_ref.astype(np.float64) * xs_r[:, None] * ws_r[None, :])
+        if with_bias:
+            mag = mag + np.abs(bias)[None, :]
+        assert np.all(np.abs(y - y64) <= 1e-5 * mag)
+    else:
+        ref16 = y32.astype(np.float16).astype(np.float64)
+        assert np.all(np.abs(y - ref16) <= f16_ulp(ref16))
+
+
+def test_one_hot_rows(ql):
+    """X = e_k rows: every output is 127 * wq[k, n] in the accumulators."""
+    K, N = 256, 300
+    rng = np.random.default_rng(9)
+    wq = _rand_codes(rng, (N, K))
+    ks = np.array([0, 1, 63, 64, 128, 255])
+    a = np.zeros((ks.size, K), np.int8)
+    a[np.arange(ks.size), ks] = 127
+    acc = host(ql.gemm_w8a8_int32(dev(a), dev(wq)))
+    assert np.array_equal(acc, 127 * wq[:, ks].T.astype(np.int32))
+
+
+def test_empty(ql):
+    xq = torch.empty((0, 64), dtype=torch.int8, device=DEV)
+    wq = torch.zeros((8, 64), dtype=torch.int8, device=DEV)
+    y = ql.gemm_w8a8_per_channel(xq, torch.empty(0, device=DEV), wq, torch.ones(8, device=DEV))
+    assert y.shape == (0, 8)

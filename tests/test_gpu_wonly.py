@@ -1,0 +1,138 @@
+"""GPU parity of the weight-only paths (W8A16 per-channel, W8A16 block-asymmetric,
+W4A16 per-group) against the oracle's fp64 products.
+
+Tolerance: |y - y64| <= 2e-3 * (|y64| + rms(y64)) elementwise, with rms over the whole
+output. fp16 output rounding alone is 2^-11 ~ 4.9e-4 of |y|; fp32 accumulation in any
+order over K = 4096 terms adds well under that; a wrong code, nibble or scale index
+moves outputs by O(rms).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import DEV, Guarded, check_wonly, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ql():
+    import int8_quantized_linear_amd as ql
+    return ql
+
+
+def _w8a16_sym(ql, w: workloads.Workload, with_bias=False, group=0):
+    inp = workloads.draw(w)
+    bias = inp.bias if with_bias else None
+    if with_bias and bias is None:
+        bias = np.random.default_rng(w.seed).standard_normal(w.N).astype(np.float32) * 0.1
+    q_ref, s_ref = oracle.quant_weight_per_channel(inp.w_nk)
+    wq, ws = ql.quantize_weight_per_channel(dev(inp.w_nk))
+    assert np.array_equal(host(wq), q_ref)
+    g = Guarded((w.M, w.N), torch.float16)
+    ql.gemm_w8a16(dev(inp.x), wq, ws, None, 0, dev(bias) if bias is not None else None, y=g.view)
+    g.check()
+    y64 = oracle.w8a16_f64(inp.x, q_ref, s_ref, bias=bias)
+    return check_wonly(host(g.view), y64)
+
+
+def test_w8a16_decode_full(ql):
+    """M=1 K=4096 N=4096 decode GEMV, the benchmark's shape."""
+    _w8a16_sym(ql, workloads.W8A16_DECODE)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 64), (3, 77, 192), (17, 1000, 640), (33, 130, 256),
+                                   (70, 64, 128), (1, 9000, 256), (5, 8200, 128)])
+def test_w8a16_ragged(ql, M, N, K):
+    _w8a16_sym(ql, workloads.with_shape(workloads.W8A16_DECODE, M, K, N), with_bias=(M % 2 == 1))
+
+
+def _w8a16_block(ql, w: workloads.Workload, block=64, with_bias=False):
+    inp = workloads.draw(w)
+    bias = (np.random.default_rng(w.seed).standard_normal(w.N) * 0.1).astype(np.float32) if with_bias else None
+    q_ref, s_ref, z_ref = oracle.quant_block_asym_u8(inp.w_nk, block)
+    q, s, z = ql.quantize_weight_block_asym_u8(dev(inp.w_nk), block)
+    assert np.array_equal(host(q), q_ref) and np.array_equal(host(z), z_ref)
+    g = Guarded((w.M, w.N), torch.float16)
+    ql.gemm_w8a16(dev(inp.x), q, s, z, block, dev(bias) if bias is not None else None, y=g.view)
+    g.check()
+    y64 = oracle.w8a16_f64(inp.x, q_ref, s_ref, zero_point=z_ref, group_size=block, bias=bias)
+    return check_wonly(host(g.view), y64)
+
+
+def test_w8a16_block_full(ql):
+    """M=8 K=4096 N=4096, blocks of 64 along K with uint8 zero points."""
+    _w8a16_block(ql, workloads.W8A16_BLOCK)
+
+
+@pytest.mark.parametrize("M,N,K,block", [(1, 50, 128, 64), (8, 333, 512, 128), (20, 100, 384, 192),
+                                         (40, 9000, 128, 64), (3, 64, 256, 256)])
+def test_w8a16_block_ragged(ql, M, N, K, block):
+    _w8a16_block(ql, workloads.with_shape(workloads.W8A16_BLOCK, M, K, N), block, with_bias=True)
+
+
+def _w4a16(ql, w: workloads.Workload, group=128, with_bias=False, cols=None):
+    inp = workloads.draw(w)
+    bias = (np.random.default_rng(w.seed).standard_normal(w.N) * 0.1).astype(np.float32) if with_bias else None
+    p_ref, s_ref = oracle.quant_int4_group(inp.w_nk, group)
+    p, s = ql.quantize_weight_int4_grouped(dev(inp.w_nk), group)
+    assert np.array_equal(host(p), p_ref)
+    assert np.array_equal(host(s).view(np.uint16), s_ref.view(np.uint16))
+    g = Guarded((w.M, w.N), torch.float16)
+    ql.gemm_w4a16_grouped(dev(inp.x), p, s, group, dev(bias) if bias is not None else None, y=g.view)
+    g.check()
+    y = host(g.view)
+    if cols is None:
+        cols = np.arange(w.N)
+    y64 = oracle.w4a16_f64(inp.x, p_ref[cols], s_ref[cols], group,
+                           bias=None if bias is None else bias[cols])
+    # rms of the full output is approximated by the sampled columns' rms
+    return check_wonly(y[:, cols], y64)
+
+
+def test_w4a16_full(ql):
+    """M=32 K=4096 N=14336, group 128: every output computed on the GPU, columns sampled
+    from every 64-column tile for the oracle (plus the last ones)."""
+    w = workloads.W4A16_GROUP
+    cols = np.unique(np.concatenate([np.arange(0, w.N, 13), np.arange(w.N - 40, w.N)]))
+    _w4a16(ql, w, cols=cols)
+
+
+@pytest.mark.parametrize("M,N,K,group", [(1, 1, 128, 128), (3, 77, 256, 128), (32, 1000, 512, 64),
+                                         (17, 9000, 256, 256), (65, 96, 384, 128), (8, 70, 128, 64)])
+def test_w4a16_ragged(ql, M, N, K, group):
+    _w4a16(ql, workloads.with_shape(workloads.W4A16_GROUP, M, K, N), group, with_bias=True)
+
+
+def test_one_hot_exact(ql):
+    """x = e_k: y[n] is fp16((q[k,n] - z) * s) exactly for all three formats."""
+    N, K = 40, 256
+    rng = np.random.default_rng(17)
+    ks = [0, 7, 8, 63, 64, 130, 255]
+    x = np.zeros((len(ks), K), np.float16)
+    x[np.arange(len(ks)), ks] = 1.0
+    w = rng.standard_normal((N, K)).astype(np.float32)
+    q_ref, s_ref = oracle.quant_weight_per_channel(w)
+    wq, ws = ql.quantize_weight_per_channel(dev(w))
+    y = host(ql.gemm_w8a16(dev(x), wq, ws))
+    assert np.array_equal(y, (q_ref[:, ks].T.astype(np.float64) * s_ref[None, :]).astype(np.float16))
+    qb, sb, zb = oracle.quant_block_asym_u8(w, 64)
+    q, s, z = ql.quantize_weight_block_asym_u8(dev(w), 64)
+    y = host(ql.gemm_w8a16(dev(x), q, s, z, 64))
+    ref = np.stack([(qb[:, k].astype(np.float64) - zb[:, k // 64]) * sb[:, k // 64] for k in ks])
+    assert np.array_equal(y, ref.astype(np.float16))
+    p_ref, s16 = oracle.quant_int4_group(w, 128)
+    p, s = ql.quantize_weight_int4_grouped(dev(w), 128)
+    y = host(ql.gemm_w4a16_grouped(dev(x), p, s, 128))
+    qi = oracle.unpack_int4(p_ref, K)
+    ref = np.stack([qi[:, k].astype(np.float64) * s16[:, k // 128].astype(np.float64) for k in ks])
+    assert np.array_equal(y, ref.astype(np.float16))
+
+
+def test_empty(ql):
+    x = torch.empty((0, 64), dtype=torch.float16, device=DEV)
+    wq = torch.zeros((8, 64), dtype=torch.int8, device=DEV)
+    y = ql.gemm_w8a16(x, wq, torch.ones(8, device=DEV))
+    assert y.shape == (0, 8)
