@@ -1,6 +1,8 @@
 """Builds libql.so (the HIP library) in-tree with hipcc for gfx950.
 
-    python -m int8_quantized_linear_amd.build
+    python int8_quantized_linear_amd/build.py
+
+(Run as a script, not as ``-m``: importing the package would load the old library.)
 
 Each source is compiled on its own (in parallel), then linked into one shared
 library next to this file. Only gfx950 code objects are produced. Packed-fp32 VALU
@@ -43,7 +45,8 @@ def build(verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = OUT + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp]
+    # -z defs: an undefined symbol (e.g. a kernel stub the compiler did not emit) fails the link
+    cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-Wl,-z,defs", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))

@@ -46,16 +46,16 @@ struct Chunk {
     static constexpr int E = F16 ? 8 : 4;
     float v[E];
     __device__ inline void load(const void* p) {
-        const u32x4 raw = *reinterpret_cast<const u32x4*>(p);
         if constexpr (F16) {
-            f16x8 h = __builtin_bit_cast(f16x8, raw);
+            const f16x8 h = *reinterpret_cast<const f16x8*>(p);
 #pragma unroll
             for (int i = 0; i < 8; ++i)
                 v[i] = (float)h[i];
         } else {
+            const f32x4 f = *reinterpret_cast<const f32x4*>(p);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                v[i] = __builtin_bit_cast(float, raw[i]);
+                v[i] = f[i];
         }
     }
     __device__ inline float absmax() const {

@@ -64,6 +64,17 @@ def test_exports_every_declared_symbol(lib):
         getattr(lib, name)
 
 
+def test_no_undefined_library_symbols():
+    """Every symbol the library references from itself is defined (a kernel whose launch stub
+    the compiler did not emit would otherwise fail only when first called)."""
+    if not os.path.exists(LIB):
+        pytest.skip("libql.so not built")
+    out = subprocess.run(["nm", "-C", "-D", "--undefined-only", LIB], capture_output=True,
+                         text=True).stdout
+    own = [l for l in out.splitlines() if "ql::" in l or "stub" in l]
+    assert not own, own
+
+
 def test_library_is_gfx950_only():
     """The embedded device code objects target gfx950 and nothing else."""
     if not os.path.exists(LIB):
