@@ -113,7 +113,8 @@ ql_status quantize_weight_per_channel(const float* w, int64_t K, int64_t N, int8
  * wq      W [K,N] int8 column-major ([N][K]);  w_scale [N] fp32
  * bias    [N] fp32, or NULL for none
  * y       [M,N] row-major, fp32 (y_dtype QL_F32) or fp16 (QL_F16, rounded to nearest even)
- * Requires K > 0, K % 64 == 0 and K <= 131008 (so that |acc| < 2^31 for any codes).
+ * Requires K > 0, K % 64 == 0 and K <= 131008 (so that |acc| < 2^31 for any codes), and
+ * N <= 2^23 (the epilogue addresses 32 output rows with 31-bit byte offsets).
  */
 ql_status gemm_w8a8_per_channel(const int8_t* xq, const float* x_scale, const int8_t* wq,
                                 const float* w_scale, const float* bias, void* y,

@@ -9,6 +9,7 @@ namespace {
 
 constexpr int64_t kMaxDim = (int64_t)1 << 31;   // sizes are passed to kernels as int
 constexpr int64_t kMaxKw8a8 = 131008;           // K * 128^2 < 2^31, K % 64 == 0
+constexpr int64_t kMaxNw8a8 = (int64_t)1 << 23; // 32 output rows of 4-byte values: 2^30 bytes
 
 inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
@@ -72,7 +73,7 @@ ql_status quantize_weight_per_channel(const float* w, int64_t K, int64_t N, int8
 
 static ql_status check_w8a8(const int8_t* xq, const int8_t* wq, const void* y, int64_t M,
                             int64_t N, int64_t K) {
-    if (bad_dims(M, N, K) || K % 64 != 0 || K > kMaxKw8a8)
+    if (bad_dims(M, N, K) || K % 64 != 0 || K > kMaxKw8a8 || N > kMaxNw8a8)
         return QL_ERR_SHAPE;
     if (M == 0 || N == 0)
         return QL_OK;

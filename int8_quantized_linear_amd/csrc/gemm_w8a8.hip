@@ -11,11 +11,14 @@
 // 2048ai.net INT8 Llama-2-7B write-up §5.3: the K loop double-buffers tiles in on-chip
 // memory; here that is LDS, filled while the matrix cores work on the other buffer.
 //
-// Tile: 256 (M) x 256 (N) per workgroup of 4 waves (2 x 2); each wave owns a 128 x 128
-// block of accumulators = 8 x 8 v_mfma_i32_16x16x64_i8 tiles (256 accumulator registers
-// per lane). K advances 64 bytes per step through a ring of 4 LDS stages that global ->
-// LDS direct loads (no register staging) fill three steps ahead; each step reads the
-// next step's MFMA fragments while its own MFMAs run, with one barrier per step.
+// Tiles are 256 x 256 per workgroup of 4 waves (2 x 2); each wave owns a 128 x 128 block
+// of accumulators = 4 x 4 v_mfma_i32_32x32x32_i8 blocks (256 accumulator registers per
+// lane). K advances 64 bytes per step through a ring of LDS stages that global -> LDS
+// direct copies (no register staging) fill ahead of use; each step reads the next
+// step's MFMA fragments while its own MFMAs run, with one barrier per step. The tile
+// size is set by L2 -> CU bandwidth: a tile moves (BM + BN) bytes per k for BM * BN
+// multiply-adds. When the last round of 256 x 256 tiles would leave CUs idle, its N
+// panels are cut into 128 x 256 tiles instead.
 #include "ql_internal.h"
 
 namespace ql {
@@ -53,32 +56,157 @@ __device__ inline void lds_copy16(const void* g, int8_t* lds) {
 __device__ inline int rowhash(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
 __device__ inline int swz(int r, int c) { return r * BK + ((c ^ rowhash(r)) << 4); }
 
-// Tile geometry: BM x BN outputs per workgroup of 4 waves laid out 2 x 2, each wave
-// WM x WN = (BM/2) x (BN/2); STAGES LDS buffers of BK = 64 k-columns each.
-template <int BM_, int BN_, int STAGES_>
-struct Geo {
-    static constexpr int BM = BM_, BN = BN_, STAGES = STAGES_;
-    static constexpr int WM = BM / 2, WN = BN / 2;
-    static constexpr int FM = WM / 16, FN = WN / 16;
-    static constexpr int STAGE_A = BM * BK, STAGE = (BM + BN) * BK;
-    static constexpr int LA = BM * BK / 16 / NTHR, LB = BN * BK / 16 / NTHR;  // copies/thread
-    static constexpr int LOADS = LA + LB;
-};
+// 4 bytes per lane from global memory straight into LDS (global_load_lds_dword): lane l's
+// word lands at l * 4 past the wave-uniform LDS address.
+__device__ inline void lds_copy4(const void* g, int8_t* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds(g, (lds_ptr)lds, 4, 0, 0);
+#endif
+}
 
-template <int BM_, int BN_, int STAGES_, int YMODE>
-__global__ __launch_bounds__(NTHR, 2) void gemm_w8a8_kernel(
-    const int8_t* __restrict__ A, const float* __restrict__ xs, const int8_t* __restrict__ B,
-    const float* __restrict__ ws, const float* __restrict__ bias, void* __restrict__ Y, int M,
-    int N, int K, int tiles_m, int tiles_n) {
-    using G = Geo<BM_, BN_, STAGES_>;
-    constexpr int BM = G::BM, BN = G::BN, STAGES = G::STAGES, WM = G::WM, WN = G::WN;
-    constexpr int FM = G::FM, FN = G::FN, STAGE_A = G::STAGE_A, STAGE = G::STAGE;
-    constexpr int LA = G::LA, LB = G::LB, LOADS = G::LOADS;
-    __shared__ __attribute__((aligned(1024))) int8_t smem[STAGES * STAGE];
+// Bytes of the K ring at the start of the LDS allocation; the tile's scales follow it:
+// x_scale of its 256 rows, then w_scale and bias of its 256 columns (fp32 each).
+constexpr int RING_BYTES = 4 * 512 * BK;
+constexpr int SCALE_BYTES = 3 * 256 * 4;
 
-    const int tile = xcd_remap(blockIdx.x, tiles_m * tiles_n);
-    const int tn = tile / tiles_m, tm = tile - tn * tiles_m;  // neighbours share the W panel
-    const int m0 = tm * BM, n0 = tn * BN;
+// Each wave copies 64 of the tile's x_scale, w_scale and bias entries into LDS (indices
+// clamped into range; entries past M or N are never used). Issued before the K loop's
+// first copies, so every wait of the loop also covers them; the epilogue's barrier makes
+// them visible to all waves. Without a bias, w_scale is copied in its place (unused).
+__device__ inline void issue_scales(const float* xs, const float* ws, const float* bias, int M,
+                                    int N, int m0, int n0, int wave, int lane, int8_t* smem) {
+    int8_t* sc = smem + RING_BYTES + wave * 256;
+    const int i = wave * 64 + lane;
+    lds_copy4(xs + min(m0 + i, M - 1), sc);
+    lds_copy4(ws + min(n0 + i, N - 1), sc + 1024);
+    lds_copy4((bias != nullptr ? bias : ws) + min(n0 + i, N - 1), sc + 2048);
+}
+
+// Epilogue: the accumulators are dequantized (y = acc * x_scale[m] * w_scale[n] + bias[n])
+// in registers and leave through LDS, one 32-row band of the wave's block at a time, so
+// that global stores are whole 16-byte pieces of contiguous row segments rather than
+// 2- or 4-byte scattered writes. Element e of block (i, j) in lane l is
+// C[8 (e >> 2) + 4 (l >> 5) + (e & 3)][l & 31] of that 32 x 32 block.
+// Stores go through a buffer descriptor whose size ends at row M: the hardware drops
+// stores of rows past M, and a column piece past N gets an offset beyond the size, so no
+// store needs a branch.
+template <int WM, int WN, int FM, int FN, int YMODE>
+__device__ __forceinline__ void store_tile(const i32x16 (&acc)[FM][FN], bool has_bias,
+                                           void* __restrict__ Y, int M, int N, int mrow0,
+                                           int ncol0, int lm0, int ln0, int wave, int lane,
+                                           int8_t* smem) {
+    using OutT = typename std::conditional<YMODE == Y_F16, _Float16,
+                 typename std::conditional<YMODE == Y_F32, float, int32_t>::type>::type;
+    constexpr int SZ = sizeof(OutT);
+    constexpr int VEC = 16 / SZ;                    // elements per 16-byte store
+    constexpr int ROWB = WN * SZ + 32;              // staged row, padded: rows r, r + 4 differ in bank half
+    constexpr int LPR = WN * SZ / 16;               // lanes per staged row
+    constexpr int RPI = 64 / LPR;                   // rows per read / store instruction
+    constexpr int NRD = 32 / RPI;                   // reads (and stores) per band
+    static_assert(4 * 32 * ROWB <= RING_BYTES, "output staging fits the LDS ring");
+    // Descriptor sizes are capped at LIM = 2^30 bytes, which no in-range offset reaches
+    // (32 rows of at most 2^23 4-byte values); a column piece past N is sent to offset
+    // row + LIM, at or past the size, and row + LIM stays below 2^31.
+    constexpr int LIM = 1 << 30;
+
+    barrier_no_fence();   // the ring is no longer read; every wave's scale copies landed
+    int8_t* stage = smem + wave * 32 * ROWB;
+    const float* sx = reinterpret_cast<const float*>(smem + RING_BYTES);
+    const float* sw = sx + 256;
+    const float* sb = sx + 512;
+    float wsv[FN], bv[FN];
+    if constexpr (YMODE != Y_I32) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int c = ln0 + 32 * j + (lane & 31);
+            wsv[j] = sw[c];
+            bv[j] = has_bias ? sb[c] : 0.0f;
+        }
+    }
+    const bool vec_ok = (N % VEC) == 0;   // rows start 16-byte aligned
+    // byte offset of this lane's 16-byte piece in the first row it stores of a band
+    const int ncol = ncol0 + (lane % LPR) * VEC;
+    const int lane_off = (lane / LPR) * N * SZ + (ncol < N ? ncol * SZ : LIM);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        float xsv[16];
+        if constexpr (YMODE != Y_I32) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x4 v = *reinterpret_cast<const f32x4*>(sx + lm0 + 32 * i + 8 * g + 4 * (lane >> 5));
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    xsv[4 * g + q] = v[q];
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int r = 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                OutT v;
+                if constexpr (YMODE == Y_I32)
+                    v = acc[i][j][e];
+                else
+                    v = (OutT)((float)acc[i][j][e] * xsv[e] * wsv[j] + bv[j]);
+                *reinterpret_cast<OutT*>(stage + r * ROWB + (32 * j + (lane & 31)) * SZ) = v;
+            }
+        }
+        // The wave's LDS operations complete in order, so its reads below see all of its
+        // writes above; this only keeps the compiler from reordering them.
+        asm volatile("" ::: "memory");
+        u32x4 rv[NRD];
+#pragma unroll
+        for (int p = 0; p < NRD; ++p) {
+            const int r = p * RPI + lane / LPR, c = (lane % LPR) * VEC;
+            rv[p] = *reinterpret_cast<const u32x4*>(stage + r * ROWB + c * SZ);
+        }
+        const int row0 = mrow0 + 32 * i;
+        const int64_t left = (int64_t)(M - row0) * N * SZ;   // bytes from row0 to the end
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            reinterpret_cast<int8_t*>(Y) + (int64_t)row0 * N * SZ, 0,
+            (int)(left <= 0 ? 0 : (left < LIM ? left : LIM)), 0x00020000);
+        if (vec_ok) {
+#pragma unroll
+            for (int p = 0; p < NRD; ++p)
+                __builtin_amdgcn_raw_buffer_store_b128(rv[p], rs, lane_off + p * RPI * N * SZ, 0, 0);
+        } else {
+            const int n = ncol0 + (lane % LPR) * VEC;
+#pragma unroll
+            for (int p = 0; p < NRD; ++p) {
+                const int roff = (p * RPI + lane / LPR) * N * SZ;
+                const OutT* pv = reinterpret_cast<const OutT*>(&rv[p]);
+#pragma unroll
+                for (int q = 0; q < VEC; ++q) {
+                    const int off = roff + (n + q < N ? (n + q) * SZ : LIM);
+                    if constexpr (SZ == 2)
+                        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, pv[q]), rs, off, 0, 0);
+                    else
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, pv[q]), rs, off, 0, 0);
+                }
+            }
+        }
+        asm volatile("" ::: "memory");   // the next band's writes follow these reads
+    }
+}
+
+// One output tile of BM x BN (BM = 256 or 128, BN = 256) computed by the workgroup's 4
+// waves laid out 2 x 2; each wave owns (BM/2) x (BN/2) = FM x FN blocks of 32 x 32
+// accumulators (v_mfma_i32_32x32x32_i8, 16 int32 per lane each). K advances BK = 64
+// bytes per step through a ring of STAGES LDS buffers (two 32-deep k-substeps per step).
+template <int BM, int BN, int STAGES, int YMODE>
+__device__ __forceinline__ void gemm_tile(const int8_t* __restrict__ A, const float* __restrict__ xs,
+                                          const int8_t* __restrict__ B, const float* __restrict__ ws,
+                                          const float* __restrict__ bias, void* __restrict__ Y, int M,
+                                          int N, int K, int m0, int n0, int8_t* smem) {
+    constexpr int WM = BM / 2, WN = BN / 2;
+    constexpr int FM = WM / 32, FN = WN / 32;
+    constexpr int STAGE_A = BM * BK, STAGE = (BM + BN) * BK;
+    constexpr int LA = BM * BK / 16 / NTHR, LB = BN * BK / 16 / NTHR;  // copies per thread
+    constexpr int LOADS = LA + LB;
+    static_assert(STAGES >= 3, "the ring needs a buffer being read, one landing, one free");
+    static_assert(STAGES * STAGE <= RING_BYTES, "the ring fits its LDS");
+
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int wm = wave >> 1, wn = wave & 1;
@@ -115,35 +243,45 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_w8a8_kernel(
             lds_copy16(gb[i] + k0, st + STAGE_A + (wave * LB + i) * 1024);
     };
 
-    i32x4 acc[FM][FN];
+    i32x16 acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-            acc[i][j] = i32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                acc[i][j][e] = 0;
 
-    // Fragment reads: lane l takes row (l & 15) of a 16-row block and logical chunk (l >> 4)
-    // of the 64-byte k-step; A and B use the same k <-> (lane, byte) assignment, so their
-    // products pair the same k. rowhash depends on the low 4 row bits only, so a wave's
-    // blocks are one base address plus multiples of 1 KB.
-    const int fa_off = swz(wm * WM + (lane & 15), lane >> 4);
-    const int fb_off = STAGE_A + swz(wn * WN + (lane & 15), lane >> 4);
-    auto read_frags = [&](int kt, i32x4 (&fa)[FM], i32x4 (&fb)[FN]) {
+    // Fragment reads: for k-substep ks, lane l takes row (l & 31) of a 32-row block and
+    // logical chunk 2 ks + (l >> 5) of the 64-byte step; A and B use the same
+    // k <-> (lane, byte) assignment, so their products pair the same k. rowhash depends on
+    // the low 4 row bits only, so a wave's blocks are one base address plus multiples of 2 KB.
+    const int fa_off = wm * WM * BK, fb_off = STAGE_A + wn * WN * BK;
+    const int fr = lane & 31;
+    const int f_off0 = swz(fr, lane >> 5), f_off1 = swz(fr, 2 + (lane >> 5));
+    typedef i32x4 Frag[2][FM + FN];   // [ks][A blocks then B blocks]
+    auto read_frags = [&](int kt, Frag& f) {
         const int8_t* st = smem + (kt % STAGES) * STAGE;
-        // B first: the next step's first MFMAs use A block 0 with every B block
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-            fb[j] = *reinterpret_cast<const i32x4*>(st + fb_off + j * 16 * BK);
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-            fa[i] = *reinterpret_cast<const i32x4*>(st + fa_off + i * 16 * BK);
-    };
-    auto mfmas = [&](const i32x4 (&fa)[FM], const i32x4 (&fb)[FN]) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
+        for (int ks = 0; ks < 2; ++ks) {
+            const int fo = ks ? f_off1 : f_off0;
+            // B first: the next step's first MFMAs use A block 0 with every B block
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+                f[ks][FM + j] = *reinterpret_cast<const i32x4*>(st + fb_off + fo + j * 32 * BK);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                f[ks][i] = *reinterpret_cast<const i32x4*>(st + fa_off + fo + i * 32 * BK);
+        }
+    };
+    auto mfmas = [&](const Frag& f) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f[ks][i], f[ks][FM + j], acc[i][j], 0, 0, 0);
     };
 
     // Step kt: wait until stage kt+1 has landed (only the copies of the stages after it
@@ -152,18 +290,16 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_w8a8_kernel(
     // kt+1's fragments, and run stage kt's MFMAs with the copies and reads spread among
     // them. Past the last stage the copies repeat the last stage (the buffers they fill
     // are never read), so every step has the same shape. sched_barrier(0) keeps steps
-    // from being interleaved with each other.
-    constexpr int NMF = FM * FN, NDS = FM + FN;
-    // Before step kt's wait, stages 0 .. kt+STAGES-2 have been issued.
-    static_assert(STAGES >= 3, "the ring needs a buffer being read, one landing, one free");
-    auto step = [&](int kt, const i32x4 (&fa)[FM], const i32x4 (&fb)[FN], i32x4 (&na)[FM],
-                    i32x4 (&nb)[FN]) {
+    // from being interleaved with each other. Before step kt's wait, stages
+    // 0 .. kt+STAGES-2 have been issued.
+    constexpr int NMF = 2 * FM * FN, NDS = 2 * (FM + FN);
+    auto step = [&](int kt, const Frag& cur, Frag& nxt) {
         __builtin_amdgcn_s_waitcnt(vmcnt_le((STAGES - 3) * LOADS));
         barrier_no_fence();
         __builtin_amdgcn_sched_barrier(0);
         issue(kt + STAGES - 1);
-        read_frags(kt + 1, na, nb);
-        mfmas(fa, fb);
+        read_frags(kt + 1, nxt);
+        mfmas(cur);
 #pragma unroll
         for (int g = 0; g < LOADS; ++g) {
             __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                  // VMEM (copy)
@@ -178,7 +314,9 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_w8a8_kernel(
     // Steps run in pairs over two fragment register sets. With an odd number of steps a
     // virtual step -1 of zero fragments comes first. Before the first step k0 the copies
     // of stages k0+1 .. k0+STAGES-2 are the ones pending.
-    i32x4 f0a[FM], f0b[FN], f1a[FM], f1b[FN];
+    if constexpr (YMODE != Y_I32)
+        issue_scales(xs, ws, bias, M, N, m0, n0, wave, lane, smem);
+    Frag f0, f1;
     int k0;
     if (KT & 1) {
         k0 = -1;
@@ -186,11 +324,10 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_w8a8_kernel(
         for (int s = 0; s < STAGES - 2; ++s)
             issue(s);
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-            f0a[i] = i32x4{0, 0, 0, 0};
+        for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-            f0b[j] = i32x4{0, 0, 0, 0};
+            for (int i = 0; i < FM + FN; ++i)
+                f0[ks][i] = i32x4{0, 0, 0, 0};
     } else {
         k0 = 0;
 #pragma unroll
@@ -198,80 +335,233 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_w8a8_kernel(
             issue(s);
         __builtin_amdgcn_s_waitcnt(vmcnt_le((STAGES - 2) * LOADS));
         barrier_no_fence();
-        read_frags(0, f0a, f0b);
+        read_frags(0, f0);
     }
     for (int kt = k0; kt < KT; kt += 2) {
-        step(kt, f0a, f0b, f1a, f1b);
-        step(kt + 1, f1a, f1b, f0a, f0b);   // reads past the end on the last pair: unused
+        step(kt, f0, f1);
+        step(kt + 1, f1, f0);   // reads past the end on the last pair: never used
     }
     // No copy into LDS may still be in flight when the workgroup's LDS is released.
     __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
 
-    // Epilogue. Accumulator element r of tile (i, j) in lane l is C[4 (l >> 4) + r][l & 15]
-    // of that 16 x 16 tile.
-    const int mb = m0 + wm * WM + 4 * (lane >> 4);
-    const int nb = n0 + wn * WN + (lane & 15);
-    float wsv[FN], bv[FN];
-    if constexpr (YMODE != Y_I32) {
+    store_tile<WM, WN, FM, FN, YMODE>(acc, bias != nullptr, Y, M, N, m0 + wm * WM, n0 + wn * WN, wm * WM,
+                                      wn * WN, wave, lane, smem);
+}
+
+// Rows of 128 bytes (eight 16-byte chunks): chunk c of row r is stored at chunk position
+// c ^ h128(r), which differs across any 8 consecutive rows and, with the row parity,
+// across any 16, so the rows one fragment read touches fall in distinct bank groups.
+__device__ inline int h128(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// The same tile with 128-byte k-steps (for K % 128 == 0): each copied row piece is a whole
+// 128-byte line, which the L2 -> CU path delivers at about twice the rate of half lines.
+// Two LDS stages of (BM + BN) x 128 bytes. Fragments are read one 32-deep substep ahead
+// of the MFMAs that use them, continuously across stage boundaries; before a stage's last
+// substep each wave waits for its copies of the next stage and for its own LDS reads,
+// then a barrier frees the current stage's buffer for the stage after next.
+template <int BM, int BN, int YMODE>
+__device__ __forceinline__ void gemm_tile128(const int8_t* __restrict__ A, const float* __restrict__ xs,
+                                             const int8_t* __restrict__ B, const float* __restrict__ ws,
+                                             const float* __restrict__ bias, void* __restrict__ Y,
+                                             int M, int N, int K, int m0, int n0, int8_t* smem) {
+    constexpr int BKL = 128;
+    constexpr int WM = BM / 2, WN = BN / 2;
+    constexpr int FM = WM / 32, FN = WN / 32;
+    constexpr int STAGE_A = BM * BKL, STAGE = (BM + BN) * BKL;
+    constexpr int LA = BM * BKL / 16 / NTHR, LB = BN * BKL / 16 / NTHR;  // copies per thread
+    constexpr int LOADS = LA + LB;
+    static_assert(2 * STAGE <= RING_BYTES, "two stages fit the LDS allocation");
+
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int KT = K / BKL;
+
+    // Copy slots: slot s holds row s >> 3 at chunk position s & 7, i.e. logical chunk
+    // (s & 7) ^ h128(row); lane l of an instruction lands in slot base + l. Rows past M or
+    // N are clamped to the last row (their results are never stored).
+    const int8_t* ga[LA];
+    const int8_t* gb[LB];
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int n = nb + 16 * j;
-            wsv[j] = n < N ? ws[n] : 0.0f;
-            bv[j] = (bias != nullptr && n < N) ? bias[n] : 0.0f;
-        }
+    for (int i = 0; i < LA; ++i) {
+        const int slot = wave * (LA * 64) + i * 64 + lane;
+        const int r = slot >> 3, c = (slot & 7) ^ h128(slot >> 3);
+        ga[i] = A + (int64_t)min(m0 + r, M - 1) * K + c * 16;
     }
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+    for (int i = 0; i < LB; ++i) {
+        const int slot = wave * (LB * 64) + i * 64 + lane;
+        const int r = slot >> 3, c = (slot & 7) ^ h128(slot >> 3);
+        gb[i] = B + (int64_t)min(n0 + r, N - 1) * K + c * 16;
+    }
+    // Copies stage kt (clamped to the last stage) into buffer kt & 1.
+    auto issue = [&](int kt) {
+        int8_t* st = smem + (kt & 1) * STAGE;
+        const int k0 = min(kt, KT - 1) * BKL;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int m = mb + 16 * i + r;
-            if (m >= M)
-                continue;
-            float xsv = 0.0f;
-            if constexpr (YMODE != Y_I32)
-                xsv = xs[m];
+        for (int i = 0; i < LA; ++i)
+            lds_copy16(ga[i] + k0, st + (wave * LA + i) * 1024);
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int n = nb + 16 * j;
-                if (n >= N)
-                    continue;
-                const int64_t o = (int64_t)m * N + n;
-                if constexpr (YMODE == Y_I32) {
-                    reinterpret_cast<int32_t*>(Y)[o] = acc[i][j][r];
-                } else {
-                    const float y = (float)acc[i][j][r] * xsv * wsv[j] + bv[j];
-                    if constexpr (YMODE == Y_F32)
-                        reinterpret_cast<float*>(Y)[o] = y;
-                    else
-                        reinterpret_cast<_Float16*>(Y)[o] = (_Float16)y;
-                }
-            }
+        for (int i = 0; i < LB; ++i)
+            lds_copy16(gb[i] + k0, st + STAGE_A + (wave * LB + i) * 1024);
+    };
+
+    i32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                acc[i][j][e] = 0;
+
+    // Fragment of substep u (stage u >> 2, k-substep u & 3): lane l takes row (l & 31) of a
+    // 32-row block and logical chunk 2 (u & 3) + (l >> 5); A and B use the same
+    // k <-> (lane, byte) assignment. h128 depends on the low 4 row bits only.
+    const int lr = lane & 31;
+    const int fa_base = wm * WM * BKL + lr * BKL, fb_base = STAGE_A + wn * WN * BKL + lr * BKL;
+    typedef i32x4 Frag[FM + FN];   // A blocks then B blocks
+    auto read = [&](int u, Frag& f) {
+        const int8_t* st = smem + ((u >> 2) & 1) * STAGE;
+        const int co = ((2 * (u & 3) + (lane >> 5)) ^ h128(lr)) << 4;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            f[FM + j] = *reinterpret_cast<const i32x4*>(st + fb_base + co + j * 32 * BKL);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+            f[i] = *reinterpret_cast<const i32x4*>(st + fa_base + co + i * 32 * BKL);
+    };
+    auto mfma = [&](const Frag& f) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f[i], f[FM + j], acc[i][j], 0, 0, 0);
+    };
+    constexpr int NMF = FM * FN, NDS = FM + FN;
+    // a substep: next fragments read among this substep's MFMAs
+    auto sub = [&](int u, const Frag& cur, Frag& nxt) {
+        read(u + 1, nxt);
+        mfma(cur);
+        // MFMAs lead each group (the compiler's LDS wait before an MFMA covers every read
+        // issued so far, so reads just issued would stall it), except that the last read
+        // pair goes ahead of the last MFMA group, which then hides its latency
+        constexpr int G = NDS / 2, Q = NMF / G;
+#pragma unroll
+        for (int g = 0; g < G - 1; ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x008, Q, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS read
         }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, Q + NMF % G, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    if constexpr (YMODE != Y_I32)
+        issue_scales(xs, ws, bias, M, N, m0, n0, wave, lane, smem);
+    issue(0);
+    issue(1);
+    __builtin_amdgcn_s_waitcnt(vmcnt_le(LOADS));   // stage 0 landed
+    barrier_no_fence();
+    Frag f0, f1;
+    read(0, f0);
+    for (int kt = 0; kt < KT; ++kt) {
+        const int u = 4 * kt;
+        sub(u, f0, f1);
+        sub(u + 1, f1, f0);
+        sub(u + 2, f0, f1);
+        // last substep: stage kt+1 must be in LDS and this wave's reads of stage kt done
+        // before the barrier hands stage kt's buffer to the copies of stage kt+2
+        __builtin_amdgcn_s_waitcnt(vmcnt_le(0) & ~(0xF << 8));   // vmcnt(0) lgkmcnt(0)
+        barrier_no_fence();
+        __builtin_amdgcn_sched_barrier(0);
+        issue(kt + 2);
+        read(u + 4, f0);   // past the end on the last stage: never used
+        mfma(f1);
+        constexpr int G4 = LOADS / 4, Q4 = NMF / G4;
+#pragma unroll
+        for (int g = 0; g < G4 - 1; ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x008, Q4, 0);              // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);               // VMEM (copy)
+            __builtin_amdgcn_sched_group_barrier(0x100, NDS / G4, 0);        // DS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, NDS - (G4 - 1) * (NDS / G4), 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, NMF - (G4 - 1) * Q4, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // No copy into LDS may still be in flight when the LDS is reused or released.
+    __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
+    store_tile<WM, WN, FM, FN, YMODE>(acc, bias != nullptr, Y, M, N, m0 + wm * WM, n0 + wn * WN, wm * WM,
+                                      wn * WN, wave, lane, smem);
+}
+
+// Tiles: the first `nbig` workgroups take 256 x 256 tiles of the first `nbig / tiles_m`
+// N-panels; the rest take 128 x 256 tiles of the remaining panels. With 256 CUs, whole
+// rounds of big tiles keep every CU busy and the leftover panels run as half-height
+// tiles in a shorter final round. Within each group, workgroups are dealt to XCDs so
+// that an XCD's tiles are consecutive and share W panels (column-major tile order).
+struct TilePlan {
+    int tiles_m_big, nbig, tiles_m_small, nsmall, n_small0;
+};
+
+template <int YMODE, bool K128>
+__global__ __launch_bounds__(NTHR, 1) void gemm_w8a8_kernel(
+    const int8_t* __restrict__ A, const float* __restrict__ xs, const int8_t* __restrict__ B,
+    const float* __restrict__ ws, const float* __restrict__ bias, void* __restrict__ Y, int M,
+    int N, int K, TilePlan plan) {
+    __shared__ __attribute__((aligned(1024))) int8_t smem[RING_BYTES + SCALE_BYTES];
+    const int bid = blockIdx.x;
+    if (bid < plan.nbig) {
+        const int tile = xcd_remap(bid, plan.nbig);
+        const int tn = tile / plan.tiles_m_big, tm = tile - tn * plan.tiles_m_big;
+        if constexpr (K128)
+            gemm_tile128<256, 256, YMODE>(A, xs, B, ws, bias, Y, M, N, K, tm * 256, tn * 256, smem);
+        else
+            gemm_tile<256, 256, 4, YMODE>(A, xs, B, ws, bias, Y, M, N, K, tm * 256, tn * 256, smem);
+    } else {
+        const int tile = xcd_remap(bid - plan.nbig, plan.nsmall);
+        const int tn = tile / plan.tiles_m_small, tm = tile - tn * plan.tiles_m_small;
+        if constexpr (K128)
+            gemm_tile128<128, 256, YMODE>(A, xs, B, ws, bias, Y, M, N, K, tm * 128,
+                                          plan.n_small0 + tn * 256, smem);
+        else
+            gemm_tile<128, 256, 5, YMODE>(A, xs, B, ws, bias, Y, M, N, K, tm * 128,
+                                          plan.n_small0 + tn * 256, smem);
     }
 }
 
-template <class G>
-ql_status launch_geo(const int8_t* xq, const float* x_scale, const int8_t* wq,
-                     const float* w_scale, const float* bias, void* y, int y_mode, int64_t M,
-                     int64_t N, int64_t K, hipStream_t stream) {
-    const int tiles_m = (int)((M + G::BM - 1) / G::BM), tiles_n = (int)((N + G::BN - 1) / G::BN);
-    const dim3 grid((unsigned)(tiles_m * tiles_n)), block(NTHR);
-    const int m = (int)M, n = (int)N, k = (int)K;
-    switch (y_mode) {
-    case Y_F32:
-        hipLaunchKernelGGL((gemm_w8a8_kernel<G::BM, G::BN, G::STAGES, Y_F32>), grid, block, 0, stream, xq, x_scale, wq,
-                           w_scale, bias, y, m, n, k, tiles_m, tiles_n);
-        break;
-    case Y_F16:
-        hipLaunchKernelGGL((gemm_w8a8_kernel<G::BM, G::BN, G::STAGES, Y_F16>), grid, block, 0, stream, xq, x_scale, wq,
-                           w_scale, bias, y, m, n, k, tiles_m, tiles_n);
-        break;
-    default:
-        hipLaunchKernelGGL((gemm_w8a8_kernel<G::BM, G::BN, G::STAGES, Y_I32>), grid, block, 0, stream, xq, x_scale, wq,
-                           w_scale, bias, y, m, n, k, tiles_m, tiles_n);
-        break;
+int cu_count() {
+    static int n = 0;
+    if (n == 0) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            n = v;
+        else
+            n = 256;
     }
-    return launch_status();
+    return n;
+}
+
+TilePlan plan_tiles(int64_t M, int64_t N) {
+    TilePlan p{};
+    const int tm = (int)((M + 255) / 256), tn = (int)((N + 255) / 256);
+    const int total = tm * tn, cus = cu_count();
+    int small_panels = 0;
+    if (M <= 128) {
+        small_panels = tn;                      // every tile is half height
+    } else if (total > cus) {
+        const int left = total % cus;           // tiles of the last, partial round
+        if (left > 0 && left <= cus / 2)
+            small_panels = (left + tm - 1) / tm;
+    }
+    p.tiles_m_big = tm;
+    p.nbig = (tn - small_panels) * tm;
+    p.tiles_m_small = (int)((M + 127) / 128);
+    p.nsmall = small_panels * p.tiles_m_small;
+    p.n_small0 = (tn - small_panels) * 256;
+    return p;
 }
 
 }  // namespace
@@ -281,8 +571,26 @@ ql_status launch_gemm_w8a8(const int8_t* xq, const float* x_scale, const int8_t*
                            int64_t M, int64_t N, int64_t K, hipStream_t stream) {
     if (M == 0 || N == 0)
         return QL_OK;
-    return launch_geo<Geo<256, 128, 3>>(xq, x_scale, wq, w_scale, bias, y, y_mode, M, N, K,
-                                        stream);
+    const TilePlan plan = plan_tiles(M, N);
+    const dim3 grid((unsigned)(plan.nbig + plan.nsmall)), block(NTHR);
+    const int m = (int)M, n = (int)N, k = (int)K;
+#define QL_LAUNCH(MODE, K128)                                                                   \
+    hipLaunchKernelGGL((gemm_w8a8_kernel<MODE, K128>), grid, block, 0, stream, xq, x_scale, wq,  \
+                       w_scale, bias, y, m, n, k, plan)
+    const bool k128 = K % 128 == 0;
+    switch (y_mode) {
+    case Y_F32:
+        if (k128) QL_LAUNCH(Y_F32, true); else QL_LAUNCH(Y_F32, false);
+        break;
+    case Y_F16:
+        if (k128) QL_LAUNCH(Y_F16, true); else QL_LAUNCH(Y_F16, false);
+        break;
+    default:
+        if (k128) QL_LAUNCH(Y_I32, true); else QL_LAUNCH(Y_I32, false);
+        break;
+    }
+#undef QL_LAUNCH
+    return launch_status();
 }
 
 }  // namespace ql

@@ -39,6 +39,19 @@ def test_int32_bit_exact(ql, M, N, K):
     assert np.array_equal(host(acc), oracle.gemm_i32(a, b))
 
 
+@pytest.mark.parametrize("M,N,K", [(2000, 8300, 64), (2048, 11008, 192)])
+def test_int32_mixed_tile_plan(ql, M, N, K):
+    """Shapes with more 256 x 256 tiles than CUs, where the last N panels run as 128-row
+    tiles in the same launch (ragged M and N in the first case); rows sampled from every
+    128-row band are checked bit-exactly."""
+    rng = np.random.default_rng(M + N + K)
+    a = _rand_codes(rng, (M, K), -128)
+    b = _rand_codes(rng, (N, K), -128)
+    acc = host(ql.gemm_w8a8_int32(dev(a), dev(b)))
+    rows = np.unique(np.concatenate([np.arange(0, M, 61), np.arange(M - 5, M)]))
+    assert np.array_equal(acc[rows], oracle.gemm_i32(a[rows], b))
+
+
 def test_int32_extremes(ql):
     """The largest K the boundary accepts with the most negative products."""
     K = 131008
