@@ -40,7 +40,8 @@
  *     QL_ERR_NULL  a required pointer is NULL
  *     QL_ERR_SHAPE a size is negative or breaks the divisibility stated per call
  *     QL_ERR_ALIGN a large operand (X, W, Y, codes) is not 16-byte aligned, or a
- *                  scale/bias/zero array is not aligned to its element size
+ *                  scale/bias/zero array is not aligned to its element size (to 4
+ *                  bytes for the weight-only calls' scale and zero-point arrays)
  *     QL_ERR_DTYPE an unknown dtype code
  *     QL_ERR_DEVICE the HIP launch reported an error (hipGetLastError)
  *   - Inputs are assumed finite (no NaN or Inf).
@@ -142,11 +143,11 @@ ql_status gemm_w8a8_int32(const int8_t* xq, const int8_t* wq, int32_t* acc, int6
  * wq         W [K,N] column-major ([N][K]): int8 codes if zero_point is NULL, else
  *            uint8 codes
  * w_scale    fp32: [N] if group_size == 0, else [K/group_size, N] column-major
- * zero_point NULL (symmetric), or uint8 with the same shape as w_scale
+ * zero_point NULL (symmetric), or uint8 with the same shape as w_scale (4-byte aligned)
  * group_size 0 (one scale per output column) or a multiple of 64 dividing K
  * bias       [N] fp32, or NULL
  * y          [M,N] fp16 row-major (out)
- * Requires K > 0, K % 64 == 0.
+ * Requires K > 0, K % 64 == 0 and K <= 2^22.
  */
 ql_status gemm_w8a16(const void* x, const void* wq, const float* w_scale,
                      const uint8_t* zero_point, int64_t group_size, const float* bias, void* y,
@@ -162,11 +163,11 @@ ql_status gemm_w8a16(const void* x, const void* wq, const float* w_scale,
  * x          [M,K] fp16 row-major
  * wq_packed  int32 [N][K/8]: word w of column n holds k = 8w + j in bits [4j, 4j+3],
  *            two's complement (values -8..7)
- * scales     fp16 [K/group_size, N] column-major ([N][K/group_size])
+ * scales     fp16 [K/group_size, N] column-major ([N][K/group_size]), 4-byte aligned
  * group_size a multiple of 64 dividing K
  * bias       [N] fp32, or NULL
  * y          [M,N] fp16 row-major (out)
- * Requires K > 0, K % 64 == 0.
+ * Requires K > 0, K % 64 == 0 and K <= 2^22.
  */
 ql_status gemm_w4a16_grouped(const void* x, const int32_t* wq_packed, const void* scales,
                              int64_t group_size, const float* bias, void* y, int64_t M,

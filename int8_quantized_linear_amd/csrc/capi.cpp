@@ -10,6 +10,7 @@ namespace {
 constexpr int64_t kMaxDim = (int64_t)1 << 31;   // sizes are passed to kernels as int
 constexpr int64_t kMaxKw8a8 = 131008;           // K * 128^2 < 2^31, K % 64 == 0
 constexpr int64_t kMaxNw8a8 = (int64_t)1 << 23; // 32 output rows of 4-byte values: 2^30 bytes
+constexpr int64_t kMaxKwonly = (int64_t)1 << 22; // 64 rows of fp16 X and 64 weight columns < 2^31 bytes
 
 inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
@@ -113,7 +114,7 @@ ql_status gemm_w8a8_int32(const int8_t* xq, const int8_t* wq, int32_t* acc, int6
 ql_status gemm_w8a16(const void* x, const void* wq, const float* w_scale,
                      const uint8_t* zero_point, int64_t group_size, const float* bias, void* y,
                      int64_t M, int64_t N, int64_t K, void* stream) {
-    if (bad_dims(M, N, K) || K % 64 != 0 || group_size < 0 ||
+    if (bad_dims(M, N, K) || K % 64 != 0 || K > kMaxKwonly || group_size < 0 ||
         (group_size > 0 && (group_size % 64 != 0 || K % group_size != 0)))
         return QL_ERR_SHAPE;
     if (M == 0 || N == 0)
@@ -121,7 +122,7 @@ ql_status gemm_w8a16(const void* x, const void* wq, const float* w_scale,
     if (!x || !wq || !w_scale || !y)
         return QL_ERR_NULL;
     if (!aligned(x, 16) || !aligned(wq, 16) || !aligned(y, 16) || !aligned(w_scale, 4) ||
-        (bias && !aligned(bias, 4)))
+        (zero_point && !aligned(zero_point, 4)) || (bias && !aligned(bias, 4)))
         return QL_ERR_ALIGN;
     return ql::launch_wonly(x, wq, zero_point ? ql::W_UINT8_ZP : ql::W_INT8_SYM, w_scale,
                             zero_point, group_size, bias, y, M, N, K, as_stream(stream));
@@ -130,14 +131,14 @@ ql_status gemm_w8a16(const void* x, const void* wq, const float* w_scale,
 ql_status gemm_w4a16_grouped(const void* x, const int32_t* wq_packed, const void* scales,
                              int64_t group_size, const float* bias, void* y, int64_t M, int64_t N,
                              int64_t K, void* stream) {
-    if (bad_dims(M, N, K) || K % 64 != 0 || group_size <= 0 || group_size % 64 != 0 ||
+    if (bad_dims(M, N, K) || K % 64 != 0 || K > kMaxKwonly || group_size <= 0 || group_size % 64 != 0 ||
         K % group_size != 0)
         return QL_ERR_SHAPE;
     if (M == 0 || N == 0)
         return QL_OK;
     if (!x || !wq_packed || !scales || !y)
         return QL_ERR_NULL;
-    if (!aligned(x, 16) || !aligned(wq_packed, 16) || !aligned(y, 16) || !aligned(scales, 2) ||
+    if (!aligned(x, 16) || !aligned(wq_packed, 16) || !aligned(y, 16) || !aligned(scales, 4) ||
         (bias && !aligned(bias, 4)))
         return QL_ERR_ALIGN;
     return ql::launch_wonly(x, wq_packed, ql::W_INT4_SYM, scales, nullptr, group_size, bias, y, M,
