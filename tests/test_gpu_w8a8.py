@@ -29,9 +29,12 @@ def _rand_codes(rng, shape, lo=-127):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 64), (16, 256, 256), (300, 520, 384), (257, 129, 192),
-                                   (512, 768, 1024), (33, 1000, 192), (256, 256, 64)])
+                                   (512, 768, 1024), (33, 1000, 192), (256, 256, 64),
+                                   (100, 1000, 384), (128, 300, 128), (64, 256, 640), (127, 513, 256)])
 def test_int32_bit_exact(ql, M, N, K):
-    """Several tiles in M and N, ragged tails, K with a half k-tile tail, codes including -128."""
+    """Several tiles in M and N, ragged tails, K with a half k-tile tail, codes including -128.
+    M <= 128 runs every tile at half height (K split between the workgroup's two wave
+    groups), with 1, 2, 3 and 5 128-deep stages."""
     rng = np.random.default_rng(M * 1000 + N + K)
     a = _rand_codes(rng, (M, K), -128)
     b = _rand_codes(rng, (N, K), -128)
@@ -39,7 +42,8 @@ def test_int32_bit_exact(ql, M, N, K):
     assert np.array_equal(host(acc), oracle.gemm_i32(a, b))
 
 
-@pytest.mark.parametrize("M,N,K", [(2000, 8300, 64), (2048, 11008, 192)])
+@pytest.mark.parametrize("M,N,K", [(2000, 8300, 64), (2048, 11008, 192), (2048, 11008, 384),
+                                   (2000, 8300, 256)])
 def test_int32_mixed_tile_plan(ql, M, N, K):
     """Shapes with more 256 x 256 tiles than CUs, where the last N panels run as 128-row
     tiles in the same launch (ragged M and N in the first case); rows sampled from every
