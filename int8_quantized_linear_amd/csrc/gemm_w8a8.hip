@@ -11,27 +11,21 @@
 // 2048ai.net INT8 Llama-2-7B write-up §5.3: the K loop double-buffers tiles in on-chip
 // memory; here that is LDS, filled while the matrix cores work on the other buffer.
 //
-// Tiles are 256 x 256 per workgroup of 4 waves (2 x 2); each wave owns a 128 x 128 block
-// of accumulators = 4 x 4 v_mfma_i32_32x32x32_i8 blocks (256 accumulator registers per
-// lane). K advances 64 bytes per step through a ring of LDS stages that global -> LDS
-// direct copies (no register staging) fill ahead of use; each step reads the next
-// step's MFMA fragments while its own MFMAs run, with one barrier per step. The tile
+// A workgroup of 8 waves (two per SIMD) computes a 256 x 256 output tile on
+// v_mfma_i32_32x32x32_i8. K advances 128 bytes per stage through LDS buffers filled by
+// direct buffer -> LDS copies (no register staging), whole 128-byte row pieces. The tile
 // size is set by L2 -> CU bandwidth: a tile moves (BM + BN) bytes per k for BM * BN
-// multiply-adds. When the last round of 256 x 256 tiles would leave CUs idle, its N
-// panels are cut into 128 x 256 tiles instead.
+// multiply-adds. The two 4-wave groups alternate between MFMA phases and phases of LDS
+// fragment reads and copies, so a SIMD's MFMA stream never waits behind its own memory
+// instructions. When the last round of 256 x 256 tiles would leave CUs idle, its N
+// panels run as 128 x 256 tiles whose K is split between the two groups. K % 128 == 64
+// runs a last stage whose upper half reads zeros.
 #include "ql_internal.h"
 
 namespace ql {
 namespace {
 
-constexpr int BK = 64;
-constexpr int NTHR = 256;   // threads of the 64-byte ring path
-#ifndef GEMM_WAVES_K128
-#define GEMM_WAVES_K128 8
-#endif
-#ifndef GEMM_PINGPONG
-#define GEMM_PINGPONG 1
-#endif
+constexpr int NWAVES = 8;
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
@@ -40,27 +34,12 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 constexpr int vmcnt_le(int n) { return (n & 0xF) | (0x7 << 4) | (0xF << 8) | (((n >> 4) & 3) << 14); }
 
 // Workgroup barrier without a memory fence: __syncthreads() would also wait for every
-// pending global -> LDS copy, including the stages still being prefetched. Each wave
-// instead waits (vmcnt) for its own copies of the stage about to be read, and LDS reads
-// are complete before the MFMAs that consume them, so after the barrier the stage is
-// visible and the oldest buffer is free. The "memory" clobber keeps the compiler from
-// moving LDS accesses across the barrier.
+// pending copy into LDS, including the stages still being prefetched. Each wave instead
+// waits (vmcnt) for its own copies of the stage about to be read and (lgkmcnt) for its
+// own LDS reads of the buffer about to be refilled, so after the barrier the stage is
+// visible and the buffer is free. The "memory" clobber keeps the compiler from moving
+// LDS accesses across the barrier.
 __device__ inline void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
-
-// 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4): lane
-// l's bytes land at l * 16 past the wave-uniform LDS address. Compiled in the device pass
-// only: in the host pass the builtin makes clang drop the kernel's launch stub silently.
-__device__ inline void lds_copy16(const void* g, int8_t* lds) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_global_load_lds(g, (lds_ptr)lds, 16, 0, 0);
-#endif
-}
-
-// Row r of a staged tile is 64 bytes = four 16-byte chunks. Chunk c of row r is stored
-// at chunk position c ^ rowhash(r), so that the 16 rows read together by one fragment
-// load fall in distinct bank groups (for 8- and for 16-lane LDS access phases).
-__device__ inline int rowhash(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
-__device__ inline int swz(int r, int c) { return r * BK + ((c ^ rowhash(r)) << 4); }
 
 // 4 bytes per lane from global memory straight into LDS (global_load_lds_dword): lane l's
 // word lands at l * 4 past the wave-uniform LDS address.
@@ -199,164 +178,6 @@ __device__ __forceinline__ void store_tile(const i32x16 (&acc)[FM][FN], bool has
     }
 }
 
-// One output tile of BM x BN (BM = 256 or 128, BN = 256) computed by the workgroup's 4
-// waves laid out 2 x 2; each wave owns (BM/2) x (BN/2) = FM x FN blocks of 32 x 32
-// accumulators (v_mfma_i32_32x32x32_i8, 16 int32 per lane each). K advances BK = 64
-// bytes per step through a ring of STAGES LDS buffers (two 32-deep k-substeps per step).
-template <int BM, int BN, int STAGES, int YMODE>
-__device__ __forceinline__ void gemm_tile(const int8_t* __restrict__ A, const float* __restrict__ xs,
-                                          const int8_t* __restrict__ B, const float* __restrict__ ws,
-                                          const float* __restrict__ bias, void* __restrict__ Y, int M,
-                                          int N, int K, int m0, int n0, int8_t* smem) {
-    constexpr int WM = BM / 2, WN = BN / 2;
-    constexpr int FM = WM / 32, FN = WN / 32;
-    constexpr int STAGE_A = BM * BK, STAGE = (BM + BN) * BK;
-    constexpr int LA = BM * BK / 16 / NTHR, LB = BN * BK / 16 / NTHR;  // copies per thread
-    constexpr int LOADS = LA + LB;
-    static_assert(STAGES >= 3, "the ring needs a buffer being read, one landing, one free");
-    static_assert(STAGES * STAGE <= RING_BYTES, "the ring fits its LDS");
-
-    const int t = threadIdx.x, lane = t & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
-    const int KT = K / BK;
-
-    // Global -> LDS copy. Wave w fills a contiguous run of 16-byte slots of each operand's
-    // stage, 64 slots per instruction; lane l of an instruction lands in slot base + l.
-    // Slot s holds row s >> 2 at chunk position s & 3, i.e. logical chunk
-    // (s & 3) ^ rowhash(row). Rows past M or N are clamped to the last row (their results
-    // are never stored).
-    const int8_t* ga[LA];
-    const int8_t* gb[LB];
-#pragma unroll
-    for (int i = 0; i < LA; ++i) {
-        const int slot = wave * (LA * 64) + i * 64 + lane;
-        const int r = slot >> 2, c = (slot & 3) ^ rowhash(slot >> 2);
-        ga[i] = A + (int64_t)min(m0 + r, M - 1) * K + c * 16;
-    }
-#pragma unroll
-    for (int i = 0; i < LB; ++i) {
-        const int slot = wave * (LB * 64) + i * 64 + lane;
-        const int r = slot >> 2, c = (slot & 3) ^ rowhash(slot >> 2);
-        gb[i] = B + (int64_t)min(n0 + r, N - 1) * K + c * 16;
-    }
-    // Copies stage kt (its K columns clamped to the last stage) into ring buffer kt % STAGES.
-    auto issue = [&](int kt) {
-        int8_t* st = smem + (kt % STAGES) * STAGE;
-        const int k0 = min(kt, KT - 1) * BK;
-#pragma unroll
-        for (int i = 0; i < LA; ++i)
-            lds_copy16(ga[i] + k0, st + (wave * LA + i) * 1024);
-#pragma unroll
-        for (int i = 0; i < LB; ++i)
-            lds_copy16(gb[i] + k0, st + STAGE_A + (wave * LB + i) * 1024);
-    };
-
-    i32x16 acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-                acc[i][j][e] = 0;
-
-    // Fragment reads: for k-substep ks, lane l takes row (l & 31) of a 32-row block and
-    // logical chunk 2 ks + (l >> 5) of the 64-byte step; A and B use the same
-    // k <-> (lane, byte) assignment, so their products pair the same k. rowhash depends on
-    // the low 4 row bits only, so a wave's blocks are one base address plus multiples of 2 KB.
-    const int fa_off = wm * WM * BK, fb_off = STAGE_A + wn * WN * BK;
-    const int fr = lane & 31;
-    const int f_off0 = swz(fr, lane >> 5), f_off1 = swz(fr, 2 + (lane >> 5));
-    typedef i32x4 Frag[2][FM + FN];   // [ks][A blocks then B blocks]
-    auto read_frags = [&](int kt, Frag& f) {
-        const int8_t* st = smem + (kt % STAGES) * STAGE;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int fo = ks ? f_off1 : f_off0;
-            // B first: the next step's first MFMAs use A block 0 with every B block
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-                f[ks][FM + j] = *reinterpret_cast<const i32x4*>(st + fb_off + fo + j * 32 * BK);
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-                f[ks][i] = *reinterpret_cast<const i32x4*>(st + fa_off + fo + i * 32 * BK);
-        }
-    };
-    auto mfmas = [&](const Frag& f) {
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f[ks][i], f[ks][FM + j], acc[i][j], 0, 0, 0);
-    };
-
-    // Step kt: wait until stage kt+1 has landed (only the copies of the stages after it
-    // may still be pending), barrier, issue stage kt+STAGES-1 into the buffer that held
-    // stage kt-1 (every wave consumed those fragments before the barrier), read stage
-    // kt+1's fragments, and run stage kt's MFMAs with the copies and reads spread among
-    // them. Past the last stage the copies repeat the last stage (the buffers they fill
-    // are never read), so every step has the same shape. sched_barrier(0) keeps steps
-    // from being interleaved with each other. Before step kt's wait, stages
-    // 0 .. kt+STAGES-2 have been issued.
-    constexpr int NMF = 2 * FM * FN, NDS = 2 * (FM + FN);
-    auto step = [&](int kt, const Frag& cur, Frag& nxt) {
-        __builtin_amdgcn_s_waitcnt(vmcnt_le((STAGES - 3) * LOADS));
-        barrier_no_fence();
-        __builtin_amdgcn_sched_barrier(0);
-        issue(kt + STAGES - 1);
-        read_frags(kt + 1, nxt);
-        mfmas(cur);
-#pragma unroll
-        for (int g = 0; g < LOADS; ++g) {
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                  // VMEM (copy)
-            __builtin_amdgcn_sched_group_barrier(0x100, NDS / LOADS, 0);        // DS read
-            __builtin_amdgcn_sched_group_barrier(0x008, NMF / LOADS, 0);        // MFMA
-        }
-        __builtin_amdgcn_sched_group_barrier(0x100, NDS % LOADS, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, NMF % LOADS, 0);
-        __builtin_amdgcn_sched_barrier(0);
-    };
-
-    // Steps run in pairs over two fragment register sets. With an odd number of steps a
-    // virtual step -1 of zero fragments comes first. Before the first step k0 the copies
-    // of stages k0+1 .. k0+STAGES-2 are the ones pending.
-    if constexpr (YMODE != Y_I32)
-        issue_scales(xs, ws, bias, M, N, m0, n0, wave, lane, smem);
-    Frag f0, f1;
-    int k0;
-    if (KT & 1) {
-        k0 = -1;
-#pragma unroll
-        for (int s = 0; s < STAGES - 2; ++s)
-            issue(s);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int i = 0; i < FM + FN; ++i)
-                f0[ks][i] = i32x4{0, 0, 0, 0};
-    } else {
-        k0 = 0;
-#pragma unroll
-        for (int s = 0; s < STAGES - 1; ++s)
-            issue(s);
-        __builtin_amdgcn_s_waitcnt(vmcnt_le((STAGES - 2) * LOADS));
-        barrier_no_fence();
-        read_frags(0, f0);
-    }
-    for (int kt = k0; kt < KT; kt += 2) {
-        step(kt, f0, f1);
-        step(kt + 1, f1, f0);   // reads past the end on the last pair: never used
-    }
-    // No copy into LDS may still be in flight when the workgroup's LDS is released.
-    __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
-
-    store_tile<WM, WN, FM, FN, YMODE, 4>(acc, bias != nullptr, Y, M, N, m0 + wm * WM, n0 + wn * WN, wm * WM,
-                                         wn * WN, wave, lane, smem);
-}
-
 // Rows of 128 bytes (eight 16-byte chunks): chunk c of row r is stored at chunk position
 // c ^ h128(r), which differs across any 8 consecutive rows and, with the row parity,
 // across any 16, so the rows one fragment read touches fall in distinct bank groups.
@@ -371,166 +192,7 @@ __device__ inline void lds_copy16_buf(__amdgpu_buffer_rsrc_t r, int voff, int so
 #endif
 }
 
-// The same tile with 128-byte k-steps (for K % 128 == 0): each copied row piece is a whole
-// 128-byte line, which the L2 -> CU path delivers at about twice the rate of half lines.
-// Two LDS stages of (BM + BN) x 128 bytes. The workgroup's WGM x WGN waves each own a
-// (BM / WGM) x (BN / WGN) block; with 8 waves (two per SIMD) a wave's block is half as
-// wide, which costs half again as many LDS fragment reads per multiply, but two waves per
-// SIMD issue LDS reads about twice as fast as one and cover each other's waits.
-// Fragments are read two 32-deep substeps ahead of the MFMAs that use them (four
-// fragment register sets), so an LDS read has two substeps to return. Halfway through
-// stage kt every fragment of stage kt has been read: each wave waits for its own LDS
-// reads and for its copies of stage kt + 1, and after a barrier stage kt's buffer takes
-// the copies of stage kt + 2 while the reads move on to stage kt + 1.
-template <int BM, int BN, int WGM, int WGN, int YMODE>
-__device__ __forceinline__ void gemm_tile128(const int8_t* __restrict__ A, const float* __restrict__ xs,
-                                             const int8_t* __restrict__ B, const float* __restrict__ ws,
-                                             const float* __restrict__ bias, void* __restrict__ Y,
-                                             int M, int N, int K, int m0, int n0, int8_t* smem) {
-    constexpr int BKL = 128;
-    constexpr int NWV = WGM * WGN, NT = 64 * NWV;
-    constexpr int WM = BM / WGM, WN = BN / WGN;
-    constexpr int FM = WM / 32, FN = WN / 32;
-    constexpr int STAGE_A = BM * BKL, STAGE = (BM + BN) * BKL;
-    constexpr int LA = BM * BKL / 16 / NT, LB = BN * BKL / 16 / NT;  // copies per thread
-    constexpr int LOADS = LA + LB;
-    static_assert(LA * 16 * NT == BM * BKL && LB * 16 * NT == BN * BKL, "copies divide evenly");
-    static_assert(2 * STAGE <= RING_BYTES, "two stages fit the LDS allocation");
-
-    const int t = threadIdx.x, lane = t & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int wm = wave / WGN, wn = wave % WGN;
-    const int KT = K / BKL;
-
-    // Copy slots: slot s holds row s >> 3 at chunk position s & 7, i.e. logical chunk
-    // (s & 7) ^ h128(row); lane l of an instruction lands in slot base + l. Rows past M or
-    // N are clamped to the last row (their results are never stored). The descriptors
-    // start at the tile's first row, so offsets stay below 256 K bytes.
-    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<int8_t*>(A) + (int64_t)m0 * K, 0, (int)((int64_t)(M - m0 < BM ? M - m0 : BM) * K), 0x00020000);
-    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<int8_t*>(B) + (int64_t)n0 * K, 0, (int)((int64_t)(N - n0 < BN ? N - n0 : BN) * K), 0x00020000);
-    int va[LA], vb[LB];
-#pragma unroll
-    for (int i = 0; i < LA; ++i) {
-        const int slot = wave * (LA * 64) + i * 64 + lane;
-        const int r = slot >> 3, c = (slot & 7) ^ h128(slot >> 3);
-        va[i] = min(r, M - 1 - m0) * K + c * 16;
-    }
-#pragma unroll
-    for (int i = 0; i < LB; ++i) {
-        const int slot = wave * (LB * 64) + i * 64 + lane;
-        const int r = slot >> 3, c = (slot & 7) ^ h128(slot >> 3);
-        vb[i] = min(r, N - 1 - n0) * K + c * 16;
-    }
-    // Copies q0 .. q1 - 1 (A's then B's) of stage kt (clamped to the last stage) into
-    // buffer kt & 1.
-    auto issue_part = [&](int kt, int q0, int q1) {
-        int8_t* st = smem + (kt & 1) * STAGE;
-        const int k0 = __builtin_amdgcn_readfirstlane(min(kt, KT - 1) * BKL);
-#pragma unroll
-        for (int q = q0; q < q1; ++q) {
-            if (q < LA)
-                lds_copy16_buf(ra, va[q], k0, st + (wave * LA + q) * 1024);
-            else
-                lds_copy16_buf(rb, vb[q - LA], k0, st + STAGE_A + (wave * LB + q - LA) * 1024);
-        }
-    };
-    auto issue = [&](int kt) { issue_part(kt, 0, LOADS); };
-
-    i32x16 acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-                acc[i][j][e] = 0;
-
-    // Fragment of substep u (stage u >> 2, k-substep u & 3): lane l takes row (l & 31) of a
-    // 32-row block and logical chunk 2 (u & 3) + (l >> 5); A and B use the same
-    // k <-> (lane, byte) assignment. h128 depends on the low 4 row bits only.
-    const int lr = lane & 31;
-    const int fa_base = wm * WM * BKL + lr * BKL, fb_base = STAGE_A + wn * WN * BKL + lr * BKL;
-    typedef i32x4 Frag[FM + FN];   // A blocks then B blocks
-    auto read = [&](int u, Frag& f) {
-        const int8_t* st = smem + ((u >> 2) & 1) * STAGE;
-        const int co = ((2 * (u & 3) + (lane >> 5)) ^ h128(lr)) << 4;
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-            f[FM + j] = *reinterpret_cast<const i32x4*>(st + fb_base + co + j * 32 * BKL);
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-            f[i] = *reinterpret_cast<const i32x4*>(st + fa_base + co + i * 32 * BKL);
-    };
-    auto mfma = [&](const Frag& f) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f[i], f[FM + j], acc[i][j], 0, 0, 0);
-    };
-    constexpr int NMF = FM * FN, NDS = FM + FN;
-    constexpr int CPS = (LOADS + 3) / 4;   // copies per substep when a stage's are spread over 4
-    // A substep: the MFMAs of substep u with the reads of substep u + 2 and copies
-    // q0 .. q1 - 1 of stage kc spread among them, so that neither the LDS queue nor the
-    // copy path takes a burst that would hold up the wave's MFMA issue.
-    auto sub = [&](int u, const Frag& cur, Frag& ahead, int kc, int q0, int q1) {
-        read(u + 2, ahead);
-        issue_part(kc, q0, q1);
-        mfma(cur);
-        constexpr int G = NDS / 2, Q = NMF / G;
-#pragma unroll
-        for (int g = 0; g < G - 1; ++g) {
-            __builtin_amdgcn_sched_group_barrier(0x008, Q, 0);   // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM (copy), if any
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS read
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, NMF - (G - 1) * Q, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, CPS, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, NDS - (G - 1) * 2, 0);
-        __builtin_amdgcn_sched_barrier(0);
-    };
-
-    if constexpr (YMODE != Y_I32)
-        issue_scales(xs, ws, bias, M, N, m0, n0, wave, lane, smem);
-    issue(0);
-    issue(1);
-    __builtin_amdgcn_s_waitcnt(vmcnt_le(LOADS) & ~(0xF << 8));   // stage 0 landed (this wave's copies)
-    barrier_no_fence();
-    Frag f0, f1, f2, f3;
-    read(0, f0);
-    read(1, f1);
-    sub(0, f0, f2, 0, 0, 0);
-    sub(1, f1, f3, 0, 0, 0);
-    // Each iteration runs the second half of stage kt and the first half of stage kt + 1.
-    // It starts right after a wait and barrier that leave no LDS read pending (so the
-    // compiler's waits inside count exactly): stage kt + 1 is complete in LDS and stage
-    // kt is fully read, so its buffer takes the copies of stage kt + 2.
-    __builtin_amdgcn_s_waitcnt(vmcnt_le(0) & ~(0xF << 8));   // vmcnt(0) lgkmcnt(0)
-    barrier_no_fence();
-    for (int kt = 0; kt + 1 < KT; ++kt) {
-        const int u = 4 * kt;
-        // stage kt + 2's copies, a quarter per substep (past the end they repeat the last
-        // stage, never read)
-        sub(u + 2, f2, f0, kt + 2, 0, CPS);
-        sub(u + 3, f3, f1, kt + 2, CPS, min(2 * CPS, LOADS));
-        sub(u + 4, f0, f2, kt + 2, min(2 * CPS, LOADS), min(3 * CPS, LOADS));
-        sub(u + 5, f1, f3, kt + 2, min(3 * CPS, LOADS), LOADS);
-        __builtin_amdgcn_s_waitcnt(vmcnt_le(0) & ~(0xF << 8));
-        barrier_no_fence();
-    }
-    // the last stage's second half
-    mfma(f2);
-    mfma(f3);
-    // No copy into LDS may still be in flight when the LDS is reused or released.
-    __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
-    store_tile<WM, WN, FM, FN, YMODE, NWV>(acc, bias != nullptr, Y, M, N, m0 + wm * WM, n0 + wn * WN,
-                                           wm * WM, wn * WN, wave, lane, smem);
-}
-
-// A BM x BN tile (256 x 256 or 128 x 256) on 8 waves with a ping-pong schedule
-// (K % 128 == 0). Waves 0-3
+// A BM x BN tile on 8 waves with a ping-pong schedule. Waves 0-3
 // (group 0) and 4-7 (group 1) put one wave of each group on every SIMD, and the two
 // groups alternate between phases separated by workgroup barriers: in each phase one
 // group issues nothing but the 32 MFMAs of a whole 128-deep stage (its fragments already
@@ -561,7 +223,7 @@ __device__ __forceinline__ void gemm_tile_pp(const int8_t* __restrict__ A, const
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int grp = wave >> 2, q = wave & 3;
     const int wm = wave & 1, wn = wave >> 1;
-    const int KT = K / BKL;
+    const int KT = (K + BKL - 1) / BKL;   // the last stage may be half deep (K % 128 == 64)
 
     // Group-0 wave q copies rows (BM / 4) q .. of A and (BN / 4) q .. of B: copy c moves 8
     // rows x 128 bytes, lane l row R q + 8 c + (l >> 3), logical chunk (l & 7) ^ h128(row)
@@ -580,18 +242,22 @@ __device__ __forceinline__ void gemm_tile_pp(const int8_t* __restrict__ A, const
     const int cx = (lane & 7) ^ ((lane >> 3) & 7);
     const int va0 = cra * K + (cx << 4), va1 = cra * K + ((cx ^ 1) << 4);
     const int vb0 = crb * K + (cx << 4), vb1 = crb * K + ((cx ^ 1) << 4);
+    // The lane's logical chunk is cx ^ (c & 1): in the upper half (k 64..127 of the stage)
+    // exactly when cx >= 4. A half-deep last stage reads zeros there.
+    const bool tail_hi = (K & (BKL - 1)) != 0 && cx >= 4;
     auto copies = [&](int kt, int buf) {
         int8_t* st = smem + buf * STAGE;
+        const bool cut = tail_hi && kt == KT - 1;
 #pragma unroll
         for (int c = 0; c < CA; ++c) {
             const int so = __builtin_amdgcn_readfirstlane(kt * BKL + 8 * c * K);
-            lds_copy16_buf(ra, cra + 8 * c < rows_a ? ((c & 1) ? va1 : va0) : 0x7FFFFFF0, so,
+            lds_copy16_buf(ra, cra + 8 * c < rows_a && !cut ? ((c & 1) ? va1 : va0) : 0x7FFFFFF0, so,
                            st + ((BM / 4) * q + 8 * c) * BKL);
         }
 #pragma unroll
         for (int c = 0; c < CB; ++c) {
             const int so = __builtin_amdgcn_readfirstlane(kt * BKL + 8 * c * K);
-            lds_copy16_buf(rb, crb + 8 * c < rows_b ? ((c & 1) ? vb1 : vb0) : 0x7FFFFFF0, so,
+            lds_copy16_buf(rb, crb + 8 * c < rows_b && !cut ? ((c & 1) ? vb1 : vb0) : 0x7FFFFFF0, so,
                            st + STAGE_A + ((BN / 4) * q + 8 * c) * BKL);
         }
     };
@@ -682,7 +348,7 @@ __device__ __forceinline__ void gemm_tile_pp(const int8_t* __restrict__ A, const
                                          wm * WM, wn * WN, wave, lane, smem);
 }
 
-// A 128 x 256 tile on 8 waves with K split between two groups (K % 128 == 0). Group 0
+// A 128 x 256 tile on 8 waves with K split between two groups. Group 0
 // (waves 0-3) accumulates the even 128-deep stages and group 1 (waves 4-7) the odd ones,
 // each over the whole tile with a 2 x 2 arrangement of 64 x 128 wave blocks, so one wave
 // of each group sits on every SIMD. Stage j is computed in phase j: its group issues only
@@ -705,7 +371,7 @@ __device__ __forceinline__ void gemm_tile_ks(const int8_t* __restrict__ A, const
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int grp = wave >> 2, q = wave & 3;
     const int wm = q & 1, wn = q >> 1;
-    const int KT = K / BKL;
+    const int KT = (K + BKL - 1) / BKL;   // the last stage may be half deep (K % 128 == 64)
 
     // Copies (either group, in its reading phase): wave q moves rows 32 q .. of A and
     // 64 q .. of B; copy c is 8 rows x 128 bytes, lane l row R q + 8 c + (l >> 3), whose
@@ -720,19 +386,21 @@ __device__ __forceinline__ void gemm_tile_ks(const int8_t* __restrict__ A, const
     const int cx = (lane & 7) ^ ((lane >> 3) & 7);
     const int va0 = cra * K + (cx << 4), va1 = cra * K + ((cx ^ 1) << 4);
     const int vb0 = crb * K + (cx << 4), vb1 = crb * K + ((cx ^ 1) << 4);
+    const bool tail_hi = (K & (BKL - 1)) != 0 && cx >= 4;   // upper half of a half-deep last stage
     auto copies = [&](int kt) {
         int8_t* st = smem + (kt % 3) * STAGE;
         const int kc = min(kt, KT - 1);
+        const bool cut = tail_hi && kc == KT - 1;
 #pragma unroll
         for (int c = 0; c < CA; ++c) {
             const int so = __builtin_amdgcn_readfirstlane(kc * BKL + 8 * c * K);
-            lds_copy16_buf(ra, cra + 8 * c < rows_a ? ((c & 1) ? va1 : va0) : 0x7FFFFFF0, so,
+            lds_copy16_buf(ra, cra + 8 * c < rows_a && !cut ? ((c & 1) ? va1 : va0) : 0x7FFFFFF0, so,
                            st + ((BM / 4) * q + 8 * c) * BKL);
         }
 #pragma unroll
         for (int c = 0; c < CB; ++c) {
             const int so = __builtin_amdgcn_readfirstlane(kc * BKL + 8 * c * K);
-            lds_copy16_buf(rb, crb + 8 * c < rows_b ? ((c & 1) ? vb1 : vb0) : 0x7FFFFFF0, so,
+            lds_copy16_buf(rb, crb + 8 * c < rows_b && !cut ? ((c & 1) ? vb1 : vb0) : 0x7FFFFFF0, so,
                            st + STAGE_A + ((BN / 4) * q + 8 * c) * BKL);
         }
     };
@@ -879,37 +547,21 @@ struct TilePlan {
     int tiles_m_big, nbig, tiles_m_small, nsmall, n_small0;
 };
 
-// K % 128 == 0 runs 8 waves (2 x 4) per workgroup on the 128-byte path; other K run 4
-// waves (2 x 2) on the 64-byte ring.
-template <int YMODE, bool K128, int NWV>
-__global__ __launch_bounds__(64 * NWV, 1) void gemm_w8a8_kernel(
+template <int YMODE>
+__global__ __launch_bounds__(64 * NWAVES, 1) void gemm_w8a8_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ xs, const int8_t* __restrict__ B,
     const float* __restrict__ ws, const float* __restrict__ bias, void* __restrict__ Y, int M,
     int N, int K, TilePlan plan) {
-    static_assert(K128 || NWV == 4, "the 64-byte ring runs 4 waves");
-    constexpr int WGM = 2, WGN = NWV / 2;
     __shared__ __attribute__((aligned(1024))) int8_t smem[RING_BYTES + SCALE_BYTES];
     const int bid = blockIdx.x;
     if (bid < plan.nbig) {
         const int tile = xcd_remap(bid, plan.nbig);
         const int tn = tile / plan.tiles_m_big, tm = tile - tn * plan.tiles_m_big;
-        if constexpr (K128 && NWV == 8 && GEMM_PINGPONG)
-            gemm_tile_pp<256, 256, YMODE>(A, xs, B, ws, bias, Y, M, N, K, tm * 256, tn * 256, smem);
-        else if constexpr (K128)
-            gemm_tile128<256, 256, WGM, WGN, YMODE>(A, xs, B, ws, bias, Y, M, N, K, tm * 256, tn * 256, smem);
-        else
-            gemm_tile<256, 256, 4, YMODE>(A, xs, B, ws, bias, Y, M, N, K, tm * 256, tn * 256, smem);
+        gemm_tile_pp<256, 256, YMODE>(A, xs, B, ws, bias, Y, M, N, K, tm * 256, tn * 256, smem);
     } else {
         const int tile = xcd_remap(bid - plan.nbig, plan.nsmall);
         const int tn = tile / plan.tiles_m_small, tm = tile - tn * plan.tiles_m_small;
-        if constexpr (K128 && NWV == 8 && GEMM_PINGPONG)
-            gemm_tile_ks<YMODE>(A, xs, B, ws, bias, Y, M, N, K, tm * 128, plan.n_small0 + tn * 256, smem);
-        else if constexpr (K128)
-            gemm_tile128<128, 256, WGM, WGN, YMODE>(A, xs, B, ws, bias, Y, M, N, K, tm * 128,
-                                                    plan.n_small0 + tn * 256, smem);
-        else
-            gemm_tile<128, 256, 5, YMODE>(A, xs, B, ws, bias, Y, M, N, K, tm * 128,
-                                          plan.n_small0 + tn * 256, smem);
+        gemm_tile_ks<YMODE>(A, xs, B, ws, bias, Y, M, N, K, tm * 128, plan.n_small0 + tn * 256, smem);
     }
 }
 
@@ -954,22 +606,20 @@ ql_status launch_gemm_w8a8(const int8_t* xq, const float* x_scale, const int8_t*
     if (M == 0 || N == 0)
         return QL_OK;
     const TilePlan plan = plan_tiles(M, N);
-    const dim3 grid((unsigned)(plan.nbig + plan.nsmall));
+    const dim3 grid((unsigned)(plan.nbig + plan.nsmall)), block(64 * NWAVES);
     const int m = (int)M, n = (int)N, k = (int)K;
-#define QL_LAUNCH(MODE, K128)                                                                   \
-    hipLaunchKernelGGL((gemm_w8a8_kernel<MODE, K128, K128 ? GEMM_WAVES_K128 : 4>), grid,          \
-                       dim3(64 * (K128 ? GEMM_WAVES_K128 : 4)), 0, stream, xq, x_scale, wq,        \
-                       w_scale, bias, y, m, n, k, plan)
-    const bool k128 = K % 128 == 0;
+#define QL_LAUNCH(MODE)                                                                          \
+    hipLaunchKernelGGL((gemm_w8a8_kernel<MODE>), grid, block, 0, stream, xq, x_scale, wq, w_scale, \
+                       bias, y, m, n, k, plan)
     switch (y_mode) {
     case Y_F32:
-        if (k128) QL_LAUNCH(Y_F32, true); else QL_LAUNCH(Y_F32, false);
+        QL_LAUNCH(Y_F32);
         break;
     case Y_F16:
-        if (k128) QL_LAUNCH(Y_F16, true); else QL_LAUNCH(Y_F16, false);
+        QL_LAUNCH(Y_F16);
         break;
     default:
-        if (k128) QL_LAUNCH(Y_I32, true); else QL_LAUNCH(Y_I32, false);
+        QL_LAUNCH(Y_I32);
         break;
     }
 #undef QL_LAUNCH
