@@ -4,9 +4,10 @@
 // producers of the block-asymmetric uint8 and per-group int4 weight formats.
 //
 // All are HBM-bound streaming kernels: each element is read once from HBM and its code
-// written once. Codes are decided in fp32 with correctly rounded division (this file is
-// compiled without fast-math, so `a / b` is the IEEE quotient) and v_rndne (rintf,
-// round half to even), the precision and rounding of the definitions:
+// written once. Codes are decided in fp32 from the correctly rounded quotient (this file
+// is compiled without fast-math, so `a / b` is the IEEE quotient; the per-row kernel
+// reaches the same quotient through the row's reciprocal, see code_u8_biased) and
+// v_rndne (rintf, round half to even), the precision and rounding of the definitions:
 //   scale = max|x| / 127, q = round(x / scale), codes in [-127, 127]
 //       2048ai.net INT8 Llama-2-7B write-up §2.2; quant67.com ch.17 §二
 //   absmax along the row, clamp_min(1e-10), torch.round (half to even)
@@ -34,10 +35,18 @@ __device__ inline float block_max(float v, float* red) {
     return r;
 }
 
-__device__ inline int8_t code_i8(float x, float s) {
-    float r = rintf(x / s);
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
-    return (int8_t)(int)r;
+// rint(x / s) clamped to [-127, 127], as (code + 128) in the byte `sel` of `acc`.
+// x / s is taken as q0 = RN(x * y), r = x - q0 * s (exact, one fma), RN(q0 + r * y) with
+// y = RN(1 / s) divided once per row: Markstein's theorem on division through a correctly
+// rounded reciprocal makes that the correctly rounded quotient (a zero may change sign,
+// which no code sees), so the code is the one the IEEE quotient gives, at three
+// operations instead of a full division.
+__device__ inline uint32_t code_u8_biased(float x, float s, float y, uint32_t sel, uint32_t acc) {
+    const float q0 = __fmul_rn(x, y);
+    const float r = fmaf(-q0, s, x);
+    const float q = rintf(fmaf(r, y, q0));
+    const float c = __builtin_amdgcn_fmed3f(q, -127.0f, 127.0f) + 128.0f;
+    return __builtin_amdgcn_cvt_pk_u8_f32(c, sel, acc);
 }
 
 // One 16-byte chunk of input as fp32 values: 8 fp16 or 4 fp32 elements.
@@ -65,15 +74,16 @@ struct Chunk {
             a = fmaxf(a, fabsf(v[i]));
         return a;
     }
-    __device__ inline void store_codes(int8_t* q, float s) const {
+    // y = 1 / s, correctly rounded.
+    __device__ inline void store_codes(int8_t* q, float s, float y) const {
         uint32_t w[E / 4];
 #pragma unroll
         for (int j = 0; j < E / 4; ++j) {
             uint32_t b = 0;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                b |= (uint32_t)(uint8_t)code_i8(v[4 * j + i], s) << (8 * i);
-            w[j] = b;
+                b = code_u8_biased(v[4 * j + i], s, y, i, b);
+            w[j] = b ^ 0x80808080u;   // code + 128 -> two's complement code
         }
         if constexpr (E == 8)
             *reinterpret_cast<u32x2*>(q) = u32x2{w[0], w[1]};
@@ -108,13 +118,14 @@ __global__ __launch_bounds__(QT) void quant_rows_i8_kernel(const void* __restric
         }
         amax = block_max(amax, red);
         const float s = fmaxf(amax, 1e-10f) / 127.0f;
+        const float y = 1.0f / s;
         if (threadIdx.x == 0)
             scale[row] = s;
 #pragma unroll
         for (int i = 0; i < QMAXC; ++i) {
             const int ch = threadIdx.x + i * QT;
             if (ch < nch)
-                c[i].store_codes(qr + (int64_t)ch * C::E, s);
+                c[i].store_codes(qr + (int64_t)ch * C::E, s, y);
         }
     } else {
         for (int ch = threadIdx.x; ch < nch; ch += QT) {
@@ -124,12 +135,13 @@ __global__ __launch_bounds__(QT) void quant_rows_i8_kernel(const void* __restric
         }
         amax = block_max(amax, red);
         const float s = fmaxf(amax, 1e-10f) / 127.0f;
+        const float y = 1.0f / s;
         if (threadIdx.x == 0)
             scale[row] = s;
         for (int ch = threadIdx.x; ch < nch; ch += QT) {
             C c;
             c.load(xr + (int64_t)ch * 16);
-            c.store_codes(qr + (int64_t)ch * C::E, s);
+            c.store_codes(qr + (int64_t)ch * C::E, s, y);
         }
     }
 }

@@ -1,0 +1,74 @@
+/*
+ * Checks an identity the per-row quantizer kernel relies on (not part of the oracle):
+ * with s a positive binary32 scale, y = RN(1/s) and, for every x,
+ *     q0 = RN(x * y),  r = fma(-q0, s, x) (exact),  q1 = RN(r * y + q0),
+ * q1 equals the correctly rounded quotient RN(x / s) (Markstein's theorem on
+ * division by a correctly rounded reciprocal and an exact remainder), up to the sign
+ * of a zero quotient. The kernel computes one IEEE division per row and three
+ * operations per element instead of one division per element, so its codes
+ * rint(x / s) equal the definition's.
+ *
+ * Domain checked: every finite binary16 x with |x| <= absmax, and random binary32
+ * x with |x| <= absmax, for absmax log-uniform in [1e-10, 65504] (s = absmax / 127).
+ * Usage: quotient_identity <trials>. Exit status 0 iff no mismatch.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+static float from_f16(uint16_t h) {
+    const int sign = h >> 15, e = (h >> 10) & 31, m = h & 1023;
+    float v;
+    if (e == 0)
+        v = ldexpf((float)m, -24);
+    else if (e == 31)
+        return NAN;
+    else
+        v = ldexpf((float)(m | 1024), e - 25);
+    return sign ? -v : v;
+}
+
+static uint64_t state = 88172645463325252ull;
+static uint32_t next(void) {
+    state ^= state << 13;
+    state ^= state >> 7;
+    state ^= state << 17;
+    return (uint32_t)state;
+}
+
+static int same(float a, float b) { return a == b; }   /* +0 == -0 */
+
+int main(int argc, char** argv) {
+    const int trials = argc > 1 ? atoi(argv[1]) : 200;
+    long checked = 0, bad = 0;
+    for (int t = 0; t < trials; ++t) {
+        const double la = log(1e-10) + (log(65504.0) - log(1e-10)) * (next() / 4294967296.0);
+        const float amax = (float)exp(la);
+        volatile float s = fmaxf(amax, 1e-10f) / 127.0f;
+        volatile float y = 1.0f / s;
+        for (uint32_t h = 0; h < 65536 + 4096; ++h) {
+            float x;
+            if (h < 65536) {
+                x = from_f16((uint16_t)h);
+                if (isnan(x) || fabsf(x) > amax)
+                    continue;
+            } else {
+                x = amax * ((float)(next() >> 8) / 16777216.0f) * ((next() & 1) ? 1.0f : -1.0f);
+            }
+            volatile float q = x / s;
+            volatile float q0 = x * y;
+            const float r = fmaf(-q0, s, x);
+            const float q1 = fmaf(r, y, q0);
+            ++checked;
+            if (!same(q, q1)) {
+                if (bad < 5)
+                    printf("mismatch: absmax %a x %a x/s %a identity %a\n", amax, x, (float)q, q1);
+                ++bad;
+            }
+        }
+    }
+    printf("checked %ld quotients, %ld mismatches\n", checked, bad);
+    return bad != 0;
+}
