@@ -15,9 +15,9 @@
 // v_mfma_i32_32x32x32_i8. K advances 128 bytes per stage through LDS buffers filled by
 // direct buffer -> LDS copies (no register staging), whole 128-byte row pieces. The tile
 // size is set by L2 -> CU bandwidth: a tile moves (BM + BN) bytes per k for BM * BN
-// multiply-adds. The two 4-wave groups alternate between MFMA phases and phases of LDS
-// fragment reads and copies, so a SIMD's MFMA stream never waits behind its own memory
-// instructions. When the last round of 256 x 256 tiles would leave CUs idle, its N
+// multiply-adds. The two 4-wave groups alternate between MFMA phases (with the copies
+// spread between the MFMAs) and phases of LDS fragment reads, so a SIMD's MFMA stream
+// never waits behind its own LDS reads. When the last round of 256 x 256 tiles would leave CUs idle, its N
 // panels run as 128 x 256 tiles whose K is split between the two groups. K % 128 == 64
 // runs a last stage whose upper half reads zeros.
 #include "ql_internal.h"
@@ -192,21 +192,52 @@ __device__ inline void lds_copy16_buf(__amdgpu_buffer_rsrc_t r, int voff, int so
 #endif
 }
 
+// Copies of a stage spread over the nm MFMAs of a phase: the index of the copy issued right
+// after MFMA n when nc copies are spread evenly, or -1.
+constexpr int spread_slot(int n, int nc, int nm) {
+    for (int c = 0; c < nc; ++c)
+        if ((c * nm) / nc == n)
+            return c;
+    return -1;
+}
+
+// Vector offset of one lane's 16 bytes of a stage copy: v (the lane's row times K plus its
+// chunk) + so (the k-step and the copy's 8-row step, wave-uniform). The row goes into the
+// vector offset, so a row past the descriptor's end is out of range (the hardware returns
+// zeros) whether or not the range check counts the scalar offset. `hi` (2^30 for a lane
+// whose chunk lies in the upper half of the stage when K % 128 == 64, else 0) masked by
+// `cutm` (all ones for the last stage) sends the lane out of range too: a half-deep last
+// stage reads zeros above its 64 bytes. Offsets stay below 2^31.
+__device__ inline int copy_voff(int v, int so, int hi, int cutm) { return (v + so) | (hi & cutm); }
+
+// The wave-uniform part of a copy offset, opaque to the compiler: otherwise it splits off
+// the loop-invariant 8-row step and keeps one hoisted vector offset per copy alive across
+// the K loop, which costs registers the fragments need.
+__device__ inline int stage_soff(int v) {
+    asm volatile("" : "+s"(v));
+    return v;
+}
+
 // A BM x BN tile on 8 waves with a ping-pong schedule. Waves 0-3
 // (group 0) and 4-7 (group 1) put one wave of each group on every SIMD, and the two
 // groups alternate between phases separated by workgroup barriers: in each phase one
-// group issues nothing but the 32 MFMAs of a whole 128-deep stage (its fragments already
-// in registers), while the other group reads the next stage's fragments from LDS and,
-// for group 0, issues the copies of the stage after. The MFMA stream of a SIMD then never
-// waits behind an LDS or copy instruction of its own wave. Wave w owns the (BM / 2) x
-// (BN / 4) block at rows (BM / 2) (w & 1), columns (BN / 4) (w >> 1).
+// group issues the 32 MFMAs of a whole 128-deep stage (its fragments already in
+// registers) with a share of the copies spread between them, while the other group reads
+// the next stage's fragments from LDS. The MFMA stream of a SIMD then never waits behind
+// an LDS read of its own wave, and the copies' address work in the texture unit (16
+// bytes a lane, one copy every ~16 clocks per CU) is spread over the whole stage. Wave w
+// owns the (BM / 2) x (BN / 4) block at rows (BM / 2) (w & 1), columns (BN / 4) (w >> 1):
+// group 0 reads all of A and the low half of B's columns, group 1 all of A and the high
+// half, so the three parts of a stage buffer (A, B low, B high) are free at different
+// times.
 //
-// Phase 2j:   group 0 runs stage j's MFMAs, then waits for its copies of stage j + 1;
-//             group 1 reads stage j's fragments.
-// Phase 2j+1: group 0 issues the copies of stage j + 2 into stage j's buffer (stage j
-//             was read in phases 2j - 1 and 2j) and reads stage j + 1's fragments;
-//             group 1 runs stage j's MFMAs.
-// Copies thus have two phases (one stage of MFMA time) to land.
+// Phase 2j (A_j):    group 0 runs stage j's MFMAs, copying B high of stage j + 1 and B low
+//                    of stage j + 2; group 1 reads stage j.
+// Phase 2j+1 (B_j):  group 0 reads stage j + 1; group 1 runs stage j's MFMAs, copying A
+//                    of stage j + 2.
+// Each part is refilled only after both of its reads are done (barriers between) and its
+// copies land at least one phase before its first read: group 0 waits for its copies at
+// the end of B_j, group 1 at the end of A_{j+1}.
 template <int BM, int BN, int YMODE>
 __device__ __forceinline__ void gemm_tile_pp(const int8_t* __restrict__ A, const float* __restrict__ xs,
                                              const int8_t* __restrict__ B, const float* __restrict__ ws,
@@ -215,9 +246,11 @@ __device__ __forceinline__ void gemm_tile_pp(const int8_t* __restrict__ A, const
     constexpr int BKL = 128;
     constexpr int WM = BM / 2, WN = BN / 4, FM = WM / 32, FN = WN / 32;
     constexpr int STAGE_A = BM * BKL, STAGE = (BM + BN) * BKL;
-    constexpr int CA = BM / 32, CB = BN / 32;   // copies of A and of B per group-0 wave (8 rows each)
+    constexpr int CA = BM / 32, CH = BN / 64;   // per wave: copies of A, and of each half of B (8 rows each)
     static_assert(2 * STAGE <= RING_BYTES, "two stages fit the LDS allocation");
-    static_assert(FM >= 1 && FN >= 1 && CA % 2 == 0 && CB % 2 == 0, "tile shape");
+    static_assert(FM >= 1 && FN >= 1 && CA % 2 == 0 && CH % 2 == 0, "tile shape");
+    constexpr int NMF = 4 * FM * FN;
+    static_assert(CA <= NMF && 2 * CH <= NMF, "copies fit between the MFMAs");
 
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -225,41 +258,34 @@ __device__ __forceinline__ void gemm_tile_pp(const int8_t* __restrict__ A, const
     const int wm = wave & 1, wn = wave >> 1;
     const int KT = (K + BKL - 1) / BKL;   // the last stage may be half deep (K % 128 == 64)
 
-    // Group-0 wave q copies rows (BM / 4) q .. of A and (BN / 4) q .. of B: copy c moves 8
-    // rows x 128 bytes, lane l row R q + 8 c + (l >> 3), logical chunk (l & 7) ^ h128(row)
-    // (landing at chunk position l & 7). Rows past M or N read as zeros (outside the
-    // descriptor).
+    // Wave q copies rows (BM / 4) q .. of A, and rows (BN / 8) q .. of each half of B: copy
+    // c moves 8 rows x 128 bytes, lane l row R + 8 c + (l >> 3), logical chunk
+    // (l & 7) ^ h128(row) (landing at chunk position l & 7). Rows past M or N read as zeros
+    // (outside the descriptor).
     const int rows_a = min(M - m0, BM), rows_b = min(N - n0, BN);
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<int8_t*>(A) + (int64_t)m0 * K, 0, rows_a * K, 0x00020000);
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<int8_t*>(B) + (int64_t)n0 * K, 0, rows_b * K, 0x00020000);
-    // Row R q + 8 c + (l >> 3) (R a multiple of 16) has h128 = ((l >> 3) & 7) ^ (c & 1), so
-    // a lane's offset is one of two values plus 8 c rows, which goes with the k-step in the
-    // scalar offset. A row past the descriptor's end gets an offset at or past it (also
-    // with the scalar part added, which stays below 2^31): the hardware returns zeros.
-    const int cra = (BM / 4) * q + (lane >> 3), crb = (BN / 4) * q + (lane >> 3);
+    // Row R + 8 c + (l >> 3) (R a multiple of 16) has h128 = ((l >> 3) & 7) ^ (c & 1), so
+    // a lane's offset is one of two values plus 8 c rows and the k-step.
+    const int cra = (BM / 4) * q + (lane >> 3), crb = (BN / 8) * q + (lane >> 3);
     const int cx = (lane & 7) ^ ((lane >> 3) & 7);
     const int va0 = cra * K + (cx << 4), va1 = cra * K + ((cx ^ 1) << 4);
     const int vb0 = crb * K + (cx << 4), vb1 = crb * K + ((cx ^ 1) << 4);
     // The lane's logical chunk is cx ^ (c & 1): in the upper half (k 64..127 of the stage)
     // exactly when cx >= 4. A half-deep last stage reads zeros there.
-    const bool tail_hi = (K & (BKL - 1)) != 0 && cx >= 4;
-    auto copies = [&](int kt, int buf) {
-        int8_t* st = smem + buf * STAGE;
-        const bool cut = tail_hi && kt == KT - 1;
-#pragma unroll
-        for (int c = 0; c < CA; ++c) {
-            const int so = __builtin_amdgcn_readfirstlane(kt * BKL + 8 * c * K);
-            lds_copy16_buf(ra, cra + 8 * c < rows_a && !cut ? ((c & 1) ? va1 : va0) : 0x7FFFFFF0, so,
-                           st + ((BM / 4) * q + 8 * c) * BKL);
-        }
-#pragma unroll
-        for (int c = 0; c < CB; ++c) {
-            const int so = __builtin_amdgcn_readfirstlane(kt * BKL + 8 * c * K);
-            lds_copy16_buf(rb, crb + 8 * c < rows_b && !cut ? ((c & 1) ? vb1 : vb0) : 0x7FFFFFF0, so,
-                           st + STAGE_A + ((BN / 4) * q + 8 * c) * BKL);
-        }
+    const int hi = (K & (BKL - 1)) != 0 && cx >= 4 ? 0x40000000 : 0;
+    // Copy c of A's rows, or of B's half h, of stage kt into buffer buf; see copy_voff.
+    auto copy_a = [&](int kt, int buf, int c) {
+        const int so = stage_soff(kt * BKL + 8 * c * K);
+        lds_copy16_buf(ra, copy_voff((c & 1) ? va1 : va0, so, hi, kt == KT - 1 ? -1 : 0), 0,
+                       smem + buf * STAGE + ((BM / 4) * q + 8 * c) * BKL);
+    };
+    auto copy_b = [&](int kt, int buf, int h, int c) {
+        const int so = stage_soff(kt * BKL + (h * (BN / 2) + 8 * c) * K);
+        lds_copy16_buf(rb, copy_voff((c & 1) ? vb1 : vb0, so, hi, kt == KT - 1 ? -1 : 0), 0,
+                       smem + buf * STAGE + STAGE_A + (h * (BN / 2) + (BN / 8) * q + 8 * c) * BKL);
     };
 
     i32x16 acc[FM][FN];
@@ -273,42 +299,75 @@ __device__ __forceinline__ void gemm_tile_pp(const int8_t* __restrict__ A, const
 
     // Fragments of a whole stage: F[ks][A blocks then B blocks], ks the 32-deep substep.
     const int lr = lane & 31;
-    const int fa_base = wm * WM * BKL + lr * BKL, fb_base = STAGE_A + wn * WN * BKL + lr * BKL;
+    // Lane l reads row l & 31 of a 32-row block, logical chunk 2 ks + (l >> 5) of substep ks,
+    // stored at chunk position (2 ks + (l >> 5)) ^ h128(row) = ((l >> 5) ^ h128(row)) ^ 2 ks:
+    // substep ks flips bit 5 and 6 of the substep-0 offset. Stage and block bases are
+    // multiples of 128, so they can be added before the flip.
+    const int rbase = lr * BKL + (((lane >> 5) ^ h128(lr)) << 4);
     i32x4 F[4][FM + FN];
     auto read_stage = [&](int kt) {
-        const int8_t* st = smem + (kt & 1) * STAGE;
+        const int sbuf = (kt & 1) * STAGE;
+        const int ta = rbase + stage_soff(sbuf + wm * WM * BKL);
+        const int tb = rbase + stage_soff(sbuf + STAGE_A + wn * WN * BKL);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            const int co = ((2 * ks + (lane >> 5)) ^ h128(lr)) << 4;
+            const int8_t* pa = smem + (ta ^ (ks << 5));
+            const int8_t* pb = smem + (tb ^ (ks << 5));
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-                F[ks][FM + j] = *reinterpret_cast<const i32x4*>(st + fb_base + co + j * 32 * BKL);
+                F[ks][FM + j] = *reinterpret_cast<const i32x4*>(pb + j * 32 * BKL);
 #pragma unroll
             for (int i = 0; i < FM; ++i)
-                F[ks][i] = *reinterpret_cast<const i32x4*>(st + fa_base + co + i * 32 * BKL);
+                F[ks][i] = *reinterpret_cast<const i32x4*>(pa + i * 32 * BKL);
         }
     };
-    auto mfma_stage = [&]() {
+    // A stage's MFMAs with `nc` copies spread evenly between them: copy(c) for c < nc runs
+    // right after MFMA (c * 32) / nc.
+    auto mfma_stage = [&](int nc, auto&& copy) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < FN; ++j)
+                for (int j = 0; j < FN; ++j) {
                     acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(F[ks][i], F[ks][FM + j], acc[i][j], 0, 0, 0);
+                    const int c = spread_slot((ks * FM + i) * FN + j, nc, NMF);
+                    if (c >= 0) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        copy(c);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
     };
+    auto no_copy = [](int) {};
 
+    // Prologue: group 0 copies all of stage 0 and stage 1 but its B high (copied in A_0),
+    // and waits for them.
     if constexpr (YMODE != Y_I32)
         issue_scales(xs, ws, bias, M, N, m0, n0, wave, lane, smem);
     if (grp == 0) {
-        copies(0, 0);
-        copies(min(1, KT - 1), 1);   // with one stage, a second copy of it (never read)
-        __builtin_amdgcn_s_waitcnt(vmcnt_le(CA + CB) & ~(0xF << 8));   // stage 0 landed
+#pragma unroll
+        for (int c = 0; c < CA; ++c)
+            copy_a(0, 0, c);
+#pragma unroll
+        for (int c = 0; c < 2 * CH; ++c)
+            copy_b(0, 0, c / CH, c % CH);
+        if (KT > 1) {
+#pragma unroll
+            for (int c = 0; c < CA; ++c)
+                copy_a(1, 1, c);
+#pragma unroll
+            for (int c = 0; c < CH; ++c)
+                copy_b(1, 1, 0, c);
+        }
+        __builtin_amdgcn_s_waitcnt(vmcnt_le(0) & ~(0xF << 8));
     }
     barrier_no_fence();
-    // Each group runs its own straight-line loop; both execute the same barriers in the
+    // Each group runs its own straight-line loops; both execute the same barriers in the
     // same order (two per stage). sched_barrier keeps the compiler from moving MFMAs (which
-    // the barrier's memory clobber does not pin) from one phase into another.
+    // the barrier's memory clobber does not pin) from one phase into another. Stages near
+    // the end have fewer copies; they run in loops of their own (a branch inside one loop
+    // would make the compiler keep two sets of fragment registers).
     auto phase_end = [&]() {
         __builtin_amdgcn_sched_barrier(0);
         barrier_no_fence();
@@ -318,28 +377,51 @@ __device__ __forceinline__ void gemm_tile_pp(const int8_t* __restrict__ A, const
         read_stage(0);
         __builtin_amdgcn_s_waitcnt(vmcnt_le(63) & ~(0xF << 8));   // lgkmcnt(0)
         phase_end();
-        for (int j = 0; j < KT; ++j) {
-            // phase 2j: stage j's MFMAs, then this wave's copies of stage j + 1 have landed
-            mfma_stage();
-            __builtin_amdgcn_sched_barrier(0);
-            __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
-            phase_end();
-            // phase 2j + 1: copies of stage j + 2 into stage j's buffer, reads of stage j + 1
-            // (past the end they repeat the last stage into the free buffer: never used)
-            copies(min(j + 2, KT - 1), j & 1);
+        // B_j: reads of stage j + 1 (past the end a repeat, never used); this wave's copies
+        // issued in A_j have landed
+        auto read_phase = [&](int j) {
             read_stage(min(j + 1, KT - 1));
-            __builtin_amdgcn_s_waitcnt(vmcnt_le(63) & ~(0xF << 8));   // lgkmcnt(0)
+            __builtin_amdgcn_s_waitcnt(vmcnt_le(0) & ~(0xF << 8));
             phase_end();
+        };
+        int j = 0;
+        for (; j + 2 < KT; ++j) {
+            mfma_stage(2 * CH, [&](int c) {
+                if (c < CH)
+                    copy_b(j + 1, (j + 1) & 1, 1, c);
+                else
+                    copy_b(j + 2, j & 1, 0, c - CH);
+            });
+            phase_end();
+            read_phase(j);
+        }
+        for (; j + 1 < KT; ++j) {
+            mfma_stage(CH, [&](int c) { copy_b(j + 1, (j + 1) & 1, 1, c); });
+            phase_end();
+            read_phase(j);
+        }
+        for (; j < KT; ++j) {
+            mfma_stage(0, no_copy);
+            phase_end();
+            read_phase(j);
         }
     } else {
         phase_end();   // while group 0 reads stage 0
-        for (int j = 0; j < KT; ++j) {
-            // phase 2j: reads of stage j
+        // A_j: reads of stage j; this wave's copies issued in B_{j-1} have landed
+        auto read_phase = [&](int j) {
             read_stage(j);
-            __builtin_amdgcn_s_waitcnt(vmcnt_le(63) & ~(0xF << 8));   // lgkmcnt(0)
+            __builtin_amdgcn_s_waitcnt(vmcnt_le(0) & ~(0xF << 8));
             phase_end();
-            // phase 2j + 1: stage j's MFMAs
-            mfma_stage();
+        };
+        int j = 0;
+        for (; j + 2 < KT; ++j) {
+            read_phase(j);
+            mfma_stage(CA, [&](int c) { copy_a(j + 2, j & 1, c); });
+            phase_end();
+        }
+        for (; j < KT; ++j) {
+            read_phase(j);
+            mfma_stage(0, no_copy);
             phase_end();
         }
     }
@@ -351,10 +433,10 @@ __device__ __forceinline__ void gemm_tile_pp(const int8_t* __restrict__ A, const
 // A 128 x 256 tile on 8 waves with K split between two groups. Group 0
 // (waves 0-3) accumulates the even 128-deep stages and group 1 (waves 4-7) the odd ones,
 // each over the whole tile with a 2 x 2 arrangement of 64 x 128 wave blocks, so one wave
-// of each group sits on every SIMD. Stage j is computed in phase j: its group issues only
-// the stage's 32 MFMAs per wave (fragments already in registers) while the other group
-// reads stage j + 1's fragments from LDS and issues the copies of stage j + 3. Three LDS
-// buffers give the copies two phases to land. At the end group 1's int32 sums are added
+// of each group sits on every SIMD. Stage j is computed in phase j: its group issues the
+// stage's 32 MFMAs per wave (fragments already in registers) with the copies of stage
+// j + 3 spread between them, while the other group reads stage j + 1's fragments from
+// LDS. Three LDS buffers give the copies a phase to land before their stage is read. At the end group 1's int32 sums are added
 // to group 0's through LDS (exact) and group 0 writes the tile.
 template <int YMODE>
 __device__ __forceinline__ void gemm_tile_ks(const int8_t* __restrict__ A, const float* __restrict__ xs,
@@ -386,23 +468,26 @@ __device__ __forceinline__ void gemm_tile_ks(const int8_t* __restrict__ A, const
     const int cx = (lane & 7) ^ ((lane >> 3) & 7);
     const int va0 = cra * K + (cx << 4), va1 = cra * K + ((cx ^ 1) << 4);
     const int vb0 = crb * K + (cx << 4), vb1 = crb * K + ((cx ^ 1) << 4);
-    const bool tail_hi = (K & (BKL - 1)) != 0 && cx >= 4;   // upper half of a half-deep last stage
-    auto copies = [&](int kt) {
+    const int hi = (K & (BKL - 1)) != 0 && cx >= 4 ? 0x40000000 : 0;   // upper half of a half-deep last stage
+    // Copy c (< CA: of A, else of B) of stage kt (< KT) into buffer kt % 3; see copy_voff.
+    auto copy_one = [&](int kt, int c) {
         int8_t* st = smem + (kt % 3) * STAGE;
-        const int kc = min(kt, KT - 1);
-        const bool cut = tail_hi && kc == KT - 1;
-#pragma unroll
-        for (int c = 0; c < CA; ++c) {
-            const int so = __builtin_amdgcn_readfirstlane(kc * BKL + 8 * c * K);
-            lds_copy16_buf(ra, cra + 8 * c < rows_a && !cut ? ((c & 1) ? va1 : va0) : 0x7FFFFFF0, so,
+        const int cutm = kt == KT - 1 ? -1 : 0;
+        if (c < CA) {
+            const int so = stage_soff(kt * BKL + 8 * c * K);
+            lds_copy16_buf(ra, copy_voff((c & 1) ? va1 : va0, so, hi, cutm), 0,
                            st + ((BM / 4) * q + 8 * c) * BKL);
+        } else {
+            const int cb = c - CA;
+            const int so = stage_soff(kt * BKL + 8 * cb * K);
+            lds_copy16_buf(rb, copy_voff((cb & 1) ? vb1 : vb0, so, hi, cutm), 0,
+                           st + STAGE_A + ((BN / 4) * q + 8 * cb) * BKL);
         }
+    };
+    auto copies = [&](int kt) {
 #pragma unroll
-        for (int c = 0; c < CB; ++c) {
-            const int so = __builtin_amdgcn_readfirstlane(kc * BKL + 8 * c * K);
-            lds_copy16_buf(rb, crb + 8 * c < rows_b && !cut ? ((c & 1) ? vb1 : vb0) : 0x7FFFFFF0, so,
-                           st + STAGE_A + ((BN / 4) * q + 8 * c) * BKL);
-        }
+        for (int c = 0; c < CA + CB; ++c)
+            copy_one(kt, c);
     };
 
     i32x16 acc[FM][FN];
@@ -415,19 +500,26 @@ __device__ __forceinline__ void gemm_tile_ks(const int8_t* __restrict__ A, const
                 acc[i][j][e] = 0;
 
     const int lr = lane & 31;
-    const int fa_base = wm * WM * BKL + lr * BKL, fb_base = STAGE_A + wn * WN * BKL + lr * BKL;
+    // Lane l reads row l & 31 of a 32-row block, logical chunk 2 ks + (l >> 5) of substep ks,
+    // stored at chunk position (2 ks + (l >> 5)) ^ h128(row) = ((l >> 5) ^ h128(row)) ^ 2 ks:
+    // substep ks flips bit 5 and 6 of the substep-0 offset. Stage and block bases are
+    // multiples of 128, so they can be added before the flip.
+    const int rbase = lr * BKL + (((lane >> 5) ^ h128(lr)) << 4);
     i32x4 F[4][FM + FN];
     auto read_stage = [&](int kt) {
-        const int8_t* st = smem + (kt % 3) * STAGE;
+        const int sbuf = (kt % 3) * STAGE;
+        const int ta = rbase + stage_soff(sbuf + wm * WM * BKL);
+        const int tb = rbase + stage_soff(sbuf + STAGE_A + wn * WN * BKL);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            const int co = ((2 * ks + (lane >> 5)) ^ h128(lr)) << 4;
+            const int8_t* pa = smem + (ta ^ (ks << 5));
+            const int8_t* pb = smem + (tb ^ (ks << 5));
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-                F[ks][FM + j] = *reinterpret_cast<const i32x4*>(st + fb_base + co + j * 32 * BKL);
+                F[ks][FM + j] = *reinterpret_cast<const i32x4*>(pb + j * 32 * BKL);
 #pragma unroll
             for (int i = 0; i < FM; ++i)
-                F[ks][i] = *reinterpret_cast<const i32x4*>(st + fa_base + co + i * 32 * BKL);
+                F[ks][i] = *reinterpret_cast<const i32x4*>(pa + i * 32 * BKL);
         }
     };
     auto mfma_stage = [&]() {
@@ -438,6 +530,26 @@ __device__ __forceinline__ void gemm_tile_ks(const int8_t* __restrict__ A, const
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(F[ks][i], F[ks][FM + j], acc[i][j], 0, 0, 0);
+    };
+    // The same MFMAs with the copies of stage kt spread evenly between them, so the copies'
+    // address work runs in the shadow of the matrix cores.
+    static_assert(CA + CB <= 4 * FM * FN, "copies fit between the MFMAs");
+    auto mfma_stage_copying = [&](int kt) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const int n = (ks * FM + i) * FN + j;
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(F[ks][i], F[ks][FM + j], acc[i][j], 0, 0, 0);
+                    const int c = spread_slot(n, CA + CB, 4 * FM * FN);
+                    if (c >= 0) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        copy_one(kt, c);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
     };
     auto phase_end = [&]() {
         __builtin_amdgcn_sched_barrier(0);
@@ -452,19 +564,33 @@ __device__ __forceinline__ void gemm_tile_ks(const int8_t* __restrict__ A, const
         issue_scales(xs, ws, bias, M, N, m0, n0, wave, lane, smem);
     if (grp == 0) {
         copies(0);
-        copies(2);   // past the end: a repeat of the last stage, never read
-        __builtin_amdgcn_s_waitcnt(vmcnt_le(CA + CB) & ~(0xF << 8));   // stage 0 landed
-    } else {
+        if (KT > 2) {
+            copies(2);
+            __builtin_amdgcn_s_waitcnt(vmcnt_le(CA + CB) & ~(0xF << 8));   // stage 0 landed
+        } else {
+            __builtin_amdgcn_s_waitcnt(vmcnt_le(0) & ~(0xF << 8));
+        }
+    } else if (KT > 1) {
         copies(1);
     }
     phase_end();
-    // Phase j: group (j & 1) runs stage j's MFMAs and then waits for the copies it issued
-    // in phase j - 1 (stage j + 2); the other group issues stage j + 3's copies into stage
-    // j's buffer (read in phase j - 1) and reads stage j + 1. Every wave runs the same
-    // barriers (one per phase). Before phase 0 group 0 reads stage 0 while group 1 waits
-    // for its stage-1 copies.
+    // Phase j: group (j & 1) runs stage j's MFMAs with the copies of stage j + 3 (into
+    // stage j's buffer, read in phase j - 1) between them, and then has the copies it
+    // issued before this phase landed (in phase 0: group 0's stage 2 from the prologue);
+    // the other group reads stage j + 1 and waits for the copies it issued in phase j - 1
+    // (stage j + 2, read in phase j + 1). Every wave runs the same barriers (one per
+    // phase). Before phase 0 group 0 reads stage 0 while group 1 waits for its stage-1
+    // copies.
     // Each group runs its own straight-line loop over pairs of phases (a branch per phase
     // inside one loop would make the compiler keep two copies of the fragments).
+    // The last three stages have no copies; their phases run in loops of their own (a
+    // branch inside one loop would make the compiler keep two sets of fragment registers).
+    auto mfma_phase_copying = [&](int j) {
+        mfma_stage_copying(j + 3);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(vmcnt_le(CA + CB));
+        phase_end();
+    };
     auto mfma_phase = [&]() {
         mfma_stage();
         __builtin_amdgcn_sched_barrier(0);
@@ -472,9 +598,8 @@ __device__ __forceinline__ void gemm_tile_ks(const int8_t* __restrict__ A, const
         phase_end();
     };
     auto read_phase = [&](int j) {
-        copies(j + 3);
         read_stage(min(j + 1, KT - 1));   // past the end: a repeat, never used
-        __builtin_amdgcn_s_waitcnt(LGKM0);
+        __builtin_amdgcn_s_waitcnt(vmcnt_le(0) & ~(0xF << 8));
         phase_end();
     };
     if (grp == 0) {
@@ -482,22 +607,31 @@ __device__ __forceinline__ void gemm_tile_ks(const int8_t* __restrict__ A, const
         __builtin_amdgcn_s_waitcnt(LGKM0);
         phase_end();
         int j = 0;
+        for (; j + 3 < KT; j += 2) {
+            mfma_phase_copying(j);   // phase j
+            read_phase(j + 1);       // phase j + 1
+        }
         for (; j + 1 < KT; j += 2) {
-            mfma_phase();        // phase j
-            read_phase(j + 1);   // phase j + 1
+            mfma_phase();
+            read_phase(j + 1);
         }
         if (j < KT)
             mfma_phase();
     } else {
         __builtin_amdgcn_s_waitcnt(vmcnt_le(0));   // stage 1 landed
         phase_end();
-        int j = 0;
+        read_phase(0);   // phase 0
+        int j = 1;
+        for (; j + 3 < KT; j += 2) {
+            mfma_phase_copying(j);   // phase j
+            read_phase(j + 1);       // phase j + 1
+        }
         for (; j + 1 < KT; j += 2) {
-            read_phase(j);       // phase j
-            mfma_phase();        // phase j + 1
+            mfma_phase();
+            read_phase(j + 1);
         }
         if (j < KT)
-            read_phase(j);
+            mfma_phase();
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
 
