@@ -143,36 +143,43 @@ __device__ __forceinline__ void store_tile(const i32x16 (&acc)[FM][FN], bool has
         // The wave's LDS operations complete in order, so its reads below see all of its
         // writes above; this only keeps the compiler from reordering them.
         asm volatile("" ::: "memory");
-        u32x4 rv[NRD];
-#pragma unroll
-        for (int p = 0; p < NRD; ++p) {
-            const int r = p * RPI + lane / LPR, c = (lane % LPR) * VEC;
-            rv[p] = *reinterpret_cast<const u32x4*>(stage + r * ROWB + c * SZ);
-        }
         const int row0 = mrow0 + 32 * i;
         const int64_t left = (int64_t)(M - row0) * N * SZ;   // bytes from row0 to the end
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
             reinterpret_cast<int8_t*>(Y) + (int64_t)row0 * N * SZ, 0,
             (int)(left <= 0 ? 0 : (left < LIM ? left : LIM)), 0x00020000);
-        if (vec_ok) {
+        // Reads and stores go in batches of at most four 16-byte pieces per lane, which
+        // keeps the band's registers few beside the accumulators.
+        constexpr int PB = NRD < 4 ? NRD : 4;
 #pragma unroll
-            for (int p = 0; p < NRD; ++p)
-                __builtin_amdgcn_raw_buffer_store_b128(rv[p], rs, lane_off + p * RPI * N * SZ, 0, 0);
-        } else {
-            const int n = ncol0 + (lane % LPR) * VEC;
+        for (int p0 = 0; p0 < NRD; p0 += PB) {
+            u32x4 rv[PB];
 #pragma unroll
-            for (int p = 0; p < NRD; ++p) {
-                const int roff = (p * RPI + lane / LPR) * N * SZ;
-                const OutT* pv = reinterpret_cast<const OutT*>(&rv[p]);
+            for (int b = 0; b < PB; ++b) {
+                const int r = (p0 + b) * RPI + lane / LPR, c = (lane % LPR) * VEC;
+                rv[b] = *reinterpret_cast<const u32x4*>(stage + r * ROWB + c * SZ);
+            }
+            if (vec_ok) {
 #pragma unroll
-                for (int q = 0; q < VEC; ++q) {
-                    const int off = roff + (n + q < N ? (n + q) * SZ : LIM);
-                    if constexpr (SZ == 2)
-                        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, pv[q]), rs, off, 0, 0);
-                    else
-                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, pv[q]), rs, off, 0, 0);
+                for (int b = 0; b < PB; ++b)
+                    __builtin_amdgcn_raw_buffer_store_b128(rv[b], rs, lane_off + (p0 + b) * RPI * N * SZ, 0, 0);
+            } else {
+                const int n = ncol0 + (lane % LPR) * VEC;
+#pragma unroll
+                for (int b = 0; b < PB; ++b) {
+                    const int roff = ((p0 + b) * RPI + lane / LPR) * N * SZ;
+                    const OutT* pv = reinterpret_cast<const OutT*>(&rv[b]);
+#pragma unroll
+                    for (int q = 0; q < VEC; ++q) {
+                        const int off = roff + (n + q < N ? (n + q) * SZ : LIM);
+                        if constexpr (SZ == 2)
+                            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, pv[q]), rs, off, 0, 0);
+                        else
+                            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, pv[q]), rs, off, 0, 0);
+                    }
                 }
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
         asm volatile("" ::: "memory");   // the next band's writes follow these reads
     }
@@ -651,17 +658,25 @@ __device__ __forceinline__ void gemm_tile_ks(const int8_t* __restrict__ A, const
     }
     phase_end();
     if (grp == 0) {
+        // One block (16 ints a lane) at a time, each sum formed here (the empty asm keeps
+        // the compiler from sinking the adds into the epilogue), so that group 1's sums
+        // never all sit in registers beside the accumulators.
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
+            for (int j = 0; j < FN; ++j) {
 #pragma unroll
                 for (int e4 = 0; e4 < 4; ++e4) {
                     const i32x4 v = *reinterpret_cast<const i32x4*>(xch + ((i * FN + j) * 4 + e4) * 256 + lane * 4);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        acc[i][j][4 * e4 + r] += v[r];
+                    for (int r = 0; r < 4; ++r) {
+                        int sum = acc[i][j][4 * e4 + r] + v[r];
+                        asm volatile("" : "+v"(sum));
+                        acc[i][j][4 * e4 + r] = sum;
+                    }
                 }
+                __builtin_amdgcn_sched_barrier(0);
+            }
     }
     __builtin_amdgcn_s_waitcnt(LGKM0);
     if (grp == 0) {

@@ -63,18 +63,26 @@ __device__ inline void bytes_to_f16(const u32x4 w, uint32_t flip, _Float16 sub, 
     hi = __builtin_bit_cast(f16x8, b) - s;
 }
 
-// Two 4-bit offset codes (bits 0-3 and 16-19 of v, other bits zero) -> fp16 pair 1024+u.
-__device__ inline uint32_t magic_pair(uint32_t v) { return v | 0x64006400u; }
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-// One int32 word of eight int4 codes (element j in bits 4j..4j+3) -> fp16x8 in the order
-// [q0, q4, q1, q5, q2, q6, q3, q7]; the activation operand uses the same order.
+// One int32 word of eight int4 codes (element j in bits 4j..4j+3, two's complement) ->
+// fp16x8 [q0, q4, q1, q5, q2, q6, q3, q7], exactly. For a nibble n the offset code is
+// u = q + 8 = n ^ 8. Masking a nibble pair and XORing with the fp16 pattern of 1024 (with
+// bit 3 of each nibble field set) gives in one bitwise step the fp16 pair 1024 + u (low
+// nibbles of a byte) or 1024 + 16 u (high nibbles; the fp16 spacing on [1024, 2048) is 1, so
+// both are exact); then q = (1024 + u) - 1032 and q = (1024 + 16 u) / 16 - 72, each one
+// exact packed fp16 operation.
 __device__ inline f16x8 int4_to_f16(uint32_t w) {
-    const uint32_t v = w ^ 0x88888888u;  // two's complement -> offset binary q + 8
-    const u32x4 a{magic_pair(v & 0x000F000Fu), magic_pair((v >> 4) & 0x000F000Fu),
-                  magic_pair((v >> 8) & 0x000F000Fu), magic_pair((v >> 12) & 0x000F000Fu)};
-    const _Float16 c = (_Float16)1032.0f;
-    const f16x8 s{c, c, c, c, c, c, c, c};
-    return __builtin_bit_cast(f16x8, a) - s;
+    const uint32_t w8 = w >> 8;
+    const f16x2 lo_sub{(_Float16)1032.0f, (_Float16)1032.0f};
+    const f16x2 hi_mul{(_Float16)0.0625f, (_Float16)0.0625f}, hi_add{(_Float16)-72.0f, (_Float16)-72.0f};
+    const f16x2 a = __builtin_bit_cast(f16x2, (w & 0x000F000Fu) ^ 0x64086408u) - lo_sub;     // q0, q4
+    const f16x2 b = __builtin_elementwise_fma(__builtin_bit_cast(f16x2, (w & 0x00F000F0u) ^ 0x64806480u),
+                                              hi_mul, hi_add);                            // q1, q5
+    const f16x2 c = __builtin_bit_cast(f16x2, (w8 & 0x000F000Fu) ^ 0x64086408u) - lo_sub;    // q2, q6
+    const f16x2 d = __builtin_elementwise_fma(__builtin_bit_cast(f16x2, (w8 & 0x00F000F0u) ^ 0x64806480u),
+                                              hi_mul, hi_add);                            // q3, q7
+    return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
 // Reorders eight consecutive activations x0..x7 to [x0, x4, x1, x5, x2, x6, x3, x7].
