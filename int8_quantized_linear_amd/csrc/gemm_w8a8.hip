@@ -349,7 +349,7 @@ __device__ __forceinline__ void gemm_tile_pp(const int8_t* __restrict__ A, const
     auto no_copy = [](int) {};
 
     // Prologue: group 0 copies all of stage 0 and stage 1 but its B high (copied in A_0),
-    // and waits for them.
+    // and waits for stage 0; stage 1 has until the end of A_0.
     if constexpr (YMODE != Y_I32)
         issue_scales(xs, ws, bias, M, N, m0, n0, wave, lane, smem);
     if (grp == 0) {
@@ -366,8 +366,10 @@ __device__ __forceinline__ void gemm_tile_pp(const int8_t* __restrict__ A, const
 #pragma unroll
             for (int c = 0; c < CH; ++c)
                 copy_b(1, 1, 0, c);
+            __builtin_amdgcn_s_waitcnt(vmcnt_le(CA + CH) & ~(0xF << 8));
+        } else {
+            __builtin_amdgcn_s_waitcnt(vmcnt_le(0) & ~(0xF << 8));
         }
-        __builtin_amdgcn_s_waitcnt(vmcnt_le(0) & ~(0xF << 8));
     }
     barrier_no_fence();
     // Each group runs its own straight-line loops; both execute the same barriers in the
@@ -391,6 +393,8 @@ __device__ __forceinline__ void gemm_tile_pp(const int8_t* __restrict__ A, const
             __builtin_amdgcn_s_waitcnt(vmcnt_le(0) & ~(0xF << 8));
             phase_end();
         };
+        // A_j ends with every copy but the ones just issued landed: a no-op except in A_0,
+        // where it covers the prologue's stage 1
         int j = 0;
         for (; j + 2 < KT; ++j) {
             mfma_stage(2 * CH, [&](int c) {
@@ -399,11 +403,15 @@ __device__ __forceinline__ void gemm_tile_pp(const int8_t* __restrict__ A, const
                 else
                     copy_b(j + 2, j & 1, 0, c - CH);
             });
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt(vmcnt_le(2 * CH));
             phase_end();
             read_phase(j);
         }
         for (; j + 1 < KT; ++j) {
             mfma_stage(CH, [&](int c) { copy_b(j + 1, (j + 1) & 1, 1, c); });
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt(vmcnt_le(CH));
             phase_end();
             read_phase(j);
         }
@@ -687,11 +695,11 @@ __device__ __forceinline__ void gemm_tile_ks(const int8_t* __restrict__ A, const
     }
 }
 
-// Tiles: the first `nbig` workgroups take 256 x 256 tiles of the first `nbig / tiles_m`
-// N-panels; the rest take 128 x 256 tiles of the remaining panels. With 256 CUs, whole
-// rounds of big tiles keep every CU busy and the leftover panels run as half-height
-// tiles in a shorter final round. Within each group, workgroups are dealt to XCDs so
-// that an XCD's tiles are consecutive and share W panels (column-major tile order).
+// Tiles: `nbig` 256 x 256 tiles cover the first `nbig / tiles_m` N-panels and `nsmall`
+// 128 x 256 tiles the remaining panels; workgroup b takes big tile b, then half tile b.
+// With 256 CUs, whole rounds of big tiles keep every CU busy and the leftover panels run
+// as half-height tiles in a shorter final round. Within each kind, tiles are dealt to
+// XCDs so that an XCD's tiles are consecutive and share W panels (column-major order).
 struct TilePlan {
     int tiles_m_big, nbig, tiles_m_small, nsmall, n_small0;
 };
@@ -707,8 +715,15 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void gemm_w8a8_kernel(
         const int tile = xcd_remap(bid, plan.nbig);
         const int tn = tile / plan.tiles_m_big, tm = tile - tn * plan.tiles_m_big;
         gemm_tile_pp<256, 256, YMODE>(A, xs, B, ws, bias, Y, M, N, K, tm * 256, tn * 256, smem);
-    } else {
-        const int tile = xcd_remap(bid - plan.nbig, plan.nsmall);
+        if (bid >= plan.nsmall)
+            return;
+        // The big tile's epilogue has read all it needs from LDS (its stores may still be in
+        // flight): the half tile may refill the LDS.
+        __builtin_amdgcn_s_waitcnt(vmcnt_le(63) & ~(0xF << 8));   // lgkmcnt(0)
+        barrier_no_fence();
+    }
+    if (bid < plan.nsmall) {
+        const int tile = xcd_remap(bid, plan.nsmall);
         const int tn = tile / plan.tiles_m_small, tm = tile - tn * plan.tiles_m_small;
         gemm_tile_ks<YMODE>(A, xs, B, ws, bias, Y, M, N, K, tm * 128, plan.n_small0 + tn * 256, smem);
     }
@@ -755,7 +770,10 @@ ql_status launch_gemm_w8a8(const int8_t* xq, const float* x_scale, const int8_t*
     if (M == 0 || N == 0)
         return QL_OK;
     const TilePlan plan = plan_tiles(M, N);
-    const dim3 grid((unsigned)(plan.nbig + plan.nsmall)), block(64 * NWAVES);
+    // Workgroup b runs big tile b (b < nbig) and then half tile b (b < nsmall), so the
+    // half tiles start on the first CUs to finish a big tile without a new dispatch and
+    // their first copies overlap the big tile's last stores.
+    const dim3 grid((unsigned)(plan.nbig > plan.nsmall ? plan.nbig : plan.nsmall)), block(64 * NWAVES);
     const int m = (int)M, n = (int)N, k = (int)K;
 #define QL_LAUNCH(MODE)                                                                          \
     hipLaunchKernelGGL((gemm_w8a8_kernel<MODE>), grid, block, 0, stream, xq, x_scale, wq, w_scale, \
