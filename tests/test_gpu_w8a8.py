@@ -43,11 +43,13 @@ def test_int32_bit_exact(ql, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(2000, 8300, 64), (2048, 11008, 192), (2048, 11008, 384),
-                                   (2000, 8300, 256)])
+                                   (2000, 8300, 256), (4096, 8400, 128), (8192, 2100, 64)])
 def test_int32_mixed_tile_plan(ql, M, N, K):
     """Shapes with more 256 x 256 tiles than CUs, where the last N panels run as 128-row
-    tiles in the same launch (ragged M and N in the first case); rows sampled from every
-    128-row band are checked bit-exactly."""
+    tiles in the same launch, each after a big tile in the same workgroup (ragged M and N
+    in the first case; two rounds of big tiles before the half tiles in the fifth; a ragged
+    half-tile panel in the last); rows sampled from every 128-row band are checked
+    bit-exactly."""
     rng = np.random.default_rng(M + N + K)
     a = _rand_codes(rng, (M, K), -128)
     b = _rand_codes(rng, (N, K), -128)
