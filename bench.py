@@ -16,6 +16,12 @@ Printed: one JSON line. ``value`` is the W8A8 prefill layer's throughput in TOPS
 (2*M*N*K integer ops over the average time of steps 1 + 2); the decode workloads'
 GB/s are reported alongside. Kernel times come from HIP events recorded around each
 launch on the stream the kernels run on, inside the timed region.
+
+After the timed region, measured ceilings (libqlprobe.so, not part of the layer) are
+reported beside the published peaks: the int8 MFMA rate from registers alone, with
+random and with constant operands (the chip's power limit sets its clock, and MFMA power
+depends on the operand bits), and the rate one launch reads a buffer of each
+memory-bound kernel's byte count from HBM.
 """
 from __future__ import annotations
 
@@ -102,6 +108,68 @@ def cpu_baseline(target_s: float):
             "seconds": dt, "host": platform.processor() or platform.machine()}
 
 
+def measured_ceilings(dev, byte_counts, progress):
+    """Ceilings measured with libqlprobe.so: int8 MFMA TOPS from registers (random and
+    constant operands) and the GB/s of one cold streaming read of each byte count."""
+    import ctypes
+
+    import torch
+
+    path = os.path.join(ROOT, "int8_quantized_linear_amd", "libqlprobe.so")
+    if not os.path.exists(path):
+        raise RuntimeError("libqlprobe.so is not built at %s" % path)
+    P = ctypes.CDLL(path)
+    P.qlp_cu_count.restype = ctypes.c_int
+    P.qlp_mfma_i8.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    P.qlp_mfma_i8.restype = ctypes.c_int
+    P.qlp_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    P.qlp_stream_read.restype = ctypes.c_int
+    cus = P.qlp_cu_count()
+    if cus <= 0:
+        raise RuntimeError("qlp_cu_count failed")
+    stream = torch.cuda.current_stream(dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    sink = torch.empty(cus * 256, dtype=torch.int32, device=dev)
+
+    def check(rc, what):
+        if rc != 0:
+            raise RuntimeError("%s failed with %d" % (what, rc))
+
+    def timed(fn, reps):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for i, (a, b) in enumerate(evs):
+            a.record(stream)
+            fn(i)
+            b.record(stream)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in evs) / reps * 1e-3   # seconds per launch
+
+    progress("measured ceilings")
+    out = {"mfma_i8_TOPS": {}, "stream_read_GB_per_s": {}}
+    iters = 2000
+    ops = float(cus) * 4 * iters * 16 * 65536
+    for name, rnd in (("random_operands", 1), ("constant_operands", 0)):
+        check(P.qlp_mfma_i8(100, rnd, ctypes.c_void_p(sink.data_ptr()), sh), "qlp_mfma_i8")
+        dt = timed(lambda i: check(P.qlp_mfma_i8(iters, rnd, ctypes.c_void_p(sink.data_ptr()), sh),
+                                   "qlp_mfma_i8"), 5)
+        out["mfma_i8_TOPS"][name] = ops / dt / 1e12
+    for name, nbytes in byte_counts.items():
+        nb = (nbytes + 15) // 16 * 16
+        nbuf = max(2, math.ceil(ROTATE_BYTES / nb))
+        bufs = [torch.ones(nb, dtype=torch.uint8, device=dev) for _ in range(nbuf)]
+        torch.cuda.synchronize()
+        reps = 2 * nbuf
+        dt = timed(lambda i: check(P.qlp_stream_read(ctypes.c_void_p(bufs[i % nbuf].data_ptr()), nb,
+                                                     ctypes.c_void_p(sink.data_ptr()), sh),
+                                   "qlp_stream_read"), reps)
+        out["stream_read_GB_per_s"][name] = nb / dt / 1e9
+        del bufs
+    out["note"] = ("MFMA: %d workgroups x 4 waves issuing v_mfma_i32_32x32x32_i8 from registers; "
+                   "stream read: one launch reading a cold buffer of each kernel's algorithmic "
+                   "byte count (buffers rotated over more than 512 MiB)" % cus)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -109,6 +177,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", dest="cpu", action="store_false")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-ceilings", dest="ceilings", action="store_false",
+                    help="skip the measured ceilings (MFMA-only and streaming-read probes)")
     ap.add_argument("--calib-copy-mib", type=int, default=256,
                     help="size of the plain device copy run once before the timed region "
                          "(reference point for hardware byte counters)")
@@ -262,6 +332,18 @@ def main():
         "decode": decode,
         "device": torch.cuda.get_device_name(0),
     }
+    if args.ceilings:
+        del set2, set4, set5, dec2, dec4, dec5
+        ceil = measured_ceilings(dev, {"quant": ab["quant"], "w8a16": ab["w8a16"],
+                                       "w8a16_block": ab["w8a16_block"], "w4a16": ab["w4a16"]}, progress)
+        out["ceilings"] = ceil
+        mc = ceil["mfma_i8_TOPS"]["random_operands"]
+        out["roofline"]["measured_ceiling"] = mc
+        out["roofline"]["frac_of_measured_ceiling"] = gemm_tops / mc
+        rd = ceil["stream_read_GB_per_s"]
+        out["quantizer"]["frac_of_stream_read"] = gbs("quant") / rd["quant"]
+        for name in decode:
+            decode[name]["frac_of_stream_read"] = decode[name]["GB_per_s"] / rd[name]
     if args.cpu:
         progress("cpu baseline (oracle) ~%.0f s" % args.cpu_seconds)
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

@@ -171,3 +171,25 @@ def test_producer_validation(lib):
     assert g(None, 256, 8, 128, A, A, None) == NULL
     assert g(A, 256, 8, 96, A, A, None) == SHAPE
     assert g(A, 256, 8, 128, MIS, A, None) == ALIGN
+
+
+PROBE_HEADER = os.path.join(ROOT, "include", "ql_probe.h")
+PROBE_LIB = os.path.join(ROOT, "int8_quantized_linear_amd", "libqlprobe.so")
+
+
+def test_probe_library_exports_its_header():
+    """The benchmark's measurement probes (a library of their own, not the layer) export
+    every function their header declares, and reject bad arguments without launching."""
+    if not os.path.exists(PROBE_LIB):
+        pytest.skip("libqlprobe.so not built")
+    text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
+    names = set(re.findall(r"^\s*int\s+([a-z_0-9]+)\s*\(", text, re.M))
+    assert names == {"qlp_cu_count", "qlp_mfma_i8", "qlp_stream_read"}
+    out = subprocess.run(["nm", "-D", "--defined-only", PROBE_LIB], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert names <= exported
+    L = ctypes.CDLL(PROBE_LIB)
+    L.qlp_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    L.qlp_stream_read.restype = ctypes.c_int
+    # no GPU here: the device query fails first and nothing is launched
+    assert L.qlp_stream_read(A, 16, A, None) == -1
