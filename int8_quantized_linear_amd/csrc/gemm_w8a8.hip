@@ -199,15 +199,6 @@ __device__ inline void lds_copy16_buf(__amdgpu_buffer_rsrc_t r, int voff, int so
 #endif
 }
 
-// Copies of a stage spread over the nm MFMAs of a phase: the index of the copy issued right
-// after MFMA n when nc copies are spread evenly, or -1.
-constexpr int spread_slot(int n, int nc, int nm) {
-    for (int c = 0; c < nc; ++c)
-        if ((c * nm) / nc == n)
-            return c;
-    return -1;
-}
-
 // Vector offset of one lane's 16 bytes of a stage copy: v (the lane's row times K plus its
 // chunk) + so (the k-step and the copy's 8-row step, wave-uniform). The row goes into the
 // vector offset, so a row past the descriptor's end is out of range (the hardware returns
@@ -228,23 +219,23 @@ __device__ inline int stage_soff(int v) {
 // A BM x BN tile on 8 waves with a ping-pong schedule. Waves 0-3
 // (group 0) and 4-7 (group 1) put one wave of each group on every SIMD, and the two
 // groups alternate between phases separated by workgroup barriers: in each phase one
-// group issues the 32 MFMAs of a whole 128-deep stage (its fragments already in
-// registers) with a share of the copies spread between them, while the other group reads
-// the next stage's fragments from LDS. The MFMA stream of a SIMD then never waits behind
-// an LDS read of its own wave, and the copies' address work in the texture unit (16
-// bytes a lane, one copy every ~16 clocks per CU) is spread over the whole stage. Wave w
-// owns the (BM / 2) x (BN / 4) block at rows (BM / 2) (w & 1), columns (BN / 4) (w >> 1):
-// group 0 reads all of A and the low half of B's columns, group 1 all of A and the high
-// half, so the three parts of a stage buffer (A, B low, B high) are free at different
-// times.
+// group issues nothing but the 32 MFMAs of a whole 128-deep stage (its fragments already
+// in registers), while the other group reads the next stage's fragments from LDS and then
+// issues its share of the copies. The MFMA stream of a SIMD never waits behind an LDS
+// read or a copy of its own wave, and the copies' address work in the texture unit (16
+// bytes a lane, one copy every ~16 clocks per CU) is split evenly between the two phases.
+// Wave w owns the (BM / 2) x (BN / 4) block at rows (BM / 2) (w & 1), columns (BN / 4)
+// (w >> 1): group 0 reads all of A and the low half of B's columns, group 1 all of A and
+// the high half, so the three parts of a stage buffer (A, B low, B high) fall free at
+// different times.
 //
-// Phase 2j (A_j):    group 0 runs stage j's MFMAs, copying B high of stage j + 1 and B low
-//                    of stage j + 2; group 1 reads stage j.
-// Phase 2j+1 (B_j):  group 0 reads stage j + 1; group 1 runs stage j's MFMAs, copying A
-//                    of stage j + 2.
-// Each part is refilled only after both of its reads are done (barriers between) and its
-// copies land at least one phase before its first read: group 0 waits for its copies at
-// the end of B_j, group 1 at the end of A_{j+1}.
+// Phase 2j (A_j):    group 0 runs stage j's MFMAs; group 1 reads stage j, then copies B
+//                    high of stage j + 1 and B low of stage j + 2.
+// Phase 2j+1 (B_j):  group 0 reads stage j + 1, then copies A of stage j + 2; group 1 runs
+//                    stage j's MFMAs.
+// Each part is refilled only after both of its reads are done (barriers between), and
+// each wave waits for its copies at the end of its next (MFMA) phase, a phase before
+// their first read.
 template <int BM, int BN, int YMODE>
 __device__ __forceinline__ void gemm_tile_pp(const int8_t* __restrict__ A, const float* __restrict__ xs,
                                              const int8_t* __restrict__ B, const float* __restrict__ ws,
@@ -256,8 +247,6 @@ __device__ __forceinline__ void gemm_tile_pp(const int8_t* __restrict__ A, const
     constexpr int CA = BM / 32, CH = BN / 64;   // per wave: copies of A, and of each half of B (8 rows each)
     static_assert(2 * STAGE <= RING_BYTES, "two stages fit the LDS allocation");
     static_assert(FM >= 1 && FN >= 1 && CA % 2 == 0 && CH % 2 == 0, "tile shape");
-    constexpr int NMF = 4 * FM * FN;
-    static_assert(CA <= NMF && 2 * CH <= NMF, "copies fit between the MFMAs");
 
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -328,25 +317,15 @@ __device__ __forceinline__ void gemm_tile_pp(const int8_t* __restrict__ A, const
                 F[ks][i] = *reinterpret_cast<const i32x4*>(pa + i * 32 * BKL);
         }
     };
-    // A stage's MFMAs with `nc` copies spread evenly between them: copy(c) for c < nc runs
-    // right after MFMA (c * 32) / nc.
-    auto mfma_stage = [&](int nc, auto&& copy) {
+    auto mfma_stage = [&]() {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < FN; ++j) {
+                for (int j = 0; j < FN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(F[ks][i], F[ks][FM + j], acc[i][j], 0, 0, 0);
-                    const int c = spread_slot((ks * FM + i) * FN + j, nc, NMF);
-                    if (c >= 0) {
-                        __builtin_amdgcn_sched_barrier(0);
-                        copy(c);
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
-                }
     };
-    auto no_copy = [](int) {};
 
     // Prologue: group 0 copies all of stage 0 and stage 1 but its B high (copied in A_0),
     // and waits for stage 0; stage 1 has until the end of A_0.
@@ -382,62 +361,68 @@ __device__ __forceinline__ void gemm_tile_pp(const int8_t* __restrict__ A, const
         barrier_no_fence();
         __builtin_amdgcn_sched_barrier(0);
     };
+    constexpr int LGKM0 = vmcnt_le(63) & ~(0xF << 8);   // lgkmcnt(0), vmcnt left alone
+    // An MFMA phase: the stage's MFMAs, then this wave's copies (all issued in its reading
+    // phase before) have landed.
+    auto mfma_phase = [&]() {
+        mfma_stage();
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
+        phase_end();
+    };
     if (grp == 0) {
         read_stage(0);
-        __builtin_amdgcn_s_waitcnt(vmcnt_le(63) & ~(0xF << 8));   // lgkmcnt(0)
+        __builtin_amdgcn_s_waitcnt(LGKM0);
         phase_end();
-        // B_j: reads of stage j + 1 (past the end a repeat, never used); this wave's copies
-        // issued in A_j have landed
-        auto read_phase = [&](int j) {
-            read_stage(min(j + 1, KT - 1));
-            __builtin_amdgcn_s_waitcnt(vmcnt_le(0) & ~(0xF << 8));
-            phase_end();
-        };
-        // A_j ends with every copy but the ones just issued landed: a no-op except in A_0,
-        // where it covers the prologue's stage 1
+        // A_j: MFMAs of stage j (in A_0 the prologue's stage 1 lands). B_j: reads of stage
+        // j + 1 (past the end a repeat, never used), then the copies of A of stage j + 2.
         int j = 0;
         for (; j + 2 < KT; ++j) {
-            mfma_stage(2 * CH, [&](int c) {
-                if (c < CH)
-                    copy_b(j + 1, (j + 1) & 1, 1, c);
-                else
-                    copy_b(j + 2, j & 1, 0, c - CH);
-            });
-            __builtin_amdgcn_sched_barrier(0);
-            __builtin_amdgcn_s_waitcnt(vmcnt_le(2 * CH));
+            mfma_phase();
+            read_stage(j + 1);
+#pragma unroll
+            for (int c = 0; c < CA; ++c)
+                copy_a(j + 2, j & 1, c);
+            __builtin_amdgcn_s_waitcnt(vmcnt_le(CA) & ~(0xF << 8));
             phase_end();
-            read_phase(j);
-        }
-        for (; j + 1 < KT; ++j) {
-            mfma_stage(CH, [&](int c) { copy_b(j + 1, (j + 1) & 1, 1, c); });
-            __builtin_amdgcn_sched_barrier(0);
-            __builtin_amdgcn_s_waitcnt(vmcnt_le(CH));
-            phase_end();
-            read_phase(j);
         }
         for (; j < KT; ++j) {
-            mfma_stage(0, no_copy);
+            mfma_phase();
+            read_stage(min(j + 1, KT - 1));
+            __builtin_amdgcn_s_waitcnt(LGKM0);
             phase_end();
-            read_phase(j);
         }
     } else {
         phase_end();   // while group 0 reads stage 0
-        // A_j: reads of stage j; this wave's copies issued in B_{j-1} have landed
-        auto read_phase = [&](int j) {
-            read_stage(j);
-            __builtin_amdgcn_s_waitcnt(vmcnt_le(0) & ~(0xF << 8));
-            phase_end();
-        };
+        // A_j: reads of stage j, then the copies of B high of stage j + 1 and B low of stage
+        // j + 2. B_j: MFMAs of stage j.
         int j = 0;
         for (; j + 2 < KT; ++j) {
-            read_phase(j);
-            mfma_stage(CA, [&](int c) { copy_a(j + 2, j & 1, c); });
+            read_stage(j);
+#pragma unroll
+            for (int c = 0; c < CH; ++c)
+                copy_b(j + 1, (j + 1) & 1, 1, c);
+#pragma unroll
+            for (int c = 0; c < CH; ++c)
+                copy_b(j + 2, j & 1, 0, c);
+            __builtin_amdgcn_s_waitcnt(vmcnt_le(2 * CH) & ~(0xF << 8));
             phase_end();
+            mfma_phase();
+        }
+        for (; j + 1 < KT; ++j) {
+            read_stage(j);
+#pragma unroll
+            for (int c = 0; c < CH; ++c)
+                copy_b(j + 1, (j + 1) & 1, 1, c);
+            __builtin_amdgcn_s_waitcnt(vmcnt_le(CH) & ~(0xF << 8));
+            phase_end();
+            mfma_phase();
         }
         for (; j < KT; ++j) {
-            read_phase(j);
-            mfma_stage(0, no_copy);
+            read_stage(j);
+            __builtin_amdgcn_s_waitcnt(LGKM0);
             phase_end();
+            mfma_phase();
         }
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
