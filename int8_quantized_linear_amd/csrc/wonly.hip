@@ -13,9 +13,16 @@
 // Design. Decode is bound by HBM bandwidth, and at these sizes by how many bytes are in
 // flight: a CU's share of the weights (64 KB for 4096 x 4096 int8 over 256 CUs) is about
 // what HBM latency times the CU's share of bandwidth asks for. So each wave keeps a ring
-// of D k-steps of loads in flight in registers, issued D steps ahead of use, and the
-// columns are spread so that every CU gets a share (a workgroup covers ceil(N / CUs)
-// columns, rounded up to 8; its 4 waves split K four ways).
+// of D k-steps of loads in flight, issued D steps ahead of use, and the columns are
+// spread so that every CU gets a share (a workgroup covers ceil(N / CUs) columns, rounded
+// up to 8; its 4 waves split K four ways).
+//
+// Every global load is laid out so that the four lanes of a quad read one contiguous
+// piece: the L1 then serves a quad with one request, where four lanes on four rows or
+// columns (the MFMA operand layout) cost four, which caps a CU at about a third of the
+// rate. Weights come into registers that way and a lane permute puts them in MFMA order;
+// activations are copied straight into a ring in LDS (16 bytes a lane, whole row pieces)
+// and read back in MFMA order.
 //
 // Codes are turned into fp16 numbers that are the integers (q - z) exactly: an 8-bit
 // offset code u is placed in the low byte of fp16 1024.0 (bits 0x6400), giving exactly
@@ -29,6 +36,9 @@
 // Loads go through buffer descriptors: a lane whose column is past N, a row past M, or
 // a step past the wave's K range gets an offset beyond the descriptor's size, and the
 // hardware returns zeros without touching memory, so the ring needs no branches.
+#include <type_traits>
+#include <utility>
+
 #include "ql_internal.h"
 
 namespace ql {
@@ -101,6 +111,24 @@ __device__ inline void lds_copy4(const void* g, void* lds) {
 #endif
 }
 
+// 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at l * 16 past
+// the wave-uniform LDS address. An offset past the descriptor's size writes zeros.
+__device__ inline void lds_copy16(__amdgpu_buffer_rsrc_t r, int voff, int soff, void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds, 16, voff, soff, 0, 0);
+#endif
+}
+
+template <typename F, int... I>
+__device__ inline void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, in order.
+template <int N, typename F>
+__device__ inline void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // s_waitcnt immediate: at most n vector-memory operations pending (gfx9 encoding: vmcnt in
 // bits 3:0 and 15:14; expcnt and lgkmcnt left at their maxima).
 constexpr int vmcnt_le(int n) { return (n & 0xF) | (0x7 << 4) | (0xF << 8) | (((n >> 4) & 3) << 14); }
@@ -119,22 +147,60 @@ struct Geo {
     static_assert(WB == 8 || WB == 16, "a lane loads 8 or 16 bytes of a column per step");
 };
 
-// Scales (and zero points) of the workgroup's columns, staged in LDS when they fit.
-constexpr int SL_WORDS = 8192;   // 32 KB
+// Activation ring in LDS. A slot holds one k-step of the launch's 16 MT rows: RB bytes per
+// row, filled by NXC copies of 1 KiB (RPC rows each). Chunk c (16 bytes) of row r sits at
+// position c ^ (r & XM) of its row, so that the 16 lanes of an MFMA-layout read (16 rows,
+// one chunk) fall on 16 different bank groups, while the 4 lanes of a copy quad still read
+// one aligned 64-byte piece. With 8 rows per copy (128-byte rows) a 16-byte pad after each
+// copy moves rows 8..15 to the other bank groups.
+template <int KS, int MT>
+struct XRing {
+    static constexpr int RB = KS * 2;
+    static constexpr int CPR = RB / 16;               // chunks per row
+    static constexpr int RPC = 1024 / RB;             // rows per copy
+    static constexpr int XM = CPR - 1;                // swizzle mask
+    static constexpr int PAD = RPC == 8 ? 16 : 0;
+    static constexpr int CSTRIDE = 1024 + PAD;        // bytes per copy in LDS
+    static constexpr int NXC = MT * 16 / RPC;         // copies per slot
+    static constexpr int SLOT = NXC * CSTRIDE;
+    static constexpr int ISTRIDE = (16 / RPC) * CSTRIDE;   // bytes between 16-row blocks
+    static constexpr int QV = CPR / RPC > 1 ? CPR / RPC : 1;   // copies before the swizzle repeats
+    static constexpr int QROWS = QV * RPC;
+};
 
-// Ring depth: as many k-steps of loads in flight as fit in about 250 registers per lane
-// beside the accumulators and the operands of the step being computed, as a power of two
-// (at most 16) so that it divides a wave's step count when K is a multiple of 4 * KS * D
-// (the loop is padded to whole rings with zero-filled steps).
-template <int FMT, int KS, int MT, int NT, bool GLOAD, int NW>
+// Waves per workgroup: two per SIMD at 17..32 rows, where each step carries enough work
+// (dequantization and MFMAs) that a second wave per SIMD hides one wave's waits; one per
+// SIMD otherwise, leaving LDS to deeper rings.
+template <int MT>
+constexpr int nwaves() { return MT == 2 ? 8 : 4; }
+constexpr int LDS_BUDGET = 150 * 1024;  // activation rings + partial sums + scales
+
+// Scales (and zero points) of the workgroup's columns, staged in LDS when they fit.
+constexpr int SL_WORDS = 4096;   // 16 KB
+
+// Ring depth: as many k-steps in flight as the weight registers (about 280 per lane beside
+// the accumulators and the operands of the step being computed) and the LDS activation
+// ring allow, as a power of two (at most 16) so that it divides a wave's step count when
+// K is a multiple of 4 * KS * D (the loop is padded to whole rings with zero-filled steps).
+// The waves' partial sums share the first ring slot when they fit in it.
+template <int KS, int MT, int NT>
+constexpr int red_extra() {
+    constexpr int red = nwaves<MT>() * MT * NT * 64 * 16, slot = nwaves<MT>() * XRing<KS, MT>::SLOT;
+    return red > slot ? red : 0;
+}
+
+template <int FMT, int KS, int MT, int NT, bool GLOAD>
 constexpr int ring_depth() {
     using G = Geo<FMT, KS>;
-    constexpr int per_step = NT * (G::WB / 4) + MT * G::HN * 4 + (GLOAD ? NT * (FMT == W_UINT8_ZP ? 2 : 1) : 0);
-    constexpr int fixed = MT * NT * 4 + MT * G::HN * 4 + 12 + NT * 2 + MT + 24;
-    // one wave per SIMD (NW = 4) may use about 280 registers (VGPRs and AGPRs); two
-    // (NW = 8) share the file and get about 200 each
-    constexpr int d = ((NW == 4 ? 280 : 200) - fixed) / per_step;
-    return d >= 16 ? 16 : d >= 8 ? 8 : d >= 4 ? 4 : 2;
+    constexpr int per_step = NT * (G::WB / 4) + (GLOAD ? NT * (FMT == W_UINT8_ZP ? 2 : 1) : 0);
+    constexpr int fixed = MT * NT * 4 + 2 * MT * G::HN * 4 + 12 + NT * 2 + MT + 24 + G::HN;
+    // one wave per SIMD may use about 280 registers (VGPRs and AGPRs); two share the file
+    // and get about 200 each
+    constexpr int dr = ((nwaves<MT>() == 4 ? 280 : 200) - fixed) / per_step;
+    constexpr int dl = (LDS_BUDGET - SL_WORDS * 4 - red_extra<KS, MT, NT>()) / (nwaves<MT>() * XRing<KS, MT>::SLOT);
+    constexpr int d = dr < dl ? dr : dl;
+    // at most 8: each slot is its own LDS array (see the kernel)
+    return d >= 8 ? 8 : d >= 4 ? 4 : 2;
 }
 
 // One workgroup of NW waves: `cols` (<= 16 NT) consecutive columns from col0, all M
@@ -142,19 +208,37 @@ constexpr int ring_depth() {
 // column col0 + 16 j + ln of block j. SCALES: 0 = one scale per column (applied at the
 // end), 1 = per group, staged in LDS, 2 = per group, loaded from global memory each step
 // (blocks too large for LDS).
-template <int FMT, int KS, int MT, int NT, int SCALES, int D, int NW>
-__global__ __launch_bounds__(64 * NW) void wonly_kernel(
+template <int FMT, int KS, int MT, int NT, int SCALES, int D>
+__global__ __launch_bounds__(64 * nwaves<MT>()) void wonly_kernel(
     const _Float16* __restrict__ X, const uint8_t* __restrict__ Wc, const void* __restrict__ scale,
     const uint8_t* __restrict__ zp, int group, const float* __restrict__ bias,
     _Float16* __restrict__ Y, int M, int N, int K, int cols) {
     using G = Geo<FMT, KS>;
+    using XG = XRing<KS, MT>;
     using WR = typename G::WR;
+    constexpr int NW = nwaves<MT>();
     constexpr int HN = G::HN;
     constexpr bool GROUPED = SCALES != 0;
     constexpr bool ZP = FMT == W_UINT8_ZP;
     constexpr int SB = FMT == W_INT4_SYM ? 2 : 4;   // bytes per scale
-    __shared__ f32x4 red[NW * MT * NT * 64];
+    // Ring slot u of all waves is an LDS array of its own: the compiler's wait before an
+    // LDS read then covers only the copies into the slot read (the array's latest
+    // copies), not every copy in flight. After the K loop the waves' partial sums go to
+    // slot 0, or to an array of their own when larger.
+    static_assert(D <= 8, "one LDS array per ring slot");
+    constexpr int SLOTB = NW * XG::SLOT, REDX = red_extra<KS, MT, NT>();
+    __shared__ __attribute__((aligned(16))) char xs0[SLOTB];
+    __shared__ __attribute__((aligned(16))) char xs1[D > 1 ? SLOTB : 16];
+    __shared__ __attribute__((aligned(16))) char xs2[D > 2 ? SLOTB : 16];
+    __shared__ __attribute__((aligned(16))) char xs3[D > 3 ? SLOTB : 16];
+    __shared__ __attribute__((aligned(16))) char xs4[D > 4 ? SLOTB : 16];
+    __shared__ __attribute__((aligned(16))) char xs5[D > 5 ? SLOTB : 16];
+    __shared__ __attribute__((aligned(16))) char xs6[D > 6 ? SLOTB : 16];
+    __shared__ __attribute__((aligned(16))) char xs7[D > 7 ? SLOTB : 16];
+    __shared__ __attribute__((aligned(16))) char redx[REDX ? REDX : 16];
     __shared__ uint32_t sl[SCALES == 1 ? SL_WORDS : 1];
+    char* const xslot[8] = {xs0, xs1, xs2, xs3, xs4, xs5, xs6, xs7};
+    f32x4* red = reinterpret_cast<f32x4*>(REDX ? redx : xs0);
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -198,22 +282,39 @@ __global__ __launch_bounds__(64 * NW) void wonly_kernel(
     // scalar offset. A lane outside the columns or rows gets OOB, which stays past every
     // descriptor size when the step's bytes (below 2^22) are added, so the hardware
     // returns zeros.
+    //
+    // Weights are loaded with the lanes of a quad on one column (lane l: column
+    // 16 j + (l >> 2), chunk l & 3), so that each quad reads one contiguous 4 WB-byte piece:
+    // the L1 serves a quad in one request, against one request per lane when the four lanes
+    // of a quad sit on four columns as in the MFMA layout (3x the load rate per CU). A lane
+    // permute then moves chunk lg of column ln to MFMA lane (ln, lg).
     int woff[NT], soff[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-        const int c = 16 * j + ln;
-        woff[j] = c < ncols ? c * wrow + s0 * G::WSTEP + lg * G::WB : OOB;
-        soff[j] = min(c, ncols - 1) * ngroups;   // clamped column: scale and zero index
+        const int cq = 16 * j + (lane >> 2);
+        woff[j] = cq < ncols ? cq * wrow + s0 * G::WSTEP + (lane & 3) * G::WB : OOB;
+        soff[j] = min(16 * j + ln, ncols - 1) * ngroups;   // clamped column: scale and zero index
     }
-    int xoff[MT];
+    const int wperm = (4 * ln + lg) * 4;   // ds_bpermute byte address of the source lane
+    // Activation copies: lane l of copy q takes row q RPC + l / CPR and chunk (l % CPR) ^
+    // (row & XM); the row sits in the vector offset, so rows past M read zeros. The
+    // swizzle repeats every QV copies.
+    int xcv[XG::QV];
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
-        const int m = 16 * i + ln;
-        xoff[i] = m < M ? m * K * 2 + s0 * KS * 2 + lg * G::KSL * 2 : OOB;
+    for (int v = 0; v < XG::QV; ++v) {
+        const int r = v * XG::RPC + lane / XG::CPR;
+        xcv[v] = r * K * 2 + s0 * KS * 2 + (((lane % XG::CPR) ^ (r & XG::XM)) * 16);
+    }
+    // Fragment reads: row 16 i + ln, chunk HN lg + h, in this wave's ring.
+    int xfo[HN];
+    {
+        const int row = (ln / XG::RPC) * XG::CSTRIDE + (ln % XG::RPC) * XG::RB;
+#pragma unroll
+        for (int h = 0; h < HN; ++h)
+            xfo[h] = wave * XG::SLOT + row + (((HN * lg + h) ^ (ln & XG::XM)) * 16);
     }
 
     WR w[D][NT];
-    u32x4 x[D][MT][HN];
     float sc[D][NT];
     int zq[D][NT];
     // group of the next step loaded, and the step within it (loads come in step order)
@@ -231,6 +332,11 @@ __global__ __launch_bounds__(64 * NW) void wonly_kernel(
         // past the range: OR every offset up to OOB or beyond (a uniform mask, so that the
         // compiler keeps one straight-line path)
         const int oob = __builtin_amdgcn_readfirstlane(t < T ? 0 : OOB);
+        char* xs = xslot[u] + wave * XG::SLOT;
+#pragma unroll
+        for (int q = 0; q < XG::NXC; ++q)
+            lds_copy16(xr, (xcv[q % XG::QV] + (q / XG::QV) * XG::QROWS * K * 2) | oob, t * KS * 2,
+                       xs + q * XG::CSTRIDE);
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
             const int vo = woff[j] | oob;
@@ -238,13 +344,6 @@ __global__ __launch_bounds__(64 * NW) void wonly_kernel(
                 w[u][j] = __builtin_bit_cast(WR, __builtin_amdgcn_raw_buffer_load_b64(wr, vo, t * G::WSTEP, 0));
             else
                 w[u][j] = __builtin_bit_cast(WR, __builtin_amdgcn_raw_buffer_load_b128(wr, vo, t * G::WSTEP, 0));
-        }
-#pragma unroll
-        for (int i = 0; i < MT; ++i) {
-            const int vo = xoff[i] | oob;
-#pragma unroll
-            for (int h = 0; h < HN; ++h)
-                x[u][i][h] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, vo + h * 16, t * KS * 2, 0));
         }
         if constexpr (SCALES == 2) {
             const int g = next_group();
@@ -283,30 +382,44 @@ __global__ __launch_bounds__(64 * NW) void wonly_kernel(
         for (int j = 0; j < NT; ++j)
             acc[i][j] = f32x4{0, 0, 0, 0};
 
-    auto compute = [&](int u) {
+    // Vector-memory operations of one step, in issue order: the activation copies, the
+    // weight loads, the scale (and zero-point) loads.
+    constexpr int NSC = SCALES == 2 ? NT * (ZP ? 2 : 1) : 0;
+    constexpr int NL = XG::NXC + NT + NSC;
+    // Step u of the ring, with `after` later steps already issued: its activation copies are
+    // complete once no more than the step's own later loads and those steps are pending.
+    auto compute = [&](int u, auto after) {
+        constexpr int pending = NT + NSC + decltype(after)::value * NL;
+        __builtin_amdgcn_s_waitcnt(vmcnt_le(pending < 63 ? pending : 63));
+        __builtin_amdgcn_sched_barrier(0);
         // the next step's scales are read from LDS one step ahead, so that their latency
         // hides behind this step's work
         if constexpr (SCALES == 1)
             lds_scales((u + 1) % D);
         f16x8 xa[MT][HN];
+        const char* xs = xslot[u];
 #pragma unroll
         for (int i = 0; i < MT; ++i)
 #pragma unroll
             for (int h = 0; h < HN; ++h) {
-                const f16x8 v = __builtin_bit_cast(f16x8, x[u][i][h]);
+                const f16x8 v = *reinterpret_cast<const f16x8*>(xs + xfo[h] + i * XG::ISTRIDE);
                 xa[i][h] = FMT == W_INT4_SYM ? interleave4(v) : v;
             }
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
+            WR wv;
+#pragma unroll
+            for (int d = 0; d < G::WB / 4; ++d)
+                wv[d] = (uint32_t)__builtin_amdgcn_ds_bpermute(wperm, (int)w[u][j][d]);
             f16x8 wb[HN];
             if constexpr (FMT == W_INT4_SYM) {
 #pragma unroll
                 for (int h = 0; h < HN; ++h)
-                    wb[h] = int4_to_f16(w[u][j][h]);
+                    wb[h] = int4_to_f16(wv[h]);
             } else if constexpr (FMT == W_INT8_SYM) {
-                bytes_to_f16(w[u][j], 0x80808080u, (_Float16)1152.0f, wb[0], wb[1]);
+                bytes_to_f16(wv, 0x80808080u, (_Float16)1152.0f, wb[0], wb[1]);
             } else {
-                bytes_to_f16(w[u][j], 0u, (_Float16)(float)(1024 + zq[u][j]), wb[0], wb[1]);
+                bytes_to_f16(wv, 0u, (_Float16)(float)(1024 + zq[u][j]), wb[0], wb[1]);
             }
 #pragma unroll
             for (int i = 0; i < MT; ++i) {
@@ -331,7 +444,7 @@ __global__ __launch_bounds__(64 * NW) void wonly_kernel(
     if constexpr (SCALES == 1) {
         // This wave's copies into LDS are older than the D steps of loads just issued; then
         // the barrier makes every wave's copies visible.
-        constexpr int younger = D * (NT + MT * HN);
+        constexpr int younger = D * NL;
         __builtin_amdgcn_s_waitcnt(vmcnt_le(younger < 63 ? younger : 63));
         asm volatile("s_barrier" ::: "memory");
         lds_scales(0);
@@ -341,29 +454,55 @@ __global__ __launch_bounds__(64 * NW) void wonly_kernel(
     for (int tb = 0; tb + D < TP; tb += D) {
 #pragma unroll
         for (int u = 0; u < D; ++u) {
-            compute(u);
+            compute(u, std::integral_constant<int, D - 1>{});
+            // the slot's reads have completed: their values feed this step's MFMAs
+            __builtin_amdgcn_sched_barrier(0);
             load(u, tb + D + u);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-#pragma unroll
-    for (int u = 0; u < D; ++u) {
-        compute(u);
+    static_for<D>([&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        compute(u, std::integral_constant<int, D - 1 - u>{});
         __builtin_amdgcn_sched_barrier(0);
-    }
+    });
 
-    // The waves' partial sums meet in LDS; wave w then finishes blocks b = w (mod NW).
+    // The waves' partial sums meet in LDS (over the rings: every wave must be done with
+    // its ring first); wave w then finishes blocks b = w (mod NW). Their per-column
+    // factors are loaded first, before any store: a vector-memory wait also waits for the
+    // stores already issued, so a load between two blocks' stores would hold the second
+    // block until the first one's stores had completed.
+    constexpr int NB = (MT * NT + NW - 1) / NW;   // blocks per wave, at most
+    float cscale[NB], cbias[NB];
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+        const int b = wave + k * NW;
+        const int n = col0 + min(16 * (b % NT) + ln, ncols - 1);
+        cscale[k] = 1.0f;
+        cbias[k] = 0.0f;
+        if (b < MT * NT) {
+            if constexpr (!GROUPED)
+                cscale[k] = reinterpret_cast<const float*>(scale)[n];
+            if (bias)
+                cbias[k] = bias[n];
+        }
+    }
+    __syncthreads();
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
         for (int j = 0; j < NT; ++j)
             red[((wave * MT + i) * NT + j) * 64 + lane] = acc[i][j];
     __syncthreads();
+    // The factors have arrived (nothing else is pending): said once here, so that the
+    // compiler sees no load outstanding at the per-row store branches below.
+    __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
     // Output element r of block (i, j) in lane l is C[4 (l >> 4) + r][l & 15].
 #pragma unroll
-    for (int b = 0; b < MT * NT; ++b) {
-        if (b % NW != wave)
-            continue;
+    for (int k = 0; k < NB; ++k) {
+        const int b = wave + k * NW;
+        if (b >= MT * NT)
+            break;
         const int i = b / NT, j = b % NT;
         f32x4 v = red[b * 64 + lane];
 #pragma unroll
@@ -374,13 +513,12 @@ __global__ __launch_bounds__(64 * NW) void wonly_kernel(
             continue;
         const int n = col0 + c;
         if constexpr (!GROUPED)
-            v *= reinterpret_cast<const float*>(scale)[n];
-        const float bb = bias ? bias[n] : 0.0f;
+            v *= cscale[k];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int m = 16 * i + 4 * lg + r;
             if (m < M)
-                Y[(int64_t)m * N + n] = (_Float16)(v[r] + bb);
+                Y[(int64_t)m * N + n] = (_Float16)(v[r] + cbias[k]);
         }
     }
 }
@@ -398,13 +536,13 @@ int cu_count() {
     return n;
 }
 
-template <int FMT, int KS, int MT, int NT, int SCALES, int NW>
+template <int FMT, int KS, int MT, int NT, int SCALES>
 ql_status launch_cfg(const void* x, const void* codes, const void* scale, const uint8_t* zp,
                      int64_t group, const float* bias, void* y, int64_t M, int64_t N, int64_t K,
                      int cols, hipStream_t stream) {
-    constexpr int D = ring_depth<FMT, KS, MT, NT, SCALES == 2, NW>();
-    const dim3 grid((unsigned)((N + cols - 1) / cols)), block(64 * NW);
-    hipLaunchKernelGGL((wonly_kernel<FMT, KS, MT, NT, SCALES, D, NW>), grid, block, 0, stream,
+    constexpr int D = ring_depth<FMT, KS, MT, NT, SCALES == 2>();
+    const dim3 grid((unsigned)((N + cols - 1) / cols)), block(64 * nwaves<MT>());
+    hipLaunchKernelGGL((wonly_kernel<FMT, KS, MT, NT, SCALES, D>), grid, block, 0, stream,
                        reinterpret_cast<const _Float16*>(x), reinterpret_cast<const uint8_t*>(codes),
                        scale, zp, (int)group, bias, reinterpret_cast<_Float16*>(y), (int)M, (int)N,
                        (int)K, cols);
@@ -415,13 +553,11 @@ template <int FMT, int KS, int MT, int SCALES>
 ql_status launch_nt(const void* x, const void* codes, const void* scale, const uint8_t* zp,
                     int64_t group, const float* bias, void* y, int64_t M, int64_t N, int64_t K,
                     int cols, hipStream_t stream) {
-    // Two waves per SIMD where one wave's registers cannot hold enough steps in flight.
-    constexpr int NW = MT == 2 ? 8 : 4;
     if (cols <= 16)
-        return launch_cfg<FMT, KS, MT, 1, SCALES, NW>(x, codes, scale, zp, group, bias, y, M, N, K, cols, stream);
+        return launch_cfg<FMT, KS, MT, 1, SCALES>(x, codes, scale, zp, group, bias, y, M, N, K, cols, stream);
     if (cols <= 32)
-        return launch_cfg<FMT, KS, MT, 2, SCALES, NW>(x, codes, scale, zp, group, bias, y, M, N, K, cols, stream);
-    return launch_cfg<FMT, KS, MT, 4, SCALES, NW>(x, codes, scale, zp, group, bias, y, M, N, K, cols, stream);
+        return launch_cfg<FMT, KS, MT, 2, SCALES>(x, codes, scale, zp, group, bias, y, M, N, K, cols, stream);
+    return launch_cfg<FMT, KS, MT, 4, SCALES>(x, codes, scale, zp, group, bias, y, M, N, K, cols, stream);
 }
 
 template <int FMT, int KS, int MT>
