@@ -106,6 +106,34 @@ def test_w4a16_ragged(ql, M, N, K, group):
     _w4a16(ql, workloads.with_shape(workloads.W4A16_GROUP, M, K, N), group, with_bias=True)
 
 
+@pytest.mark.parametrize("fmt,M,N,K,group", [
+    ("u8", 8, 16384, 4096, 64),     # 64 columns x 64 blocks: scales + zero points exceed LDS
+    ("i8", 20, 16384, 4096, 64),    # int8 with group scales, 64 x 64 fp32 scales: over LDS
+    ("int4", 40, 3000, 1024, 64),   # 33..64 rows with 64-deep int4 steps
+])
+def test_large_scale_blocks_and_row_tiles(ql, fmt, M, N, K, group):
+    """Plans whose scale block is too large for LDS (scales and zero points loaded from
+    global memory every step, beside the activation ring), and four row tiles with 64-deep
+    int4 steps."""
+    if fmt == "int4":
+        _w4a16(ql, workloads.with_shape(workloads.W4A16_GROUP, M, K, N, seed=M + N), group,
+               with_bias=True, cols=np.arange(0, N, 7))
+        return
+    if fmt == "u8":
+        _w8a16_block(ql, workloads.with_shape(workloads.W8A16_BLOCK, M, K, N, seed=M + N), group,
+                     with_bias=True)
+        return
+    w = workloads.with_shape(workloads.W8A16_DECODE, M, K, N, seed=M + N)
+    inp = workloads.draw(w)
+    rng = np.random.default_rng(M * N + K)
+    q_ref = rng.integers(-127, 128, (N, K), dtype=np.int8)
+    s_ref = rng.uniform(1e-3, 1e-2, (N, K // group)).astype(np.float32)
+    g = Guarded((M, N), torch.float16)
+    ql.gemm_w8a16(dev(inp.x), dev(q_ref), dev(s_ref), None, group, None, y=g.view)
+    g.check()
+    check_wonly(host(g.view), oracle.w8a16_f64(inp.x, q_ref, s_ref, group_size=group))
+
+
 def test_one_hot_exact(ql):
     """x = e_k: y[n] is fp16((q[k,n] - z) * s) exactly for all three formats."""
     N, K = 40, 256
