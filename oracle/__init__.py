@@ -61,6 +61,7 @@ def _declare(L):
     L.oracle_quant_block_asym_u8.argtypes = [_P, _I64, _I64, _I64, _P, _P, _P]
     L.oracle_quant_int4_group.argtypes = [_P, _I64, _I64, _I64, _P, _P]
     L.oracle_num_threads.restype = ctypes.c_int
+    L.oracle_activation_f64.argtypes = [_P, _I64, ctypes.c_int]
 
 
 def _ptr(a: Optional[np.ndarray]):
@@ -170,6 +171,15 @@ class Oracle:
         self.L.oracle_wonly_f64(_ptr(xf), M, K, _ptr(codes), kind, _ptr(s), _ptr(z), group_size,
                                _ptr(b), N, _ptr(y64))
         return y64
+
+    ACT_NONE, ACT_GELU, ACT_SILU = 0, 1, 2
+
+    def activation_f64(self, y, act: int) -> np.ndarray:
+        """The epilogue's activation of an fp64 output, elementwise: 1 = GELU (exact,
+        y * Phi(y)), 2 = SiLU (y * sigmoid(y)), 0 = none. Returns a new array."""
+        out = np.array(y, dtype=np.float64, order="C", copy=True)
+        self.L.oracle_activation_f64(_ptr(out), out.size, int(act))
+        return out
 
     def w4a16_f64(self, x, packed_nk8, scale16, group_size: int, bias=None) -> np.ndarray:
         """fp64 W4A16 product; scale16 is fp16 (or its uint16 bits) [N, K/group]."""

@@ -338,6 +338,29 @@ void oracle_quant_int4_group(const float* w, int64_t N, int64_t K, int64_t group
     }
 }
 
+/* ------------------------------------------------------------ activations */
+
+/* The activation the epilogue applies to the layer's output (after the scales and the
+ * bias, before the output is rounded), elementwise and in place, in fp64:
+ *   act 1, GELU: y * Phi(y), Phi the standard normal distribution function,
+ *          Phi(y) = (1 + erf(y / sqrt 2)) / 2, the exact form (the pages name GELU and
+ *          give no approximation)
+ *   act 2, SiLU: y * sigmoid(y) = y / (1 + exp(-y))
+ *   act 0: none.
+ * quant67.com ch.17 §四 (scales, bias and the activation applied in the epilogue while
+ * the result is in registers); xdnf.cn INT4/FP16 mixed GEMM §8 (GELU fused after the
+ * INT4 GEMM, with no intermediate write-back). */
+void oracle_activation_f64(double* y, int64_t n, int act)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        double v = y[i];
+        if (act == 1)
+            y[i] = v * (0.5 * (1.0 + erf(v / sqrt(2.0))));
+        else if (act == 2)
+            y[i] = v / (1.0 + exp(-v));
+    }
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP

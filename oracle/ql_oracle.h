@@ -30,6 +30,7 @@ void oracle_quant_block_asym_u8(const float* w, int64_t N, int64_t K, int64_t bl
 void oracle_quant_int4_group(const float* w, int64_t N, int64_t K, int64_t group,
                              int32_t* packed, uint16_t* scale16);
 
+void oracle_activation_f64(double* y, int64_t n, int act);
 int oracle_num_threads(void);
 
 #endif

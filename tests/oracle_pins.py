@@ -419,4 +419,40 @@ def pin_footprint_golden(orc):
         assert abs(size - float(printed)) <= 0.5 * 10 ** -nd + 1e-9, (params, bits, size, printed)
 
 
+# Standard normal distribution function at tabulated points (values from a normal table,
+# to 16 significant digits); 1.959963984540054 is the 0.975 quantile.
+PHI_TABLE = {-3.0: 0.001349898031630095, -0.5: 0.3085375387259869, 0.0: 0.5,
+             1.0: 0.8413447460685429, 2.0: 0.9772498680518208, 1.959963984540054: 0.975}
+
+
+def pin_activation_values(orc):
+    """GELU(y) = y Phi(y) at tabulated points of Phi; SiLU(y) = y sigmoid(y) where sigmoid
+    is rational (sigmoid(0) = 1/2, sigmoid(ln 3) = 3/4, sigmoid(-ln 3) = 1/4) or
+    e / (1 + e) at 1; act 0 is the identity."""
+    ys = np.array(sorted(PHI_TABLE))
+    got = orc.activation_f64(ys, 1)
+    want = ys * np.array([PHI_TABLE[v] for v in ys])
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-300), (got, want)
+    s = np.array([0.0, np.log(3.0), -np.log(3.0), 1.0])
+    got = orc.activation_f64(s, 2)
+    want = s * np.array([0.5, 0.75, 0.25, np.e / (1.0 + np.e)])
+    assert np.allclose(got, want, rtol=1e-14, atol=0.0), (got, want)
+    r = np.random.default_rng(71).standard_normal(64) * 5
+    assert np.array_equal(orc.activation_f64(r, 0), r)
+
+
+def pin_activation_invariants(orc):
+    """For both activations act(y) - act(-y) = y (Phi(-y) = 1 - Phi(y) and
+    sigmoid(-y) = 1 - sigmoid(y)); act(y) -> y for large y and -> 0 for very negative y;
+    both are increasing for y >= 0."""
+    y = np.random.default_rng(72).standard_normal(4096) * 4
+    for act in (1, 2):
+        a, b = orc.activation_f64(y, act), orc.activation_f64(-y, act)
+        assert np.allclose(a - b, y, rtol=0, atol=1e-12 * (1 + np.abs(y)).max())
+        big = orc.activation_f64(np.array([40.0, -40.0]), act)
+        assert abs(big[0] - 40.0) < 1e-12 and abs(big[1]) < 1e-12
+        pos = orc.activation_f64(np.linspace(0, 10, 1001), act)
+        assert np.all(np.diff(pos) > 0)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -43,6 +43,11 @@ MUTANTS = [
     ("block_range_254", "float s = (mx - mn) / 255.0f;", "float s = (mx - mn) / 254.0f;"),
     ("f16_ties_away", "double r = nearbyint(ldexp(a, 10 - E));", "double r = round(ldexp(a, 10 - E));"),
     ("f16_subnormal_scale", "v = ldexp((double)f, -24);", "v = ldexp((double)f, -25);"),
+    ("gelu_tanh_form", "y[i] = v * (0.5 * (1.0 + erf(v / sqrt(2.0))));",
+     "y[i] = 0.5 * v * (1.0 + tanh(0.7978845608028654 * (v + 0.044715 * v * v * v)));"),
+    ("gelu_no_sqrt2", "erf(v / sqrt(2.0))", "erf(v)"),
+    ("silu_exp_sign", "y[i] = v / (1.0 + exp(-v));", "y[i] = v / (1.0 + exp(v));"),
+    ("act_codes_swapped", "if (act == 1)\n            y[i] = v * (0.5", "if (act == 2)\n            y[i] = v * (0.5"),
 ]
 
 
