@@ -108,6 +108,45 @@ def cpu_baseline(target_s: float):
             "seconds": dt, "host": platform.processor() or platform.machine()}
 
 
+def fused_activation_timings(ql, n, gemm, dec5, r5, make_gemm, make_dec, ops, w4_bytes, gemm_name,
+                             dec_name, progress):
+    """The epilogue with a fused activation (GELU, SiLU) against the plain epilogue: the
+    W8A8 GEMM at the prefill shape and W4A16 at the decode shape, each launch event-timed
+    on the launch stream. Plain and fused launches alternate so that both run at the same
+    clock; the decode weights rotate as in the step loop."""
+    import torch
+    progress("fused activations: %d launches each" % n)
+    gelu, silu = ql.ACTIVATIONS["gelu"], ql.ACTIVATIONS["silu"]
+    runs = {"w8a8_plain": lambda i: gemm(), "w8a8_gelu": (lambda f: lambda i: f())(make_gemm(gelu)),
+            "w8a8_silu": (lambda f: lambda i: f())(make_gemm(silu)),
+            "w4a16_plain": lambda i: dec5[i % r5]()}
+    dec_g = make_dec(gelu)
+    runs["w4a16_gelu"] = lambda i: dec_g[i % r5]()
+    ev = {k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+          for k in runs}
+    for i in range(3):
+        for f in runs.values():
+            f(i)
+    torch.cuda.synchronize()
+    for i in range(n):
+        for k, f in runs.items():
+            ev[k][i][0].record()
+            f(i)
+            ev[k][i][1].record()
+    torch.cuda.synchronize()
+    us = {k: 1e3 * sum(a.elapsed_time(b) for a, b in v) / n for k, v in ev.items()}
+    return {
+        gemm_name: {"plain_us": us["w8a8_plain"], "gelu_us": us["w8a8_gelu"], "silu_us": us["w8a8_silu"],
+                    "gelu_TOPS": ops / (us["w8a8_gelu"] * 1e-6) / 1e12,
+                    "gelu_overhead": us["w8a8_gelu"] / us["w8a8_plain"] - 1,
+                    "silu_overhead": us["w8a8_silu"] / us["w8a8_plain"] - 1},
+        dec_name: {"plain_us": us["w4a16_plain"], "gelu_us": us["w4a16_gelu"],
+                   "gelu_GB_per_s": w4_bytes / (us["w4a16_gelu"] * 1e-6) / 1e9,
+                   "gelu_overhead": us["w4a16_gelu"] / us["w4a16_plain"] - 1},
+        "note": "launches alternate plain / fused; event-timed per launch",
+    }
+
+
 def measured_ceilings(dev, byte_counts, progress):
     """Ceilings measured with libqlprobe.so: int8 MFMA TOPS from registers (random and
     constant operands) and the GB/s of one cold streaming read of each byte count."""
@@ -177,6 +216,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", dest="cpu", action="store_false")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--act-steps", type=int, default=20,
+                    help="launches of each fused-activation variant timed after the step loop (0: skip)")
     ap.add_argument("--no-ceilings", dest="ceilings", action="store_false",
                     help="skip the measured ceilings (MFMA-only and streaming-read probes)")
     ap.add_argument("--calib-copy-mib", type=int, default=256,
@@ -332,6 +373,14 @@ def main():
         "decode": decode,
         "device": torch.cuda.get_device_name(0),
     }
+    if args.act_steps > 0:
+        out["fused_activation"] = fused_activation_timings(
+            ql, args.act_steps, gemm, dec5, r5,
+            lambda code: ql.prepare("gemm_w8a8_per_channel_act", xq3, xs3, wq3, ws3, b3, code, y3, F16,
+                                    w3.M, w3.N, w3.K),
+            lambda code: [ql.prepare("gemm_w4a16_grouped_act", x5, p, s, 128, None, code, y5, w5.M, w5.N,
+                                     w5.K) for p, s in set5],
+            ops, ab["w4a16"], w3.name, w5.name, progress)
     if args.ceilings:
         del set2, set4, set5, dec2, dec4, dec5
         ceil = measured_ceilings(dev, {"quant": ab["quant"], "w8a16": ab["w8a16"],

@@ -69,6 +69,14 @@ typedef enum {
 
 typedef enum { QL_F32 = 0, QL_F16 = 1 } ql_dtype;
 
+/* Activation an epilogue applies to the output after the scales and the bias, in fp32,
+ * before the output is rounded: GELU in its exact form y * Phi(y), Phi the standard
+ * normal distribution function ((1 + erf(y / sqrt 2)) / 2), or SiLU y / (1 + exp(-y)).
+ * [quant67] §四 (scales, bias and activation in the epilogue, while the result is in
+ * registers); [xdnf] §8 (GELU fused after the INT4 GEMM, no intermediate write-back).
+ * An unknown value is QL_ERR_DTYPE. */
+typedef enum { QL_ACT_NONE = 0, QL_ACT_GELU = 1, QL_ACT_SILU = 2 } ql_activation;
+
 /* Human-readable name of a status code (a static string). */
 const char* ql_status_str(ql_status s);
 
@@ -123,6 +131,16 @@ ql_status gemm_w8a8_per_channel(const int8_t* xq, const float* x_scale, const in
                                 void* stream);
 
 /*
+ * gemm_w8a8_per_channel with an activation fused into the epilogue:
+ *   y[m,n] = act(x_scale[m] * w_scale[n] * acc[m,n] + bias[n])
+ * Arguments as for gemm_w8a8_per_channel; act as ql_activation above.
+ */
+ql_status gemm_w8a8_per_channel_act(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                                    const float* w_scale, const float* bias, ql_activation act,
+                                    void* y, ql_dtype y_dtype, int64_t M, int64_t N, int64_t K,
+                                    void* stream);
+
+/*
  * The W8A8 integer accumulators alone, acc[m,n] = sum_k xq[m,k] * wq[k,n] as int32
  * [M,N] row-major. A checking aid for the exact integer stage of
  * gemm_w8a8_per_channel (same main loop); [hotelren] "W8A8矩阵乘法" scheme 1 names
@@ -172,6 +190,15 @@ ql_status gemm_w8a16(const void* x, const void* wq, const float* w_scale,
 ql_status gemm_w4a16_grouped(const void* x, const int32_t* wq_packed, const void* scales,
                              int64_t group_size, const float* bias, void* y, int64_t M,
                              int64_t N, int64_t K, void* stream);
+
+/*
+ * gemm_w4a16_grouped with an activation fused into the epilogue ([xdnf] §8):
+ *   y[m,n] = act(sum_g s[g,n] * sum_{k in g} x[m,k] * q[k,n] + bias[n])
+ * Arguments as for gemm_w4a16_grouped; act as ql_activation above.
+ */
+ql_status gemm_w4a16_grouped_act(const void* x, const int32_t* wq_packed, const void* scales,
+                                 int64_t group_size, const float* bias, ql_activation act, void* y,
+                                 int64_t M, int64_t N, int64_t K, void* stream);
 
 /*
  * Producer of the block-asymmetric uint8 weight format consumed by gemm_w8a16.

@@ -19,6 +19,7 @@ __all__ = [
     "QLError", "lib", "library_path", "quantize_per_row_int8", "quantize_weight_per_channel",
     "gemm_w8a8_per_channel", "gemm_w8a8_int32", "gemm_w8a16", "gemm_w4a16_grouped",
     "quantize_weight_block_asym_u8", "quantize_weight_int4_grouped", "linear_w8a8", "prepare",
+    "gemm_w8a8_per_channel_act", "gemm_w4a16_grouped_act", "ACTIVATIONS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -36,6 +37,8 @@ _I64 = ctypes.c_int64
 _I = ctypes.c_int
 
 QL_F32, QL_F16 = 0, 1
+# ql_activation: applied by the epilogue after the scales and the bias
+ACTIVATIONS = {"none": 0, "gelu": 1, "silu": 2}
 STATUS = {0: "QL_OK", 1: "QL_ERR_NULL", 2: "QL_ERR_SHAPE", 3: "QL_ERR_ALIGN", 4: "QL_ERR_DTYPE",
           5: "QL_ERR_DEVICE"}
 
@@ -46,6 +49,8 @@ _SIGS = {
     "gemm_w8a8_int32": [_P, _P, _P, _I64, _I64, _I64, _P],
     "gemm_w8a16": [_P, _P, _P, _P, _I64, _P, _P, _I64, _I64, _I64, _P],
     "gemm_w4a16_grouped": [_P, _P, _P, _I64, _P, _P, _I64, _I64, _I64, _P],
+    "gemm_w8a8_per_channel_act": [_P, _P, _P, _P, _P, _I, _P, _I, _I64, _I64, _I64, _P],
+    "gemm_w4a16_grouped_act": [_P, _P, _P, _I64, _P, _I, _P, _I64, _I64, _I64, _P],
     "quantize_weight_block_asym_u8": [_P, _I64, _I64, _I64, _P, _P, _P, _P],
     "quantize_weight_int4_grouped": [_P, _I64, _I64, _I64, _P, _P, _P],
 }
@@ -158,8 +163,25 @@ def quantize_weight_int4_grouped(w_nk: torch.Tensor, group: int = 128):
 
 # --------------------------------------------------------------------- GEMMs
 
+def _act_code(act: str) -> int:
+    if act not in ACTIVATIONS:
+        raise ValueError("act must be one of %s" % sorted(ACTIVATIONS))
+    return ACTIVATIONS[act]
+
+
 def gemm_w8a8_per_channel(xq, x_scale, wq, w_scale, bias=None, out_dtype=torch.float16, y=None):
     """y [M, N] = float(xq @ wq^T) * x_scale[:, None] * w_scale[None, :] + bias."""
+    return _gemm_w8a8(xq, x_scale, wq, w_scale, bias, None, out_dtype, y)
+
+
+def gemm_w8a8_per_channel_act(xq, x_scale, wq, w_scale, bias=None, act: str = "gelu",
+                              out_dtype=torch.float16, y=None):
+    """y [M, N] = act(float(xq @ wq^T) * x_scale[:, None] * w_scale[None, :] + bias),
+    act in ACTIVATIONS, applied in the GEMM's epilogue."""
+    return _gemm_w8a8(xq, x_scale, wq, w_scale, bias, _act_code(act), out_dtype, y)
+
+
+def _gemm_w8a8(xq, x_scale, wq, w_scale, bias, act, out_dtype, y):
     _check(xq, "xq", (torch.int8,))
     M, K = xq.shape
     dev = xq.device
@@ -173,8 +195,13 @@ def gemm_w8a8_per_channel(xq, x_scale, wq, w_scale, bias=None, out_dtype=torch.f
     if out_dtype not in (torch.float16, torch.float32):
         raise TypeError("out_dtype must be float16 or float32")
     y = _out(y, "y", (M, N), out_dtype, dev)
-    _call("gemm_w8a8_per_channel", _ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale), _ptr(bias),
-          _ptr(y), QL_F16 if out_dtype == torch.float16 else QL_F32, M, N, K, _stream(xq))
+    ydt = QL_F16 if out_dtype == torch.float16 else QL_F32
+    if act is None:
+        _call("gemm_w8a8_per_channel", _ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale), _ptr(bias),
+              _ptr(y), ydt, M, N, K, _stream(xq))
+    else:
+        _call("gemm_w8a8_per_channel_act", _ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale), _ptr(bias),
+              act, _ptr(y), ydt, M, N, K, _stream(xq))
     return y
 
 
@@ -211,6 +238,15 @@ def gemm_w8a16(x, wq, w_scale, zero_point=None, group_size: int = 0, bias=None, 
 
 def gemm_w4a16_grouped(x, wq_packed, scales, group_size: int, bias=None, y=None):
     """W4A16: x fp16 [M, K]; wq_packed int32 [N, K/8]; scales fp16 [N, K/group_size]."""
+    return _gemm_w4a16(x, wq_packed, scales, group_size, bias, None, y)
+
+
+def gemm_w4a16_grouped_act(x, wq_packed, scales, group_size: int, bias=None, act: str = "gelu", y=None):
+    """gemm_w4a16_grouped with act (in ACTIVATIONS) fused into the epilogue."""
+    return _gemm_w4a16(x, wq_packed, scales, group_size, bias, _act_code(act), y)
+
+
+def _gemm_w4a16(x, wq_packed, scales, group_size, bias, act, y):
     _check(x, "x", (torch.float16,))
     M, K = x.shape
     dev = x.device
@@ -220,8 +256,12 @@ def gemm_w4a16_grouped(x, wq_packed, scales, group_size: int, bias=None, y=None)
     if bias is not None:
         _check(bias, "bias", (torch.float32,), (N,), dev)
     y = _out(y, "y", (M, N), torch.float16, dev)
-    _call("gemm_w4a16_grouped", _ptr(x), _ptr(wq_packed), _ptr(scales), group_size, _ptr(bias),
-          _ptr(y), M, N, K, _stream(x))
+    if act is None:
+        _call("gemm_w4a16_grouped", _ptr(x), _ptr(wq_packed), _ptr(scales), group_size, _ptr(bias),
+              _ptr(y), M, N, K, _stream(x))
+    else:
+        _call("gemm_w4a16_grouped_act", _ptr(x), _ptr(wq_packed), _ptr(scales), group_size, _ptr(bias),
+              act, _ptr(y), M, N, K, _stream(x))
     return y
 
 

@@ -85,10 +85,13 @@ static ql_status check_w8a8(const int8_t* xq, const int8_t* wq, const void* y, i
     return QL_OK;
 }
 
-ql_status gemm_w8a8_per_channel(const int8_t* xq, const float* x_scale, const int8_t* wq,
-                                const float* w_scale, const float* bias, void* y,
-                                ql_dtype y_dtype, int64_t M, int64_t N, int64_t K, void* stream) {
+ql_status gemm_w8a8_per_channel_act(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                                    const float* w_scale, const float* bias, ql_activation act,
+                                    void* y, ql_dtype y_dtype, int64_t M, int64_t N, int64_t K,
+                                    void* stream) {
     if (y_dtype != QL_F32 && y_dtype != QL_F16)
+        return QL_ERR_DTYPE;
+    if (act != QL_ACT_NONE && act != QL_ACT_GELU && act != QL_ACT_SILU)
         return QL_ERR_DTYPE;
     ql_status st = check_w8a8(xq, wq, y, M, N, K);
     if (st != QL_OK || M == 0 || N == 0)
@@ -98,8 +101,15 @@ ql_status gemm_w8a8_per_channel(const int8_t* xq, const float* x_scale, const in
     if (!aligned(x_scale, 4) || !aligned(w_scale, 4) || (bias && !aligned(bias, 4)))
         return QL_ERR_ALIGN;
     return ql::launch_gemm_w8a8(xq, x_scale, wq, w_scale, bias, y,
-                                y_dtype == QL_F32 ? ql::Y_F32 : ql::Y_F16, M, N, K,
+                                y_dtype == QL_F32 ? ql::Y_F32 : ql::Y_F16, (int)act, M, N, K,
                                 as_stream(stream));
+}
+
+ql_status gemm_w8a8_per_channel(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                                const float* w_scale, const float* bias, void* y,
+                                ql_dtype y_dtype, int64_t M, int64_t N, int64_t K, void* stream) {
+    return gemm_w8a8_per_channel_act(xq, x_scale, wq, w_scale, bias, QL_ACT_NONE, y, y_dtype, M, N,
+                                     K, stream);
 }
 
 ql_status gemm_w8a8_int32(const int8_t* xq, const int8_t* wq, int32_t* acc, int64_t M, int64_t N,
@@ -107,8 +117,8 @@ ql_status gemm_w8a8_int32(const int8_t* xq, const int8_t* wq, int32_t* acc, int6
     ql_status st = check_w8a8(xq, wq, acc, M, N, K);
     if (st != QL_OK || M == 0 || N == 0)
         return st;
-    return ql::launch_gemm_w8a8(xq, nullptr, wq, nullptr, nullptr, acc, ql::Y_I32, M, N, K,
-                                as_stream(stream));
+    return ql::launch_gemm_w8a8(xq, nullptr, wq, nullptr, nullptr, acc, ql::Y_I32, ql::ACT_NONE, M,
+                                N, K, as_stream(stream));
 }
 
 ql_status gemm_w8a16(const void* x, const void* wq, const float* w_scale,
@@ -125,12 +135,14 @@ ql_status gemm_w8a16(const void* x, const void* wq, const float* w_scale,
         (zero_point && !aligned(zero_point, 4)) || (bias && !aligned(bias, 4)))
         return QL_ERR_ALIGN;
     return ql::launch_wonly(x, wq, zero_point ? ql::W_UINT8_ZP : ql::W_INT8_SYM, w_scale,
-                            zero_point, group_size, bias, y, M, N, K, as_stream(stream));
+                            zero_point, group_size, bias, y, M, N, K, ql::ACT_NONE, as_stream(stream));
 }
 
-ql_status gemm_w4a16_grouped(const void* x, const int32_t* wq_packed, const void* scales,
-                             int64_t group_size, const float* bias, void* y, int64_t M, int64_t N,
-                             int64_t K, void* stream) {
+ql_status gemm_w4a16_grouped_act(const void* x, const int32_t* wq_packed, const void* scales,
+                                 int64_t group_size, const float* bias, ql_activation act, void* y,
+                                 int64_t M, int64_t N, int64_t K, void* stream) {
+    if (act != QL_ACT_NONE && act != QL_ACT_GELU && act != QL_ACT_SILU)
+        return QL_ERR_DTYPE;
     if (bad_dims(M, N, K) || K % 64 != 0 || K > kMaxKwonly || group_size <= 0 || group_size % 64 != 0 ||
         K % group_size != 0)
         return QL_ERR_SHAPE;
@@ -142,7 +154,14 @@ ql_status gemm_w4a16_grouped(const void* x, const int32_t* wq_packed, const void
         (bias && !aligned(bias, 4)))
         return QL_ERR_ALIGN;
     return ql::launch_wonly(x, wq_packed, ql::W_INT4_SYM, scales, nullptr, group_size, bias, y, M,
-                            N, K, as_stream(stream));
+                            N, K, (int)act, as_stream(stream));
+}
+
+ql_status gemm_w4a16_grouped(const void* x, const int32_t* wq_packed, const void* scales,
+                             int64_t group_size, const float* bias, void* y, int64_t M, int64_t N,
+                             int64_t K, void* stream) {
+    return gemm_w4a16_grouped_act(x, wq_packed, scales, group_size, bias, QL_ACT_NONE, y, M, N, K,
+                                  stream);
 }
 
 ql_status quantize_weight_block_asym_u8(const float* w, int64_t K, int64_t N, int64_t block,

@@ -78,7 +78,7 @@ __device__ inline void issue_scales(const float* xs, const float* ws, const floa
 // Stores go through a buffer descriptor whose size ends at row M: the hardware drops
 // stores of rows past M, and a column piece past N gets an offset beyond the size, so no
 // store needs a branch.
-template <int WM, int WN, int FM, int FN, int YMODE, int NWV>
+template <int WM, int WN, int FM, int FN, int YMODE, int NWV, int ACT>
 __device__ __forceinline__ void store_tile(const i32x16 (&acc)[FM][FN], bool has_bias,
                                            void* __restrict__ Y, int M, int N, int mrow0,
                                            int ncol0, int lm0, int ln0, int wave, int lane,
@@ -136,7 +136,7 @@ __device__ __forceinline__ void store_tile(const i32x16 (&acc)[FM][FN], bool has
                 if constexpr (YMODE == Y_I32)
                     v = acc[i][j][e];
                 else
-                    v = (OutT)((float)acc[i][j][e] * xsv[e] * wsv[j] + bv[j]);
+                    v = (OutT)activation<ACT>((float)acc[i][j][e] * xsv[e] * wsv[j] + bv[j]);
                 *reinterpret_cast<OutT*>(stage + r * ROWB + (32 * j + (lane & 31)) * SZ) = v;
             }
         }
@@ -240,7 +240,7 @@ template <int BM, int BN, int YMODE>
 __device__ __forceinline__ void gemm_tile_pp(const int8_t* __restrict__ A, const float* __restrict__ xs,
                                              const int8_t* __restrict__ B, const float* __restrict__ ws,
                                              const float* __restrict__ bias, void* __restrict__ Y,
-                                             int M, int N, int K, int m0, int n0, int8_t* smem) {
+                                             int M, int N, int K, int m0, int n0, int act, int8_t* smem) {
     constexpr int BKL = 128;
     constexpr int WM = BM / 2, WN = BN / 4, FM = WM / 32, FN = WN / 32;
     constexpr int STAGE_A = BM * BKL, STAGE = (BM + BN) * BKL;
@@ -426,8 +426,16 @@ __device__ __forceinline__ void gemm_tile_pp(const int8_t* __restrict__ A, const
         }
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
-    store_tile<WM, WN, FM, FN, YMODE, 8>(acc, bias != nullptr, Y, M, N, m0 + wm * WM, n0 + wn * WN,
-                                         wm * WM, wn * WN, wave, lane, smem);
+    // the activation is uniform: one epilogue per kind, so that none costs the others
+    if (act == ACT_GELU)
+        store_tile<WM, WN, FM, FN, YMODE, 8, ACT_GELU>(acc, bias != nullptr, Y, M, N, m0 + wm * WM,
+                                                       n0 + wn * WN, wm * WM, wn * WN, wave, lane, smem);
+    else if (act == ACT_SILU)
+        store_tile<WM, WN, FM, FN, YMODE, 8, ACT_SILU>(acc, bias != nullptr, Y, M, N, m0 + wm * WM,
+                                                       n0 + wn * WN, wm * WM, wn * WN, wave, lane, smem);
+    else
+        store_tile<WM, WN, FM, FN, YMODE, 8, ACT_NONE>(acc, bias != nullptr, Y, M, N, m0 + wm * WM,
+                                                       n0 + wn * WN, wm * WM, wn * WN, wave, lane, smem);
 }
 
 // A 128 x 256 tile on 8 waves with K split between two groups. Group 0
@@ -442,7 +450,7 @@ template <int YMODE>
 __device__ __forceinline__ void gemm_tile_ks(const int8_t* __restrict__ A, const float* __restrict__ xs,
                                              const int8_t* __restrict__ B, const float* __restrict__ ws,
                                              const float* __restrict__ bias, void* __restrict__ Y,
-                                             int M, int N, int K, int m0, int n0, int8_t* smem) {
+                                             int M, int N, int K, int m0, int n0, int act, int8_t* smem) {
     constexpr int BM = 128, BN = 256, BKL = 128;
     constexpr int WM = 64, WN = 128, FM = WM / 32, FN = WN / 32;
     constexpr int STAGE_A = BM * BKL, STAGE = (BM + BN) * BKL;
@@ -657,8 +665,15 @@ __device__ __forceinline__ void gemm_tile_ks(const int8_t* __restrict__ A, const
     }
     __builtin_amdgcn_s_waitcnt(LGKM0);
     if (grp == 0) {
-        store_tile<WM, WN, FM, FN, YMODE, 4>(acc, bias != nullptr, Y, M, N, m0 + wm * WM, n0 + wn * WN,
-                                             wm * WM, wn * WN, q, lane, smem);
+        if (act == ACT_GELU)
+            store_tile<WM, WN, FM, FN, YMODE, 4, ACT_GELU>(acc, bias != nullptr, Y, M, N, m0 + wm * WM,
+                                                           n0 + wn * WN, wm * WM, wn * WN, q, lane, smem);
+        else if (act == ACT_SILU)
+            store_tile<WM, WN, FM, FN, YMODE, 4, ACT_SILU>(acc, bias != nullptr, Y, M, N, m0 + wm * WM,
+                                                           n0 + wn * WN, wm * WM, wn * WN, q, lane, smem);
+        else
+            store_tile<WM, WN, FM, FN, YMODE, 4, ACT_NONE>(acc, bias != nullptr, Y, M, N, m0 + wm * WM,
+                                                           n0 + wn * WN, wm * WM, wn * WN, q, lane, smem);
     } else {
         barrier_no_fence();   // the one barrier store_tile runs
     }
@@ -677,13 +692,13 @@ template <int YMODE>
 __global__ __launch_bounds__(64 * NWAVES, 1) void gemm_w8a8_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ xs, const int8_t* __restrict__ B,
     const float* __restrict__ ws, const float* __restrict__ bias, void* __restrict__ Y, int M,
-    int N, int K, TilePlan plan) {
+    int N, int K, int act, TilePlan plan) {
     __shared__ __attribute__((aligned(1024))) int8_t smem[RING_BYTES + SCALE_BYTES];
     const int bid = blockIdx.x;
     if (bid < plan.nbig) {
         const int tile = xcd_remap(bid, plan.nbig);
         const int tn = tile / plan.tiles_m_big, tm = tile - tn * plan.tiles_m_big;
-        gemm_tile_pp<256, 256, YMODE>(A, xs, B, ws, bias, Y, M, N, K, tm * 256, tn * 256, smem);
+        gemm_tile_pp<256, 256, YMODE>(A, xs, B, ws, bias, Y, M, N, K, tm * 256, tn * 256, act, smem);
         if (bid >= plan.nsmall)
             return;
         // The big tile's epilogue has read all it needs from LDS (its stores may still be in
@@ -694,7 +709,7 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void gemm_w8a8_kernel(
     if (bid < plan.nsmall) {
         const int tile = xcd_remap(bid, plan.nsmall);
         const int tn = tile / plan.tiles_m_small, tm = tile - tn * plan.tiles_m_small;
-        gemm_tile_ks<YMODE>(A, xs, B, ws, bias, Y, M, N, K, tm * 128, plan.n_small0 + tn * 256, smem);
+        gemm_tile_ks<YMODE>(A, xs, B, ws, bias, Y, M, N, K, tm * 128, plan.n_small0 + tn * 256, act, smem);
     }
 }
 
@@ -734,7 +749,7 @@ TilePlan plan_tiles(int64_t M, int64_t N) {
 }  // namespace
 
 ql_status launch_gemm_w8a8(const int8_t* xq, const float* x_scale, const int8_t* wq,
-                           const float* w_scale, const float* bias, void* y, int y_mode,
+                           const float* w_scale, const float* bias, void* y, int y_mode, int act,
                            int64_t M, int64_t N, int64_t K, hipStream_t stream) {
     if (M == 0 || N == 0)
         return QL_OK;
@@ -746,7 +761,7 @@ ql_status launch_gemm_w8a8(const int8_t* xq, const float* x_scale, const int8_t*
     const int m = (int)M, n = (int)N, k = (int)K;
 #define QL_LAUNCH(MODE)                                                                          \
     hipLaunchKernelGGL((gemm_w8a8_kernel<MODE>), grid, block, 0, stream, xq, x_scale, wq, w_scale, \
-                       bias, y, m, n, k, plan)
+                       bias, y, m, n, k, act, plan)
     switch (y_mode) {
     case Y_F32:
         QL_LAUNCH(Y_F32);

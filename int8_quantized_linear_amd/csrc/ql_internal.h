@@ -26,14 +26,53 @@ ql_status launch_quant_block_asym_u8(const float* w, int64_t K, int64_t N, int64
 ql_status launch_quant_int4_group(const float* w, int64_t K, int64_t N, int64_t group,
                                   int32_t* packed, void* scales, hipStream_t stream);
 ql_status launch_gemm_w8a8(const int8_t* xq, const float* x_scale, const int8_t* wq,
-                           const float* w_scale, const float* bias, void* y, int y_mode,
+                           const float* w_scale, const float* bias, void* y, int y_mode, int act,
                            int64_t M, int64_t N, int64_t K, hipStream_t stream);
 ql_status launch_wonly(const void* x, const void* codes, int fmt, const void* scale,
                        const uint8_t* zp, int64_t group, const float* bias, void* y, int64_t M,
-                       int64_t N, int64_t K, hipStream_t stream);
+                       int64_t N, int64_t K, int act, hipStream_t stream);
 
 // y_mode of launch_gemm_w8a8
 enum { Y_F32 = 0, Y_F16 = 1, Y_I32 = 2 };
+// activation applied by an epilogue (values of ql_activation)
+enum { ACT_NONE = 0, ACT_GELU = 1, ACT_SILU = 2 };
+
+// erfc(x) for all x from the Chebyshev fit of Numerical Recipes (Press et al., 2nd ed.,
+// §6.2, "erfcc"): with z = |x| and t = 1 / (1 + z / 2),
+//   erfc(z) ~ t exp(-z^2 - 1.26551223 + t P(t)),   P a degree-8 polynomial,
+// fractional error below 1.2e-7 for every z >= 0; erfc(-z) = 2 - erfc(z). One
+// reciprocal, nine fused multiply-adds and one exponential, with no range branches (the
+// library's erfc branches by range, and lanes of a wave then run several ranges).
+__device__ inline float erfc_fit(float x) {
+    const float z = fabsf(x);
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.5f, z, 1.0f));
+    float p = 0.17087277f;
+    p = fmaf(p, t, -0.82215223f);
+    p = fmaf(p, t, 1.48851587f);
+    p = fmaf(p, t, -1.13520398f);
+    p = fmaf(p, t, 0.27886807f);
+    p = fmaf(p, t, -0.18628806f);
+    p = fmaf(p, t, 0.09678418f);
+    p = fmaf(p, t, 0.37409196f);
+    p = fmaf(p, t, 1.00002368f);
+    const float r = t * __expf(fmaf(-z, z, fmaf(t, p, -1.26551223f)));
+    return x >= 0.0f ? r : 2.0f - r;
+}
+
+// The epilogue's activation of an fp32 value: GELU in its exact form y * Phi(y), or SiLU
+// y * sigmoid(y). Phi(y) = erfc(-y / sqrt 2) / 2, the same function as
+// (1 + erf(y / sqrt 2)) / 2 without its cancellation for negative y (near -5 the sum
+// keeps only a few bits of Phi in fp32). Relative error a few 1e-6 at most: below the
+// fp32 epilogue's own for the values that matter, and far below an fp16 step.
+template <int ACT>
+__device__ inline float activation(float y) {
+    if constexpr (ACT == ACT_GELU)
+        return 0.5f * y * erfc_fit(-y * 0.70710678118654752f);
+    else if constexpr (ACT == ACT_SILU)
+        return y * __builtin_amdgcn_rcpf(1.0f + __expf(-y));
+    else
+        return y;
+}
 // fmt of launch_wonly
 enum { W_INT8_SYM = 0, W_UINT8_ZP = 1, W_INT4_SYM = 2 };
 

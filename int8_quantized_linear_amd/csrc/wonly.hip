@@ -212,7 +212,7 @@ template <int FMT, int KS, int MT, int NT, int SCALES, int D>
 __global__ __launch_bounds__(64 * nwaves<MT>()) void wonly_kernel(
     const _Float16* __restrict__ X, const uint8_t* __restrict__ Wc, const void* __restrict__ scale,
     const uint8_t* __restrict__ zp, int group, const float* __restrict__ bias,
-    _Float16* __restrict__ Y, int M, int N, int K, int cols) {
+    _Float16* __restrict__ Y, int M, int N, int K, int cols, int act) {
     using G = Geo<FMT, KS>;
     using XG = XRing<KS, MT>;
     using WR = typename G::WR;
@@ -497,30 +497,40 @@ __global__ __launch_bounds__(64 * nwaves<MT>()) void wonly_kernel(
     // The factors have arrived (nothing else is pending): said once here, so that the
     // compiler sees no load outstanding at the per-row store branches below.
     __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
-    // Output element r of block (i, j) in lane l is C[4 (l >> 4) + r][l & 15].
+    // Output element r of block (i, j) in lane l is C[4 (l >> 4) + r][l & 15]. The
+    // activation is uniform: one store loop per kind.
+    auto finish = [&](auto act_c) {
+        constexpr int ACT = decltype(act_c)::value;
 #pragma unroll
-    for (int k = 0; k < NB; ++k) {
-        const int b = wave + k * NW;
-        if (b >= MT * NT)
-            break;
-        const int i = b / NT, j = b % NT;
-        f32x4 v = red[b * 64 + lane];
+        for (int k = 0; k < NB; ++k) {
+            const int b = wave + k * NW;
+            if (b >= MT * NT)
+                break;
+            const int i = b / NT, j = b % NT;
+            f32x4 v = red[b * 64 + lane];
 #pragma unroll
-        for (int q = 1; q < NW; ++q)
-            v += red[(q * MT * NT + b) * 64 + lane];
-        const int c = 16 * j + ln;
-        if (c >= ncols)
-            continue;
-        const int n = col0 + c;
-        if constexpr (!GROUPED)
-            v *= cscale[k];
+            for (int q = 1; q < NW; ++q)
+                v += red[(q * MT * NT + b) * 64 + lane];
+            const int c = 16 * j + ln;
+            if (c >= ncols)
+                continue;
+            const int n = col0 + c;
+            if constexpr (!GROUPED)
+                v *= cscale[k];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int m = 16 * i + 4 * lg + r;
-            if (m < M)
-                Y[(int64_t)m * N + n] = (_Float16)(v[r] + cbias[k]);
+            for (int r = 0; r < 4; ++r) {
+                const int m = 16 * i + 4 * lg + r;
+                if (m < M)
+                    Y[(int64_t)m * N + n] = (_Float16)activation<ACT>(v[r] + cbias[k]);
+            }
         }
-    }
+    };
+    if (act == ACT_GELU)
+        finish(std::integral_constant<int, ACT_GELU>{});
+    else if (act == ACT_SILU)
+        finish(std::integral_constant<int, ACT_SILU>{});
+    else
+        finish(std::integral_constant<int, ACT_NONE>{});
 }
 
 int cu_count() {
@@ -539,50 +549,50 @@ int cu_count() {
 template <int FMT, int KS, int MT, int NT, int SCALES>
 ql_status launch_cfg(const void* x, const void* codes, const void* scale, const uint8_t* zp,
                      int64_t group, const float* bias, void* y, int64_t M, int64_t N, int64_t K,
-                     int cols, hipStream_t stream) {
+                     int cols, int act, hipStream_t stream) {
     constexpr int D = ring_depth<FMT, KS, MT, NT, SCALES == 2>();
     const dim3 grid((unsigned)((N + cols - 1) / cols)), block(64 * nwaves<MT>());
     hipLaunchKernelGGL((wonly_kernel<FMT, KS, MT, NT, SCALES, D>), grid, block, 0, stream,
                        reinterpret_cast<const _Float16*>(x), reinterpret_cast<const uint8_t*>(codes),
                        scale, zp, (int)group, bias, reinterpret_cast<_Float16*>(y), (int)M, (int)N,
-                       (int)K, cols);
+                       (int)K, cols, act);
     return launch_status();
 }
 
 template <int FMT, int KS, int MT, int SCALES>
 ql_status launch_nt(const void* x, const void* codes, const void* scale, const uint8_t* zp,
                     int64_t group, const float* bias, void* y, int64_t M, int64_t N, int64_t K,
-                    int cols, hipStream_t stream) {
+                    int cols, int act, hipStream_t stream) {
     if (cols <= 16)
-        return launch_cfg<FMT, KS, MT, 1, SCALES>(x, codes, scale, zp, group, bias, y, M, N, K, cols, stream);
+        return launch_cfg<FMT, KS, MT, 1, SCALES>(x, codes, scale, zp, group, bias, y, M, N, K, cols, act, stream);
     if (cols <= 32)
-        return launch_cfg<FMT, KS, MT, 2, SCALES>(x, codes, scale, zp, group, bias, y, M, N, K, cols, stream);
-    return launch_cfg<FMT, KS, MT, 4, SCALES>(x, codes, scale, zp, group, bias, y, M, N, K, cols, stream);
+        return launch_cfg<FMT, KS, MT, 2, SCALES>(x, codes, scale, zp, group, bias, y, M, N, K, cols, act, stream);
+    return launch_cfg<FMT, KS, MT, 4, SCALES>(x, codes, scale, zp, group, bias, y, M, N, K, cols, act, stream);
 }
 
 template <int FMT, int KS, int MT>
 ql_status launch_mt(const void* x, const void* codes, const void* scale, const uint8_t* zp,
                     int64_t group, const float* bias, void* y, int64_t M, int64_t N, int64_t K,
-                    bool grouped, hipStream_t stream) {
+                    bool grouped, int act, hipStream_t stream) {
     // Columns per workgroup: an equal share per CU, in multiples of 8, at most 64.
     int64_t cols = (N + cu_count() - 1) / cu_count();
     cols = (cols + 7) / 8 * 8;
     if (cols > 64)
         cols = 64;
     if (!grouped)
-        return launch_nt<FMT, KS, MT, 0>(x, codes, scale, zp, group, bias, y, M, N, K, (int)cols, stream);
+        return launch_nt<FMT, KS, MT, 0>(x, codes, scale, zp, group, bias, y, M, N, K, (int)cols, act, stream);
     // The scale block (and zero-point block after it, at a 64-word boundary) must fit in LDS.
     const int64_t ng = K / group, sb = FMT == W_INT4_SYM ? 2 : 4;
     const int64_t words = ((cols * ng * sb + 3) / 4 + 63) / 64 * 64 + (FMT == W_UINT8_ZP ? (cols * ng + 3) / 4 : 0);
     if (words + 63 <= SL_WORDS)
-        return launch_nt<FMT, KS, MT, 1>(x, codes, scale, zp, group, bias, y, M, N, K, (int)cols, stream);
-    return launch_nt<FMT, KS, MT, 2>(x, codes, scale, zp, group, bias, y, M, N, K, (int)cols, stream);
+        return launch_nt<FMT, KS, MT, 1>(x, codes, scale, zp, group, bias, y, M, N, K, (int)cols, act, stream);
+    return launch_nt<FMT, KS, MT, 2>(x, codes, scale, zp, group, bias, y, M, N, K, (int)cols, act, stream);
 }
 
 template <int FMT, int KS>
 ql_status launch_rows(const void* x, const void* codes, const void* scale, const uint8_t* zp,
                       int64_t group, const float* bias, void* y, int64_t M, int64_t N, int64_t K,
-                      bool grouped, hipStream_t stream) {
+                      bool grouped, int act, hipStream_t stream) {
     // Rows are processed 64 at a time (MT = 4 blocks of 16); smaller M uses fewer blocks.
     for (int64_t m0 = 0; m0 < M; m0 += 64) {
         const int64_t mc = M - m0 < 64 ? M - m0 : 64;
@@ -590,11 +600,11 @@ ql_status launch_rows(const void* x, const void* codes, const void* scale, const
         void* ys = reinterpret_cast<_Float16*>(y) + m0 * N;
         ql_status st;
         if (mc <= 16)
-            st = launch_mt<FMT, KS, 1>(xs, codes, scale, zp, group, bias, ys, mc, N, K, grouped, stream);
+            st = launch_mt<FMT, KS, 1>(xs, codes, scale, zp, group, bias, ys, mc, N, K, grouped, act, stream);
         else if (mc <= 32)
-            st = launch_mt<FMT, KS, 2>(xs, codes, scale, zp, group, bias, ys, mc, N, K, grouped, stream);
+            st = launch_mt<FMT, KS, 2>(xs, codes, scale, zp, group, bias, ys, mc, N, K, grouped, act, stream);
         else
-            st = launch_mt<FMT, KS, 4>(xs, codes, scale, zp, group, bias, ys, mc, N, K, grouped, stream);
+            st = launch_mt<FMT, KS, 4>(xs, codes, scale, zp, group, bias, ys, mc, N, K, grouped, act, stream);
         if (st != QL_OK)
             return st;
     }
@@ -605,22 +615,22 @@ ql_status launch_rows(const void* x, const void* codes, const void* scale, const
 
 ql_status launch_wonly(const void* x, const void* codes, int fmt, const void* scale,
                        const uint8_t* zp, int64_t group, const float* bias, void* y, int64_t M,
-                       int64_t N, int64_t K, hipStream_t stream) {
+                       int64_t N, int64_t K, int act, hipStream_t stream) {
     if (M == 0 || N == 0)
         return QL_OK;
     switch (fmt) {
     case W_INT8_SYM:
         if (group == 0 || group == K)
-            return launch_rows<W_INT8_SYM, 64>(x, codes, scale, zp, K, bias, y, M, N, K, false, stream);
-        return launch_rows<W_INT8_SYM, 64>(x, codes, scale, zp, group, bias, y, M, N, K, true, stream);
+            return launch_rows<W_INT8_SYM, 64>(x, codes, scale, zp, K, bias, y, M, N, K, false, act, stream);
+        return launch_rows<W_INT8_SYM, 64>(x, codes, scale, zp, group, bias, y, M, N, K, true, act, stream);
     case W_UINT8_ZP:
         return launch_rows<W_UINT8_ZP, 64>(x, codes, scale, zp, group == 0 ? K : group, bias, y, M, N,
-                                           K, true, stream);
+                                           K, true, act, stream);
     default:
         // 128-k steps (16-byte loads) when a step never straddles a group
         if (group % 128 == 0 && K % 128 == 0)
-            return launch_rows<W_INT4_SYM, 128>(x, codes, scale, zp, group, bias, y, M, N, K, true, stream);
-        return launch_rows<W_INT4_SYM, 64>(x, codes, scale, zp, group, bias, y, M, N, K, true, stream);
+            return launch_rows<W_INT4_SYM, 128>(x, codes, scale, zp, group, bias, y, M, N, K, true, act, stream);
+        return launch_rows<W_INT4_SYM, 64>(x, codes, scale, zp, group, bias, y, M, N, K, true, act, stream);
     }
 }
 

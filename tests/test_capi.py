@@ -37,6 +37,8 @@ def lib():
         "gemm_w8a8_int32": [P, P, P, I64, I64, I64, P],
         "gemm_w8a16": [P, P, P, P, I64, P, P, I64, I64, I64, P],
         "gemm_w4a16_grouped": [P, P, P, I64, P, P, I64, I64, I64, P],
+        "gemm_w8a8_per_channel_act": [P, P, P, P, P, I, P, I, I64, I64, I64, P],
+        "gemm_w4a16_grouped_act": [P, P, P, I64, P, I, P, I64, I64, I64, P],
         "quantize_weight_block_asym_u8": [P, I64, I64, I64, P, P, P, P],
         "quantize_weight_int4_grouped": [P, I64, I64, I64, P, P, P],
     }
@@ -52,7 +54,8 @@ def test_header_declares_the_entry_points():
     names = declared()
     for n in ("quantize_per_row_int8", "quantize_weight_per_channel", "gemm_w8a8_per_channel",
               "gemm_w8a16", "gemm_w4a16_grouped", "gemm_w8a8_int32", "ql_status_str",
-              "quantize_weight_block_asym_u8", "quantize_weight_int4_grouped"):
+              "quantize_weight_block_asym_u8", "quantize_weight_int4_grouped",
+              "gemm_w8a8_per_channel_act", "gemm_w4a16_grouped_act"):
         assert n in names
 
 
@@ -159,6 +162,26 @@ def test_gemm_w4a16_validation(lib):
     assert f(A, MIS, A, 128, None, A, 32, 64, 256, None) == ALIGN
     assert f(A, A, MIS, 128, None, A, 32, 64, 256, None) == ALIGN
     assert f(None, None, None, 128, None, None, 32, 0, 256, None) == OK
+
+
+def test_fused_activation_validation(lib):
+    """The activation entry points validate like the plain ones, plus the activation code."""
+    f = lib.gemm_w8a8_per_channel_act
+    for act in (0, 1, 2):
+        assert f(None, None, None, None, None, act, None, F16, 0, 8, 64, None) == OK
+        assert f(A, A, A, A, None, act, None, F16, 8, 8, 64, None) == NULL
+        assert f(A, A, A, A, None, act, A, F16, 8, 8, 96, None) == SHAPE
+        assert f(A, A, MIS, A, None, act, A, F16, 8, 8, 64, None) == ALIGN
+    assert f(A, A, A, A, None, 3, A, F16, 8, 8, 64, None) == DTYPE
+    assert f(A, A, A, A, None, -1, A, F16, 8, 8, 64, None) == DTYPE
+    assert f(A, A, A, A, None, 1, A, 3, 8, 8, 64, None) == DTYPE
+    g = lib.gemm_w4a16_grouped_act
+    for act in (0, 1, 2):
+        assert g(None, None, None, 128, None, act, None, 32, 0, 256, None) == OK
+        assert g(None, A, A, 128, None, act, A, 32, 64, 256, None) == NULL
+        assert g(A, A, A, 96, None, act, A, 32, 64, 384, None) == SHAPE
+        assert g(A, A, MIS, 128, None, act, A, 32, 64, 256, None) == ALIGN
+    assert g(A, A, A, 128, None, 7, A, 32, 64, 256, None) == DTYPE
 
 
 def test_producer_validation(lib):

@@ -146,6 +146,56 @@ def test_one_hot_rows(ql):
     assert np.array_equal(acc, 127 * wq[:, ks].T.astype(np.int32))
 
 
+ACT = {"gelu": 1, "silu": 2}
+
+
+@pytest.mark.parametrize("act", ["gelu", "silu"])
+@pytest.mark.parametrize("M,N,K,out", [(16, 256, 256, torch.float32), (300, 520, 384, torch.float16),
+                                       (300, 520, 384, torch.float32), (2000, 8300, 64, torch.float16)])
+def test_fused_activation(ql, act, M, N, K, out):
+    """act(acc * x_scale * w_scale + bias) from the epilogue, against the oracle's fp64
+    activation of its fp64 epilogue; half-height-only, mixed and big-tile plans.
+    Scales put the pre-activation values at a few units, where both activations bend.
+    fp32: |y - act(y64)| <= 1.2e-5 * (|acc xs ws| + |bias|) + 2e-6 |act(y64)| (the
+    epilogue's error times |act'| <= 1.13, plus the activation's own fp32 evaluation);
+    fp16: within one fp16 step of fp16(act(y64))."""
+    rng = np.random.default_rng(M + 7 * N + K)
+    a = _rand_codes(rng, (M, K))
+    b = _rand_codes(rng, (N, K))
+    xs = (rng.uniform(0.5, 1.5, M) / (127.0 * np.sqrt(K))).astype(np.float32)
+    ws = (rng.uniform(0.5, 1.5, N) * 3.0 / 127.0).astype(np.float32)
+    bias = rng.standard_normal(N).astype(np.float32)
+    g = Guarded((M, N), out)
+    ql.gemm_w8a8_per_channel_act(dev(a), dev(xs), dev(b), dev(ws), dev(bias), act, out, y=g.view)
+    g.check()
+    rows = np.arange(M) if M <= 512 else np.unique(np.concatenate([np.arange(0, M, 37), [M - 1]]))
+    acc_ref = oracle.gemm_i32(a[rows], b)
+    _, y64 = oracle.epilogue_w8a8(acc_ref, xs[rows], ws, bias)
+    ref = oracle.activation_f64(y64, ACT[act])
+    y = host(g.view)[rows].astype(np.float64)
+    assert np.all(np.isfinite(y))
+    if out == torch.float32:
+        mag = np.abs(acc_ref.astype(np.float64) * xs[rows][:, None] * ws[None, :]) + np.abs(bias)[None, :]
+        assert np.all(np.abs(y - ref) <= 1.2e-5 * mag + 2e-6 * np.abs(ref))
+    else:
+        ref16 = ref.astype(np.float16).astype(np.float64)
+        assert np.all(np.abs(y - ref16) <= f16_ulp(ref16))
+    # the pre-activation values span the bend of both activations
+    assert (y64 < -2).mean() > 0.05 and (y64 > 2).mean() > 0.05
+
+
+def test_fused_activation_none_is_plain(ql):
+    """act = none through the activation entry point is the plain epilogue, bit for bit."""
+    rng = np.random.default_rng(5)
+    M, N, K = 300, 520, 384
+    a, b = dev(_rand_codes(rng, (M, K))), dev(_rand_codes(rng, (N, K)))
+    xs, ws = dev(rng.uniform(1e-5, 1e-4, M).astype(np.float32)), dev(rng.uniform(1e-3, 1e-2, N).astype(np.float32))
+    bias = dev(rng.standard_normal(N).astype(np.float32))
+    y0 = host(ql.gemm_w8a8_per_channel(a, xs, b, ws, bias, torch.float16))
+    y1 = host(ql.gemm_w8a8_per_channel_act(a, xs, b, ws, bias, "none", torch.float16))
+    assert np.array_equal(y0.view(np.uint16), y1.view(np.uint16))
+
+
 def test_empty(ql):
     xq = torch.empty((0, 64), dtype=torch.int8, device=DEV)
     wq = torch.zeros((8, 64), dtype=torch.int8, device=DEV)

@@ -134,6 +134,31 @@ def test_large_scale_blocks_and_row_tiles(ql, fmt, M, N, K, group):
     check_wonly(host(g.view), oracle.w8a16_f64(inp.x, q_ref, s_ref, group_size=group))
 
 
+@pytest.mark.parametrize("act", ["gelu", "silu"])
+@pytest.mark.parametrize("M,N,K,group", [(32, 14336, 4096, 128), (3, 77, 256, 128), (40, 1000, 512, 64)])
+def test_w4a16_fused_activation(ql, act, M, N, K, group):
+    """act(W4A16 + bias) from the decode epilogue ([xdnf] §8), against the oracle's fp64
+    activation of its fp64 product: the weight-only bound 2e-3 (|y64| + rms) on the
+    pre-activation value, times max |act'| = 1.13 (the fp16 rounding of act(y) is within
+    it since |act(y)| <= |y|). The full decode shape is checked on sampled columns."""
+    code = {"gelu": 1, "silu": 2}[act]
+    w = workloads.with_shape(workloads.W4A16_GROUP, M, K, N, seed=M + N + code)
+    inp = workloads.draw(w)
+    rng = np.random.default_rng(M + N)
+    bias = (rng.standard_normal(N) * 0.5).astype(np.float32)
+    p_ref, s_ref = oracle.quant_int4_group(inp.w_nk, group)
+    p, s = ql.quantize_weight_int4_grouped(dev(inp.w_nk), group)
+    g = Guarded((M, N), torch.float16)
+    ql.gemm_w4a16_grouped_act(dev(inp.x), p, s, group, dev(bias), act, y=g.view)
+    g.check()
+    cols = np.arange(N) if N <= 2000 else np.unique(np.concatenate([np.arange(0, N, 13), np.arange(N - 40, N)]))
+    y64 = oracle.w4a16_f64(inp.x, p_ref[cols], s_ref[cols], group, bias=bias[cols])
+    ref = oracle.activation_f64(y64, code)
+    y = host(g.view)[:, cols].astype(np.float64)
+    rms = float(np.sqrt(np.mean(y64 ** 2)))
+    assert np.all(np.abs(y - ref) <= 1.13 * 2e-3 * (np.abs(y64) + rms))
+
+
 def test_one_hot_exact(ql):
     """x = e_k: y[n] is fp16((q[k,n] - z) * s) exactly for all three formats."""
     N, K = 40, 256
