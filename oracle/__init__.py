@@ -62,6 +62,9 @@ def _declare(L):
     L.oracle_quant_int4_group.argtypes = [_P, _I64, _I64, _I64, _P, _P]
     L.oracle_num_threads.restype = ctypes.c_int
     L.oracle_activation_f64.argtypes = [_P, _I64, ctypes.c_int]
+    L.oracle_quant_rows_i8_asym.argtypes = [_P, _I64, _I64, _P, _P, _P]
+    L.oracle_column_sums_i8.argtypes = [_P, _I64, _I64, _P]
+    L.oracle_w8a8_asym_f64.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]
 
 
 def _ptr(a: Optional[np.ndarray]):
@@ -170,6 +173,38 @@ class Oracle:
         y64 = np.empty((M, N), np.float64)
         self.L.oracle_wonly_f64(_ptr(xf), M, K, _ptr(codes), kind, _ptr(s), _ptr(z), group_size,
                                _ptr(b), N, _ptr(y64))
+        return y64
+
+    def quant_rows_i8_asym(self, x) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+        """Asymmetric int8 per row of x [M, K] (fp16 or fp32): (q int8, scale fp32 [M],
+        zero fp32 [M]) with x ~ scale * (q - zero)."""
+        xf = self._as_f32(x)
+        M, K = xf.shape
+        q = np.empty((M, K), np.int8)
+        s = np.empty(M, np.float32)
+        z = np.empty(M, np.float32)
+        self.L.oracle_quant_rows_i8_asym(_ptr(xf), M, K, _ptr(q), _ptr(s), _ptr(z))
+        return q, s, z
+
+    def column_sums_i8(self, wq_nk) -> np.ndarray:
+        """int32 [N]: the sum of each column's codes (W stored [N][K])."""
+        w = _c(wq_nk, np.int8)
+        N, K = w.shape
+        out = np.empty(N, np.int32)
+        self.L.oracle_column_sums_i8(_ptr(w), N, K, _ptr(out))
+        return out
+
+    def w8a8_asym_f64(self, xq, x_scale, x_zero, wq_nk, w_scale, bias=None) -> np.ndarray:
+        """fp64 layer output with asymmetric activations, from the definition."""
+        xq = _c(xq, np.int8)
+        wq = _c(wq_nk, np.int8)
+        M, K = xq.shape
+        N = wq.shape[0]
+        xs, xz, ws = _c(x_scale, np.float32), _c(x_zero, np.float32), _c(w_scale, np.float32)
+        b = None if bias is None else _c(bias, np.float32)
+        y64 = np.empty((M, N), np.float64)
+        self.L.oracle_w8a8_asym_f64(_ptr(xq), _ptr(xs), _ptr(xz), _ptr(wq), _ptr(ws), _ptr(b), M, N, K,
+                                    _ptr(y64))
         return y64
 
     ACT_NONE, ACT_GELU, ACT_SILU = 0, 1, 2

@@ -143,6 +143,76 @@ float oracle_quant_tensor_i8(const float* x, int64_t n, int8_t* q)
     return quant_vec_i8(x, n, q);
 }
 
+/* ----------------------------------------------- asymmetric int8 (per row) */
+
+/* Asymmetric int8 quantization of each row of a row-major [rows, cols] fp32 array, as the
+ * asymmetric branch of hotelren.com's per_channel_quant_int8 computes it, in fp32:
+ *   lo, hi = min, max of the row;   s = max((hi - lo) / 255, 1e-8)
+ *   z = -lo / s - 128       (kept as a float: the page does not round the zero point)
+ *   q = clamp(rne(x / s + z), -128, 127)
+ * so that x ~ s (q - z) (quant67.com ch.17 §二, asymmetric form). */
+void oracle_quant_rows_i8_asym(const float* x, int64_t rows, int64_t cols, int8_t* q,
+                               float* scale, float* zero)
+{
+    for (int64_t r = 0; r < rows; ++r) {
+        const float* v = x + r * cols;
+        float lo = v[0], hi = v[0];
+        for (int64_t i = 1; i < cols; ++i) {
+            if (v[i] < lo)
+                lo = v[i];
+            if (v[i] > hi)
+                hi = v[i];
+        }
+        float s = (hi - lo) / 255.0f;
+        if (s < 1e-8f)
+            s = 1e-8f;
+        const float z = -lo / s - 128.0f;
+        for (int64_t i = 0; i < cols; ++i) {
+            const float t = v[i] / s + z;
+            float rq = nearbyintf(t);
+            if (rq > 127.0f)
+                rq = 127.0f;
+            if (rq < -128.0f)
+                rq = -128.0f;
+            q[r * cols + i] = (int8_t)rq;
+        }
+        scale[r] = s;
+        zero[r] = z;
+    }
+}
+
+/* colsum[n] = sum_k wq[n][k]: W's per-column code sums ([N][K] storage). */
+void oracle_column_sums_i8(const int8_t* wq, int64_t N, int64_t K, int32_t* colsum)
+{
+    for (int64_t n = 0; n < N; ++n) {
+        int64_t t = 0;
+        for (int64_t k = 0; k < K; ++k)
+            t += wq[n * K + k];
+        colsum[n] = (int32_t)t;
+    }
+}
+
+/* The layer with asymmetric activations and symmetric per-channel weights, from its
+ * definition, in fp64:  y[m][n] = sum_k x_scale[m] (xq[m][k] - x_zero[m]) * w_scale[n] wq[n][k]
+ * + bias[n]  (quant67.com ch.17 §二: x ~ s_x (q_x - z_x), w ~ s_w q_w). bias may be NULL. */
+void oracle_w8a8_asym_f64(const int8_t* xq, const float* x_scale, const float* x_zero,
+                          const int8_t* wq, const float* w_scale, const float* bias, int64_t M,
+                          int64_t N, int64_t K, double* y64)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += ((double)xq[m * K + k] - (double)x_zero[m]) * (double)wq[n * K + k];
+            double y = acc * (double)x_scale[m] * (double)w_scale[n];
+            if (bias)
+                y += (double)bias[n];
+            y64[m * N + n] = y;
+        }
+    }
+}
+
 /* ---------------------------------------------------------- integer GEMM */
 
 /* acc[m][n] = sum_k xq[m][k] * wq[n][k]; xq is [M][K] row-major, wq is W [K,N]

@@ -419,6 +419,75 @@ def pin_footprint_golden(orc):
         assert abs(size - float(printed)) <= 0.5 * 10 ** -nd + 1e-9, (params, bits, size, printed)
 
 
+def pin_asym_quant_rows(orc):
+    """Asymmetric rows (hotelren.com per_channel_quant_int8, asymmetric branch): the row
+    minimum codes to -128 and the maximum to 127; every element dequantizes to within half
+    a step, |s (q - z) - x| <= s (1/2 + 2^-14 (|x|/s + 256)) for fp32's roundings; the zero
+    point is 255 (-lo) / (hi - lo) - 128 up to fp32 rounding, not rounded to an integer; a
+    constant row takes the 1e-8 scale floor, codes -128 and dequantizes to itself."""
+    rng = np.random.default_rng(81)
+    x = (rng.standard_normal((64, 300)) * np.exp2(rng.integers(-6, 6, (64, 1)))
+         + rng.uniform(-3, 3, (64, 1))).astype(np.float32)
+    q, s, z = orc.quant_rows_i8_asym(x)
+    r = np.arange(64)
+    assert np.all(q[r, x.argmin(1)] == -128) and np.all(q[r, x.argmax(1)] == 127)
+    sd = s.astype(np.float64)[:, None]
+    deq = sd * (q.astype(np.float64) - z.astype(np.float64)[:, None])
+    assert np.all(np.abs(deq - x) <= sd * (0.5 + 2.0 ** -14 * (np.abs(x) / sd + 256)))
+    lo, hi = x.min(1).astype(np.float64), x.max(1).astype(np.float64)
+    zr = 255.0 * (-lo) / (hi - lo) - 128.0
+    assert np.all(np.abs(z - zr) <= 1e-4 * (1 + np.abs(zr)))
+    frac = np.abs(z - np.round(z))
+    assert (frac > 0.01).mean() > 0.5          # the zero point is kept as a float
+    c = np.full((3, 40), [[0.75], [-2.5], [1e-3]], np.float32)
+    qc, sc, zc = orc.quant_rows_i8_asym(c)
+    assert np.all(qc == -128) and np.all(sc == np.float32(1e-8))
+    dc = sc.astype(np.float64) * (-128.0 - zc.astype(np.float64))
+    assert np.allclose(dc, c[:, 0], rtol=1e-5, atol=0)
+
+
+def pin_asym_quant_relu_rows(orc):
+    """A row with minimum 0 whose values are exact multiples k of a power-of-two step with
+    k up to 255: the scale is the step, the zero point is -128 and the codes are k - 128."""
+    rng = np.random.default_rng(82)
+    for e in (-3, 0, 5):
+        k = rng.permutation(np.concatenate([[0, 255], rng.integers(0, 256, 98)]))
+        row = (k * 2.0 ** e).astype(np.float32)[None, :]
+        q, s, z = orc.quant_rows_i8_asym(row)
+        assert s[0] == np.float32(2.0 ** e) and z[0] == -128.0
+        assert np.array_equal(q[0].astype(np.int64), k - 128)
+
+
+def pin_asym_layer(orc):
+    """The asymmetric layer against exact rational arithmetic on tiny inputs, and against
+    numpy's fp64 product of the dequantized operands, s_x (q_x - z_x) @ (s_w q_w)^T + b;
+    column sums against numpy."""
+    rng = np.random.default_rng(83)
+    M, N, K = 3, 4, 8
+    xq = rng.integers(-128, 128, (M, K), dtype=np.int8)
+    wq = rng.integers(-127, 128, (N, K), dtype=np.int8)
+    xs = rng.uniform(0.01, 0.1, M).astype(np.float32)
+    xz = rng.uniform(-100, 100, M).astype(np.float32)
+    ws = rng.uniform(0.01, 0.1, N).astype(np.float32)
+    b = rng.standard_normal(N).astype(np.float32)
+    y = orc.w8a8_asym_f64(xq, xs, xz, wq, ws, b)
+    for m in range(M):
+        for n in range(N):
+            t = sum((Fraction(int(xq[m, k])) - Fraction(float(xz[m]))) * int(wq[n, k]) for k in range(K))
+            exact = t * Fraction(float(xs[m])) * Fraction(float(ws[n])) + Fraction(float(b[n]))
+            assert abs(Fraction(y[m, n]) - exact) <= Fraction(1, 10 ** 12) * (abs(exact) + 1)
+    M, N, K = 50, 60, 300
+    xq = rng.integers(-128, 128, (M, K), dtype=np.int8)
+    wq = rng.integers(-127, 128, (N, K), dtype=np.int8)
+    xs, xz = rng.uniform(0.01, 0.1, M).astype(np.float32), rng.uniform(-128, 127, M).astype(np.float32)
+    ws, b = rng.uniform(0.01, 0.1, N).astype(np.float32), rng.standard_normal(N).astype(np.float32)
+    xd = xs.astype(np.float64)[:, None] * (xq.astype(np.float64) - xz.astype(np.float64)[:, None])
+    wd = ws.astype(np.float64)[:, None] * wq.astype(np.float64)
+    ref = xd @ wd.T + b.astype(np.float64)[None, :]
+    assert np.allclose(orc.w8a8_asym_f64(xq, xs, xz, wq, ws, b), ref, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(orc.column_sums_i8(wq), wq.astype(np.int64).sum(1))
+
+
 # Standard normal distribution function at tabulated points (values from a normal table,
 # to 16 significant digits); 1.959963984540054 is the 0.975 quantile.
 PHI_TABLE = {-3.0: 0.001349898031630095, -0.5: 0.3085375387259869, 0.0: 0.5,

@@ -47,6 +47,14 @@ MUTANTS = [
      "y[i] = 0.5 * v * (1.0 + tanh(0.7978845608028654 * (v + 0.044715 * v * v * v)));"),
     ("gelu_no_sqrt2", "erf(v / sqrt(2.0))", "erf(v)"),
     ("silu_exp_sign", "y[i] = v / (1.0 + exp(-v));", "y[i] = v / (1.0 + exp(v));"),
+    ("asym_zero_no_offset", "const float z = -lo / s - 128.0f;", "const float z = -lo / s;"),
+    ("asym_zero_rounded", "const float z = -lo / s - 128.0f;", "const float z = nearbyintf(-lo / s) - 128.0f;"),
+    ("asym_scale_254", "float s = (hi - lo) / 255.0f;", "float s = (hi - lo) / 254.0f;"),
+    ("asym_min_is_max", "if (v[i] < lo)\n                lo = v[i];", "if (v[i] > lo)\n                lo = v[i];"),
+    ("asym_clamp_127", "if (rq < -128.0f)\n                rq = -128.0f;", "if (rq < -127.0f)\n                rq = -127.0f;"),
+    ("asym_no_scale_floor", "if (s < 1e-8f)\n            s = 1e-8f;", "if (s < 0.0f)\n            s = 1e-8f;"),
+    ("asym_layer_zero_sign", "((double)xq[m * K + k] - (double)x_zero[m])", "((double)xq[m * K + k] + (double)x_zero[m])"),
+    ("colsum_wrong_index", "t += wq[n * K + k];", "t += wq[(k % N) * K + (n % K)];"),
     ("act_codes_swapped", "if (act == 1)\n            y[i] = v * (0.5", "if (act == 2)\n            y[i] = v * (0.5"),
 ]
 
