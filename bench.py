@@ -147,6 +147,33 @@ def fused_activation_timings(ql, n, gemm, dec5, r5, make_gemm, make_dec, ops, w4
     }
 
 
+def asym_timings(n, runs, ops, quant_bytes, name, progress):
+    """The layer with asymmetric per-row activations (quantizer with a float zero point, GEMM
+    with the zero-point correction in the epilogue) against the symmetric one at the same
+    shape: each launch event-timed, the four alternating."""
+    import torch
+    progress("asymmetric activations: %d launches each" % n)
+    ev = {k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+          for k in runs}
+    for f in runs.values():
+        f()
+    torch.cuda.synchronize()
+    for i in range(n):
+        for k, f in runs.items():
+            ev[k][i][0].record()
+            f()
+            ev[k][i][1].record()
+    torch.cuda.synchronize()
+    us = {k: 1e3 * sum(a.elapsed_time(b) for a, b in v) / n for k, v in ev.items()}
+    layer = us["quant_asym"] + us["gemm_asym"]
+    return {name: {"quant_us": us["quant_asym"], "gemm_us": us["gemm_asym"],
+                   "quant_GB_per_s": quant_bytes / (us["quant_asym"] * 1e-6) / 1e9 + 0.0,
+                   "layer_TOPS": ops / (layer * 1e-6) / 1e12,
+                   "symmetric_quant_us": us["quant_symmetric"], "symmetric_gemm_us": us["gemm_symmetric"],
+                   "gemm_overhead": us["gemm_asym"] / us["gemm_symmetric"] - 1},
+            "note": "quantizer bytes: fp16 X in, int8 codes out, scale and zero point per row"}
+
+
 def measured_ceilings(dev, byte_counts, progress):
     """Ceilings measured with libqlprobe.so: int8 MFMA TOPS from registers (random and
     constant operands) and the GB/s of one cold streaming read of each byte count."""
@@ -381,6 +408,16 @@ def main():
             lambda code: [ql.prepare("gemm_w4a16_grouped_act", x5, p, s, 128, None, code, y5, w5.M, w5.N,
                                      w5.K) for p, s in set5],
             ops, ab["w4a16"], w3.name, w5.name, progress)
+    if args.act_steps > 0:
+        xz3 = torch.empty((w3.M,), dtype=torch.float32, device=dev)
+        cs3 = ql.weight_column_sums_i8(wq3)
+        out["asymmetric_activations"] = asym_timings(
+            args.act_steps, {
+                "quant_symmetric": quant, "gemm_symmetric": gemm,
+                "quant_asym": ql.prepare("quantize_per_row_int8_asym", x3, F16, w3.M, w3.K, xq3, xs3, xz3),
+                "gemm_asym": ql.prepare("gemm_w8a8_asym", xq3, xs3, xz3, wq3, ws3, cs3, b3, 0, y3, F16,
+                                        w3.M, w3.N, w3.K)},
+            ops, ab["quant"] + 4 * w3.M, w3.name, progress)
     if args.ceilings:
         del set2, set4, set5, dec2, dec4, dec5
         ceil = measured_ceilings(dev, {"quant": ab["quant"], "w8a16": ab["w8a16"],

@@ -141,6 +141,41 @@ ql_status gemm_w8a8_per_channel_act(const int8_t* xq, const float* x_scale, cons
                                     void* stream);
 
 /*
+ * Asymmetric activations ([hotelren] per_channel_quant_int8, its asymmetric branch;
+ * [quant67] §二, x ~ s (q - z) and the expansion of the integer product). Per row m of X,
+ * with lo, hi the row's minimum and maximum, in fp32:
+ *   s = max((hi - lo) / 255, 1e-8);  z = -lo / s - 128 (kept as a float, as on the page);
+ *   q = clamp(round(x / s + z), -128, 127)          (x / s correctly rounded, then + z)
+ * x       [M,K] row-major, fp32 (QL_F32) or fp16 (QL_F16)
+ * xq      [M,K] int8 row-major (out);  x_scale, x_zero fp32 [M] (out)
+ * Requires K > 0 and K % 16 == 0.
+ */
+ql_status quantize_per_row_int8_asym(const void* x, ql_dtype x_dtype, int64_t M, int64_t K,
+                                     int8_t* xq, float* x_scale, float* x_zero, void* stream);
+
+/*
+ * colsum[n] = sum_k wq[k,n]: the per-column code sums of W, the weight-side term of the
+ * asymmetric expansion sum_k (q_x - z_x) q_w = sum_k q_x q_w - z_x sum_k q_w ([quant67] §二).
+ * An offline step beside the weight quantizer.
+ * wq      W [K,N] int8 column-major ([N][K]);  colsum int32 [N] (out)
+ * Requires K > 0 and K % 16 == 0.
+ */
+ql_status weight_column_sums_i8(const int8_t* wq, int64_t K, int64_t N, int32_t* colsum,
+                                void* stream);
+
+/*
+ * The layer with asymmetric activations and symmetric per-channel weights:
+ *   y[m,n] = act(x_scale[m] * w_scale[n] * (acc[m,n] - x_zero[m] * w_colsum[n]) + bias[n])
+ * with acc the exact int32 product of the codes and the correction taken in fp32 with one
+ * rounding. Arguments as for gemm_w8a8_per_channel_act, plus x_zero (fp32 [M], from
+ * quantize_per_row_int8_asym) and w_colsum (int32 [N], from weight_column_sums_i8).
+ */
+ql_status gemm_w8a8_asym(const int8_t* xq, const float* x_scale, const float* x_zero,
+                         const int8_t* wq, const float* w_scale, const int32_t* w_colsum,
+                         const float* bias, ql_activation act, void* y, ql_dtype y_dtype,
+                         int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
  * The W8A8 integer accumulators alone, acc[m,n] = sum_k xq[m,k] * wq[k,n] as int32
  * [M,N] row-major. A checking aid for the exact integer stage of
  * gemm_w8a8_per_channel (same main loop); [hotelren] "W8A8矩阵乘法" scheme 1 names

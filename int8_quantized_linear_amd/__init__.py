@@ -20,6 +20,7 @@ __all__ = [
     "gemm_w8a8_per_channel", "gemm_w8a8_int32", "gemm_w8a16", "gemm_w4a16_grouped",
     "quantize_weight_block_asym_u8", "quantize_weight_int4_grouped", "linear_w8a8", "prepare",
     "gemm_w8a8_per_channel_act", "gemm_w4a16_grouped_act", "ACTIVATIONS",
+    "quantize_per_row_int8_asym", "weight_column_sums_i8", "gemm_w8a8_asym", "linear_w8a8_asym",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -51,6 +52,9 @@ _SIGS = {
     "gemm_w4a16_grouped": [_P, _P, _P, _I64, _P, _P, _I64, _I64, _I64, _P],
     "gemm_w8a8_per_channel_act": [_P, _P, _P, _P, _P, _I, _P, _I, _I64, _I64, _I64, _P],
     "gemm_w4a16_grouped_act": [_P, _P, _P, _I64, _P, _I, _P, _I64, _I64, _I64, _P],
+    "quantize_per_row_int8_asym": [_P, _I, _I64, _I64, _P, _P, _P, _P],
+    "weight_column_sums_i8": [_P, _I64, _I64, _P, _P],
+    "gemm_w8a8_asym": [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I64, _I64, _I64, _P],
     "quantize_weight_block_asym_u8": [_P, _I64, _I64, _I64, _P, _P, _P, _P],
     "quantize_weight_int4_grouped": [_P, _I64, _I64, _I64, _P, _P, _P],
 }
@@ -118,6 +122,30 @@ def quantize_per_row_int8(x: torch.Tensor, xq: Optional[torch.Tensor] = None,
     _call("quantize_per_row_int8", _ptr(x), QL_F16 if x.dtype == torch.float16 else QL_F32, M, K,
           _ptr(xq), _ptr(x_scale), _stream(x))
     return xq, x_scale
+
+
+def quantize_per_row_int8_asym(x: torch.Tensor):
+    """Asymmetric int8 per row of x [M, K] (fp16 or fp32): (xq int8 [M, K], x_scale fp32
+    [M], x_zero fp32 [M]) with x ~ x_scale * (xq - x_zero)."""
+    _check(x, "x", (torch.float16, torch.float32))
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, K]")
+    M, K = x.shape
+    xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    xs = torch.empty((M,), dtype=torch.float32, device=x.device)
+    xz = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _call("quantize_per_row_int8_asym", _ptr(x), QL_F16 if x.dtype == torch.float16 else QL_F32, M, K,
+          _ptr(xq), _ptr(xs), _ptr(xz), _stream(x))
+    return xq, xs, xz
+
+
+def weight_column_sums_i8(wq: torch.Tensor) -> torch.Tensor:
+    """int32 [N]: the code sum of each column of W, given as its [N, K] storage."""
+    _check(wq, "wq", (torch.int8,))
+    N, K = wq.shape
+    out = torch.empty((N,), dtype=torch.int32, device=wq.device)
+    _call("weight_column_sums_i8", _ptr(wq), K, N, _ptr(out), _stream(wq))
+    return out
 
 
 def quantize_weight_per_channel(w_nk: torch.Tensor, wq: Optional[torch.Tensor] = None,
@@ -263,6 +291,36 @@ def _gemm_w4a16(x, wq_packed, scales, group_size, bias, act, y):
         _call("gemm_w4a16_grouped_act", _ptr(x), _ptr(wq_packed), _ptr(scales), group_size, _ptr(bias),
               act, _ptr(y), M, N, K, _stream(x))
     return y
+
+
+def gemm_w8a8_asym(xq, x_scale, x_zero, wq, w_scale, w_colsum, bias=None, act: str = "none",
+                   out_dtype=torch.float16, y=None):
+    """y = act(x_scale[m] w_scale[n] (xq @ wq^T - x_zero[m] w_colsum[n]) + bias[n])."""
+    _check(xq, "xq", (torch.int8,))
+    M, K = xq.shape
+    dev = xq.device
+    N = wq.shape[0]
+    _check(wq, "wq", (torch.int8,), (N, K), dev)
+    _check(x_scale, "x_scale", (torch.float32,), (M,), dev)
+    _check(x_zero, "x_zero", (torch.float32,), (M,), dev)
+    _check(w_scale, "w_scale", (torch.float32,), (N,), dev)
+    _check(w_colsum, "w_colsum", (torch.int32,), (N,), dev)
+    if bias is not None:
+        _check(bias, "bias", (torch.float32,), (N,), dev)
+    if out_dtype not in (torch.float16, torch.float32):
+        raise TypeError("out_dtype must be float16 or float32")
+    y = _out(y, "y", (M, N), out_dtype, dev)
+    _call("gemm_w8a8_asym", _ptr(xq), _ptr(x_scale), _ptr(x_zero), _ptr(wq), _ptr(w_scale), _ptr(w_colsum),
+          _ptr(bias), _act_code(act), _ptr(y), QL_F16 if out_dtype == torch.float16 else QL_F32, M, N, K,
+          _stream(xq))
+    return y
+
+
+def linear_w8a8_asym(x, wq, w_scale, w_colsum, bias=None, act: str = "none", out_dtype=None):
+    """The layer with asymmetric per-row activations: quantize x, then the GEMM."""
+    xq, xs, xz = quantize_per_row_int8_asym(x)
+    od = out_dtype or (torch.float32 if x.dtype == torch.float32 else torch.float16)
+    return gemm_w8a8_asym(xq, xs, xz, wq, w_scale, w_colsum, bias, act, od)
 
 
 def linear_w8a8(x, wq, w_scale, bias=None, out_dtype=None):

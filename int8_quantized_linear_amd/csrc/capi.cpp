@@ -85,6 +85,56 @@ static ql_status check_w8a8(const int8_t* xq, const int8_t* wq, const void* y, i
     return QL_OK;
 }
 
+ql_status quantize_per_row_int8_asym(const void* x, ql_dtype x_dtype, int64_t M, int64_t K,
+                                     int8_t* xq, float* x_scale, float* x_zero, void* stream) {
+    if (x_dtype != QL_F32 && x_dtype != QL_F16)
+        return QL_ERR_DTYPE;
+    if (bad_dims(M, 1, K) || K % 16 != 0)
+        return QL_ERR_SHAPE;
+    if (M == 0)
+        return QL_OK;
+    if (!x || !xq || !x_scale || !x_zero)
+        return QL_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(x_scale, 4) || !aligned(x_zero, 4))
+        return QL_ERR_ALIGN;
+    return ql::launch_quant_rows_i8_asym(x, x_dtype == QL_F16, M, K, xq, x_scale, x_zero,
+                                         as_stream(stream));
+}
+
+ql_status weight_column_sums_i8(const int8_t* wq, int64_t K, int64_t N, int32_t* colsum,
+                                void* stream) {
+    if (bad_dims(1, N, K) || K % 16 != 0)
+        return QL_ERR_SHAPE;
+    if (N == 0)
+        return QL_OK;
+    if (!wq || !colsum)
+        return QL_ERR_NULL;
+    if (!aligned(wq, 16) || !aligned(colsum, 4))
+        return QL_ERR_ALIGN;
+    return ql::launch_column_sums_i8(wq, K, N, colsum, as_stream(stream));
+}
+
+ql_status gemm_w8a8_asym(const int8_t* xq, const float* x_scale, const float* x_zero,
+                         const int8_t* wq, const float* w_scale, const int32_t* w_colsum,
+                         const float* bias, ql_activation act, void* y, ql_dtype y_dtype,
+                         int64_t M, int64_t N, int64_t K, void* stream) {
+    if (y_dtype != QL_F32 && y_dtype != QL_F16)
+        return QL_ERR_DTYPE;
+    if (act != QL_ACT_NONE && act != QL_ACT_GELU && act != QL_ACT_SILU)
+        return QL_ERR_DTYPE;
+    ql_status st = check_w8a8(xq, wq, y, M, N, K);
+    if (st != QL_OK || M == 0 || N == 0)
+        return st;
+    if (!x_scale || !x_zero || !w_scale || !w_colsum)
+        return QL_ERR_NULL;
+    if (!aligned(x_scale, 4) || !aligned(x_zero, 4) || !aligned(w_scale, 4) || !aligned(w_colsum, 4) ||
+        (bias && !aligned(bias, 4)))
+        return QL_ERR_ALIGN;
+    return ql::launch_gemm_w8a8(xq, x_scale, wq, w_scale, bias, y,
+                                y_dtype == QL_F32 ? ql::Y_F32 : ql::Y_F16, (int)act, x_zero, w_colsum,
+                                M, N, K, as_stream(stream));
+}
+
 ql_status gemm_w8a8_per_channel_act(const int8_t* xq, const float* x_scale, const int8_t* wq,
                                     const float* w_scale, const float* bias, ql_activation act,
                                     void* y, ql_dtype y_dtype, int64_t M, int64_t N, int64_t K,
@@ -101,7 +151,7 @@ ql_status gemm_w8a8_per_channel_act(const int8_t* xq, const float* x_scale, cons
     if (!aligned(x_scale, 4) || !aligned(w_scale, 4) || (bias && !aligned(bias, 4)))
         return QL_ERR_ALIGN;
     return ql::launch_gemm_w8a8(xq, x_scale, wq, w_scale, bias, y,
-                                y_dtype == QL_F32 ? ql::Y_F32 : ql::Y_F16, (int)act, M, N, K,
+                                y_dtype == QL_F32 ? ql::Y_F32 : ql::Y_F16, (int)act, nullptr, nullptr, M, N, K,
                                 as_stream(stream));
 }
 
@@ -117,8 +167,8 @@ ql_status gemm_w8a8_int32(const int8_t* xq, const int8_t* wq, int32_t* acc, int6
     ql_status st = check_w8a8(xq, wq, acc, M, N, K);
     if (st != QL_OK || M == 0 || N == 0)
         return st;
-    return ql::launch_gemm_w8a8(xq, nullptr, wq, nullptr, nullptr, acc, ql::Y_I32, ql::ACT_NONE, M,
-                                N, K, as_stream(stream));
+    return ql::launch_gemm_w8a8(xq, nullptr, wq, nullptr, nullptr, acc, ql::Y_I32, ql::ACT_NONE, nullptr,
+                                nullptr, M, N, K, as_stream(stream));
 }
 
 ql_status gemm_w8a16(const void* x, const void* wq, const float* w_scale,

@@ -20,6 +20,8 @@
 // never waits behind its own LDS reads. When the last round of 256 x 256 tiles would leave CUs idle, its N
 // panels run as 128 x 256 tiles whose K is split between the two groups. K % 128 == 64
 // runs a last stage whose upper half reads zeros.
+#include <type_traits>
+
 #include "ql_internal.h"
 
 namespace ql {
@@ -51,16 +53,49 @@ __device__ inline void lds_copy4(const void* g, int8_t* lds) {
 
 // Bytes of the K ring at the start of the LDS allocation (three stages of a 128 x 256 tile
 // with 128-byte k-steps); the tile's scales follow it: x_scale of its 256 rows, then
-// w_scale and bias of its 256 columns (fp32 each).
+// w_scale and bias of its 256 columns, then (asymmetric activations only) x_zero of the
+// rows and the code sums of the columns (4 bytes each).
 constexpr int RING_BYTES = 3 * 384 * 128;
-constexpr int SCALE_BYTES = 3 * 256 * 4;
+constexpr int SCALE_BYTES = 5 * 256 * 4;
+
+// The epilogue's optional asymmetric-activation terms: the rows' zero points and W's
+// column code sums (both NULL for symmetric activations).
+struct Asym {
+    const float* x_zero;
+    const int32_t* colsum;
+};
+
+// f(activation, asymmetric) as compile-time constants for the launch's uniform choice: one
+// epilogue instance per pair, so that none costs the others. The int32 output has neither.
+template <int YMODE, typename F>
+__device__ __forceinline__ void with_epilogue(int act, bool asym, F&& f) {
+    using T = std::true_type;
+    using U = std::false_type;
+    if constexpr (YMODE == Y_I32) {
+        f(std::integral_constant<int, ACT_NONE>{}, U{});
+    } else if (asym) {
+        if (act == ACT_GELU)
+            f(std::integral_constant<int, ACT_GELU>{}, T{});
+        else if (act == ACT_SILU)
+            f(std::integral_constant<int, ACT_SILU>{}, T{});
+        else
+            f(std::integral_constant<int, ACT_NONE>{}, T{});
+    } else {
+        if (act == ACT_GELU)
+            f(std::integral_constant<int, ACT_GELU>{}, U{});
+        else if (act == ACT_SILU)
+            f(std::integral_constant<int, ACT_SILU>{}, U{});
+        else
+            f(std::integral_constant<int, ACT_NONE>{}, U{});
+    }
+}
 
 // Waves 0-3 each copy 64 of the tile's x_scale, w_scale and bias entries into LDS
 // (indices clamped into range; entries past M or N are never used). Issued before the K
 // loop's first copies, so every wait of the loop also covers them; the epilogue's barrier
 // makes them visible to all waves. Without a bias, w_scale is copied in its place (unused).
-__device__ inline void issue_scales(const float* xs, const float* ws, const float* bias, int M,
-                                    int N, int m0, int n0, int wave, int lane, int8_t* smem) {
+__device__ inline void issue_scales(const float* xs, const float* ws, const float* bias, Asym asym,
+                                    int M, int N, int m0, int n0, int wave, int lane, int8_t* smem) {
     if (wave >= 4)
         return;
     int8_t* sc = smem + RING_BYTES + wave * 256;
@@ -68,6 +103,10 @@ __device__ inline void issue_scales(const float* xs, const float* ws, const floa
     lds_copy4(xs + min(m0 + i, M - 1), sc);
     lds_copy4(ws + min(n0 + i, N - 1), sc + 1024);
     lds_copy4((bias != nullptr ? bias : ws) + min(n0 + i, N - 1), sc + 2048);
+    if (asym.x_zero != nullptr) {
+        lds_copy4(asym.x_zero + min(m0 + i, M - 1), sc + 3072);
+        lds_copy4(asym.colsum + min(n0 + i, N - 1), sc + 4096);
+    }
 }
 
 // Epilogue: the accumulators are dequantized (y = acc * x_scale[m] * w_scale[n] + bias[n])
@@ -78,7 +117,7 @@ __device__ inline void issue_scales(const float* xs, const float* ws, const floa
 // Stores go through a buffer descriptor whose size ends at row M: the hardware drops
 // stores of rows past M, and a column piece past N gets an offset beyond the size, so no
 // store needs a branch.
-template <int WM, int WN, int FM, int FN, int YMODE, int NWV, int ACT>
+template <int WM, int WN, int FM, int FN, int YMODE, int NWV, int ACT, bool ASYM>
 __device__ __forceinline__ void store_tile(const i32x16 (&acc)[FM][FN], bool has_bias,
                                            void* __restrict__ Y, int M, int N, int mrow0,
                                            int ncol0, int lm0, int ln0, int wave, int lane,
@@ -102,13 +141,17 @@ __device__ __forceinline__ void store_tile(const i32x16 (&acc)[FM][FN], bool has
     const float* sx = reinterpret_cast<const float*>(smem + RING_BYTES);
     const float* sw = sx + 256;
     const float* sb = sx + 512;
-    float wsv[FN], bv[FN];
+    const float* sz = sx + 768;
+    const int32_t* scs = reinterpret_cast<const int32_t*>(sx + 1024);
+    float wsv[FN], bv[FN], csv[FN];
     if constexpr (YMODE != Y_I32) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
             const int c = ln0 + 32 * j + (lane & 31);
             wsv[j] = sw[c];
             bv[j] = has_bias ? sb[c] : 0.0f;
+            if constexpr (ASYM)
+                csv[j] = (float)scs[c];   // exact: |sum| <= 128 K < 2^24
         }
     }
     const bool vec_ok = (N % VEC) == 0;   // rows start 16-byte aligned
@@ -117,7 +160,7 @@ __device__ __forceinline__ void store_tile(const i32x16 (&acc)[FM][FN], bool has
     const int lane_off = (lane / LPR) * N * SZ + (ncol < N ? ncol * SZ : LIM);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-        float xsv[16];
+        float xsv[16], zsv[16];
         if constexpr (YMODE != Y_I32) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
@@ -125,6 +168,12 @@ __device__ __forceinline__ void store_tile(const i32x16 (&acc)[FM][FN], bool has
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
                     xsv[4 * g + q] = v[q];
+                if constexpr (ASYM) {
+                    const f32x4 zv = *reinterpret_cast<const f32x4*>(sz + lm0 + 32 * i + 8 * g + 4 * (lane >> 5));
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        zsv[4 * g + q] = zv[q];
+                }
             }
         }
 #pragma unroll
@@ -133,10 +182,15 @@ __device__ __forceinline__ void store_tile(const i32x16 (&acc)[FM][FN], bool has
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
                 OutT v;
-                if constexpr (YMODE == Y_I32)
+                if constexpr (YMODE == Y_I32) {
                     v = acc[i][j][e];
-                else
+                } else if constexpr (ASYM) {
+                    // sum_k (q_x - z_x) q_w = acc - z_x colsum, with one rounding
+                    const float t = fmaf(-zsv[e], csv[j], (float)acc[i][j][e]);
+                    v = (OutT)activation<ACT>(t * xsv[e] * wsv[j] + bv[j]);
+                } else {
                     v = (OutT)activation<ACT>((float)acc[i][j][e] * xsv[e] * wsv[j] + bv[j]);
+                }
                 *reinterpret_cast<OutT*>(stage + r * ROWB + (32 * j + (lane & 31)) * SZ) = v;
             }
         }
@@ -240,7 +294,8 @@ template <int BM, int BN, int YMODE>
 __device__ __forceinline__ void gemm_tile_pp(const int8_t* __restrict__ A, const float* __restrict__ xs,
                                              const int8_t* __restrict__ B, const float* __restrict__ ws,
                                              const float* __restrict__ bias, void* __restrict__ Y,
-                                             int M, int N, int K, int m0, int n0, int act, int8_t* smem) {
+                                             int M, int N, int K, int m0, int n0, int act, Asym asym,
+                                             int8_t* smem) {
     constexpr int BKL = 128;
     constexpr int WM = BM / 2, WN = BN / 4, FM = WM / 32, FN = WN / 32;
     constexpr int STAGE_A = BM * BKL, STAGE = (BM + BN) * BKL;
@@ -330,7 +385,7 @@ __device__ __forceinline__ void gemm_tile_pp(const int8_t* __restrict__ A, const
     // Prologue: group 0 copies all of stage 0 and stage 1 but its B high (copied in A_0),
     // and waits for stage 0; stage 1 has until the end of A_0.
     if constexpr (YMODE != Y_I32)
-        issue_scales(xs, ws, bias, M, N, m0, n0, wave, lane, smem);
+        issue_scales(xs, ws, bias, asym, M, N, m0, n0, wave, lane, smem);
     if (grp == 0) {
 #pragma unroll
         for (int c = 0; c < CA; ++c)
@@ -426,16 +481,10 @@ __device__ __forceinline__ void gemm_tile_pp(const int8_t* __restrict__ A, const
         }
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
-    // the activation is uniform: one epilogue per kind, so that none costs the others
-    if (act == ACT_GELU)
-        store_tile<WM, WN, FM, FN, YMODE, 8, ACT_GELU>(acc, bias != nullptr, Y, M, N, m0 + wm * WM,
-                                                       n0 + wn * WN, wm * WM, wn * WN, wave, lane, smem);
-    else if (act == ACT_SILU)
-        store_tile<WM, WN, FM, FN, YMODE, 8, ACT_SILU>(acc, bias != nullptr, Y, M, N, m0 + wm * WM,
-                                                       n0 + wn * WN, wm * WM, wn * WN, wave, lane, smem);
-    else
-        store_tile<WM, WN, FM, FN, YMODE, 8, ACT_NONE>(acc, bias != nullptr, Y, M, N, m0 + wm * WM,
-                                                       n0 + wn * WN, wm * WM, wn * WN, wave, lane, smem);
+    with_epilogue<YMODE>(act, asym.x_zero != nullptr, [&](auto act_c, auto asym_c) {
+        store_tile<WM, WN, FM, FN, YMODE, 8, decltype(act_c)::value, decltype(asym_c)::value>(
+            acc, bias != nullptr, Y, M, N, m0 + wm * WM, n0 + wn * WN, wm * WM, wn * WN, wave, lane, smem);
+    });
 }
 
 // A 128 x 256 tile on 8 waves with K split between two groups. Group 0
@@ -450,7 +499,8 @@ template <int YMODE>
 __device__ __forceinline__ void gemm_tile_ks(const int8_t* __restrict__ A, const float* __restrict__ xs,
                                              const int8_t* __restrict__ B, const float* __restrict__ ws,
                                              const float* __restrict__ bias, void* __restrict__ Y,
-                                             int M, int N, int K, int m0, int n0, int act, int8_t* smem) {
+                                             int M, int N, int K, int m0, int n0, int act, Asym asym,
+                                             int8_t* smem) {
     constexpr int BM = 128, BN = 256, BKL = 128;
     constexpr int WM = 64, WN = 128, FM = WM / 32, FN = WN / 32;
     constexpr int STAGE_A = BM * BKL, STAGE = (BM + BN) * BKL;
@@ -549,7 +599,7 @@ __device__ __forceinline__ void gemm_tile_ks(const int8_t* __restrict__ A, const
     // Prologue: group 0 copies stages 0 and 2, group 1 stage 1 (stage 2 is needed in phase
     // 1, before any phase-0 copy could land); group 0 reads stage 0.
     if constexpr (YMODE != Y_I32)
-        issue_scales(xs, ws, bias, M, N, m0, n0, wave, lane, smem);
+        issue_scales(xs, ws, bias, asym, M, N, m0, n0, wave, lane, smem);
     if (grp == 0) {
         copies(0);
         if (KT > 2) {
@@ -665,15 +715,10 @@ __device__ __forceinline__ void gemm_tile_ks(const int8_t* __restrict__ A, const
     }
     __builtin_amdgcn_s_waitcnt(LGKM0);
     if (grp == 0) {
-        if (act == ACT_GELU)
-            store_tile<WM, WN, FM, FN, YMODE, 4, ACT_GELU>(acc, bias != nullptr, Y, M, N, m0 + wm * WM,
-                                                           n0 + wn * WN, wm * WM, wn * WN, q, lane, smem);
-        else if (act == ACT_SILU)
-            store_tile<WM, WN, FM, FN, YMODE, 4, ACT_SILU>(acc, bias != nullptr, Y, M, N, m0 + wm * WM,
-                                                           n0 + wn * WN, wm * WM, wn * WN, q, lane, smem);
-        else
-            store_tile<WM, WN, FM, FN, YMODE, 4, ACT_NONE>(acc, bias != nullptr, Y, M, N, m0 + wm * WM,
-                                                           n0 + wn * WN, wm * WM, wn * WN, q, lane, smem);
+        with_epilogue<YMODE>(act, asym.x_zero != nullptr, [&](auto act_c, auto asym_c) {
+            store_tile<WM, WN, FM, FN, YMODE, 4, decltype(act_c)::value, decltype(asym_c)::value>(
+                acc, bias != nullptr, Y, M, N, m0 + wm * WM, n0 + wn * WN, wm * WM, wn * WN, q, lane, smem);
+        });
     } else {
         barrier_no_fence();   // the one barrier store_tile runs
     }
@@ -692,13 +737,13 @@ template <int YMODE>
 __global__ __launch_bounds__(64 * NWAVES, 1) void gemm_w8a8_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ xs, const int8_t* __restrict__ B,
     const float* __restrict__ ws, const float* __restrict__ bias, void* __restrict__ Y, int M,
-    int N, int K, int act, TilePlan plan) {
+    int N, int K, int act, Asym asym, TilePlan plan) {
     __shared__ __attribute__((aligned(1024))) int8_t smem[RING_BYTES + SCALE_BYTES];
     const int bid = blockIdx.x;
     if (bid < plan.nbig) {
         const int tile = xcd_remap(bid, plan.nbig);
         const int tn = tile / plan.tiles_m_big, tm = tile - tn * plan.tiles_m_big;
-        gemm_tile_pp<256, 256, YMODE>(A, xs, B, ws, bias, Y, M, N, K, tm * 256, tn * 256, act, smem);
+        gemm_tile_pp<256, 256, YMODE>(A, xs, B, ws, bias, Y, M, N, K, tm * 256, tn * 256, act, asym, smem);
         if (bid >= plan.nsmall)
             return;
         // The big tile's epilogue has read all it needs from LDS (its stores may still be in
@@ -709,7 +754,7 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void gemm_w8a8_kernel(
     if (bid < plan.nsmall) {
         const int tile = xcd_remap(bid, plan.nsmall);
         const int tn = tile / plan.tiles_m_small, tm = tile - tn * plan.tiles_m_small;
-        gemm_tile_ks<YMODE>(A, xs, B, ws, bias, Y, M, N, K, tm * 128, plan.n_small0 + tn * 256, act, smem);
+        gemm_tile_ks<YMODE>(A, xs, B, ws, bias, Y, M, N, K, tm * 128, plan.n_small0 + tn * 256, act, asym, smem);
     }
 }
 
@@ -750,7 +795,8 @@ TilePlan plan_tiles(int64_t M, int64_t N) {
 
 ql_status launch_gemm_w8a8(const int8_t* xq, const float* x_scale, const int8_t* wq,
                            const float* w_scale, const float* bias, void* y, int y_mode, int act,
-                           int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+                           const float* x_zero, const int32_t* colsum, int64_t M, int64_t N,
+                           int64_t K, hipStream_t stream) {
     if (M == 0 || N == 0)
         return QL_OK;
     const TilePlan plan = plan_tiles(M, N);
@@ -761,7 +807,7 @@ ql_status launch_gemm_w8a8(const int8_t* xq, const float* x_scale, const int8_t*
     const int m = (int)M, n = (int)N, k = (int)K;
 #define QL_LAUNCH(MODE)                                                                          \
     hipLaunchKernelGGL((gemm_w8a8_kernel<MODE>), grid, block, 0, stream, xq, x_scale, wq, w_scale, \
-                       bias, y, m, n, k, act, plan)
+                       bias, y, m, n, k, act, (Asym{x_zero, colsum}), plan)
     switch (y_mode) {
     case Y_F32:
         QL_LAUNCH(Y_F32);

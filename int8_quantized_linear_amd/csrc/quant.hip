@@ -49,6 +49,40 @@ __device__ inline uint32_t code_u8_biased(float x, float s, float y, uint32_t se
     return __builtin_amdgcn_cvt_pk_u8_f32(c, sel, acc);
 }
 
+// Asymmetric: rint(x / s + z) clamped to [-128, 127], as (code + 128) in the byte `sel` of
+// `acc`. The quotient is the correctly rounded one (as in code_u8_biased), then z is added
+// with its own rounding, the two fp32 operations of x / s + z.
+__device__ inline uint32_t code_u8_asym(float x, float s, float y, float z, uint32_t sel, uint32_t acc) {
+    const float q0 = __fmul_rn(x, y);
+    const float r = fmaf(-q0, s, x);
+    const float d = fmaf(r, y, q0);   // x / s, correctly rounded
+    const float q = rintf(__fadd_rn(d, z));
+    const float c = __builtin_amdgcn_fmed3f(q, -128.0f, 127.0f) + 128.0f;
+    return __builtin_amdgcn_cvt_pk_u8_f32(c, sel, acc);
+}
+
+// Block-wide maximum of hi and of -lo together (one pair of LDS slots per wave).
+__device__ inline void block_minmax(float& lo, float& hi, float* red) {
+#pragma unroll
+    for (int o = WAVE / 2; o > 0; o >>= 1) {
+        hi = fmaxf(hi, __shfl_xor(hi, o, WAVE));
+        lo = fminf(lo, __shfl_xor(lo, o, WAVE));
+    }
+    const int w = threadIdx.x / WAVE;
+    if ((threadIdx.x & (WAVE - 1)) == 0) {
+        red[2 * w] = hi;
+        red[2 * w + 1] = lo;
+    }
+    __syncthreads();
+    hi = red[0];
+    lo = red[1];
+#pragma unroll
+    for (int i = 1; i < QT / WAVE; ++i) {
+        hi = fmaxf(hi, red[2 * i]);
+        lo = fminf(lo, red[2 * i + 1]);
+    }
+}
+
 // One 16-byte chunk of input as fp32 values: 8 fp16 or 4 fp32 elements.
 template <bool F16>
 struct Chunk {
@@ -73,6 +107,29 @@ struct Chunk {
         for (int i = 0; i < E; ++i)
             a = fmaxf(a, fabsf(v[i]));
         return a;
+    }
+    __device__ inline void minmax(float& lo, float& hi) const {
+#pragma unroll
+        for (int i = 0; i < E; ++i) {
+            lo = fminf(lo, v[i]);
+            hi = fmaxf(hi, v[i]);
+        }
+    }
+    // Asymmetric codes; y = 1 / s correctly rounded, z the row's zero point.
+    __device__ inline void store_codes_asym(int8_t* q, float s, float y, float z) const {
+        uint32_t w[E / 4];
+#pragma unroll
+        for (int j = 0; j < E / 4; ++j) {
+            uint32_t b = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                b = code_u8_asym(v[4 * j + i], s, y, z, i, b);
+            w[j] = b ^ 0x80808080u;
+        }
+        if constexpr (E == 8)
+            *reinterpret_cast<u32x2*>(q) = u32x2{w[0], w[1]};
+        else
+            *reinterpret_cast<uint32_t*>(q) = w[0];
     }
     // y = 1 / s, correctly rounded.
     __device__ inline void store_codes(int8_t* q, float s, float y) const {
@@ -143,6 +200,97 @@ __global__ __launch_bounds__(QT) void quant_rows_i8_kernel(const void* __restric
             c.load(xr + (int64_t)ch * 16);
             c.store_codes(qr + (int64_t)ch * C::E, s, y);
         }
+    }
+}
+
+// Asymmetric per-row int8 (hotelren.com "量化算法的本质", per_channel_quant_int8, the
+// asymmetric branch), per row with lo, hi its minimum and maximum:
+//   s = max((hi - lo) / 255, 1e-8);  z = -lo / s - 128 (a float);
+//   q = clamp(round(x / s + z), -128, 127)      (fp32, round half to even)
+// so that x ~ s (q - z). One workgroup per row, as quant_rows_i8_kernel.
+template <bool F16>
+__global__ __launch_bounds__(QT) void quant_rows_i8_asym_kernel(const void* __restrict__ x, int64_t K,
+                                                               int8_t* __restrict__ q,
+                                                               float* __restrict__ scale,
+                                                               float* __restrict__ zero) {
+    using C = Chunk<F16>;
+    __shared__ float red[2 * (QT / WAVE)];
+    const int64_t row = blockIdx.x;
+    const char* xr = reinterpret_cast<const char*>(x) + row * K * (F16 ? 2 : 4);
+    int8_t* qr = q + row * K;
+    const int nch = (int)(K / C::E);
+    float lo = INFINITY, hi = -INFINITY;
+    auto params = [&](float& s, float& y, float& z) {
+        block_minmax(lo, hi, red);
+        s = fmaxf((hi - lo) / 255.0f, 1e-8f);
+        y = 1.0f / s;
+        z = __fsub_rn(-lo / s, 128.0f);
+        if (threadIdx.x == 0) {
+            scale[row] = s;
+            zero[row] = z;
+        }
+    };
+    float s, y, z;
+    if (nch <= QT * QMAXC) {
+        C c[QMAXC];
+#pragma unroll
+        for (int i = 0; i < QMAXC; ++i) {
+            const int ch = threadIdx.x + i * QT;
+            if (ch < nch) {
+                c[i].load(xr + (int64_t)ch * 16);
+                c[i].minmax(lo, hi);
+            }
+        }
+        params(s, y, z);
+#pragma unroll
+        for (int i = 0; i < QMAXC; ++i) {
+            const int ch = threadIdx.x + i * QT;
+            if (ch < nch)
+                c[i].store_codes_asym(qr + (int64_t)ch * C::E, s, y, z);
+        }
+    } else {
+        for (int ch = threadIdx.x; ch < nch; ch += QT) {
+            C c;
+            c.load(xr + (int64_t)ch * 16);
+            c.minmax(lo, hi);
+        }
+        params(s, y, z);
+        for (int ch = threadIdx.x; ch < nch; ch += QT) {
+            C c;
+            c.load(xr + (int64_t)ch * 16);
+            c.store_codes_asym(qr + (int64_t)ch * C::E, s, y, z);
+        }
+    }
+}
+
+// Column sums of int8 codes stored [N][K] (W column-major): the per-column term of the
+// asymmetric expansion sum_k (q_x - z_x) q_w = sum_k q_x q_w - z_x sum_k q_w
+// (quant67.com ch.17 §二). One workgroup per column; an offline producer.
+__global__ __launch_bounds__(QT) void column_sums_i8_kernel(const int8_t* __restrict__ wq, int64_t K,
+                                                           int32_t* __restrict__ colsum) {
+    __shared__ int red[QT / WAVE];
+    const int8_t* col = wq + (int64_t)blockIdx.x * K;
+    int t = 0;
+    for (int64_t c = threadIdx.x; c < K / 16; c += QT) {
+        const i32x4 v = *reinterpret_cast<const i32x4*>(col + c * 16);
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                t += (int)(int8_t)(v[d] >> (8 * b));
+    }
+#pragma unroll
+    for (int o = WAVE / 2; o > 0; o >>= 1)
+        t += __shfl_xor(t, o, WAVE);
+    if ((threadIdx.x & (WAVE - 1)) == 0)
+        red[threadIdx.x / WAVE] = t;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int r = 0;
+#pragma unroll
+        for (int i = 0; i < QT / WAVE; ++i)
+            r += red[i];
+        colsum[blockIdx.x] = r;
     }
 }
 
@@ -239,6 +387,26 @@ ql_status launch_quant_rows_i8(const void* x, int x_is_f16, int64_t rows, int64_
         hipLaunchKernelGGL(quant_rows_i8_kernel<true>, grid, block, 0, stream, x, K, q, scale);
     else
         hipLaunchKernelGGL(quant_rows_i8_kernel<false>, grid, block, 0, stream, x, K, q, scale);
+    return launch_status();
+}
+
+ql_status launch_quant_rows_i8_asym(const void* x, int x_is_f16, int64_t rows, int64_t K, int8_t* q,
+                                    float* scale, float* zero, hipStream_t stream) {
+    if (rows == 0)
+        return QL_OK;
+    const dim3 grid((unsigned)rows), block(QT);
+    if (x_is_f16)
+        hipLaunchKernelGGL(quant_rows_i8_asym_kernel<true>, grid, block, 0, stream, x, K, q, scale, zero);
+    else
+        hipLaunchKernelGGL(quant_rows_i8_asym_kernel<false>, grid, block, 0, stream, x, K, q, scale, zero);
+    return launch_status();
+}
+
+ql_status launch_column_sums_i8(const int8_t* wq, int64_t K, int64_t N, int32_t* colsum,
+                                hipStream_t stream) {
+    if (N == 0)
+        return QL_OK;
+    hipLaunchKernelGGL(column_sums_i8_kernel, dim3((unsigned)N), dim3(QT), 0, stream, wq, K, colsum);
     return launch_status();
 }
 

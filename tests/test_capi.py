@@ -39,6 +39,9 @@ def lib():
         "gemm_w4a16_grouped": [P, P, P, I64, P, P, I64, I64, I64, P],
         "gemm_w8a8_per_channel_act": [P, P, P, P, P, I, P, I, I64, I64, I64, P],
         "gemm_w4a16_grouped_act": [P, P, P, I64, P, I, P, I64, I64, I64, P],
+        "quantize_per_row_int8_asym": [P, I, I64, I64, P, P, P, P],
+        "weight_column_sums_i8": [P, I64, I64, P, P],
+        "gemm_w8a8_asym": [P, P, P, P, P, P, P, I, P, I, I64, I64, I64, P],
         "quantize_weight_block_asym_u8": [P, I64, I64, I64, P, P, P, P],
         "quantize_weight_int4_grouped": [P, I64, I64, I64, P, P, P],
     }
@@ -55,7 +58,8 @@ def test_header_declares_the_entry_points():
     for n in ("quantize_per_row_int8", "quantize_weight_per_channel", "gemm_w8a8_per_channel",
               "gemm_w8a16", "gemm_w4a16_grouped", "gemm_w8a8_int32", "ql_status_str",
               "quantize_weight_block_asym_u8", "quantize_weight_int4_grouped",
-              "gemm_w8a8_per_channel_act", "gemm_w4a16_grouped_act"):
+              "gemm_w8a8_per_channel_act", "gemm_w4a16_grouped_act", "quantize_per_row_int8_asym",
+              "weight_column_sums_i8", "gemm_w8a8_asym"):
         assert n in names
 
 
@@ -182,6 +186,29 @@ def test_fused_activation_validation(lib):
         assert g(A, A, A, 96, None, act, A, 32, 64, 384, None) == SHAPE
         assert g(A, A, MIS, 128, None, act, A, 32, 64, 256, None) == ALIGN
     assert g(A, A, A, 128, None, 7, A, 32, 64, 256, None) == DTYPE
+
+
+def test_asymmetric_validation(lib):
+    f = lib.quantize_per_row_int8_asym
+    assert f(A, F16, 0, 64, None, None, None, None) == OK
+    assert f(A, 7, 4, 64, A, A, A, None) == DTYPE
+    assert f(A, F16, 4, 40, A, A, A, None) == SHAPE
+    assert f(A, F16, 4, 64, A, A, None, None) == NULL
+    assert f(A, F16, 4, 64, A, A, MIS, None) == ALIGN
+    g = lib.weight_column_sums_i8
+    assert g(None, 64, 0, None, None) == OK
+    assert g(A, 40, 8, A, None) == SHAPE
+    assert g(None, 64, 8, A, None) == NULL
+    assert g(MIS, 64, 8, A, None) == ALIGN
+    h = lib.gemm_w8a8_asym
+    assert h(None, None, None, None, None, None, None, 0, None, F16, 0, 8, 64, None) == OK
+    assert h(A, A, None, A, A, A, None, 0, A, F16, 8, 8, 64, None) == NULL     # no zero points
+    assert h(A, A, A, A, A, None, None, 0, A, F16, 8, 8, 64, None) == NULL     # no column sums
+    assert h(A, A, A, A, A, A, None, 3, A, F16, 8, 8, 64, None) == DTYPE
+    assert h(A, A, A, A, A, A, None, 1, A, 5, 8, 8, 64, None) == DTYPE
+    assert h(A, A, A, A, A, A, None, 0, A, F16, 8, 8, 96, None) == SHAPE
+    assert h(A, A, MIS, A, A, A, None, 0, A, F16, 8, 8, 64, None) == ALIGN
+    assert h(A, A, A, A, A, MIS, None, 0, A, F16, 8, 8, 64, None) == ALIGN
 
 
 def test_producer_validation(lib):

@@ -118,3 +118,45 @@ def test_int4_producer(ql, N, K, group):
     p, s = ql.quantize_weight_int4_grouped(dev(w_nk), group)
     assert np.array_equal(host(s).view(np.uint16), s_ref.view(np.uint16))
     assert np.array_equal(host(p), p_ref)
+
+
+# ------------------------------------------------------------ asymmetric rows
+
+def _check_asym(ql, x):
+    q_ref, s_ref, z_ref = oracle.quant_rows_i8_asym(x)
+    q, s, z = ql.quantize_per_row_int8_asym(dev(x))
+    assert np.array_equal(host(s).view(np.uint32), s_ref.view(np.uint32))
+    assert np.array_equal(host(z).view(np.uint32), z_ref.view(np.uint32))
+    assert np.array_equal(host(q), q_ref)
+
+
+@pytest.mark.parametrize("M,K,dtype", [(1, 16, np.float32), (37, 4096, np.float16), (5, 8256, np.float16),
+                                       (3, 4112, np.float32), (130, 1024, np.float16), (64, 48, np.float32)])
+def test_asym_rows_bit_exact(ql, M, K, dtype):
+    """Codes, scales and float zero points bit for bit: offset and scaled normal rows,
+    rows longer than the registers hold (re-read), fp16 and fp32 inputs."""
+    rng = np.random.default_rng(M * 13 + K)
+    x = (rng.standard_normal((M, K)) * np.exp2(rng.integers(-6, 6, (M, 1)))
+         + rng.uniform(-4, 4, (M, 1))).astype(dtype)
+    _check_asym(ql, x)
+
+
+def test_asym_special_rows(ql):
+    """Rows with minimum 0 (zero point -128), constant rows (scale floor), a single
+    nonzero, all-negative rows, and ties of x / s + z at .5."""
+    rng = np.random.default_rng(91)
+    K = 256
+    rows = [np.abs(rng.standard_normal(K)), np.full(K, 0.75), np.zeros(K), -np.abs(rng.standard_normal(K)) - 3,
+            np.eye(1, K, 17)[0] * 5.0, (rng.integers(0, 256, K) * 0.125) - 3.0, np.arange(K) * 0.5]
+    x = np.stack(rows).astype(np.float32)
+    _check_asym(ql, x)
+    _check_asym(ql, x.astype(np.float16))
+
+
+def test_column_sums(ql):
+    rng = np.random.default_rng(92)
+    for N, K in [(1, 16), (77, 4096), (11008, 256), (300, 4112)]:
+        wq = rng.integers(-127, 128, (N, K), dtype=np.int8)
+        assert np.array_equal(host(ql.weight_column_sums_i8(dev(wq))), oracle.column_sums_i8(wq))
+    wq = np.full((3, 131008), -128, np.int8)
+    assert np.all(host(ql.weight_column_sums_i8(dev(wq))) == -128 * 131008)

@@ -196,6 +196,47 @@ def test_fused_activation_none_is_plain(ql):
     assert np.array_equal(y0.view(np.uint16), y1.view(np.uint16))
 
 
+@pytest.mark.parametrize("M,N,K,out,act", [(16, 256, 256, torch.float32, "none"), (300, 520, 384, torch.float16, "none"),
+                                           (257, 129, 192, torch.float32, "gelu"), (2000, 8300, 64, torch.float16, "silu"),
+                                           (2048, 11008, 4096, torch.float16, "none")])
+def test_asymmetric_layer(ql, M, N, K, out, act):
+    """Asymmetric activations end to end on the GPU (quantizer bit-exact, column sums exact)
+    against the oracle's layer from its definition, sum_k s_x (q_x - z_x) s_w q_w + b.
+    The kernel takes acc - z_x colsum with one rounding: fp32 outputs within
+    1e-5 (s_x s_w (|acc| + |z_x colsum|) + |b|), times max |act'| = 1.13 when an activation
+    follows, plus 2e-6 |act(y64)|; fp16 outputs additionally one fp16 step. Activations
+    are ReLU-like on half the rows (non-negative, zero point -128)."""
+    w = workloads.with_shape(workloads.W8A8_PREFILL, M, K, N)
+    inp = workloads.draw(w)
+    x = inp.x.astype(np.float32)
+    x[::2] = np.maximum(x[::2], 0)
+    x = x.astype(inp.x.dtype)
+    wq_r, ws_r = oracle.quant_weight_per_channel(inp.w_nk)
+    wq, ws = ql.quantize_weight_per_channel(dev(inp.w_nk))
+    cs = ql.weight_column_sums_i8(wq)
+    assert np.array_equal(host(cs), oracle.column_sums_i8(wq_r))
+    rows = np.arange(M) if M <= 512 else np.unique(np.concatenate([np.arange(0, M, 97), [M - 1]]))
+    xq_r, xs_r, xz_r = oracle.quant_rows_i8_asym(x)
+    xq, xs, xz = ql.quantize_per_row_int8_asym(dev(x))
+    assert np.array_equal(host(xq), xq_r) and np.array_equal(host(xz), xz_r)
+    g = Guarded((M, N), out)
+    ql.gemm_w8a8_asym(xq, xs, xz, wq, ws, cs, dev(inp.bias), act, out, y=g.view)
+    g.check()
+    y64 = oracle.w8a8_asym_f64(xq_r[rows], xs_r[rows], xz_r[rows], wq_r, ws_r, inp.bias)
+    acc = oracle.gemm_i32(xq_r[rows], wq_r).astype(np.float64)
+    colsum = oracle.column_sums_i8(wq_r).astype(np.float64)
+    mag = (xs_r[rows].astype(np.float64)[:, None] * ws_r.astype(np.float64)[None, :]
+           * (np.abs(acc) + np.abs(xz_r[rows].astype(np.float64)[:, None] * colsum[None, :]))
+           + np.abs(inp.bias.astype(np.float64))[None, :])
+    code = {"none": 0, "gelu": 1, "silu": 2}[act]
+    ref = oracle.activation_f64(y64, code)
+    tol = (1.13 if code else 1.0) * 1e-5 * mag + 2e-6 * np.abs(ref)
+    y = host(g.view)[rows].astype(np.float64)
+    if out == torch.float16:
+        tol = tol + f16_ulp(ref)
+    assert np.all(np.abs(y - ref) <= tol)
+
+
 def test_empty(ql):
     xq = torch.empty((0, 64), dtype=torch.int8, device=DEV)
     wq = torch.zeros((8, 64), dtype=torch.int8, device=DEV)
