@@ -63,6 +63,12 @@ def _declare(L):
     L.oracle_num_threads.restype = ctypes.c_int
     L.oracle_activation_f64.argtypes = [_P, _I64, ctypes.c_int]
     L.oracle_quant_rows_i8_asym.argtypes = [_P, _I64, _I64, _P, _P, _P]
+    L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+    L.oracle_e4m3_decode.restype = ctypes.c_double
+    L.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+    L.oracle_e4m3_encode.restype = ctypes.c_uint8
+    L.oracle_quant_rows_e4m3.argtypes = [_P, _I64, _I64, _P, _P]
+    L.oracle_gemm_e4m3_f64.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P]
     L.oracle_column_sums_i8.argtypes = [_P, _I64, _I64, _P]
     L.oracle_w8a8_asym_f64.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]
 
@@ -206,6 +212,38 @@ class Oracle:
         self.L.oracle_w8a8_asym_f64(_ptr(xq), _ptr(xs), _ptr(xz), _ptr(wq), _ptr(ws), _ptr(b), M, N, K,
                                     _ptr(y64))
         return y64
+
+    def e4m3_decode(self, codes) -> np.ndarray:
+        """fp64 values of OCP e4m3 codes (NaN for S.1111.111)."""
+        c = np.asarray(codes, np.uint8)
+        return np.array([self.L.oracle_e4m3_decode(int(v)) for v in c.ravel()]).reshape(c.shape)
+
+    def e4m3_encode(self, x) -> np.ndarray:
+        """e4m3 codes of fp32 values with |x| <= 448, nearest, ties to even."""
+        a = np.asarray(x, np.float32)
+        return np.array([self.L.oracle_e4m3_encode(float(v)) for v in a.ravel()], np.uint8).reshape(a.shape)
+
+    def quant_rows_e4m3(self, x) -> Tuple[np.ndarray, np.ndarray]:
+        """Per-row fp8 of x [M, K] (fp16 or fp32): (codes uint8 [M, K], scale fp32 [M])."""
+        xf = self._as_f32(x)
+        M, K = xf.shape
+        q = np.empty((M, K), np.uint8)
+        s = np.empty(M, np.float32)
+        self.L.oracle_quant_rows_e4m3(_ptr(xf), M, K, _ptr(q), _ptr(s))
+        return q, s
+
+    def gemm_e4m3_f64(self, xq, x_scale, wq_nk, w_scale, bias=None) -> Tuple[np.ndarray, np.ndarray]:
+        """(y64, mag): the fp8 layer in fp64, and x_scale w_scale sum_k |products|."""
+        xq = _c(xq, np.uint8)
+        wq = _c(wq_nk, np.uint8)
+        M, K = xq.shape
+        N = wq.shape[0]
+        xs, ws = _c(x_scale, np.float32), _c(w_scale, np.float32)
+        b = None if bias is None else _c(bias, np.float32)
+        y64 = np.empty((M, N), np.float64)
+        mag = np.empty((M, N), np.float64)
+        self.L.oracle_gemm_e4m3_f64(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(b), M, N, K, _ptr(y64), _ptr(mag))
+        return y64, mag
 
     ACT_NONE, ACT_GELU, ACT_SILU = 0, 1, 2
 

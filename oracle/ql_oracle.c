@@ -213,6 +213,90 @@ void oracle_w8a8_asym_f64(const int8_t* xq, const float* x_scale, const float* x
     }
 }
 
+/* ------------------------------------------------------------ fp8 (e4m3) */
+
+/* The OCP 8-bit float E4M3 ("e4m3fn"): sign, 4 exponent bits (bias 7), 3 mantissa bits;
+ * exponent field 0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN; no infinities; the largest
+ * finite value is S.1111.110 = 448. */
+double oracle_e4m3_decode(uint8_t c)
+{
+    const int sgn = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    if (e == 15 && m == 7)
+        return NAN;
+    const double v = e == 0 ? ldexp(m / 8.0, -6) : ldexp(1.0 + m / 8.0, e - 7);
+    return sgn ? -v : v;
+}
+
+/* The e4m3 code nearest to x (|x| <= 448), ties to the code with an even mantissa (round
+ * half to even), found by search over the finite magnitudes. */
+uint8_t oracle_e4m3_encode(float x)
+{
+    const double a = fabs((double)x);
+    int best = 0;
+    double bd = a;   /* distance to code 0 */
+    for (int c = 1; c < 127; ++c) {   /* 0x7F is NaN */
+        const double d = fabs(oracle_e4m3_decode((uint8_t)c) - a);
+        if (d < bd || (d == bd && (c & 1) == 0 && (best & 1) == 1)) {
+            bd = d;
+            best = c;
+        }
+    }
+    return (uint8_t)(best | (signbit(x) ? 0x80 : 0));
+}
+
+/* Per-row fp8 quantization (hotelren.com: per_channel_quant_fp8 differs from the int8
+ * quantizer only in the result type): s = max(absmax, 1e-10) / 448 (fp32), q = e4m3(x / s)
+ * with x / s correctly rounded in fp32, then rounded to e4m3 half to even. */
+void oracle_quant_rows_e4m3(const float* x, int64_t rows, int64_t cols, uint8_t* q, float* scale)
+{
+    for (int64_t r = 0; r < rows; ++r) {
+        const float* v = x + r * cols;
+        float a = 0.0f;
+        for (int64_t i = 0; i < cols; ++i) {
+            const float t = fabsf(v[i]);
+            if (t > a)
+                a = t;
+        }
+        const float s = (a > 1e-10f ? a : 1e-10f) / 448.0f;
+        for (int64_t i = 0; i < cols; ++i) {
+            float t = v[i] / s;
+            if (t > 448.0f)
+                t = 448.0f;
+            if (t < -448.0f)
+                t = -448.0f;
+            q[r * cols + i] = oracle_e4m3_encode(t);
+        }
+        scale[r] = s;
+    }
+}
+
+/* The fp8 layer in fp64: y[m][n] = x_scale[m] w_scale[n] sum_k dec(xq[m][k]) dec(wq[n][k])
+ * + bias[n]. Also returns mag[m][n] = x_scale w_scale sum_k |dec(xq) dec(wq)| (the scale of
+ * an fp32 summation's error) when mag is not NULL. */
+void oracle_gemm_e4m3_f64(const uint8_t* xq, const float* x_scale, const uint8_t* wq,
+                          const float* w_scale, const float* bias, int64_t M, int64_t N,
+                          int64_t K, double* y64, double* mag)
+{
+    double lut[256];
+    for (int c = 0; c < 256; ++c)
+        lut[c] = oracle_e4m3_decode((uint8_t)c);
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0, am = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const double p = lut[xq[m * K + k]] * lut[wq[n * K + k]];
+                acc += p;
+                am += fabs(p);
+            }
+            const double sc = (double)x_scale[m] * (double)w_scale[n];
+            y64[m * N + n] = acc * sc + (bias ? (double)bias[n] : 0.0);
+            if (mag)
+                mag[m * N + n] = am * sc;
+        }
+    }
+}
+
 /* ---------------------------------------------------------- integer GEMM */
 
 /* acc[m][n] = sum_k xq[m][k] * wq[n][k]; xq is [M][K] row-major, wq is W [K,N]

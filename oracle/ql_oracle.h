@@ -31,6 +31,12 @@ void oracle_quant_int4_group(const float* w, int64_t N, int64_t K, int64_t group
                              int32_t* packed, uint16_t* scale16);
 
 void oracle_activation_f64(double* y, int64_t n, int act);
+double oracle_e4m3_decode(uint8_t c);
+uint8_t oracle_e4m3_encode(float x);
+void oracle_quant_rows_e4m3(const float* x, int64_t rows, int64_t cols, uint8_t* q, float* scale);
+void oracle_gemm_e4m3_f64(const uint8_t* xq, const float* x_scale, const uint8_t* wq,
+                          const float* w_scale, const float* bias, int64_t M, int64_t N,
+                          int64_t K, double* y64, double* mag);
 void oracle_quant_rows_i8_asym(const float* x, int64_t rows, int64_t cols, int8_t* q,
                                float* scale, float* zero);
 void oracle_column_sums_i8(const int8_t* wq, int64_t N, int64_t K, int32_t* colsum);

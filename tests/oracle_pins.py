@@ -488,6 +488,74 @@ def pin_asym_layer(orc):
     assert np.array_equal(orc.column_sums_i8(wq), wq.astype(np.int64).sum(1))
 
 
+def _e4m3_table(orc):
+    vals = orc.e4m3_decode(np.arange(256))
+    return vals
+
+
+def pin_e4m3_format(orc):
+    """The OCP E4M3 format's fixed points: 1.0 is 0x38, the largest finite value 448 is
+    0x7E, the smallest normal 2^-6 is 0x08, the smallest subnormal 2^-9 is 0x01, NaN is
+    exactly 0x7F and 0xFF, 0x80 is -0, the sign bit negates, the 127 non-negative finite
+    codes increase strictly, and consecutive normals of one binade are 2^(e-10) apart."""
+    v = _e4m3_table(orc)
+    assert v[0x38] == 1.0 and v[0x7E] == 448.0 and v[0x08] == 2.0 ** -6 and v[0x01] == 2.0 ** -9
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF]) and np.isnan(v).sum() == 2
+    assert v[0x80] == 0.0 and np.signbit(v[0x80])
+    pos = v[:0x7F]
+    assert np.all(np.diff(pos) > 0)
+    assert np.array_equal(v[0x80:0xFF], -pos)
+    for e in range(1, 15):
+        b = pos[8 * e:8 * e + 8]
+        assert np.allclose(np.diff(b), 2.0 ** (e - 10), rtol=0, atol=0)
+
+
+def pin_e4m3_encode(orc):
+    """Encoding is round to nearest with ties to an even mantissa: every midpoint between
+    consecutive finite values goes to the even code, and random values land within half a
+    spacing of their value (checked by bisection of the sorted value table)."""
+    v = _e4m3_table(orc)
+    pos = v[:0x7F]
+    mids = (pos[:-1] + pos[1:]) / 2
+    got = orc.e4m3_encode(mids.astype(np.float32))
+    want = np.where(np.arange(1, 127) % 2 == 0, np.arange(1, 127), np.arange(0, 126))
+    assert np.array_equal(got.astype(np.int64), want)
+    assert np.array_equal(orc.e4m3_encode(-mids.astype(np.float32)).astype(np.int64), want | 0x80)
+    x = np.random.default_rng(101).uniform(-448, 448, 4000).astype(np.float32)
+    x[:1000] *= np.float32(2.0 ** -8)
+    q = orc.e4m3_encode(x)
+    a = np.abs(x.astype(np.float64))
+    i = np.clip(np.searchsorted(pos, a), 1, 126)
+    near = np.minimum(np.abs(pos[i] - a), np.abs(pos[i - 1] - a))
+    assert np.all(np.abs(np.abs(v[q]) - a) <= near * (1 + 1e-12))
+    assert np.all((q >> 7) == np.signbit(x))
+
+
+def pin_e4m3_quant_and_layer(orc):
+    """Per-row fp8: each row's absmax element codes to +-448 and every normal-range element
+    dequantizes within 2^-4 relative (three mantissa bits); an all-zero row takes the floor
+    scale 1e-10/448. The fp8 layer equals numpy's fp64 product of the decoded codes, and its
+    magnitude bounds |y - bias|."""
+    rng = np.random.default_rng(102)
+    x = (rng.standard_normal((40, 256)) * np.exp2(rng.integers(-8, 8, (40, 1)))).astype(np.float32)
+    x[3] = 0
+    q, s = orc.quant_rows_e4m3(x)
+    v = _e4m3_table(orc)
+    r = np.arange(40)
+    am = np.abs(x).argmax(1)
+    assert np.all(np.abs(v[q[r, am]][r != 3]) == 448.0)
+    assert s[3] == np.float32(np.float32(1e-10) / np.float32(448.0)) and np.all(q[3] == 0)
+    deq = v[q] * s.astype(np.float64)[:, None]
+    normal = np.abs(x) >= 2.0 ** -6 * s[:, None]
+    assert np.all(np.abs(deq - x)[normal] <= 2.0 ** -4 * np.abs(x)[normal])
+    wq, ws = orc.quant_rows_e4m3(rng.standard_normal((30, 256)).astype(np.float32))
+    b = rng.standard_normal(30).astype(np.float32)
+    y, mag = orc.gemm_e4m3_f64(q, s, wq, ws, b)
+    ref = (v[q] * s.astype(np.float64)[:, None]) @ (v[wq] * ws.astype(np.float64)[:, None]).T + b[None, :]
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-300)
+    assert np.all(np.abs(y - b[None, :]) <= mag * (1 + 1e-12) + 1e-300)
+
+
 # Standard normal distribution function at tabulated points (values from a normal table,
 # to 16 significant digits); 1.959963984540054 is the 0.975 quantile.
 PHI_TABLE = {-3.0: 0.001349898031630095, -0.5: 0.3085375387259869, 0.0: 0.5,

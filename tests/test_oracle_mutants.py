@@ -55,6 +55,12 @@ MUTANTS = [
     ("asym_no_scale_floor", "if (s < 1e-8f)\n            s = 1e-8f;", "if (s < 0.0f)\n            s = 1e-8f;"),
     ("asym_layer_zero_sign", "((double)xq[m * K + k] - (double)x_zero[m])", "((double)xq[m * K + k] + (double)x_zero[m])"),
     ("colsum_wrong_index", "t += wq[n * K + k];", "t += wq[(k % N) * K + (n % K)];"),
+    ("e4m3_bias_8", "ldexp(1.0 + m / 8.0, e - 7)", "ldexp(1.0 + m / 8.0, e - 8)"),
+    ("e4m3_subnormal_exponent", "ldexp(m / 8.0, -6)", "ldexp(m / 8.0, -7)"),
+    ("e4m3_ties_up", "(d == bd && (c & 1) == 0 && (best & 1) == 1)", "(d == bd)"),
+    ("e4m3_scale_127", "const float s = (a > 1e-10f ? a : 1e-10f) / 448.0f;",
+     "const float s = (a > 1e-10f ? a : 1e-10f) / 127.0f;"),
+    ("e4m3_gemm_abs_sum", "acc += p;", "acc += fabs(p);"),
     ("act_codes_swapped", "if (act == 1)\n            y[i] = v * (0.5", "if (act == 2)\n            y[i] = v * (0.5"),
 ]
 
