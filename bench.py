@@ -40,6 +40,7 @@ if ROOT not in sys.path:
 
 METRIC = "W8A8 per-channel GEMM TOPS at Llama-7B shapes; W8A16 decode GEMV GB/s"
 PEAK_INT8_TOPS = 5000.0        # MI355X dense int8 MFMA, 5.0 POP/s
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA, 5.0 PFLOP/s
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 ROTATE_BYTES = 512 << 20
 
@@ -147,12 +148,10 @@ def fused_activation_timings(ql, n, gemm, dec5, r5, make_gemm, make_dec, ops, w4
     }
 
 
-def asym_timings(n, runs, ops, quant_bytes, name, progress):
-    """The layer with asymmetric per-row activations (quantizer with a float zero point, GEMM
-    with the zero-point correction in the epilogue) against the symmetric one at the same
-    shape: each launch event-timed, the four alternating."""
+def _alternate(n, runs):
+    """Mean microseconds per launch of each zero-argument callable in runs: one warm-up
+    round, then n rounds in which the launches alternate, each bracketed by events."""
     import torch
-    progress("asymmetric activations: %d launches each" % n)
     ev = {k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
           for k in runs}
     for f in runs.values():
@@ -164,7 +163,15 @@ def asym_timings(n, runs, ops, quant_bytes, name, progress):
             f()
             ev[k][i][1].record()
     torch.cuda.synchronize()
-    us = {k: 1e3 * sum(a.elapsed_time(b) for a, b in v) / n for k, v in ev.items()}
+    return {k: 1e3 * sum(a.elapsed_time(b) for a, b in v) / n for k, v in ev.items()}
+
+
+def asym_timings(n, runs, ops, quant_bytes, name, progress):
+    """The layer with asymmetric per-row activations (quantizer with a float zero point, GEMM
+    with the zero-point correction in the epilogue) against the symmetric one at the same
+    shape: each launch event-timed, the four alternating."""
+    progress("asymmetric activations: %d launches each" % n)
+    us = _alternate(n, runs)
     layer = us["quant_asym"] + us["gemm_asym"]
     return {name: {"quant_us": us["quant_asym"], "gemm_us": us["gemm_asym"],
                    "quant_GB_per_s": quant_bytes / (us["quant_asym"] * 1e-6) / 1e9 + 0.0,
@@ -172,6 +179,21 @@ def asym_timings(n, runs, ops, quant_bytes, name, progress):
                    "symmetric_quant_us": us["quant_symmetric"], "symmetric_gemm_us": us["gemm_symmetric"],
                    "gemm_overhead": us["gemm_asym"] / us["gemm_symmetric"] - 1},
             "note": "quantizer bytes: fp16 X in, int8 codes out, scale and zero point per row"}
+
+
+def fp8_timings(n, runs, ops, quant_bytes, name, progress):
+    """The fp8 (E4M3) layer at the prefill shape (per-row fp8 quantizer, fp8 GEMM with fp32
+    accumulation and the same epilogue) against the int8 layer, launches alternating."""
+    progress("fp8 layer: %d launches each" % n)
+    us = _alternate(n, runs)
+    tf = ops / (us["gemm_e4m3"] * 1e-6) / 1e12
+    return {name: {"quant_us": us["quant_e4m3"], "gemm_us": us["gemm_e4m3"],
+                   "quant_GB_per_s": quant_bytes / (us["quant_e4m3"] * 1e-6) / 1e9,
+                   "gemm_TFLOPS": tf, "frac_fp8_peak": tf / PEAK_FP8_TFLOPS,
+                   "layer_TFLOPS": ops / ((us["quant_e4m3"] + us["gemm_e4m3"]) * 1e-6) / 1e12,
+                   "int8_quant_us": us["quant_int8"], "int8_gemm_us": us["gemm_int8"],
+                   "gemm_time_vs_int8": us["gemm_e4m3"] / us["gemm_int8"]},
+            "note": "2*M*N*K flops per GEMM launch against the dense fp8 MFMA peak (5.0 PFLOP/s)"}
 
 
 def measured_ceilings(dev, byte_counts, progress):
@@ -282,6 +304,8 @@ def main():
     xq3 = torch.empty((w3.M, w3.K), dtype=torch.int8, device=dev)
     xs3 = torch.empty((w3.M,), dtype=torch.float32, device=dev)
     y3 = torch.empty((w3.M, w3.N), dtype=torch.float16, device=dev)
+    if args.act_steps > 0:
+        wq8, ws8 = ql.quantize_weight_per_channel_e4m3(up(i3.w_nk))
     del i3
 
     def rotations(nbytes):
@@ -418,6 +442,16 @@ def main():
                 "gemm_asym": ql.prepare("gemm_w8a8_asym", xq3, xs3, xz3, wq3, ws3, cs3, b3, 0, y3, F16,
                                         w3.M, w3.N, w3.K)},
             ops, ab["quant"] + 4 * w3.M, w3.name, progress)
+    if args.act_steps > 0:
+        xq8 = torch.empty((w3.M, w3.K), dtype=torch.float8_e4m3fn, device=dev)
+        xs8 = torch.empty((w3.M,), dtype=torch.float32, device=dev)
+        out["fp8"] = fp8_timings(
+            args.act_steps, {
+                "quant_int8": quant, "gemm_int8": gemm,
+                "quant_e4m3": ql.prepare("quantize_per_row_e4m3", x3, F16, w3.M, w3.K, xq8, xs8),
+                "gemm_e4m3": ql.prepare("gemm_e4m3_per_channel", xq8, xs8, wq8, ws8, b3, 0, y3, F16,
+                                        w3.M, w3.N, w3.K)},
+            ops, ab["quant"], w3.name, progress)
     if args.ceilings:
         del set2, set4, set5, dec2, dec4, dec5
         ceil = measured_ceilings(dev, {"quant": ab["quant"], "w8a16": ab["w8a16"],

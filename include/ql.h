@@ -176,6 +176,48 @@ ql_status gemm_w8a8_asym(const int8_t* xq, const float* x_scale, const float* x_
                          int64_t M, int64_t N, int64_t K, void* stream);
 
 /*
+ * FP8 (OCP E4M3) variant of the per-row quantizer. [hotelren] "量化算法的本质": the fp8
+ * per-channel quantizer is the int8 one with another result type; [quant67] ch.17 (INT8 /
+ * FP8). E4M3 (bias 7, 3 mantissa bits, largest finite value 448, S.1111.111 NaN, no
+ * infinities) takes the place of [-127, 127]:
+ *   x_scale[m] = max(a[m], 1e-10) / 448   (fp32)
+ *   xq[m,k]    = e4m3(clamp(x[m,k] / x_scale[m], -448, 448))
+ * with x / s correctly rounded in fp32 and e4m3() rounding to nearest, ties to even; a
+ * value that rounds to zero keeps its sign (code 0x80 for a negative one).
+ * x       [M,K] row-major, fp32 (QL_F32) or fp16 (QL_F16)
+ * xq      [M,K] E4M3 codes, one byte each, row-major (out);  x_scale [M] fp32 (out)
+ * Requires K > 0 and K % 16 == 0.
+ */
+ql_status quantize_per_row_e4m3(const void* x, ql_dtype x_dtype, int64_t M, int64_t K,
+                                uint8_t* xq, float* x_scale, void* stream);
+
+/*
+ * Per-output-channel E4M3 weights: quantize_per_row_e4m3's arithmetic per column n.
+ * w       W [K,N] fp32 column-major ([N][K])
+ * wq      W [K,N] E4M3 codes, column-major ([N][K]) (out);  w_scale [N] fp32 (out)
+ * Requires K > 0 and K % 16 == 0.
+ */
+ql_status quantize_weight_per_channel_e4m3(const float* w, int64_t K, int64_t N, uint8_t* wq,
+                                           float* w_scale, void* stream);
+
+/*
+ * The layer with E4M3 operands ([hotelren] "W8A8矩阵乘法" with fp8 codes; [quant67] §四,
+ * scales and bias in the epilogue):
+ *   y[m,n] = act(x_scale[m] * w_scale[n] * sum_k dec(xq[m,k]) * dec(wq[k,n]) + bias[n])
+ * Precision of the sum (gfx950's fp8 matrix cores, as measured): the products are summed
+ * in groups of 8 consecutive k, each product truncated toward zero to a multiple of
+ * 2^(E - 13), E the group's largest exponent sum e_x + e_w; group sums are accumulated in
+ * fp32. So |y - exact| <= x_scale w_scale sum_g 8 * 2^(E_g - 13) plus fp32 rounding of
+ * K/8 + 4 additions -- about 2^-13 relative to the largest products, far below the E4M3
+ * codes' own 2^-4 spacing. Arguments, layouts and requirements as for
+ * gemm_w8a8_per_channel_act, with one-byte E4M3 codes in place of int8 codes. Codes
+ * must not be NaN (0x7F, 0xFF).
+ */
+ql_status gemm_e4m3_per_channel(const uint8_t* xq, const float* x_scale, const uint8_t* wq,
+                                const float* w_scale, const float* bias, ql_activation act, void* y,
+                                ql_dtype y_dtype, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
  * The W8A8 integer accumulators alone, acc[m,n] = sum_k xq[m,k] * wq[k,n] as int32
  * [M,N] row-major. A checking aid for the exact integer stage of
  * gemm_w8a8_per_channel (same main loop); [hotelren] "W8A8矩阵乘法" scheme 1 names

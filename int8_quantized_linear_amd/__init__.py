@@ -21,6 +21,8 @@ __all__ = [
     "quantize_weight_block_asym_u8", "quantize_weight_int4_grouped", "linear_w8a8", "prepare",
     "gemm_w8a8_per_channel_act", "gemm_w4a16_grouped_act", "ACTIVATIONS",
     "quantize_per_row_int8_asym", "weight_column_sums_i8", "gemm_w8a8_asym", "linear_w8a8_asym",
+    "quantize_per_row_e4m3", "quantize_weight_per_channel_e4m3", "gemm_e4m3_per_channel",
+    "linear_e4m3",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -55,6 +57,9 @@ _SIGS = {
     "quantize_per_row_int8_asym": [_P, _I, _I64, _I64, _P, _P, _P, _P],
     "weight_column_sums_i8": [_P, _I64, _I64, _P, _P],
     "gemm_w8a8_asym": [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I64, _I64, _I64, _P],
+    "quantize_per_row_e4m3": [_P, _I, _I64, _I64, _P, _P, _P],
+    "quantize_weight_per_channel_e4m3": [_P, _I64, _I64, _P, _P, _P],
+    "gemm_e4m3_per_channel": [_P, _P, _P, _P, _P, _I, _P, _I, _I64, _I64, _I64, _P],
     "quantize_weight_block_asym_u8": [_P, _I64, _I64, _I64, _P, _P, _P, _P],
     "quantize_weight_int4_grouped": [_P, _I64, _I64, _I64, _P, _P, _P],
 }
@@ -158,6 +163,34 @@ def quantize_weight_per_channel(w_nk: torch.Tensor, wq: Optional[torch.Tensor] =
     w_scale = _out(w_scale, "w_scale", (N,), torch.float32, w_nk.device)
     _call("quantize_weight_per_channel", _ptr(w_nk), K, N, _ptr(wq), _ptr(w_scale), _stream(w_nk))
     return wq, w_scale
+
+
+# E4M3 codes travel as torch.float8_e4m3fn (the OCP format) or as their raw bytes (uint8).
+_FP8 = (torch.float8_e4m3fn, torch.uint8)
+
+
+def quantize_per_row_e4m3(x: torch.Tensor):
+    """Per-row fp8 (E4M3) of x [M, K] (fp16 or fp32): (xq float8_e4m3fn [M, K], x_scale fp32 [M])."""
+    _check(x, "x", (torch.float16, torch.float32))
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, K]")
+    M, K = x.shape
+    xq = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=x.device)
+    xs = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _call("quantize_per_row_e4m3", _ptr(x), QL_F16 if x.dtype == torch.float16 else QL_F32, M, K,
+          _ptr(xq), _ptr(xs), _stream(x))
+    return xq, xs
+
+
+def quantize_weight_per_channel_e4m3(w_nk: torch.Tensor):
+    """Per-output-channel fp8 (E4M3) of W ([N, K] storage, fp32): (wq float8_e4m3fn [N, K],
+    w_scale fp32 [N])."""
+    _check(w_nk, "w", (torch.float32,))
+    N, K = w_nk.shape
+    wq = torch.empty((N, K), dtype=torch.float8_e4m3fn, device=w_nk.device)
+    ws = torch.empty((N,), dtype=torch.float32, device=w_nk.device)
+    _call("quantize_weight_per_channel_e4m3", _ptr(w_nk), K, N, _ptr(wq), _ptr(ws), _stream(w_nk))
+    return wq, ws
 
 
 def quantize_weight_block_asym_u8(w_nk: torch.Tensor, block: int = 64):
@@ -314,6 +347,35 @@ def gemm_w8a8_asym(xq, x_scale, x_zero, wq, w_scale, w_colsum, bias=None, act: s
           _ptr(bias), _act_code(act), _ptr(y), QL_F16 if out_dtype == torch.float16 else QL_F32, M, N, K,
           _stream(xq))
     return y
+
+
+def gemm_e4m3_per_channel(xq, x_scale, wq, w_scale, bias=None, act: str = "none",
+                          out_dtype=torch.float16, y=None):
+    """y = act(x_scale[m] w_scale[n] sum_k xq[m,k] wq[n,k] + bias[n]) with E4M3 codes
+    (float8_e4m3fn or uint8 tensors), fp32 accumulation."""
+    _check(xq, "xq", _FP8)
+    M, K = xq.shape
+    dev = xq.device
+    N = wq.shape[0]
+    _check(wq, "wq", _FP8, (N, K), dev)
+    _check(x_scale, "x_scale", (torch.float32,), (M,), dev)
+    _check(w_scale, "w_scale", (torch.float32,), (N,), dev)
+    if bias is not None:
+        _check(bias, "bias", (torch.float32,), (N,), dev)
+    if out_dtype not in (torch.float16, torch.float32):
+        raise TypeError("out_dtype must be float16 or float32")
+    y = _out(y, "y", (M, N), out_dtype, dev)
+    _call("gemm_e4m3_per_channel", _ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale), _ptr(bias),
+          _act_code(act), _ptr(y), QL_F16 if out_dtype == torch.float16 else QL_F32, M, N, K,
+          _stream(xq))
+    return y
+
+
+def linear_e4m3(x, wq, w_scale, bias=None, act: str = "none", out_dtype=None):
+    """The fp8 layer: per-row E4M3 quantization of x, then the fused GEMM."""
+    xq, xs = quantize_per_row_e4m3(x)
+    od = out_dtype or (torch.float32 if x.dtype == torch.float32 else torch.float16)
+    return gemm_e4m3_per_channel(xq, xs, wq, w_scale, bias, act, od)
 
 
 def linear_w8a8_asym(x, wq, w_scale, w_colsum, bias=None, act: str = "none", out_dtype=None):

@@ -155,6 +155,55 @@ ql_status gemm_w8a8_per_channel_act(const int8_t* xq, const float* x_scale, cons
                                 as_stream(stream));
 }
 
+ql_status quantize_per_row_e4m3(const void* x, ql_dtype x_dtype, int64_t M, int64_t K, uint8_t* xq,
+                               float* x_scale, void* stream) {
+    if (x_dtype != QL_F32 && x_dtype != QL_F16)
+        return QL_ERR_DTYPE;
+    if (bad_dims(M, 1, K) || K % 16 != 0)
+        return QL_ERR_SHAPE;
+    if (M == 0)
+        return QL_OK;
+    if (!x || !xq || !x_scale)
+        return QL_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(x_scale, 4))
+        return QL_ERR_ALIGN;
+    return ql::launch_quant_rows_e4m3(x, x_dtype == QL_F16, M, K, xq, x_scale, as_stream(stream));
+}
+
+ql_status quantize_weight_per_channel_e4m3(const float* w, int64_t K, int64_t N, uint8_t* wq,
+                                           float* w_scale, void* stream) {
+    if (bad_dims(1, N, K) || K % 16 != 0)
+        return QL_ERR_SHAPE;
+    if (N == 0)
+        return QL_OK;
+    if (!w || !wq || !w_scale)
+        return QL_ERR_NULL;
+    if (!aligned(w, 16) || !aligned(wq, 16) || !aligned(w_scale, 4))
+        return QL_ERR_ALIGN;
+    return ql::launch_quant_rows_e4m3(w, 0, N, K, wq, w_scale, as_stream(stream));
+}
+
+ql_status gemm_e4m3_per_channel(const uint8_t* xq, const float* x_scale, const uint8_t* wq,
+                                const float* w_scale, const float* bias, ql_activation act, void* y,
+                                ql_dtype y_dtype, int64_t M, int64_t N, int64_t K, void* stream) {
+    if (y_dtype != QL_F32 && y_dtype != QL_F16)
+        return QL_ERR_DTYPE;
+    if (act != QL_ACT_NONE && act != QL_ACT_GELU && act != QL_ACT_SILU)
+        return QL_ERR_DTYPE;
+    const int8_t* xc = reinterpret_cast<const int8_t*>(xq);
+    const int8_t* wc = reinterpret_cast<const int8_t*>(wq);
+    ql_status st = check_w8a8(xc, wc, y, M, N, K);
+    if (st != QL_OK || M == 0 || N == 0)
+        return st;
+    if (!x_scale || !w_scale)
+        return QL_ERR_NULL;
+    if (!aligned(x_scale, 4) || !aligned(w_scale, 4) || (bias && !aligned(bias, 4)))
+        return QL_ERR_ALIGN;
+    return ql::launch_gemm_w8a8(xc, x_scale, wc, w_scale, bias, y,
+                                y_dtype == QL_F32 ? ql::Y_F32 : ql::Y_F16, (int)act, nullptr, nullptr, M, N, K,
+                                as_stream(stream), true);
+}
+
 ql_status gemm_w8a8_per_channel(const int8_t* xq, const float* x_scale, const int8_t* wq,
                                 const float* w_scale, const float* bias, void* y,
                                 ql_dtype y_dtype, int64_t M, int64_t N, int64_t K, void* stream) {

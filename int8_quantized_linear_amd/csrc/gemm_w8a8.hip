@@ -65,6 +65,52 @@ struct Asym {
     const int32_t* colsum;
 };
 
+// Operand element type: int8 codes (v_mfma_i32_32x32x32_i8, exact int32 sums) or OCP E4M3
+// fp8 codes (v_mfma_f32_32x32x64_f8f6f4, fp32 sums). The bytes move the same way (copies,
+// LDS layout and fragment reads are shared); one fp8 MFMA takes the two 16-byte fragments
+// that two consecutive int8 substeps read, as the k order inside one MFMA is free as long as
+// A and B agree.
+enum { EL_I8 = 0, EL_E4M3 = 1 };
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+template <int ELEM>
+using AccT = typename std::conditional<ELEM == EL_E4M3, f32x16, i32x16>::type;
+
+// The bits of a scalar as another 32-bit type. Taking the value by copy matters: applied
+// to a vector element (acc[i][j][e]) directly, __builtin_bit_cast reads element 0.
+template <typename T, typename S>
+__device__ __forceinline__ T bits_as(S s) {
+    static_assert(sizeof(T) == sizeof(S), "same size");
+    return __builtin_bit_cast(T, s);
+}
+
+__device__ inline i32x8 cat8(i32x4 lo, i32x4 hi) { return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7); }
+
+// The four 32-deep substeps of a 128-deep stage (F[ks][block]) into acc[i][j].
+template <int ELEM, int FM, int FN>
+__device__ __forceinline__ void mfma_stage_of(AccT<ELEM> (&acc)[FM][FN], const i32x4 (&F)[4][FM + FN]) {
+    if constexpr (ELEM == EL_I8) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(F[ks][i], F[ks][FM + j], acc[i][j], 0, 0, 0);
+    } else {
+        // format 0 (E4M3) for A and B, no block scales
+#pragma unroll
+        for (int kp = 0; kp < 2; ++kp)
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        cat8(F[2 * kp][i], F[2 * kp + 1][i]), cat8(F[2 * kp][FM + j], F[2 * kp + 1][FM + j]),
+                        acc[i][j], 0, 0, 0, 0, 0, 0);
+    }
+}
+
 // f(activation, asymmetric) as compile-time constants for the launch's uniform choice: one
 // epilogue instance per pair, so that none costs the others. The int32 output has neither.
 template <int YMODE, typename F>
@@ -117,8 +163,8 @@ __device__ inline void issue_scales(const float* xs, const float* ws, const floa
 // Stores go through a buffer descriptor whose size ends at row M: the hardware drops
 // stores of rows past M, and a column piece past N gets an offset beyond the size, so no
 // store needs a branch.
-template <int WM, int WN, int FM, int FN, int YMODE, int NWV, int ACT, bool ASYM>
-__device__ __forceinline__ void store_tile(const i32x16 (&acc)[FM][FN], bool has_bias,
+template <int WM, int WN, int FM, int FN, int YMODE, int NWV, int ACT, bool ASYM, typename ACC>
+__device__ __forceinline__ void store_tile(const ACC (&acc)[FM][FN], bool has_bias,
                                            void* __restrict__ Y, int M, int N, int mrow0,
                                            int ncol0, int lm0, int ln0, int wave, int lane,
                                            int8_t* smem) {
@@ -290,7 +336,7 @@ __device__ inline int stage_soff(int v) {
 // Each part is refilled only after both of its reads are done (barriers between), and
 // each wave waits for its copies at the end of its next (MFMA) phase, a phase before
 // their first read.
-template <int BM, int BN, int YMODE>
+template <int BM, int BN, int YMODE, int ELEM>
 __device__ __forceinline__ void gemm_tile_pp(const int8_t* __restrict__ A, const float* __restrict__ xs,
                                              const int8_t* __restrict__ B, const float* __restrict__ ws,
                                              const float* __restrict__ bias, void* __restrict__ Y,
@@ -339,7 +385,7 @@ __device__ __forceinline__ void gemm_tile_pp(const int8_t* __restrict__ A, const
                        smem + buf * STAGE + STAGE_A + (h * (BN / 2) + (BN / 8) * q + 8 * c) * BKL);
     };
 
-    i32x16 acc[FM][FN];
+    AccT<ELEM> acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -372,15 +418,7 @@ __device__ __forceinline__ void gemm_tile_pp(const int8_t* __restrict__ A, const
                 F[ks][i] = *reinterpret_cast<const i32x4*>(pa + i * 32 * BKL);
         }
     };
-    auto mfma_stage = [&]() {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(F[ks][i], F[ks][FM + j], acc[i][j], 0, 0, 0);
-    };
+    auto mfma_stage = [&]() { mfma_stage_of<ELEM, FM, FN>(acc, F); };
 
     // Prologue: group 0 copies all of stage 0 and stage 1 but its B high (copied in A_0),
     // and waits for stage 0; stage 1 has until the end of A_0.
@@ -482,7 +520,7 @@ __device__ __forceinline__ void gemm_tile_pp(const int8_t* __restrict__ A, const
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
     with_epilogue<YMODE>(act, asym.x_zero != nullptr, [&](auto act_c, auto asym_c) {
-        store_tile<WM, WN, FM, FN, YMODE, 8, decltype(act_c)::value, decltype(asym_c)::value>(
+        store_tile<WM, WN, FM, FN, YMODE, 8, decltype(act_c)::value, decltype(asym_c)::value, AccT<ELEM>>(
             acc, bias != nullptr, Y, M, N, m0 + wm * WM, n0 + wn * WN, wm * WM, wn * WN, wave, lane, smem);
     });
 }
@@ -495,7 +533,7 @@ __device__ __forceinline__ void gemm_tile_pp(const int8_t* __restrict__ A, const
 // j + 3 spread between them, while the other group reads stage j + 1's fragments from
 // LDS. Three LDS buffers give the copies a phase to land before their stage is read. At the end group 1's int32 sums are added
 // to group 0's through LDS (exact) and group 0 writes the tile.
-template <int YMODE>
+template <int YMODE, int ELEM>
 __device__ __forceinline__ void gemm_tile_ks(const int8_t* __restrict__ A, const float* __restrict__ xs,
                                              const int8_t* __restrict__ B, const float* __restrict__ ws,
                                              const float* __restrict__ bias, void* __restrict__ Y,
@@ -548,7 +586,7 @@ __device__ __forceinline__ void gemm_tile_ks(const int8_t* __restrict__ A, const
             copy_one(kt, c);
     };
 
-    i32x16 acc[FM][FN];
+    AccT<ELEM> acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -580,15 +618,7 @@ __device__ __forceinline__ void gemm_tile_ks(const int8_t* __restrict__ A, const
                 F[ks][i] = *reinterpret_cast<const i32x4*>(pa + i * 32 * BKL);
         }
     };
-    auto mfma_stage = [&]() {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(F[ks][i], F[ks][FM + j], acc[i][j], 0, 0, 0);
-    };
+    auto mfma_stage = [&]() { mfma_stage_of<ELEM, FM, FN>(acc, F); };
     auto phase_end = [&]() {
         __builtin_amdgcn_sched_barrier(0);
         barrier_no_fence();
@@ -689,7 +719,8 @@ __device__ __forceinline__ void gemm_tile_ks(const int8_t* __restrict__ A, const
 #pragma unroll
                 for (int e4 = 0; e4 < 4; ++e4)
                     *reinterpret_cast<i32x4*>(xch + ((i * FN + j) * 4 + e4) * 256 + lane * 4) =
-                        i32x4{acc[i][j][4 * e4], acc[i][j][4 * e4 + 1], acc[i][j][4 * e4 + 2], acc[i][j][4 * e4 + 3]};
+                        i32x4{bits_as<int32_t>(acc[i][j][4 * e4]), bits_as<int32_t>(acc[i][j][4 * e4 + 1]),
+                              bits_as<int32_t>(acc[i][j][4 * e4 + 2]), bits_as<int32_t>(acc[i][j][4 * e4 + 3])};
     }
     phase_end();
     if (grp == 0) {
@@ -705,7 +736,8 @@ __device__ __forceinline__ void gemm_tile_ks(const int8_t* __restrict__ A, const
                     const i32x4 v = *reinterpret_cast<const i32x4*>(xch + ((i * FN + j) * 4 + e4) * 256 + lane * 4);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        int sum = acc[i][j][4 * e4 + r] + v[r];
+                        using E = decltype(acc[i][j][0] + 0);
+                        E sum = acc[i][j][4 * e4 + r] + bits_as<E>(v[r]);
                         asm volatile("" : "+v"(sum));
                         acc[i][j][4 * e4 + r] = sum;
                     }
@@ -716,7 +748,7 @@ __device__ __forceinline__ void gemm_tile_ks(const int8_t* __restrict__ A, const
     __builtin_amdgcn_s_waitcnt(LGKM0);
     if (grp == 0) {
         with_epilogue<YMODE>(act, asym.x_zero != nullptr, [&](auto act_c, auto asym_c) {
-            store_tile<WM, WN, FM, FN, YMODE, 4, decltype(act_c)::value, decltype(asym_c)::value>(
+            store_tile<WM, WN, FM, FN, YMODE, 4, decltype(act_c)::value, decltype(asym_c)::value, AccT<ELEM>>(
                 acc, bias != nullptr, Y, M, N, m0 + wm * WM, n0 + wn * WN, wm * WM, wn * WN, q, lane, smem);
         });
     } else {
@@ -733,7 +765,7 @@ struct TilePlan {
     int tiles_m_big, nbig, tiles_m_small, nsmall, n_small0;
 };
 
-template <int YMODE>
+template <int YMODE, int ELEM>
 __global__ __launch_bounds__(64 * NWAVES, 1) void gemm_w8a8_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ xs, const int8_t* __restrict__ B,
     const float* __restrict__ ws, const float* __restrict__ bias, void* __restrict__ Y, int M,
@@ -743,7 +775,7 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void gemm_w8a8_kernel(
     if (bid < plan.nbig) {
         const int tile = xcd_remap(bid, plan.nbig);
         const int tn = tile / plan.tiles_m_big, tm = tile - tn * plan.tiles_m_big;
-        gemm_tile_pp<256, 256, YMODE>(A, xs, B, ws, bias, Y, M, N, K, tm * 256, tn * 256, act, asym, smem);
+        gemm_tile_pp<256, 256, YMODE, ELEM>(A, xs, B, ws, bias, Y, M, N, K, tm * 256, tn * 256, act, asym, smem);
         if (bid >= plan.nsmall)
             return;
         // The big tile's epilogue has read all it needs from LDS (its stores may still be in
@@ -754,7 +786,7 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void gemm_w8a8_kernel(
     if (bid < plan.nsmall) {
         const int tile = xcd_remap(bid, plan.nsmall);
         const int tn = tile / plan.tiles_m_small, tm = tile - tn * plan.tiles_m_small;
-        gemm_tile_ks<YMODE>(A, xs, B, ws, bias, Y, M, N, K, tm * 128, plan.n_small0 + tn * 256, act, asym, smem);
+        gemm_tile_ks<YMODE, ELEM>(A, xs, B, ws, bias, Y, M, N, K, tm * 128, plan.n_small0 + tn * 256, act, asym, smem);
     }
 }
 
@@ -796,7 +828,7 @@ TilePlan plan_tiles(int64_t M, int64_t N) {
 ql_status launch_gemm_w8a8(const int8_t* xq, const float* x_scale, const int8_t* wq,
                            const float* w_scale, const float* bias, void* y, int y_mode, int act,
                            const float* x_zero, const int32_t* colsum, int64_t M, int64_t N,
-                           int64_t K, hipStream_t stream) {
+                           int64_t K, hipStream_t stream, bool e4m3) {
     if (M == 0 || N == 0)
         return QL_OK;
     const TilePlan plan = plan_tiles(M, N);
@@ -805,18 +837,25 @@ ql_status launch_gemm_w8a8(const int8_t* xq, const float* x_scale, const int8_t*
     // their first copies overlap the big tile's last stores.
     const dim3 grid((unsigned)(plan.nbig > plan.nsmall ? plan.nbig : plan.nsmall)), block(64 * NWAVES);
     const int m = (int)M, n = (int)N, k = (int)K;
-#define QL_LAUNCH(MODE)                                                                          \
-    hipLaunchKernelGGL((gemm_w8a8_kernel<MODE>), grid, block, 0, stream, xq, x_scale, wq, w_scale, \
+#define QL_LAUNCH(MODE, EL)                                                                         \
+    hipLaunchKernelGGL((gemm_w8a8_kernel<MODE, EL>), grid, block, 0, stream, xq, x_scale, wq, w_scale, \
                        bias, y, m, n, k, act, (Asym{x_zero, colsum}), plan)
+    if (e4m3) {
+        if (y_mode == Y_F32)
+            QL_LAUNCH(Y_F32, EL_E4M3);
+        else
+            QL_LAUNCH(Y_F16, EL_E4M3);
+        return launch_status();
+    }
     switch (y_mode) {
     case Y_F32:
-        QL_LAUNCH(Y_F32);
+        QL_LAUNCH(Y_F32, EL_I8);
         break;
     case Y_F16:
-        QL_LAUNCH(Y_F16);
+        QL_LAUNCH(Y_F16, EL_I8);
         break;
     default:
-        QL_LAUNCH(Y_I32);
+        QL_LAUNCH(Y_I32, EL_I8);
         break;
     }
 #undef QL_LAUNCH

@@ -21,6 +21,8 @@ constexpr int WAVE = 64;
 // QL_OK or QL_ERR_DEVICE (from hipGetLastError after the launch).
 ql_status launch_quant_rows_i8(const void* x, int x_is_f16, int64_t rows, int64_t K, int8_t* q,
                                float* scale, hipStream_t stream);
+ql_status launch_quant_rows_e4m3(const void* x, int x_is_f16, int64_t rows, int64_t K, uint8_t* q,
+                                 float* scale, hipStream_t stream);
 ql_status launch_quant_rows_i8_asym(const void* x, int x_is_f16, int64_t rows, int64_t K, int8_t* q,
                                     float* scale, float* zero, hipStream_t stream);
 ql_status launch_column_sums_i8(const int8_t* wq, int64_t K, int64_t N, int32_t* colsum,
@@ -30,10 +32,11 @@ ql_status launch_quant_block_asym_u8(const float* w, int64_t K, int64_t N, int64
 ql_status launch_quant_int4_group(const float* w, int64_t K, int64_t N, int64_t group,
                                   int32_t* packed, void* scales, hipStream_t stream);
 // x_zero (per row) and colsum (W's column code sums) are NULL for symmetric activations.
+// e4m3: xq and wq hold OCP E4M3 fp8 codes (fp32 accumulation; y_mode F32 or F16 only).
 ql_status launch_gemm_w8a8(const int8_t* xq, const float* x_scale, const int8_t* wq,
                            const float* w_scale, const float* bias, void* y, int y_mode, int act,
                            const float* x_zero, const int32_t* colsum, int64_t M, int64_t N,
-                           int64_t K, hipStream_t stream);
+                           int64_t K, hipStream_t stream, bool e4m3 = false);
 ql_status launch_wonly(const void* x, const void* codes, int fmt, const void* scale,
                        const uint8_t* zp, int64_t group, const float* bias, void* y, int64_t M,
                        int64_t N, int64_t K, int act, hipStream_t stream);

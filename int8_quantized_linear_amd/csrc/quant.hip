@@ -115,6 +115,32 @@ struct Chunk {
             hi = fmaxf(hi, v[i]);
         }
     }
+    // fp8 (OCP E4M3) codes: the correctly rounded quotient (as code_u8_biased), kept within
+    // +-448 (it cannot pass it: s = absmax / 448), then v_cvt_pk_fp8_f32, which rounds to
+    // nearest even into E4M3 (gfx950 converts to the OCP format).
+    __device__ inline void store_codes_e4m3(uint8_t* q, float s, float y) const {
+        uint32_t w[E / 4];
+#pragma unroll
+        for (int j = 0; j < E / 4; ++j) {
+            float t[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float x = v[4 * j + i];
+                const float q0 = __fmul_rn(x, y);
+                const float r = fmaf(-q0, s, x);
+                // s > 0, so the quotient has x's sign; the refinement alone would turn
+                // x = -0 into +0 (r = +0 + -0), and fp8 keeps the sign of zero.
+                t[i] = __builtin_amdgcn_fmed3f(copysignf(fmaf(r, y, q0), x), -448.0f, 448.0f);
+            }
+            int b = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
+            b = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], b, true);
+            w[j] = (uint32_t)b;
+        }
+        if constexpr (E == 8)
+            *reinterpret_cast<u32x2*>(q) = u32x2{w[0], w[1]};
+        else
+            *reinterpret_cast<uint32_t*>(q) = w[0];
+    }
     // Asymmetric codes; y = 1 / s correctly rounded, z the row's zero point.
     __device__ inline void store_codes_asym(int8_t* q, float s, float y, float z) const {
         uint32_t w[E / 4];
@@ -151,10 +177,19 @@ struct Chunk {
 
 // One workgroup per row. Rows of up to QT * QMAXC chunks stay in registers (one HBM
 // read); longer rows are read a second time for the codes (the re-read hits L2).
-template <bool F16>
+// E4M3: fp8 codes with s = max(absmax, 1e-10) / 448 (hotelren.com: the fp8 quantizer
+// differs from the int8 one only in the result type; 448 is E4M3's largest value).
+template <bool F16, bool E4M3 = false>
 __global__ __launch_bounds__(QT) void quant_rows_i8_kernel(const void* __restrict__ x, int64_t K,
                                                           int8_t* __restrict__ q,
                                                           float* __restrict__ scale) {
+    constexpr float QMAX = E4M3 ? 448.0f : 127.0f;
+    auto codes = [&](const Chunk<F16>& c, int8_t* dst, float s, float y) {
+        if constexpr (E4M3)
+            c.store_codes_e4m3(reinterpret_cast<uint8_t*>(dst), s, y);
+        else
+            c.store_codes(dst, s, y);
+    };
     using C = Chunk<F16>;
     __shared__ float red[QT / WAVE];
     const int64_t row = blockIdx.x;
@@ -174,7 +209,7 @@ __global__ __launch_bounds__(QT) void quant_rows_i8_kernel(const void* __restric
             }
         }
         amax = block_max(amax, red);
-        const float s = fmaxf(amax, 1e-10f) / 127.0f;
+        const float s = fmaxf(amax, 1e-10f) / QMAX;
         const float y = 1.0f / s;
         if (threadIdx.x == 0)
             scale[row] = s;
@@ -182,7 +217,7 @@ __global__ __launch_bounds__(QT) void quant_rows_i8_kernel(const void* __restric
         for (int i = 0; i < QMAXC; ++i) {
             const int ch = threadIdx.x + i * QT;
             if (ch < nch)
-                c[i].store_codes(qr + (int64_t)ch * C::E, s, y);
+                codes(c[i], qr + (int64_t)ch * C::E, s, y);
         }
     } else {
         for (int ch = threadIdx.x; ch < nch; ch += QT) {
@@ -191,14 +226,14 @@ __global__ __launch_bounds__(QT) void quant_rows_i8_kernel(const void* __restric
             amax = fmaxf(amax, c.absmax());
         }
         amax = block_max(amax, red);
-        const float s = fmaxf(amax, 1e-10f) / 127.0f;
+        const float s = fmaxf(amax, 1e-10f) / QMAX;
         const float y = 1.0f / s;
         if (threadIdx.x == 0)
             scale[row] = s;
         for (int ch = threadIdx.x; ch < nch; ch += QT) {
             C c;
             c.load(xr + (int64_t)ch * 16);
-            c.store_codes(qr + (int64_t)ch * C::E, s, y);
+            codes(c, qr + (int64_t)ch * C::E, s, y);
         }
     }
 }
@@ -387,6 +422,19 @@ ql_status launch_quant_rows_i8(const void* x, int x_is_f16, int64_t rows, int64_
         hipLaunchKernelGGL(quant_rows_i8_kernel<true>, grid, block, 0, stream, x, K, q, scale);
     else
         hipLaunchKernelGGL(quant_rows_i8_kernel<false>, grid, block, 0, stream, x, K, q, scale);
+    return launch_status();
+}
+
+ql_status launch_quant_rows_e4m3(const void* x, int x_is_f16, int64_t rows, int64_t K, uint8_t* q,
+                                 float* scale, hipStream_t stream) {
+    if (rows == 0)
+        return QL_OK;
+    const dim3 grid((unsigned)rows), block(QT);
+    int8_t* qs = reinterpret_cast<int8_t*>(q);
+    if (x_is_f16)
+        hipLaunchKernelGGL((quant_rows_i8_kernel<true, true>), grid, block, 0, stream, x, K, qs, scale);
+    else
+        hipLaunchKernelGGL((quant_rows_i8_kernel<false, true>), grid, block, 0, stream, x, K, qs, scale);
     return launch_status();
 }
 

@@ -42,6 +42,9 @@ def lib():
         "quantize_per_row_int8_asym": [P, I, I64, I64, P, P, P, P],
         "weight_column_sums_i8": [P, I64, I64, P, P],
         "gemm_w8a8_asym": [P, P, P, P, P, P, P, I, P, I, I64, I64, I64, P],
+        "quantize_per_row_e4m3": [P, I, I64, I64, P, P, P],
+        "quantize_weight_per_channel_e4m3": [P, I64, I64, P, P, P],
+        "gemm_e4m3_per_channel": [P, P, P, P, P, I, P, I, I64, I64, I64, P],
         "quantize_weight_block_asym_u8": [P, I64, I64, I64, P, P, P, P],
         "quantize_weight_int4_grouped": [P, I64, I64, I64, P, P, P],
     }
@@ -59,7 +62,8 @@ def test_header_declares_the_entry_points():
               "gemm_w8a16", "gemm_w4a16_grouped", "gemm_w8a8_int32", "ql_status_str",
               "quantize_weight_block_asym_u8", "quantize_weight_int4_grouped",
               "gemm_w8a8_per_channel_act", "gemm_w4a16_grouped_act", "quantize_per_row_int8_asym",
-              "weight_column_sums_i8", "gemm_w8a8_asym"):
+              "weight_column_sums_i8", "gemm_w8a8_asym", "quantize_per_row_e4m3",
+              "quantize_weight_per_channel_e4m3", "gemm_e4m3_per_channel"):
         assert n in names
 
 
@@ -209,6 +213,29 @@ def test_asymmetric_validation(lib):
     assert h(A, A, A, A, A, A, None, 0, A, F16, 8, 8, 96, None) == SHAPE
     assert h(A, A, MIS, A, A, A, None, 0, A, F16, 8, 8, 64, None) == ALIGN
     assert h(A, A, A, A, A, MIS, None, 0, A, F16, 8, 8, 64, None) == ALIGN
+
+
+def test_e4m3_validation(lib):
+    f = lib.quantize_per_row_e4m3
+    assert f(A, F16, 0, 64, None, None, None) == OK
+    assert f(A, 7, 4, 64, A, A, None) == DTYPE
+    assert f(A, F16, 4, 40, A, A, None) == SHAPE
+    assert f(A, F16, 4, 64, None, A, None) == NULL
+    assert f(MIS, F16, 4, 64, A, A, None) == ALIGN
+    g = lib.quantize_weight_per_channel_e4m3
+    assert g(None, 64, 0, None, None, None) == OK
+    assert g(A, 40, 8, A, A, None) == SHAPE
+    assert g(A, 64, 8, A, None, None) == NULL
+    assert g(A, 64, 8, MIS, A, None) == ALIGN
+    h = lib.gemm_e4m3_per_channel
+    assert h(None, None, None, None, None, 0, None, F16, 8, 0, 64, None) == OK
+    assert h(A, None, A, A, None, 0, A, F16, 8, 8, 64, None) == NULL
+    assert h(A, A, A, A, None, 3, A, F16, 8, 8, 64, None) == DTYPE
+    assert h(A, A, A, A, None, 0, A, 5, 8, 8, 64, None) == DTYPE
+    assert h(A, A, A, A, None, 0, A, F16, 8, 8, 96, None) == SHAPE
+    assert h(A, A, A, A, None, 0, A, F16, 8, 8, 131072, None) == SHAPE
+    assert h(A, A, MIS, A, None, 0, A, F16, 8, 8, 64, None) == ALIGN
+    assert h(A, A, A, A, MIS, 0, A, F16, 8, 8, 64, None) == ALIGN
 
 
 def test_producer_validation(lib):
