@@ -196,6 +196,16 @@ def fp8_timings(n, runs, ops, quant_bytes, name, progress):
             "note": "2*M*N*K flops per GEMM launch against the dense fp8 MFMA peak (5.0 PFLOP/s)"}
 
 
+def producer_timings(n, runs, nbytes, progress):
+    """The quantizers that feed the path, each event-timed with launches alternating: the
+    per-tensor quantizer on the prefill activations (four launches per call: clear, absmax,
+    codes, scale) and the offline weight producers at their workloads' shapes. GB/s counts
+    each kernel's algorithmic bytes (inputs read once, outputs written once)."""
+    progress("producers: %d launches each" % n)
+    us = _alternate(n, runs)
+    return {k: {"us": us[k], "GB_per_s": nbytes[k] / (us[k] * 1e-6) / 1e9} for k in runs}
+
+
 def measured_ceilings(dev, byte_counts, progress):
     """Ceilings measured with libqlprobe.so: int8 MFMA TOPS from registers (random and
     constant operands) and the GB/s of one cold streaming read of each byte count."""
@@ -305,7 +315,8 @@ def main():
     xs3 = torch.empty((w3.M,), dtype=torch.float32, device=dev)
     y3 = torch.empty((w3.M, w3.N), dtype=torch.float16, device=dev)
     if args.act_steps > 0:
-        wq8, ws8 = ql.quantize_weight_per_channel_e4m3(up(i3.w_nk))
+        w3f = up(i3.w_nk)
+        wq8, ws8 = ql.quantize_weight_per_channel_e4m3(w3f)
     del i3
 
     def rotations(nbytes):
@@ -452,6 +463,34 @@ def main():
                 "gemm_e4m3": ql.prepare("gemm_e4m3_per_channel", xq8, xs8, wq8, ws8, b3, 0, y3, F16,
                                         w3.M, w3.N, w3.K)},
             ops, ab["quant"], w3.name, progress)
+    if args.act_steps > 0:
+        w4f = up(wl.draw(w4, x_rows=slice(0, 1)).w_nk)
+        w5f = up(wl.draw(w5, x_rows=slice(0, 1)).w_nk)
+        xqt = torch.empty((w3.M, w3.K), dtype=torch.int8, device=dev)
+        xst = torch.empty((1,), dtype=torch.float32, device=dev)
+        pq3 = torch.empty_like(wq3)
+        ps3 = torch.empty_like(ws3)
+        pq8 = torch.empty_like(wq8)
+        pq4 = torch.empty((w4.N, w4.K), dtype=torch.uint8, device=dev)
+        ps4 = torch.empty((w4.N, w4.K // 64), dtype=torch.float32, device=dev)
+        pz4 = torch.empty((w4.N, w4.K // 64), dtype=torch.uint8, device=dev)
+        pp5 = torch.empty((w5.N, w5.K // 8), dtype=torch.int32, device=dev)
+        ps5 = torch.empty((w5.N, w5.K // 128), dtype=torch.float16, device=dev)
+        mk3, n3, n4, n5 = w3.M * w3.K, w3.N * w3.K, w4.N * w4.K, w5.N * w5.K
+        out["producers"] = producer_timings(args.act_steps, {
+            "per_tensor_int8_x_" + w3.name: ql.prepare("quantize_per_tensor_int8", x3, F16, mk3, xqt, xst),
+            "per_channel_int8_w_" + w3.name: ql.prepare("quantize_weight_per_channel", w3f, w3.K, w3.N, pq3, ps3),
+            "per_channel_e4m3_w_" + w3.name: ql.prepare("quantize_weight_per_channel_e4m3", w3f, w3.K, w3.N, pq8, ps3),
+            "block64_asym_u8_w_" + w4.name: ql.prepare("quantize_weight_block_asym_u8", w4f, w4.K, w4.N, 64, pq4, ps4, pz4),
+            "int4_g128_w_" + w5.name: ql.prepare("quantize_weight_int4_grouped", w5f, w5.K, w5.N, 128, pp5, ps5),
+        }, {
+            "per_tensor_int8_x_" + w3.name: 3 * mk3 + 4,
+            "per_channel_int8_w_" + w3.name: 5 * n3 + 4 * w3.N,
+            "per_channel_e4m3_w_" + w3.name: 5 * n3 + 4 * w3.N,
+            "block64_asym_u8_w_" + w4.name: 5 * n4 + 5 * (n4 // 64),
+            "int4_g128_w_" + w5.name: 4 * n5 + n5 // 2 + 2 * (n5 // 128),
+        }, progress)
+        del w3f, w4f, w5f
     if args.ceilings:
         del set2, set4, set5, dec2, dec4, dec5
         ceil = measured_ceilings(dev, {"quant": ab["quant"], "w8a16": ab["w8a16"],

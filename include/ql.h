@@ -97,6 +97,22 @@ ql_status quantize_per_row_int8(const void* x, ql_dtype x_dtype, int64_t M, int6
                                 int8_t* xq, float* x_scale, void* stream);
 
 /*
+ * Per-tensor symmetric int8 quantization: one scale for the whole array. [hotelren]
+ * "量化算法的本质", per_tensor_quant_int8 (global absmax, scale = absmax/127, a scale tensor
+ * of one fp32 element); "量化模型的矩阵乘法" (a scale of shape [1] means per-tensor).
+ *
+ *   a = max_i |x[i]|,  x_scale[0] = max(a, 1e-10) / 127            (fp32)
+ *   xq[i] = clamp(round_half_even(x[i] / x_scale[0]), -127, 127)
+ *
+ * x       n elements, fp32 (QL_F32) or fp16 (QL_F16), contiguous (any shape, flattened)
+ * xq      n int8 codes (out);  x_scale one fp32 (out)
+ * x_scale also serves as the running maximum while the call's kernels run: it holds its
+ * final value once the stream has passed the call. Requires n % 16 == 0.
+ */
+ql_status quantize_per_tensor_int8(const void* x, ql_dtype x_dtype, int64_t n, int8_t* xq,
+                                   float* x_scale, void* stream);
+
+/*
  * Per-output-channel symmetric int8 quantization of weights (offline, before serving).
  * [2048ai] §4.2 and §6.1 (one scale per output channel n); [hotelren]
  * per_channel_quant_int8. Same arithmetic as quantize_per_row_int8, per column n.

@@ -22,7 +22,7 @@ __all__ = [
     "gemm_w8a8_per_channel_act", "gemm_w4a16_grouped_act", "ACTIVATIONS",
     "quantize_per_row_int8_asym", "weight_column_sums_i8", "gemm_w8a8_asym", "linear_w8a8_asym",
     "quantize_per_row_e4m3", "quantize_weight_per_channel_e4m3", "gemm_e4m3_per_channel",
-    "linear_e4m3",
+    "linear_e4m3", "quantize_per_tensor_int8",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -58,6 +58,7 @@ _SIGS = {
     "weight_column_sums_i8": [_P, _I64, _I64, _P, _P],
     "gemm_w8a8_asym": [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I64, _I64, _I64, _P],
     "quantize_per_row_e4m3": [_P, _I, _I64, _I64, _P, _P, _P],
+    "quantize_per_tensor_int8": [_P, _I, _I64, _P, _P, _P],
     "quantize_weight_per_channel_e4m3": [_P, _I64, _I64, _P, _P, _P],
     "gemm_e4m3_per_channel": [_P, _P, _P, _P, _P, _I, _P, _I, _I64, _I64, _I64, _P],
     "quantize_weight_block_asym_u8": [_P, _I64, _I64, _I64, _P, _P, _P, _P],
@@ -127,6 +128,17 @@ def quantize_per_row_int8(x: torch.Tensor, xq: Optional[torch.Tensor] = None,
     _call("quantize_per_row_int8", _ptr(x), QL_F16 if x.dtype == torch.float16 else QL_F32, M, K,
           _ptr(xq), _ptr(x_scale), _stream(x))
     return xq, x_scale
+
+
+def quantize_per_tensor_int8(x: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Per-tensor symmetric int8 of x (fp16 or fp32, any shape, contiguous): (xq int8 of x's
+    shape, x_scale fp32 [1])."""
+    _check(x, "x", (torch.float16, torch.float32))
+    xq = torch.empty(x.shape, dtype=torch.int8, device=x.device)
+    xs = torch.empty((1,), dtype=torch.float32, device=x.device)
+    _call("quantize_per_tensor_int8", _ptr(x), QL_F16 if x.dtype == torch.float16 else QL_F32,
+          x.numel(), _ptr(xq), _ptr(xs), _stream(x))
+    return xq, xs
 
 
 def quantize_per_row_int8_asym(x: torch.Tensor):

@@ -58,6 +58,21 @@ ql_status quantize_per_row_int8(const void* x, ql_dtype x_dtype, int64_t M, int6
     return ql::launch_quant_rows_i8(x, x_dtype == QL_F16, M, K, xq, x_scale, as_stream(stream));
 }
 
+ql_status quantize_per_tensor_int8(const void* x, ql_dtype x_dtype, int64_t n, int8_t* xq,
+                                  float* x_scale, void* stream) {
+    if (x_dtype != QL_F32 && x_dtype != QL_F16)
+        return QL_ERR_DTYPE;
+    if (n < 0 || n >= kMaxDim * 64 || n % 16 != 0)
+        return QL_ERR_SHAPE;
+    if (n == 0)
+        return QL_OK;
+    if (!x || !xq || !x_scale)
+        return QL_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(x_scale, 4))
+        return QL_ERR_ALIGN;
+    return ql::launch_quant_tensor_i8(x, x_dtype == QL_F16, n, xq, x_scale, as_stream(stream));
+}
+
 ql_status quantize_weight_per_channel(const float* w, int64_t K, int64_t N, int8_t* wq,
                                       float* w_scale, void* stream) {
     if (bad_dims(1, N, K) || K % 16 != 0)

@@ -21,6 +21,8 @@ constexpr int WAVE = 64;
 // QL_OK or QL_ERR_DEVICE (from hipGetLastError after the launch).
 ql_status launch_quant_rows_i8(const void* x, int x_is_f16, int64_t rows, int64_t K, int8_t* q,
                                float* scale, hipStream_t stream);
+ql_status launch_quant_tensor_i8(const void* x, int x_is_f16, int64_t n, int8_t* q, float* scale,
+                                 hipStream_t stream);
 ql_status launch_quant_rows_e4m3(const void* x, int x_is_f16, int64_t rows, int64_t K, uint8_t* q,
                                  float* scale, hipStream_t stream);
 ql_status launch_quant_rows_i8_asym(const void* x, int x_is_f16, int64_t rows, int64_t K, int8_t* q,

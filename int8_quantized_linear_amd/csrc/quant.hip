@@ -238,6 +238,70 @@ __global__ __launch_bounds__(QT) void quant_rows_i8_kernel(const void* __restric
     }
 }
 
+// Per-tensor symmetric int8 (hotelren.com "量化算法的本质", per_tensor_quant_int8: one scale
+// for the whole array, s = max(absmax, 1e-10) / 127, codes as the per-row quantizer's). The
+// caller's one-float scale output is the only accumulator, so four small launches run in
+// order on the stream: zero it; fold every workgroup's absmax into it with one atomic max
+// on the float's bits (non-negative floats order like their bit patterns); write the codes,
+// each workgroup deriving s from the absmax; replace the absmax by s.
+constexpr int TCH = 4;   // 16-byte chunks per thread per step of the grid-stride loops
+
+__global__ __launch_bounds__(64) void tensor_slot_zero_kernel(float* __restrict__ slot) {
+    if (threadIdx.x == 0)
+        *slot = 0.0f;
+}
+
+template <bool F16>
+__global__ __launch_bounds__(QT) void tensor_absmax_kernel(const void* __restrict__ x, int64_t nch,
+                                                           float* __restrict__ slot) {
+    using C = Chunk<F16>;
+    __shared__ float red[QT / WAVE];
+    const char* xb = reinterpret_cast<const char*>(x);
+    const int64_t stride = (int64_t)gridDim.x * QT * TCH;
+    float amax = 0.0f;
+    for (int64_t base = (int64_t)blockIdx.x * QT * TCH + threadIdx.x; base < nch; base += stride) {
+        C c[TCH];
+#pragma unroll
+        for (int i = 0; i < TCH; ++i)
+            if (base + i * QT < nch)
+                c[i].load(xb + (base + i * QT) * 16);
+#pragma unroll
+        for (int i = 0; i < TCH; ++i)
+            if (base + i * QT < nch)
+                amax = fmaxf(amax, c[i].absmax());
+    }
+    amax = block_max(amax, red);
+    if (threadIdx.x == 0)
+        atomicMax(reinterpret_cast<unsigned int*>(slot), __float_as_uint(amax));
+}
+
+template <bool F16>
+__global__ __launch_bounds__(QT) void tensor_codes_kernel(const void* __restrict__ x, int64_t nch,
+                                                          const float* __restrict__ slot,
+                                                          int8_t* __restrict__ q) {
+    using C = Chunk<F16>;
+    const char* xb = reinterpret_cast<const char*>(x);
+    const float s = fmaxf(*slot, 1e-10f) / 127.0f;
+    const float y = 1.0f / s;
+    const int64_t stride = (int64_t)gridDim.x * QT * TCH;
+    for (int64_t base = (int64_t)blockIdx.x * QT * TCH + threadIdx.x; base < nch; base += stride) {
+        C c[TCH];
+#pragma unroll
+        for (int i = 0; i < TCH; ++i)
+            if (base + i * QT < nch)
+                c[i].load(xb + (base + i * QT) * 16);
+#pragma unroll
+        for (int i = 0; i < TCH; ++i)
+            if (base + i * QT < nch)
+                c[i].store_codes(q + (base + i * QT) * C::E, s, y);
+    }
+}
+
+__global__ __launch_bounds__(64) void tensor_slot_scale_kernel(float* __restrict__ slot) {
+    if (threadIdx.x == 0)
+        *slot = fmaxf(*slot, 1e-10f) / 127.0f;
+}
+
 // Asymmetric per-row int8 (hotelren.com "量化算法的本质", per_channel_quant_int8, the
 // asymmetric branch), per row with lo, hi its minimum and maximum:
 //   s = max((hi - lo) / 255, 1e-8);  z = -lo / s - 128 (a float);
@@ -422,6 +486,25 @@ ql_status launch_quant_rows_i8(const void* x, int x_is_f16, int64_t rows, int64_
         hipLaunchKernelGGL(quant_rows_i8_kernel<true>, grid, block, 0, stream, x, K, q, scale);
     else
         hipLaunchKernelGGL(quant_rows_i8_kernel<false>, grid, block, 0, stream, x, K, q, scale);
+    return launch_status();
+}
+
+ql_status launch_quant_tensor_i8(const void* x, int x_is_f16, int64_t n, int8_t* q, float* scale,
+                                 hipStream_t stream) {
+    if (n == 0)
+        return QL_OK;
+    const int64_t nch = n / (x_is_f16 ? 8 : 4);
+    const int64_t want = (nch + (int64_t)QT * TCH - 1) / ((int64_t)QT * TCH);
+    const dim3 grid((unsigned)(want < 2048 ? want : 2048)), block(QT), one(1), w64(64);
+    hipLaunchKernelGGL(tensor_slot_zero_kernel, one, w64, 0, stream, scale);
+    if (x_is_f16) {
+        hipLaunchKernelGGL(tensor_absmax_kernel<true>, grid, block, 0, stream, x, nch, scale);
+        hipLaunchKernelGGL(tensor_codes_kernel<true>, grid, block, 0, stream, x, nch, scale, q);
+    } else {
+        hipLaunchKernelGGL(tensor_absmax_kernel<false>, grid, block, 0, stream, x, nch, scale);
+        hipLaunchKernelGGL(tensor_codes_kernel<false>, grid, block, 0, stream, x, nch, scale, q);
+    }
+    hipLaunchKernelGGL(tensor_slot_scale_kernel, one, w64, 0, stream, scale);
     return launch_status();
 }
 

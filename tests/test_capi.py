@@ -43,6 +43,7 @@ def lib():
         "weight_column_sums_i8": [P, I64, I64, P, P],
         "gemm_w8a8_asym": [P, P, P, P, P, P, P, I, P, I, I64, I64, I64, P],
         "quantize_per_row_e4m3": [P, I, I64, I64, P, P, P],
+        "quantize_per_tensor_int8": [P, I, I64, P, P, P],
         "quantize_weight_per_channel_e4m3": [P, I64, I64, P, P, P],
         "gemm_e4m3_per_channel": [P, P, P, P, P, I, P, I, I64, I64, I64, P],
         "quantize_weight_block_asym_u8": [P, I64, I64, I64, P, P, P, P],
@@ -63,7 +64,8 @@ def test_header_declares_the_entry_points():
               "quantize_weight_block_asym_u8", "quantize_weight_int4_grouped",
               "gemm_w8a8_per_channel_act", "gemm_w4a16_grouped_act", "quantize_per_row_int8_asym",
               "weight_column_sums_i8", "gemm_w8a8_asym", "quantize_per_row_e4m3",
-              "quantize_weight_per_channel_e4m3", "gemm_e4m3_per_channel"):
+              "quantize_weight_per_channel_e4m3", "gemm_e4m3_per_channel",
+              "quantize_per_tensor_int8"):
         assert n in names
 
 
@@ -236,6 +238,16 @@ def test_e4m3_validation(lib):
     assert h(A, A, A, A, None, 0, A, F16, 8, 8, 131072, None) == SHAPE
     assert h(A, A, MIS, A, None, 0, A, F16, 8, 8, 64, None) == ALIGN
     assert h(A, A, A, A, MIS, 0, A, F16, 8, 8, 64, None) == ALIGN
+
+
+def test_per_tensor_validation(lib):
+    f = lib.quantize_per_tensor_int8
+    assert f(None, F16, 0, None, None, None) == OK
+    assert f(A, 7, 64, A, A, None) == DTYPE
+    assert f(A, F16, 40, A, A, None) == SHAPE
+    assert f(A, F16, -16, A, A, None) == SHAPE
+    assert f(A, F16, 64, A, None, None) == NULL
+    assert f(A, F16, 64, MIS, A, None) == ALIGN
 
 
 def test_producer_validation(lib):

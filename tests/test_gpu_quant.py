@@ -160,3 +160,54 @@ def test_column_sums(ql):
         assert np.array_equal(host(ql.weight_column_sums_i8(dev(wq))), oracle.column_sums_i8(wq))
     wq = np.full((3, 131008), -128, np.int8)
     assert np.all(host(ql.weight_column_sums_i8(dev(wq))) == -128 * 131008)
+
+
+def _check_tensor(ql, x: np.ndarray, xq_out=None, xs_out=None):
+    q_ref, s_ref = oracle.quant_tensor_i8(x)
+    xq, xs = ql.quantize_per_tensor_int8(dev(x))
+    assert np.array_equal(host(xs).view(np.uint32), np.array([s_ref], np.float32).view(np.uint32))
+    assert np.array_equal(host(xq), q_ref)
+
+
+@pytest.mark.parametrize("shape,dtype", [((16,), np.float32), ((3, 16), np.float16), ((16, 256), np.float32),
+                                         ((1, 4112), np.float32), ((77, 48), np.float16),
+                                         ((2048, 4096), np.float16), ((1000, 2064), np.float16)])
+def test_per_tensor(ql, shape, dtype):
+    """One scale for the whole array, bit for bit: sizes below one workgroup's step, ragged
+    sizes, the prefill activations (more chunks than the grid covers in one step, so the
+    grid-stride loops run several times) and fp16 and fp32 inputs."""
+    rng = np.random.default_rng(int(np.prod(shape)) + 3)
+    x = (rng.standard_normal(shape) * np.exp2(rng.integers(-5, 5))).astype(dtype)
+    _check_tensor(ql, x)
+
+
+def test_per_tensor_weights_full(ql):
+    """The prefill weight [11008, 4096] fp32 with a single scale (the per-tensor baseline of
+    the weight quantizer)."""
+    _check_tensor(ql, workloads.draw(workloads.W8A8_PREFILL, x_rows=slice(0, 1)).w_nk)
+
+
+def test_per_tensor_special(ql):
+    """The maximum in the very last chunk; a negative maximum; an all-zero tensor (scale
+    floor); -0; and a reused scale buffer that held a larger value before (it is cleared
+    by the call, not folded into the new maximum)."""
+    n = 2048 * 4096 + 16
+    x = np.full(n, 0.25, np.float32)
+    x[-1] = 3.0
+    _check_tensor(ql, x)
+    x[-1] = -5.0
+    _check_tensor(ql, x)
+    _check_tensor(ql, np.zeros(64, np.float32))
+    z = np.full(32, -0.0, np.float16)
+    z[7] = 1.0
+    _check_tensor(ql, z)
+    big = dev(np.full(64, 1000.0, np.float32))
+    small = np.random.default_rng(9).standard_normal(4096).astype(np.float32)
+    xq = torch.empty(4096, dtype=torch.int8, device=DEV)
+    xs = torch.empty(1, dtype=torch.float32, device=DEV)
+    xq64 = torch.empty(64, dtype=torch.int8, device=DEV)
+    ql._call("quantize_per_tensor_int8", ql._ptr(big), 0, 64, ql._ptr(xq64), ql._ptr(xs), ql._stream(big))
+    xd = dev(small)
+    ql._call("quantize_per_tensor_int8", ql._ptr(xd), 0, 4096, ql._ptr(xq), ql._ptr(xs), ql._stream(xd))
+    q_ref, s_ref = oracle.quant_tensor_i8(small)
+    assert host(xs)[0] == np.float32(s_ref) and np.array_equal(host(xq), q_ref)
