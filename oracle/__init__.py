@@ -63,6 +63,8 @@ def _declare(L):
     L.oracle_num_threads.restype = ctypes.c_int
     L.oracle_activation_f64.argtypes = [_P, _I64, ctypes.c_int]
     L.oracle_quant_rows_i8_asym.argtypes = [_P, _I64, _I64, _P, _P, _P]
+    L.oracle_channel_scales.argtypes = [_P, _I64, _I64, _P]
+    L.oracle_requant_i8.argtypes = [_P, _I64, _I64, _P, _I64, _P]
     L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
     L.oracle_e4m3_decode.restype = ctypes.c_double
     L.oracle_e4m3_encode.argtypes = [ctypes.c_float]
@@ -212,6 +214,26 @@ class Oracle:
         self.L.oracle_w8a8_asym_f64(_ptr(xq), _ptr(xs), _ptr(xz), _ptr(wq), _ptr(ws), _ptr(b), M, N, K,
                                     _ptr(y64))
         return y64
+
+    def channel_scales(self, y) -> np.ndarray:
+        """fp32 [N]: calibrated static scales max(max_m |y[m, n]|, 1e-10) / 127 of y [M, N]."""
+        yf = _c(y, np.float32)
+        M, N = yf.shape
+        s = np.empty(N, np.float32)
+        self.L.oracle_channel_scales(_ptr(yf), M, N, _ptr(s))
+        return s
+
+    def requant_i8(self, y, scale) -> np.ndarray:
+        """int8 [M, N]: clamp(rne(y / scale[n]), -127, 127) of fp32 y [M, N]; scale has N
+        entries (per channel) or one (per tensor)."""
+        yf = _c(y, np.float32)
+        M, N = yf.shape
+        sc = _c(np.atleast_1d(scale), np.float32)
+        if sc.size not in (1, N):
+            raise ValueError("scale must have 1 or N entries")
+        q = np.empty((M, N), np.int8)
+        self.L.oracle_requant_i8(_ptr(yf), M, N, _ptr(sc), sc.size, _ptr(q))
+        return q
 
     def e4m3_decode(self, codes) -> np.ndarray:
         """fp64 values of OCP e4m3 codes (NaN for S.1111.111)."""

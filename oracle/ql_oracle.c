@@ -346,6 +346,46 @@ void oracle_epilogue_w8a8(const int32_t* acc, const float* x_scale, const float*
     }
 }
 
+/* ------------------------------------------------ re-quantization of Y */
+
+/* Calibrated static scales of a layer's output, one per output channel (2048ai.net, INT8
+ * Llama-2-7B write-up, §3.2-§3.3: the maximum |output| of each channel over the
+ * calibration rows, scale = max / 127), with the absmax floor of the other quantizers:
+ *   s[n] = max(max_m |y[m][n]|, 1e-10) / 127      (fp32), y row-major [M][N] */
+void oracle_channel_scales(const float* y, int64_t M, int64_t N, float* s)
+{
+    for (int64_t n = 0; n < N; ++n) {
+        float a = 0.0f;
+        for (int64_t m = 0; m < M; ++m) {
+            const float t = fabsf(y[m * N + n]);
+            if (t > a)
+                a = t;
+        }
+        s[n] = (a > 1e-10f ? a : 1e-10f) / 127.0f;
+    }
+}
+
+/* Int8 codes of the layer's output with static scales, for a following int8 layer:
+ *   q[m][n] = clamp(rne(y[m][n] / s[n]), -127, 127)       (fp32 division)
+ * with one scale per output channel (scale_n == N; 2048ai.net §3.2-§3.3) or one for the
+ * whole output (scale_n == 1; hotelren.com "量化算法的本质", per_tensor_quant_int8). The code
+ * rule is the symmetric quantizers' (quant67.com ch.17 §二). */
+void oracle_requant_i8(const float* y, int64_t M, int64_t N, const float* s, int64_t scale_n,
+                       int8_t* q)
+{
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            const float sc = s[scale_n == 1 ? 0 : n];
+            float r = nearbyintf(y[m * N + n] / sc);
+            if (r > 127.0f)
+                r = 127.0f;
+            if (r < -127.0f)
+                r = -127.0f;
+            q[m * N + n] = (int8_t)r;
+        }
+    }
+}
+
 /* ------------------------------------------------------ weight-only paths */
 
 /* y64[m][n] = sum_k x[m][k] * (q[k][n] - z) * s, in fp64.

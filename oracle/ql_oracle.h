@@ -45,4 +45,7 @@ void oracle_w8a8_asym_f64(const int8_t* xq, const float* x_scale, const float* x
                           int64_t N, int64_t K, double* y64);
 int oracle_num_threads(void);
 
+void oracle_channel_scales(const float* y, int64_t M, int64_t N, float* s);
+void oracle_requant_i8(const float* y, int64_t M, int64_t N, const float* s, int64_t scale_n,
+                       int8_t* q);
 #endif

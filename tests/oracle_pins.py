@@ -198,6 +198,20 @@ def pin_int4_golden_ties(orc):
         assert q.tolist() == [int(v) for v in q_txt.split()], (q, q_txt)
 
 
+def pin_per_tensor_is_one_row(orc):
+    """Per-tensor quantization of a [R, C] array is per-row quantization of its flattening
+    into one row of R*C (hotelren.com: one global absmax and one scale); the global argmax
+    maps to +-127 and a row far below the maximum keeps small codes."""
+    rng = np.random.default_rng(81)
+    x = (rng.standard_normal((6, 40)) * np.exp2(rng.integers(-6, 6, (6, 1)))).astype(np.float32)
+    qt, st = orc.quant_tensor_i8(x)
+    qr, sr = orc.quant_rows_i8(x.reshape(1, -1))
+    assert np.array_equal(qt.reshape(1, -1), qr) and np.float32(st) == sr[0]
+    i = np.unravel_index(np.argmax(np.abs(x)), x.shape)
+    assert abs(int(qt[i])) == 127
+    assert np.float32(st) == np.float32(np.float32(np.abs(x).max()) / np.float32(127.0))
+
+
 def pin_per_channel_beats_per_tensor(orc):
     """On weights whose column ranges vary (log-uniform sigma in [0.005, 0.5], the small
     W8A8 workload's law), per-output-channel scales give a weight MSE at least 5x below
@@ -590,6 +604,58 @@ def pin_activation_invariants(orc):
         assert abs(big[0] - 40.0) < 1e-12 and abs(big[1]) < 1e-12
         pos = orc.activation_f64(np.linspace(0, 10, 1001), act)
         assert np.all(np.diff(pos) > 0)
+
+
+# ------------------------------------------------------- re-quantization of Y
+
+def pin_requant_golden_ties(orc):
+    """Hand-derived codes for exact quotients on ties, the clamp and scales that are not
+    powers of two (tests/golden/requant_ties.txt), with one scale for the whole output and
+    the same scale repeated per channel."""
+    for s_txt, y_txt, q_txt in _rows("requant_ties.txt"):
+        y = np.array([float(v) for v in y_txt.split()], np.float32)[None, :]
+        q_ref = np.array([int(v) for v in q_txt.split()], np.int8)
+        assert np.array_equal(orc.requant_i8(y, np.float32(s_txt))[0], q_ref), s_txt
+        per_channel = np.full(y.shape[1], np.float32(s_txt), np.float32)
+        assert np.array_equal(orc.requant_i8(y, per_channel)[0], q_ref), s_txt
+
+
+def pin_requant_exact_rational(orc):
+    """q = clamp(rne(round_f32(y / s[n])), -127, 127) in exact rational arithmetic, with a
+    different scale per output channel (so a scale taken from the wrong axis fails) and
+    values spanning the clamp."""
+    rng = np.random.default_rng(91)
+    M, N = 7, 33
+    s = (np.exp2(rng.uniform(-12, 4, N)) * rng.uniform(1, 2, N)).astype(np.float32)
+    y = (rng.standard_normal((M, N)) * s[None, :] * np.float32(60.0)).astype(np.float32)
+    q = orc.requant_i8(y, s)
+    for m in range(M):
+        for n in range(N):
+            t = rne_int(round_to_f32(Fraction(float(y[m, n])) / Fraction(float(s[n]))))
+            assert int(q[m, n]) == max(-127, min(127, t)), (m, n)
+    assert (np.abs(q) == 127).any() and (np.abs(q) < 127).any()
+
+
+def pin_channel_scales(orc):
+    """Calibrated scales: s[n] = round_f32(max(max_m |y[m, n]|, 1e-10) / 127) exactly, per
+    column (not per row); an all-zero channel gets the floor; requantized with its own
+    scales, each channel's largest |y| maps to +-127 and every code is within half a step."""
+    rng = np.random.default_rng(92)
+    M, N = 9, 12
+    y = (rng.standard_normal((M, N)) * np.exp2(rng.integers(-8, 8, (1, N)))).astype(np.float32)
+    y[:, 4] = 0.0
+    s = orc.channel_scales(y)
+    for n in range(N):
+        a = max(abs(float(v)) for v in y[:, n])
+        assert float(s[n]) == round_to_f32(Fraction(max(a, F32_1EM10)) / 127), n
+    q = orc.requant_i8(y, s)
+    for n in range(N):
+        if n != 4:
+            m = int(np.argmax(np.abs(y[:, n])))
+            assert abs(int(q[m, n])) == 127, n
+    assert np.all(q[:, 4] == 0)
+    err = np.abs(q.astype(np.float64) * s[None, :] - y.astype(np.float64))
+    assert np.all(err <= s[None, :].astype(np.float64) * (0.5 + SLOP))
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

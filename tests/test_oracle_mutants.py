@@ -61,6 +61,13 @@ MUTANTS = [
     ("e4m3_scale_127", "const float s = (a > 1e-10f ? a : 1e-10f) / 448.0f;",
      "const float s = (a > 1e-10f ? a : 1e-10f) / 127.0f;"),
     ("e4m3_gemm_abs_sum", "acc += p;", "acc += fabs(p);"),
+    ("requant_half_away", "float r = nearbyintf(y[m * N + n] / sc);", "float r = roundf(y[m * N + n] / sc);"),
+    ("requant_reciprocal", "float r = nearbyintf(y[m * N + n] / sc);", "float r = nearbyintf(y[m * N + n] * (1.0f / sc));"),
+    ("requant_scale_by_row", "const float sc = s[scale_n == 1 ? 0 : n];", "const float sc = s[scale_n == 1 ? 0 : m % N];"),
+    ("requant_clamp_128", "            if (r < -127.0f)\n                r = -127.0f;\n            q[m * N + n]",
+     "            if (r < -128.0f)\n                r = -128.0f;\n            q[m * N + n]"),
+    ("channel_scales_row_axis", "const float t = fabsf(y[m * N + n]);", "const float t = fabsf(y[(n * M + m) % (M * N)]);"),
+    ("channel_scales_no_floor", "s[n] = (a > 1e-10f ? a : 1e-10f) / 127.0f;", "s[n] = a / 127.0f;"),
     ("act_codes_swapped", "if (act == 1)\n            y[i] = v * (0.5", "if (act == 2)\n            y[i] = v * (0.5"),
 ]
 
