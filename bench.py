@@ -196,6 +196,20 @@ def fp8_timings(n, runs, ops, quant_bytes, name, progress):
             "note": "2*M*N*K flops per GEMM launch against the dense fp8 MFMA peak (5.0 PFLOP/s)"}
 
 
+def requant_timings(n, runs, ops, name, progress):
+    """The W8A8 GEMM with its output re-quantized to int8 in the epilogue (static scales)
+    against the plain fp16-output GEMM, and against the unfused pair that a per-row dynamic
+    re-quantization needs (fp16 GEMM, then the per-row quantizer over Y); alternating."""
+    progress("int8 output: %d launches each" % n)
+    us = _alternate(n, runs)
+    return {name: {"requant_gemm_us": us["gemm_requant"], "plain_fp16_gemm_us": us["gemm_fp16"],
+                   "requant_TOPS": ops / (us["gemm_requant"] * 1e-6) / 1e12,
+                   "requant_vs_plain": us["gemm_requant"] / us["gemm_fp16"],
+                   "unfused_gemm_plus_row_quant_us": us["gemm_fp16"] + us["quant_y_rows"],
+                   "row_quant_of_y_us": us["quant_y_rows"]},
+            "note": "int8 Y halves the output bytes (45 MB of fp16 to 22.5 MB)"}
+
+
 def producer_timings(n, runs, nbytes, progress):
     """The quantizers that feed the path, each event-timed with launches alternating: the
     per-tensor quantizer on the prefill activations (four launches per call: clear, absmax,
@@ -464,6 +478,15 @@ def main():
                                         w3.M, w3.N, w3.K)},
             ops, ab["quant"], w3.name, progress)
     if args.act_steps > 0:
+        s_out = torch.full((w3.N,), 0.02, dtype=torch.float32, device=dev)
+        yq3 = torch.empty((w3.M, w3.N), dtype=torch.int8, device=dev)
+        yqs = torch.empty((w3.M,), dtype=torch.float32, device=dev)
+        out["int8_output"] = requant_timings(args.act_steps, {
+            "gemm_fp16": gemm,
+            "gemm_requant": ql.prepare("gemm_w8a8_requant", xq3, xs3, wq3, ws3, b3, 0, s_out, w3.N, yq3,
+                                       w3.M, w3.N, w3.K),
+            "quant_y_rows": ql.prepare("quantize_per_row_int8", y3, F16, w3.M, w3.N, yq3, yqs),
+        }, ops, w3.name, progress)
         w4f = up(wl.draw(w4, x_rows=slice(0, 1)).w_nk)
         w5f = up(wl.draw(w5, x_rows=slice(0, 1)).w_nk)
         xqt = torch.empty((w3.M, w3.K), dtype=torch.int8, device=dev)

@@ -234,6 +234,30 @@ ql_status gemm_e4m3_per_channel(const uint8_t* xq, const float* x_scale, const u
                                 ql_dtype y_dtype, int64_t M, int64_t N, int64_t K, void* stream);
 
 /*
+ * The W8A8 layer with its output re-quantized to int8 for a following int8 layer, in the
+ * same epilogue: the result leaves as one byte per element ([quant67] §四: keep bulk data
+ * in low precision and convert on chip). The scales are static, as calibrated in [2048ai]
+ * §3.2-§3.3 (per output channel, max |output| over calibration rows / 127), or one for
+ * the whole output ([hotelren] per_tensor_quant_int8):
+ *   y[m,n]  = act(((float(acc[m,n]) * x_scale[m]) * w_scale[n]) + bias[n])
+ *             (fp32, each operation rounded on its own, in this order)
+ *   yq[m,n] = clamp(round_half_even(y[m,n] / out_scale[n or 0]), -127, 127)
+ *             (y / s correctly rounded in fp32)
+ * out_scale   fp32, out_scale_n entries: 1 (one scale for all of Y) or N (per column).
+ *             Each must be a positive normal fp32 value (a precondition: device memory is
+ *             not inspected).
+ * yq          [M,N] int8 row-major (out). Other arguments as for gemm_w8a8_per_channel_act.
+ * A following W8A8 layer takes yq as its codes with x_scale[m] = out_scale[0] for every row
+ * when out_scale_n == 1; per-column scales fold into that layer's weights instead
+ * (W'[k,n] = out_scale[k] * W[k,n]).
+ * out_scale_n other than 1 or N is QL_ERR_SHAPE.
+ */
+ql_status gemm_w8a8_requant(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                            const float* w_scale, const float* bias, ql_activation act,
+                            const float* out_scale, int64_t out_scale_n, int8_t* yq, int64_t M,
+                            int64_t N, int64_t K, void* stream);
+
+/*
  * The W8A8 integer accumulators alone, acc[m,n] = sum_k xq[m,k] * wq[k,n] as int32
  * [M,N] row-major. A checking aid for the exact integer stage of
  * gemm_w8a8_per_channel (same main loop); [hotelren] "W8A8矩阵乘法" scheme 1 names

@@ -22,7 +22,7 @@ __all__ = [
     "gemm_w8a8_per_channel_act", "gemm_w4a16_grouped_act", "ACTIVATIONS",
     "quantize_per_row_int8_asym", "weight_column_sums_i8", "gemm_w8a8_asym", "linear_w8a8_asym",
     "quantize_per_row_e4m3", "quantize_weight_per_channel_e4m3", "gemm_e4m3_per_channel",
-    "linear_e4m3", "quantize_per_tensor_int8",
+    "linear_e4m3", "quantize_per_tensor_int8", "gemm_w8a8_requant",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -59,6 +59,7 @@ _SIGS = {
     "gemm_w8a8_asym": [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I64, _I64, _I64, _P],
     "quantize_per_row_e4m3": [_P, _I, _I64, _I64, _P, _P, _P],
     "quantize_per_tensor_int8": [_P, _I, _I64, _P, _P, _P],
+    "gemm_w8a8_requant": [_P, _P, _P, _P, _P, _I, _P, _I64, _P, _I64, _I64, _I64, _P],
     "quantize_weight_per_channel_e4m3": [_P, _I64, _I64, _P, _P, _P],
     "gemm_e4m3_per_channel": [_P, _P, _P, _P, _P, _I, _P, _I, _I64, _I64, _I64, _P],
     "quantize_weight_block_asym_u8": [_P, _I64, _I64, _I64, _P, _P, _P, _P],
@@ -276,6 +277,27 @@ def _gemm_w8a8(xq, x_scale, wq, w_scale, bias, act, out_dtype, y):
         _call("gemm_w8a8_per_channel_act", _ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale), _ptr(bias),
               act, _ptr(y), ydt, M, N, K, _stream(xq))
     return y
+
+
+def gemm_w8a8_requant(xq, x_scale, wq, w_scale, out_scale, bias=None, act: str = "none", yq=None):
+    """int8 [M, N]: clamp(rne(act(((acc * x_scale[m]) * w_scale[n]) + bias[n]) / out_scale), +-127)
+    with out_scale fp32 of 1 (per tensor) or N (per output column) entries."""
+    _check(xq, "xq", (torch.int8,))
+    M, K = xq.shape
+    dev = xq.device
+    N = wq.shape[0]
+    _check(wq, "wq", (torch.int8,), (N, K), dev)
+    _check(x_scale, "x_scale", (torch.float32,), (M,), dev)
+    _check(w_scale, "w_scale", (torch.float32,), (N,), dev)
+    _check(out_scale, "out_scale", (torch.float32,), None, dev)
+    if out_scale.dim() != 1 or out_scale.numel() not in (1, N):
+        raise ValueError("out_scale must have 1 or N entries")
+    if bias is not None:
+        _check(bias, "bias", (torch.float32,), (N,), dev)
+    yq = _out(yq, "yq", (M, N), torch.int8, dev)
+    _call("gemm_w8a8_requant", _ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale), _ptr(bias), _act_code(act),
+          _ptr(out_scale), out_scale.numel(), _ptr(yq), M, N, K, _stream(xq))
+    return yq
 
 
 def gemm_w8a8_int32(xq, wq, acc=None):

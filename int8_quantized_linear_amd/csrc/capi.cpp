@@ -219,6 +219,29 @@ ql_status gemm_e4m3_per_channel(const uint8_t* xq, const float* x_scale, const u
                                 as_stream(stream), true);
 }
 
+ql_status gemm_w8a8_requant(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                            const float* w_scale, const float* bias, ql_activation act,
+                            const float* out_scale, int64_t out_scale_n, int8_t* yq, int64_t M,
+                            int64_t N, int64_t K, void* stream) {
+    if (act != QL_ACT_NONE && act != QL_ACT_GELU && act != QL_ACT_SILU)
+        return QL_ERR_DTYPE;
+    ql_status st = check_w8a8(xq, wq, yq, M, N, K);
+    if (st != QL_OK)
+        return st;
+    if (out_scale_n != 1 && out_scale_n != N)
+        return QL_ERR_SHAPE;
+    if (M == 0 || N == 0)
+        return QL_OK;
+    if (!x_scale || !w_scale || !out_scale)
+        return QL_ERR_NULL;
+    if (!aligned(x_scale, 4) || !aligned(w_scale, 4) || !aligned(out_scale, 4) ||
+        (bias && !aligned(bias, 4)))
+        return QL_ERR_ALIGN;
+    return ql::launch_gemm_w8a8(xq, x_scale, wq, w_scale, bias, yq, ql::Y_I8, (int)act, nullptr,
+                                nullptr, M, N, K, as_stream(stream), false, out_scale,
+                                (int)out_scale_n);
+}
+
 ql_status gemm_w8a8_per_channel(const int8_t* xq, const float* x_scale, const int8_t* wq,
                                 const float* w_scale, const float* bias, void* y,
                                 ql_dtype y_dtype, int64_t M, int64_t N, int64_t K, void* stream) {

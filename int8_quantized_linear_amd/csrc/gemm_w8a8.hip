@@ -54,16 +54,27 @@ __device__ inline void lds_copy4(const void* g, int8_t* lds) {
 // Bytes of the K ring at the start of the LDS allocation (three stages of a 128 x 256 tile
 // with 128-byte k-steps); the tile's scales follow it: x_scale of its 256 rows, then
 // w_scale and bias of its 256 columns, then (asymmetric activations only) x_zero of the
-// rows and the code sums of the columns (4 bytes each).
+// rows and the code sums of the columns (4 bytes each); for int8 output the columns'
+// output scales take the code sums' place.
 constexpr int RING_BYTES = 3 * 384 * 128;
 constexpr int SCALE_BYTES = 5 * 256 * 4;
 
-// The epilogue's optional asymmetric-activation terms: the rows' zero points and W's
-// column code sums (both NULL for symmetric activations).
-struct Asym {
+// The epilogue's optional terms: for asymmetric activations the rows' zero points and W's
+// column code sums (both NULL for symmetric activations); for int8 output the static output
+// scales (out_scale_n of them: 1 for the whole output, or one per column).
+struct EpiArgs {
     const float* x_zero;
     const int32_t* colsum;
+    const float* out_scale;
+    int out_scale_n;
 };
+
+// y = ((t * xs) * ws) + b with every operation rounded on its own (no fused multiply-add),
+// the order in which the int8 output's codes are defined.
+__device__ inline float epilogue_unfused(float t, float xs, float ws, float b) {
+#pragma clang fp contract(off)
+    return (t * xs) * ws + b;
+}
 
 // Operand element type: int8 codes (v_mfma_i32_32x32x32_i8, exact int32 sums) or OCP E4M3
 // fp8 codes (v_mfma_f32_32x32x64_f8f6f4, fp32 sums). The bytes move the same way (copies,
@@ -119,6 +130,13 @@ __device__ __forceinline__ void with_epilogue(int act, bool asym, F&& f) {
     using U = std::false_type;
     if constexpr (YMODE == Y_I32) {
         f(std::integral_constant<int, ACT_NONE>{}, U{});
+    } else if constexpr (YMODE == Y_I8) {
+        if (act == ACT_GELU)
+            f(std::integral_constant<int, ACT_GELU>{}, U{});
+        else if (act == ACT_SILU)
+            f(std::integral_constant<int, ACT_SILU>{}, U{});
+        else
+            f(std::integral_constant<int, ACT_NONE>{}, U{});
     } else if (asym) {
         if (act == ACT_GELU)
             f(std::integral_constant<int, ACT_GELU>{}, T{});
@@ -140,7 +158,7 @@ __device__ __forceinline__ void with_epilogue(int act, bool asym, F&& f) {
 // (indices clamped into range; entries past M or N are never used). Issued before the K
 // loop's first copies, so every wait of the loop also covers them; the epilogue's barrier
 // makes them visible to all waves. Without a bias, w_scale is copied in its place (unused).
-__device__ inline void issue_scales(const float* xs, const float* ws, const float* bias, Asym asym,
+__device__ inline void issue_scales(const float* xs, const float* ws, const float* bias, EpiArgs epi,
                                     int M, int N, int m0, int n0, int wave, int lane, int8_t* smem) {
     if (wave >= 4)
         return;
@@ -149,10 +167,12 @@ __device__ inline void issue_scales(const float* xs, const float* ws, const floa
     lds_copy4(xs + min(m0 + i, M - 1), sc);
     lds_copy4(ws + min(n0 + i, N - 1), sc + 1024);
     lds_copy4((bias != nullptr ? bias : ws) + min(n0 + i, N - 1), sc + 2048);
-    if (asym.x_zero != nullptr) {
-        lds_copy4(asym.x_zero + min(m0 + i, M - 1), sc + 3072);
-        lds_copy4(asym.colsum + min(n0 + i, N - 1), sc + 4096);
+    if (epi.x_zero != nullptr) {
+        lds_copy4(epi.x_zero + min(m0 + i, M - 1), sc + 3072);
+        lds_copy4(epi.colsum + min(n0 + i, N - 1), sc + 4096);
     }
+    if (epi.out_scale != nullptr)   // int8 output (never with zero points): the same slot
+        lds_copy4(epi.out_scale + (epi.out_scale_n == 1 ? 0 : min(n0 + i, N - 1)), sc + 4096);
 }
 
 // Epilogue: the accumulators are dequantized (y = acc * x_scale[m] * w_scale[n] + bias[n])
@@ -169,7 +189,8 @@ __device__ __forceinline__ void store_tile(const ACC (&acc)[FM][FN], bool has_bi
                                            int ncol0, int lm0, int ln0, int wave, int lane,
                                            int8_t* smem) {
     using OutT = typename std::conditional<YMODE == Y_F16, _Float16,
-                 typename std::conditional<YMODE == Y_F32, float, int32_t>::type>::type;
+                 typename std::conditional<YMODE == Y_F32, float,
+                 typename std::conditional<YMODE == Y_I8, int8_t, int32_t>::type>::type>::type;
     constexpr int SZ = sizeof(OutT);
     constexpr int VEC = 16 / SZ;                    // elements per 16-byte store
     constexpr int ROWB = WN * SZ + 32;              // staged row, padded: rows r, r + 4 differ in bank half
@@ -189,7 +210,7 @@ __device__ __forceinline__ void store_tile(const ACC (&acc)[FM][FN], bool has_bi
     const float* sb = sx + 512;
     const float* sz = sx + 768;
     const int32_t* scs = reinterpret_cast<const int32_t*>(sx + 1024);
-    float wsv[FN], bv[FN], csv[FN];
+    float wsv[FN], bv[FN], csv[FN], osv[FN], orv[FN];
     if constexpr (YMODE != Y_I32) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
@@ -198,6 +219,12 @@ __device__ __forceinline__ void store_tile(const ACC (&acc)[FM][FN], bool has_bi
             bv[j] = has_bias ? sb[c] : 0.0f;
             if constexpr (ASYM)
                 csv[j] = (float)scs[c];   // exact: |sum| <= 128 K < 2^24
+            if constexpr (YMODE == Y_I8) {
+                // the output scale and its correctly rounded reciprocal: y / s is then
+                // q0 = RN(y r), RN(q0 + fma(-q0, s, y) r), the correctly rounded quotient
+                osv[j] = reinterpret_cast<const float*>(scs)[c];
+                orv[j] = 1.0f / osv[j];
+            }
         }
     }
     const bool vec_ok = (N % VEC) == 0;   // rows start 16-byte aligned
@@ -230,6 +257,11 @@ __device__ __forceinline__ void store_tile(const ACC (&acc)[FM][FN], bool has_bi
                 OutT v;
                 if constexpr (YMODE == Y_I32) {
                     v = acc[i][j][e];
+                } else if constexpr (YMODE == Y_I8) {
+                    const float y = activation<ACT>(epilogue_unfused((float)acc[i][j][e], xsv[e], wsv[j], bv[j]));
+                    const float q0 = y * orv[j];
+                    const float qt = fmaf(fmaf(-q0, osv[j], y), orv[j], q0);
+                    v = (OutT)__builtin_amdgcn_fmed3f(rintf(qt), -127.0f, 127.0f);
                 } else if constexpr (ASYM) {
                     // sum_k (q_x - z_x) q_w = acc - z_x colsum, with one rounding
                     const float t = fmaf(-zsv[e], csv[j], (float)acc[i][j][e]);
@@ -272,7 +304,9 @@ __device__ __forceinline__ void store_tile(const ACC (&acc)[FM][FN], bool has_bi
 #pragma unroll
                     for (int q = 0; q < VEC; ++q) {
                         const int off = roff + (n + q < N ? (n + q) * SZ : LIM);
-                        if constexpr (SZ == 2)
+                        if constexpr (SZ == 1)
+                            __builtin_amdgcn_raw_buffer_store_b8(__builtin_bit_cast(uint8_t, pv[q]), rs, off, 0, 0);
+                        else if constexpr (SZ == 2)
                             __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, pv[q]), rs, off, 0, 0);
                         else
                             __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, pv[q]), rs, off, 0, 0);
@@ -340,7 +374,7 @@ template <int BM, int BN, int YMODE, int ELEM>
 __device__ __forceinline__ void gemm_tile_pp(const int8_t* __restrict__ A, const float* __restrict__ xs,
                                              const int8_t* __restrict__ B, const float* __restrict__ ws,
                                              const float* __restrict__ bias, void* __restrict__ Y,
-                                             int M, int N, int K, int m0, int n0, int act, Asym asym,
+                                             int M, int N, int K, int m0, int n0, int act, EpiArgs epi,
                                              int8_t* smem) {
     constexpr int BKL = 128;
     constexpr int WM = BM / 2, WN = BN / 4, FM = WM / 32, FN = WN / 32;
@@ -423,7 +457,7 @@ __device__ __forceinline__ void gemm_tile_pp(const int8_t* __restrict__ A, const
     // Prologue: group 0 copies all of stage 0 and stage 1 but its B high (copied in A_0),
     // and waits for stage 0; stage 1 has until the end of A_0.
     if constexpr (YMODE != Y_I32)
-        issue_scales(xs, ws, bias, asym, M, N, m0, n0, wave, lane, smem);
+        issue_scales(xs, ws, bias, epi, M, N, m0, n0, wave, lane, smem);
     if (grp == 0) {
 #pragma unroll
         for (int c = 0; c < CA; ++c)
@@ -519,7 +553,7 @@ __device__ __forceinline__ void gemm_tile_pp(const int8_t* __restrict__ A, const
         }
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
-    with_epilogue<YMODE>(act, asym.x_zero != nullptr, [&](auto act_c, auto asym_c) {
+    with_epilogue<YMODE>(act, epi.x_zero != nullptr, [&](auto act_c, auto asym_c) {
         store_tile<WM, WN, FM, FN, YMODE, 8, decltype(act_c)::value, decltype(asym_c)::value, AccT<ELEM>>(
             acc, bias != nullptr, Y, M, N, m0 + wm * WM, n0 + wn * WN, wm * WM, wn * WN, wave, lane, smem);
     });
@@ -537,7 +571,7 @@ template <int YMODE, int ELEM>
 __device__ __forceinline__ void gemm_tile_ks(const int8_t* __restrict__ A, const float* __restrict__ xs,
                                              const int8_t* __restrict__ B, const float* __restrict__ ws,
                                              const float* __restrict__ bias, void* __restrict__ Y,
-                                             int M, int N, int K, int m0, int n0, int act, Asym asym,
+                                             int M, int N, int K, int m0, int n0, int act, EpiArgs epi,
                                              int8_t* smem) {
     constexpr int BM = 128, BN = 256, BKL = 128;
     constexpr int WM = 64, WN = 128, FM = WM / 32, FN = WN / 32;
@@ -629,7 +663,7 @@ __device__ __forceinline__ void gemm_tile_ks(const int8_t* __restrict__ A, const
     // Prologue: group 0 copies stages 0 and 2, group 1 stage 1 (stage 2 is needed in phase
     // 1, before any phase-0 copy could land); group 0 reads stage 0.
     if constexpr (YMODE != Y_I32)
-        issue_scales(xs, ws, bias, asym, M, N, m0, n0, wave, lane, smem);
+        issue_scales(xs, ws, bias, epi, M, N, m0, n0, wave, lane, smem);
     if (grp == 0) {
         copies(0);
         if (KT > 2) {
@@ -747,7 +781,7 @@ __device__ __forceinline__ void gemm_tile_ks(const int8_t* __restrict__ A, const
     }
     __builtin_amdgcn_s_waitcnt(LGKM0);
     if (grp == 0) {
-        with_epilogue<YMODE>(act, asym.x_zero != nullptr, [&](auto act_c, auto asym_c) {
+        with_epilogue<YMODE>(act, epi.x_zero != nullptr, [&](auto act_c, auto asym_c) {
             store_tile<WM, WN, FM, FN, YMODE, 4, decltype(act_c)::value, decltype(asym_c)::value, AccT<ELEM>>(
                 acc, bias != nullptr, Y, M, N, m0 + wm * WM, n0 + wn * WN, wm * WM, wn * WN, q, lane, smem);
         });
@@ -769,13 +803,13 @@ template <int YMODE, int ELEM>
 __global__ __launch_bounds__(64 * NWAVES, 1) void gemm_w8a8_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ xs, const int8_t* __restrict__ B,
     const float* __restrict__ ws, const float* __restrict__ bias, void* __restrict__ Y, int M,
-    int N, int K, int act, Asym asym, TilePlan plan) {
+    int N, int K, int act, EpiArgs epi, TilePlan plan) {
     __shared__ __attribute__((aligned(1024))) int8_t smem[RING_BYTES + SCALE_BYTES];
     const int bid = blockIdx.x;
     if (bid < plan.nbig) {
         const int tile = xcd_remap(bid, plan.nbig);
         const int tn = tile / plan.tiles_m_big, tm = tile - tn * plan.tiles_m_big;
-        gemm_tile_pp<256, 256, YMODE, ELEM>(A, xs, B, ws, bias, Y, M, N, K, tm * 256, tn * 256, act, asym, smem);
+        gemm_tile_pp<256, 256, YMODE, ELEM>(A, xs, B, ws, bias, Y, M, N, K, tm * 256, tn * 256, act, epi, smem);
         if (bid >= plan.nsmall)
             return;
         // The big tile's epilogue has read all it needs from LDS (its stores may still be in
@@ -786,7 +820,7 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void gemm_w8a8_kernel(
     if (bid < plan.nsmall) {
         const int tile = xcd_remap(bid, plan.nsmall);
         const int tn = tile / plan.tiles_m_small, tm = tile - tn * plan.tiles_m_small;
-        gemm_tile_ks<YMODE, ELEM>(A, xs, B, ws, bias, Y, M, N, K, tm * 128, plan.n_small0 + tn * 256, act, asym, smem);
+        gemm_tile_ks<YMODE, ELEM>(A, xs, B, ws, bias, Y, M, N, K, tm * 128, plan.n_small0 + tn * 256, act, epi, smem);
     }
 }
 
@@ -828,7 +862,8 @@ TilePlan plan_tiles(int64_t M, int64_t N) {
 ql_status launch_gemm_w8a8(const int8_t* xq, const float* x_scale, const int8_t* wq,
                            const float* w_scale, const float* bias, void* y, int y_mode, int act,
                            const float* x_zero, const int32_t* colsum, int64_t M, int64_t N,
-                           int64_t K, hipStream_t stream, bool e4m3) {
+                           int64_t K, hipStream_t stream, bool e4m3, const float* out_scale,
+                           int out_scale_n) {
     if (M == 0 || N == 0)
         return QL_OK;
     const TilePlan plan = plan_tiles(M, N);
@@ -839,7 +874,7 @@ ql_status launch_gemm_w8a8(const int8_t* xq, const float* x_scale, const int8_t*
     const int m = (int)M, n = (int)N, k = (int)K;
 #define QL_LAUNCH(MODE, EL)                                                                         \
     hipLaunchKernelGGL((gemm_w8a8_kernel<MODE, EL>), grid, block, 0, stream, xq, x_scale, wq, w_scale, \
-                       bias, y, m, n, k, act, (Asym{x_zero, colsum}), plan)
+                       bias, y, m, n, k, act, (EpiArgs{x_zero, colsum, out_scale, out_scale_n}), plan)
     if (e4m3) {
         if (y_mode == Y_F32)
             QL_LAUNCH(Y_F32, EL_E4M3);
@@ -848,6 +883,9 @@ ql_status launch_gemm_w8a8(const int8_t* xq, const float* x_scale, const int8_t*
         return launch_status();
     }
     switch (y_mode) {
+    case Y_I8:
+        QL_LAUNCH(Y_I8, EL_I8);
+        break;
     case Y_F32:
         QL_LAUNCH(Y_F32, EL_I8);
         break;

@@ -35,16 +35,19 @@ ql_status launch_quant_int4_group(const float* w, int64_t K, int64_t N, int64_t 
                                   int32_t* packed, void* scales, hipStream_t stream);
 // x_zero (per row) and colsum (W's column code sums) are NULL for symmetric activations.
 // e4m3: xq and wq hold OCP E4M3 fp8 codes (fp32 accumulation; y_mode F32 or F16 only).
+// Y_I8: int8 codes clamp(rne(y / out_scale), -127, 127) with out_scale_n = 1 or N scales
+// (symmetric activations only).
 ql_status launch_gemm_w8a8(const int8_t* xq, const float* x_scale, const int8_t* wq,
                            const float* w_scale, const float* bias, void* y, int y_mode, int act,
                            const float* x_zero, const int32_t* colsum, int64_t M, int64_t N,
-                           int64_t K, hipStream_t stream, bool e4m3 = false);
+                           int64_t K, hipStream_t stream, bool e4m3 = false,
+                           const float* out_scale = nullptr, int out_scale_n = 0);
 ql_status launch_wonly(const void* x, const void* codes, int fmt, const void* scale,
                        const uint8_t* zp, int64_t group, const float* bias, void* y, int64_t M,
                        int64_t N, int64_t K, int act, hipStream_t stream);
 
 // y_mode of launch_gemm_w8a8
-enum { Y_F32 = 0, Y_F16 = 1, Y_I32 = 2 };
+enum { Y_F32 = 0, Y_F16 = 1, Y_I32 = 2, Y_I8 = 3 };
 // activation applied by an epilogue (values of ql_activation)
 enum { ACT_NONE = 0, ACT_GELU = 1, ACT_SILU = 2 };
 

@@ -10,6 +10,10 @@
  *
  * Domain checked: every finite binary16 x with |x| <= absmax, and random binary32
  * x with |x| <= absmax, for absmax log-uniform in [1e-10, 65504] (s = absmax / 127).
+ * A second domain covers the re-quantization epilogue, whose scales come from the caller:
+ * s any binary32 with exponent in [-100, 100] (random significands, plus all-ones and
+ * one-ulp-above-a-power significands), x = s * u with |u| <= 128, and x next to each
+ * tie (k + 1/2) s.
  * Usage: quotient_identity <trials>. Exit status 0 iff no mismatch.
  */
 #include <math.h>
@@ -65,6 +69,40 @@ int main(int argc, char** argv) {
             if (!same(q, q1)) {
                 if (bad < 5)
                     printf("mismatch: absmax %a x %a x/s %a identity %a\n", amax, x, (float)q, q1);
+                ++bad;
+            }
+        }
+    }
+    for (int t = 0; t < trials * 20; ++t) {
+        uint32_t mant = next() & 0x7FFFFFu;
+        if (t % 5 == 0)
+            mant = 0x7FFFFFu;                 /* significand 1.111...1 */
+        else if (t % 5 == 1)
+            mant = 1;                         /* one ulp above a power of two */
+        const int ex = (int)(next() % 201) - 100;
+        uint32_t bits = ((uint32_t)(ex + 127) << 23) | mant;
+        float sf;
+        memcpy(&sf, &bits, 4);
+        volatile float s = sf;
+        volatile float y = 1.0f / s;
+        for (int i = 0; i < 4096 + 256 * 3; ++i) {
+            float x;
+            if (i < 4096) {
+                x = s * (128.0f * ((float)(next() >> 8) / 16777216.0f)) * ((next() & 1) ? 1.0f : -1.0f);
+            } else {
+                const int k = (i - 4096) / 3 - 128;
+                const float tie = ((float)k + 0.5f) * s;
+                const int d = (i - 4096) % 3;
+                x = d == 0 ? tie : (d == 1 ? nextafterf(tie, INFINITY) : nextafterf(tie, -INFINITY));
+            }
+            volatile float q = x / s;
+            volatile float q0 = x * y;
+            const float r = fmaf(-q0, s, x);
+            const float q1 = fmaf(r, y, q0);
+            ++checked;
+            if (!same(q, q1)) {
+                if (bad < 5)
+                    printf("mismatch: s %a x %a x/s %a identity %a\n", (float)s, x, (float)q, q1);
                 ++bad;
             }
         }

@@ -44,6 +44,7 @@ def lib():
         "gemm_w8a8_asym": [P, P, P, P, P, P, P, I, P, I, I64, I64, I64, P],
         "quantize_per_row_e4m3": [P, I, I64, I64, P, P, P],
         "quantize_per_tensor_int8": [P, I, I64, P, P, P],
+        "gemm_w8a8_requant": [P, P, P, P, P, I, P, I64, P, I64, I64, I64, P],
         "quantize_weight_per_channel_e4m3": [P, I64, I64, P, P, P],
         "gemm_e4m3_per_channel": [P, P, P, P, P, I, P, I, I64, I64, I64, P],
         "quantize_weight_block_asym_u8": [P, I64, I64, I64, P, P, P, P],
@@ -65,7 +66,7 @@ def test_header_declares_the_entry_points():
               "gemm_w8a8_per_channel_act", "gemm_w4a16_grouped_act", "quantize_per_row_int8_asym",
               "weight_column_sums_i8", "gemm_w8a8_asym", "quantize_per_row_e4m3",
               "quantize_weight_per_channel_e4m3", "gemm_e4m3_per_channel",
-              "quantize_per_tensor_int8"):
+              "quantize_per_tensor_int8", "gemm_w8a8_requant"):
         assert n in names
 
 
@@ -248,6 +249,19 @@ def test_per_tensor_validation(lib):
     assert f(A, F16, -16, A, A, None) == SHAPE
     assert f(A, F16, 64, A, None, None) == NULL
     assert f(A, F16, 64, MIS, A, None) == ALIGN
+
+
+def test_requant_validation(lib):
+    f = lib.gemm_w8a8_requant
+    assert f(None, None, None, None, None, 0, None, 1, None, 0, 8, 64, None) == OK
+    assert f(A, A, A, A, None, 3, A, 1, A, 4, 8, 64, None) == DTYPE
+    assert f(A, A, A, A, None, 0, A, 2, A, 4, 8, 64, None) == SHAPE      # neither 1 nor N
+    assert f(A, A, A, A, None, 0, A, 0, A, 4, 8, 64, None) == SHAPE
+    assert f(A, A, A, A, None, 0, A, 1, A, 4, 8, 96, None) == SHAPE
+    assert f(A, A, A, A, None, 0, None, 1, A, 4, 8, 64, None) == NULL
+    assert f(A, None, A, A, None, 0, A, 1, A, 4, 8, 64, None) == NULL
+    assert f(A, A, A, A, None, 0, MIS, 1, A, 4, 8, 64, None) == ALIGN
+    assert f(A, A, A, A, None, 0, A, 1, MIS, 4, 8, 64, None) == ALIGN
 
 
 def test_producer_validation(lib):

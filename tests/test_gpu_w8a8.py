@@ -242,3 +242,64 @@ def test_empty(ql):
     wq = torch.zeros((8, 64), dtype=torch.int8, device=DEV)
     y = ql.gemm_w8a8_per_channel(xq, torch.empty(0, device=DEV), wq, torch.ones(8, device=DEV))
     assert y.shape == (0, 8)
+
+
+def _requant_case(ql, M, N, K, per_tensor, seed_shift=0):
+    """GPU-quantized operands (checked bit for bit), the oracle's fp32 epilogue, and static
+    output scales calibrated on another batch of the same law, so that some outputs exceed
+    the calibrated maximum and clamp."""
+    w = workloads.with_shape(workloads.W8A8_PREFILL, M, K, N)
+    inp = workloads.draw(w)
+    rows = np.arange(M) if M <= 512 else np.unique(np.concatenate([np.arange(0, M, 97), [M - 1]]))
+    wq_r, ws_r = oracle.quant_weight_per_channel(inp.w_nk)
+    xq_r, xs_r = oracle.quant_rows_i8(inp.x[rows])
+    wq, ws = ql.quantize_weight_per_channel(dev(inp.w_nk))
+    xq, xs = ql.quantize_per_row_int8(dev(inp.x))
+    assert np.array_equal(host(wq), wq_r) and np.array_equal(host(xq)[rows], xq_r)
+    cal = workloads.draw_x_only(w, 101 + seed_shift)[: min(M, 64)]
+    cq, cs = oracle.quant_rows_i8(cal)
+    y_cal = oracle.epilogue_w8a8(oracle.gemm_i32(cq, wq_r), cs, ws_r, inp.bias)[0]
+    s_out = oracle.channel_scales(y_cal) * np.float32(0.9)    # 0.9: some outputs clamp
+    if per_tensor:   # the widest channel's scale for all: half of it, so that some clamp
+        s_out = np.array([s_out.max() * np.float32(0.5)], np.float32)
+    y32, y64 = oracle.epilogue_w8a8(oracle.gemm_i32(xq_r, wq_r), xs_r, ws_r, inp.bias)
+    return inp, rows, xq, xs, wq, ws, s_out, y32
+
+
+@pytest.mark.parametrize("M,N,K,per_tensor", [(16, 256, 256, False), (16, 256, 256, True), (300, 520, 384, False),
+                                              (257, 129, 192, True), (128, 1000, 128, False),
+                                              (2000, 8300, 256, False), (2048, 11008, 4096, True)])
+def test_requant_bit_exact(ql, M, N, K, per_tensor):
+    """int8 output codes bit for bit: the kernel takes ((acc * xs) * ws) + b with separate
+    roundings, then the correctly rounded y / s, RNE and the clamp, exactly the oracle's
+    fp32 decision. Ragged N (byte stores), half-height, mixed and big tile plans, per-column
+    and per-tensor scales, the prefill shape on sampled rows."""
+    inp, rows, xq, xs, wq, ws, s_out, y32 = _requant_case(ql, M, N, K, per_tensor)
+    g = Guarded((M, N), torch.int8)
+    ql.gemm_w8a8_requant(xq, xs, wq, ws, dev(s_out), dev(inp.bias), "none", yq=g.view)
+    g.check()
+    q_ref = oracle.requant_i8(y32, s_out)
+    got = host(g.view)[rows]
+    bad = got != q_ref
+    assert not bad.any(), "%d of %d codes differ; first %s" % (bad.sum(), bad.size, np.argwhere(bad)[:3])
+    assert (np.abs(q_ref) == 127).any(), "the case should reach the clamp"
+
+
+@pytest.mark.parametrize("act", ["gelu", "silu"])
+@pytest.mark.parametrize("M,N,K", [(16, 256, 256), (300, 520, 384)])
+def test_requant_with_activation(ql, act, M, N, K):
+    """With an activation the kernel's act(y) differs from the oracle's fp64 act(y32) by the
+    activation's error (about 1e-6 relative), so a code may differ by one only where the
+    exact quotient lies that close to a rounding boundary; everywhere else codes agree."""
+    inp, rows, xq, xs, wq, ws, s_out, y32 = _requant_case(ql, M, N, K, False, 1)
+    yq = ql.gemm_w8a8_requant(xq, xs, wq, ws, dev(s_out), dev(inp.bias), act)
+    code = {"gelu": 1, "silu": 2}[act]
+    a = oracle.activation_f64(y32.astype(np.float64), code)
+    v = a / s_out.astype(np.float64)[None, :]
+    q_ref = np.clip(np.rint(v), -127, 127)
+    got = host(yq)[rows].astype(np.float64)
+    delta = (4e-6 * (np.abs(y32) + np.abs(a)) + 1e-30) / s_out.astype(np.float64)[None, :]
+    near = np.abs(np.abs(v - np.floor(v)) - 0.5) <= delta
+    assert np.all(np.abs(got - q_ref) <= 1)
+    assert np.all((got == q_ref) | near), "codes differ away from a rounding boundary"
+    assert near.sum() < 0.01 * near.size
