@@ -106,7 +106,38 @@ def cpu_baseline(target_s: float):
     return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": "rows 0..%d of X [2048,4096] through the W8A8 layer (per-row quantize, exact "
                       "int32 GEMM with W [4096,11008], fp32 epilogue, fp16 output): %.1f s" % (rows - 1, dt),
-            "seconds": dt, "host": platform.processor() or platform.machine()}
+            "seconds": dt, "host": platform.processor() or platform.machine(),
+            "single_thread": _cpu_single_thread(target_s / 4)}
+
+
+_ONE_THREAD = r"""
+import sys, time
+sys.path.insert(0, sys.argv[1])
+import numpy as np
+import oracle, workloads as wl
+w = wl.W8A8_PREFILL
+inp = wl.draw(w)
+wq, ws = oracle.quant_weight_per_channel(inp.w_nk)
+t0 = time.perf_counter(); oracle.linear_w8a8(inp.x[:1], wq, ws, inp.bias); per_row = time.perf_counter() - t0
+rows = int(max(1, min(w.M, round(float(sys.argv[2]) / per_row))))
+t0 = time.perf_counter(); r = oracle.linear_w8a8(inp.x[:rows], wq, ws, inp.bias); dt = time.perf_counter() - t0
+print(rows, dt, oracle.num_threads())
+"""
+
+
+def _cpu_single_thread(target_s: float):
+    """The same oracle sample on one thread, in a child process started with
+    OMP_NUM_THREADS=1 (the oracle reads it when its library loads)."""
+    import subprocess
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, "-c", _ONE_THREAD, ROOT, str(target_s)], env=env,
+                       capture_output=True, text=True, timeout=600)
+    if r.returncode != 0:
+        return {"error": r.stderr.strip().splitlines()[-1:] or ["failed"]}
+    rows, dt, threads = r.stdout.split()
+    rows, dt = int(rows), float(dt)
+    w = 2.0 * rows * 11008 * 4096
+    return {"value": w / dt / 1e12, "unit": "TOPS", "cores": int(threads), "rows": rows, "seconds": dt}
 
 
 def fused_activation_timings(ql, n, gemm, dec5, r5, make_gemm, make_dec, ops, w4_bytes, gemm_name,
@@ -363,6 +394,15 @@ def main():
     del i2, i4, i5
     torch.cuda.synchronize()
 
+    w1 = wl.W8A8_SMALL
+    i1 = wl.draw(w1)
+    wq1, ws1 = ql.quantize_weight_per_channel(up(i1.w_nk))
+    x1, b1 = up(i1.x), up(i1.bias)
+    xq1 = torch.empty((w1.M, w1.K), dtype=torch.int8, device=dev)
+    xs1 = torch.empty((w1.M,), dtype=torch.float32, device=dev)
+    y1 = torch.empty((w1.M, w1.N), dtype=torch.float32, device=dev)
+    del i1
+
     # ------------------------------------------------- prepared launches
     F16 = 1
     quant = ql.prepare("quantize_per_row_int8", x3, F16, w3.M, w3.K, xq3, xs3)
@@ -477,6 +517,14 @@ def main():
                 "gemm_e4m3": ql.prepare("gemm_e4m3_per_channel", xq8, xs8, wq8, ws8, b3, 0, y3, F16,
                                         w3.M, w3.N, w3.K)},
             ops, ab["quant"], w3.name, progress)
+    if args.act_steps > 0:
+        progress("small layer latency: %d launches each" % args.act_steps)
+        us1 = _alternate(args.act_steps, {
+            "quant": ql.prepare("quantize_per_row_int8", x1, 0, w1.M, w1.K, xq1, xs1),
+            "gemm": ql.prepare("gemm_w8a8_per_channel", xq1, xs1, wq1, ws1, b1, y1, 0, w1.M, w1.N, w1.K)})
+        out["small_layer"] = {"workload": w1.name, "quant_us": us1["quant"], "gemm_us": us1["gemm"],
+                              "layer_us": us1["quant"] + us1["gemm"],
+                              "note": "latency-bound: 16 quantizer workgroups (one per row), then one 128 x 256 GEMM tile; event-timed"}
     if args.act_steps > 0:
         s_out = torch.full((w3.N,), 0.02, dtype=torch.float32, device=dev)
         yq3 = torch.empty((w3.M, w3.N), dtype=torch.int8, device=dev)
