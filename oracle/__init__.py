@@ -64,6 +64,7 @@ def _declare(L):
     L.oracle_activation_f64.argtypes = [_P, _I64, ctypes.c_int]
     L.oracle_quant_rows_i8_asym.argtypes = [_P, _I64, _I64, _P, _P, _P]
     L.oracle_channel_scales.argtypes = [_P, _I64, _I64, _P]
+    L.oracle_wonly_f32seq.argtypes = [_P, _I64, _I64, _P, ctypes.c_int, _P, _P, _I64, _P, _I64, _P]
     L.oracle_requant_i8.argtypes = [_P, _I64, _I64, _P, _I64, _P]
     L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
     L.oracle_e4m3_decode.restype = ctypes.c_double
@@ -182,6 +183,21 @@ class Oracle:
         self.L.oracle_wonly_f64(_ptr(xf), M, K, _ptr(codes), kind, _ptr(s), _ptr(z), group_size,
                                _ptr(b), N, _ptr(y64))
         return y64
+
+    def w8a16_f32seq(self, x, codes_nk, scale, zero_point=None, group_size: int = 0, bias=None) -> np.ndarray:
+        """The weight-only product of w8a16_f64 summed in fp32 in k order (one fp32 order)."""
+        xf = self._as_f32(x)
+        M, K = xf.shape
+        N = codes_nk.shape[0]
+        kind = 0 if zero_point is None else 1
+        codes = _c(codes_nk, np.int8 if kind == 0 else np.uint8)
+        s = _c(scale, np.float32)
+        z = None if zero_point is None else _c(zero_point, np.uint8)
+        b = None if bias is None else _c(bias, np.float32)
+        y32 = np.empty((M, N), np.float32)
+        self.L.oracle_wonly_f32seq(_ptr(xf), M, K, _ptr(codes), kind, _ptr(s), _ptr(z), group_size,
+                                  _ptr(b), N, _ptr(y32))
+        return y32
 
     def quant_rows_i8_asym(self, x) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
         """Asymmetric int8 per row of x [M, K] (fp16 or fp32): (q int8, scale fp32 [M],

@@ -419,6 +419,37 @@ void oracle_wonly_f64(const float* x, int64_t M, int64_t K, const void* codes, i
     }
 }
 
+/* The same weight-only product summed in fp32 in k order: w = (q - z) * s rounded to fp32,
+ * then acc = RN(acc + RN(x * w)) for k = 0 .. K-1, then + bias. One legitimate fp32 order;
+ * its distance from the fp64 value shows how far fp32 summation orders spread at a shape
+ * (the tolerance of the weight-only tests must cover any of them). */
+void oracle_wonly_f32seq(const float* x, int64_t M, int64_t K, const void* codes, int codes_kind,
+                         const float* scale, const uint8_t* zp, int64_t group, const float* bias,
+                         int64_t N, float* y32)
+{
+    const int8_t* q8 = (const int8_t*)codes;
+    const uint8_t* u8 = (const uint8_t*)codes;
+    int64_t G = group > 0 ? K / group : 1;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t m = 0; m < M; ++m) {
+            float acc = 0.0f;
+            for (int64_t k = 0; k < K; ++k) {
+                int64_t g = group > 0 ? k / group : 0;
+                float q = codes_kind == 0 ? (float)q8[n * K + k] : (float)u8[n * K + k];
+                float z = zp ? (float)zp[n * G + g] : 0.0f;
+                float sc = group > 0 ? scale[n * G + g] : scale[n];
+                float w = (q - z) * sc;
+                float p = x[m * K + k] * w;
+                acc = acc + p;
+            }
+            if (bias)
+                acc = acc + bias[n];
+            y32[m * N + n] = acc;
+        }
+    }
+}
+
 /* Signed int4 code of element k from column n's packed words ([N][K/8] int32). */
 static int unpack_int4(const int32_t* packed, int64_t K, int64_t n, int64_t k)
 {

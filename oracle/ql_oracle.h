@@ -48,4 +48,7 @@ int oracle_num_threads(void);
 void oracle_channel_scales(const float* y, int64_t M, int64_t N, float* s);
 void oracle_requant_i8(const float* y, int64_t M, int64_t N, const float* s, int64_t scale_n,
                        int8_t* q);
+void oracle_wonly_f32seq(const float* x, int64_t M, int64_t K, const void* codes, int codes_kind,
+                         const float* scale, const uint8_t* zp, int64_t group, const float* bias,
+                         int64_t N, float* y32);
 #endif

@@ -606,6 +606,36 @@ def pin_activation_invariants(orc):
         assert np.all(np.diff(pos) > 0)
 
 
+def pin_wonly_f32seq(orc):
+    """The fp32 k-order sum: equal to the fp64 product where every partial sum is exact
+    (small integer activations and codes, power-of-two scales, block zero points); equal to
+    numpy's float32 cumulative sum of the float32 products in k order elsewhere; and within
+    K * 2^-24 * sum |terms| of the fp64 value."""
+    rng = np.random.default_rng(93)
+    M, K, N = 3, 128, 5
+    x = rng.integers(-8, 9, (M, K)).astype(np.float32)
+    q = rng.integers(0, 256, (N, K)).astype(np.uint8)
+    z = rng.integers(0, 256, (N, K // 64)).astype(np.uint8)
+    s = np.exp2(rng.integers(-4, 2, (N, K // 64))).astype(np.float32)
+    y32 = orc.w8a16_f32seq(x, q, s, z, 64)
+    assert np.array_equal(y32.astype(np.float64), orc.w8a16_f64(x, q, s, z, 64))
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    q8 = rng.integers(-127, 128, (N, K)).astype(np.int8)
+    s8 = rng.uniform(0.001, 0.01, N).astype(np.float32)
+    b = rng.standard_normal(N).astype(np.float32)
+    y32 = orc.w8a16_f32seq(x, q8, s8, None, 0, b)
+    w = (q8.astype(np.float32) * s8[:, None]).astype(np.float32)
+    for m in range(M):
+        for n in range(N):
+            acc = np.float32(0.0)
+            for k in range(K):
+                acc = np.float32(acc + np.float32(x[m, k] * w[n, k]))
+            assert y32[m, n] == np.float32(acc + b[n]), (m, n)
+    y64 = orc.w8a16_f64(x, q8, s8, None, 0, b)
+    terms = np.abs(x.astype(np.float64)) @ np.abs(w.astype(np.float64)).T + np.abs(b)
+    assert np.all(np.abs(y32 - y64) <= (K + 2) * 2.0 ** -24 * terms + 1e-9 * terms)
+
+
 # ------------------------------------------------------- re-quantization of Y
 
 def pin_requant_golden_ties(orc):
