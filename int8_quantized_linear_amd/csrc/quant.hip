@@ -18,7 +18,12 @@ namespace ql {
 namespace {
 
 constexpr int QT = 256;       // threads per row-quantizer workgroup
-constexpr int QMAXC = 4;      // 16-byte chunks per thread kept in registers
+// 16-byte chunks per thread kept in registers: QC_SHORT for rows of up to QT * QC_SHORT
+// chunks (8192 fp16 values), QC_LONG for longer rows (up to 16384 fp16 values stay in
+// registers, as for Llama-7B's 11008- and 14336-wide activations); the launchers pick one.
+// More chunks than a row needs cost the short rows some speed, so both are kept.
+constexpr int QC_SHORT = 4;
+constexpr int QC_LONG = 8;
 
 __device__ inline float block_max(float v, float* red) {
 #pragma unroll
@@ -177,9 +182,10 @@ struct Chunk {
 
 // One workgroup per row. Rows of up to QT * QMAXC chunks stay in registers (one HBM
 // read); longer rows are read a second time for the codes (the re-read hits L2).
+// QMAXC is QC_SHORT or QC_LONG.
 // E4M3: fp8 codes with s = max(absmax, 1e-10) / 448 (hotelren.com: the fp8 quantizer
 // differs from the int8 one only in the result type; 448 is E4M3's largest value).
-template <bool F16, bool E4M3 = false>
+template <bool F16, bool E4M3, int QMAXC>
 __global__ __launch_bounds__(QT) void quant_rows_i8_kernel(const void* __restrict__ x, int64_t K,
                                                           int8_t* __restrict__ q,
                                                           float* __restrict__ scale) {
@@ -307,7 +313,7 @@ __global__ __launch_bounds__(64) void tensor_slot_scale_kernel(float* __restrict
 //   s = max((hi - lo) / 255, 1e-8);  z = -lo / s - 128 (a float);
 //   q = clamp(round(x / s + z), -128, 127)      (fp32, round half to even)
 // so that x ~ s (q - z). One workgroup per row, as quant_rows_i8_kernel.
-template <bool F16>
+template <bool F16, int QMAXC>
 __global__ __launch_bounds__(QT) void quant_rows_i8_asym_kernel(const void* __restrict__ x, int64_t K,
                                                                int8_t* __restrict__ q,
                                                                float* __restrict__ scale,
@@ -477,15 +483,26 @@ __global__ __launch_bounds__(256) void quant_int4_group_kernel(
 
 }  // namespace
 
+// The chunk count per thread for rows of K values: short rows keep the smaller count.
+inline bool long_rows(int64_t K, int x_is_f16) { return K / (x_is_f16 ? 8 : 4) > (int64_t)QT * QC_SHORT; }
+
 ql_status launch_quant_rows_i8(const void* x, int x_is_f16, int64_t rows, int64_t K, int8_t* q,
                                float* scale, hipStream_t stream) {
     if (rows == 0)
         return QL_OK;
     const dim3 grid((unsigned)rows), block(QT);
-    if (x_is_f16)
-        hipLaunchKernelGGL(quant_rows_i8_kernel<true>, grid, block, 0, stream, x, K, q, scale);
-    else
-        hipLaunchKernelGGL(quant_rows_i8_kernel<false>, grid, block, 0, stream, x, K, q, scale);
+    const bool lg = long_rows(K, x_is_f16);
+    if (x_is_f16) {
+        if (lg)
+            hipLaunchKernelGGL((quant_rows_i8_kernel<true, false, QC_LONG>), grid, block, 0, stream, x, K, q, scale);
+        else
+            hipLaunchKernelGGL((quant_rows_i8_kernel<true, false, QC_SHORT>), grid, block, 0, stream, x, K, q, scale);
+    } else {
+        if (lg)
+            hipLaunchKernelGGL((quant_rows_i8_kernel<false, false, QC_LONG>), grid, block, 0, stream, x, K, q, scale);
+        else
+            hipLaunchKernelGGL((quant_rows_i8_kernel<false, false, QC_SHORT>), grid, block, 0, stream, x, K, q, scale);
+    }
     return launch_status();
 }
 
@@ -514,10 +531,18 @@ ql_status launch_quant_rows_e4m3(const void* x, int x_is_f16, int64_t rows, int6
         return QL_OK;
     const dim3 grid((unsigned)rows), block(QT);
     int8_t* qs = reinterpret_cast<int8_t*>(q);
-    if (x_is_f16)
-        hipLaunchKernelGGL((quant_rows_i8_kernel<true, true>), grid, block, 0, stream, x, K, qs, scale);
-    else
-        hipLaunchKernelGGL((quant_rows_i8_kernel<false, true>), grid, block, 0, stream, x, K, qs, scale);
+    const bool lg = long_rows(K, x_is_f16);
+    if (x_is_f16) {
+        if (lg)
+            hipLaunchKernelGGL((quant_rows_i8_kernel<true, true, QC_LONG>), grid, block, 0, stream, x, K, qs, scale);
+        else
+            hipLaunchKernelGGL((quant_rows_i8_kernel<true, true, QC_SHORT>), grid, block, 0, stream, x, K, qs, scale);
+    } else {
+        if (lg)
+            hipLaunchKernelGGL((quant_rows_i8_kernel<false, true, QC_LONG>), grid, block, 0, stream, x, K, qs, scale);
+        else
+            hipLaunchKernelGGL((quant_rows_i8_kernel<false, true, QC_SHORT>), grid, block, 0, stream, x, K, qs, scale);
+    }
     return launch_status();
 }
 
@@ -526,10 +551,18 @@ ql_status launch_quant_rows_i8_asym(const void* x, int x_is_f16, int64_t rows, i
     if (rows == 0)
         return QL_OK;
     const dim3 grid((unsigned)rows), block(QT);
-    if (x_is_f16)
-        hipLaunchKernelGGL(quant_rows_i8_asym_kernel<true>, grid, block, 0, stream, x, K, q, scale, zero);
-    else
-        hipLaunchKernelGGL(quant_rows_i8_asym_kernel<false>, grid, block, 0, stream, x, K, q, scale, zero);
+    const bool lg = long_rows(K, x_is_f16);
+    if (x_is_f16) {
+        if (lg)
+            hipLaunchKernelGGL((quant_rows_i8_asym_kernel<true, QC_LONG>), grid, block, 0, stream, x, K, q, scale, zero);
+        else
+            hipLaunchKernelGGL((quant_rows_i8_asym_kernel<true, QC_SHORT>), grid, block, 0, stream, x, K, q, scale, zero);
+    } else {
+        if (lg)
+            hipLaunchKernelGGL((quant_rows_i8_asym_kernel<false, QC_LONG>), grid, block, 0, stream, x, K, q, scale, zero);
+        else
+            hipLaunchKernelGGL((quant_rows_i8_asym_kernel<false, QC_SHORT>), grid, block, 0, stream, x, K, q, scale, zero);
+    }
     return launch_status();
 }
 

@@ -56,7 +56,7 @@ def test_rows_prefill_full(ql):
 
 @pytest.mark.parametrize("M,K,dtype", [(1, 16, np.float16), (37, 4096, np.float16),
                                        (5, 8256, np.float16), (3, 4112, np.float32),
-                                       (64, 48, np.float32), (130, 1024, np.float16)])
+                                       (64, 48, np.float32), (130, 1024, np.float16), (4, 11008, np.float16), (2, 14336, np.float16), (3, 16400, np.float16), (2, 8208, np.float32)])
 def test_rows_shapes(ql, M, K, dtype):
     """Ragged M, the shortest K, and rows too long to keep in registers; row magnitudes
     spread over 2^-8..2^8 so that codes reach E4M3's subnormals."""
