@@ -277,8 +277,15 @@ __global__ __launch_bounds__(QT) void tensor_absmax_kernel(const void* __restric
                 amax = fmaxf(amax, c[i].absmax());
     }
     amax = block_max(amax, red);
-    if (threadIdx.x == 0)
-        atomicMax(reinterpret_cast<unsigned int*>(slot), __float_as_uint(amax));
+    // Device-scope atomics on one address serialize at the memory side, so most workgroups
+    // skip theirs: the slot only grows, and a workgroup whose maximum does not exceed the
+    // value it reads (never more than the final one) cannot change the result.
+    if (threadIdx.x == 0) {
+        unsigned int* p = reinterpret_cast<unsigned int*>(slot);
+        const unsigned int mine = __float_as_uint(amax);
+        if (mine > __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+            atomicMax(p, mine);
+    }
 }
 
 template <bool F16>
@@ -513,12 +520,14 @@ ql_status launch_quant_tensor_i8(const void* x, int x_is_f16, int64_t n, int8_t*
     const int64_t nch = n / (x_is_f16 ? 8 : 4);
     const int64_t want = (nch + (int64_t)QT * TCH - 1) / ((int64_t)QT * TCH);
     const dim3 grid((unsigned)(want < 2048 ? want : 2048)), block(QT), one(1), w64(64);
+    // the absmax pass uses at most two workgroups per CU: fewer atomics (see the kernel)
+    const dim3 grid_max((unsigned)(want < 512 ? want : 512));
     hipLaunchKernelGGL(tensor_slot_zero_kernel, one, w64, 0, stream, scale);
     if (x_is_f16) {
-        hipLaunchKernelGGL(tensor_absmax_kernel<true>, grid, block, 0, stream, x, nch, scale);
+        hipLaunchKernelGGL(tensor_absmax_kernel<true>, grid_max, block, 0, stream, x, nch, scale);
         hipLaunchKernelGGL(tensor_codes_kernel<true>, grid, block, 0, stream, x, nch, scale, q);
     } else {
-        hipLaunchKernelGGL(tensor_absmax_kernel<false>, grid, block, 0, stream, x, nch, scale);
+        hipLaunchKernelGGL(tensor_absmax_kernel<false>, grid_max, block, 0, stream, x, nch, scale);
         hipLaunchKernelGGL(tensor_codes_kernel<false>, grid, block, 0, stream, x, nch, scale, q);
     }
     hipLaunchKernelGGL(tensor_slot_scale_kernel, one, w64, 0, stream, scale);
