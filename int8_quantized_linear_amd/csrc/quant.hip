@@ -406,76 +406,107 @@ __global__ __launch_bounds__(QT) void column_sums_i8_kernel(const int8_t* __rest
     }
 }
 
-// Block-wise asymmetric uint8 (zingnex.cn "从零实现大语言模型 INT8 量化", 核心量化流程
-// steps 1-2): per block of `block` weights along K in column n,
-//   s = max((max - min) / 255, 1e-8); zp = clamp(round(-min / s), 0, 255);
-//   q = clamp(round(w / s) + zp, 0, 255).
-// One thread per (column, block); an offline producer, not on the serving path.
+// The weight producers give each (column, group) to a sub-group of LP lanes of one wave
+// (LP the power of two at or above the group's chunk count, at most 64), so that a wave's
+// loads are contiguous runs of the column: the lanes of a sub-group stride over the group's
+// chunks, reduce with xor shuffles inside the sub-group (offsets below LP never leave it),
+// and each writes its own code words. 64 / LP groups share a wave.
+__device__ inline int producer_lanes(int chunks) {
+    int lp = 1;
+    while (lp < chunks && lp < WAVE)
+        lp <<= 1;
+    return lp;
+}
+
+// Block-asymmetric uint8 (zingnex.cn "从零实现大语言模型 INT8 量化", 核心量化流程 steps 1-2),
+// per block b of `block` weights along K and column n:
+//   s = max((max - min) / 255, 1e-8);  zp = clamp(rint(-min / s), 0, 255)
+//   q = clamp(rint(w / s) + zp, 0, 255)          (fp32, IEEE division, half to even)
+// A chunk is 4 weights (16 bytes in, one 32-bit word of codes out).
 __global__ __launch_bounds__(256) void quant_block_asym_u8_kernel(
     const float* __restrict__ w, int64_t K, int64_t N, int64_t block, uint8_t* __restrict__ q,
     float* __restrict__ scale, uint8_t* __restrict__ zp) {
     const int64_t G = K / block;
-    const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (id >= N * G)
-        return;
-    const int64_t n = id / G, g = id % G;
+    const int ch = (int)(block / 4);
+    const int lp = producer_lanes(ch);
+    const int lane = threadIdx.x & (WAVE - 1), li = lane & (lp - 1);
+    const int64_t id = ((int64_t)blockIdx.x * (blockDim.x / WAVE) + threadIdx.x / WAVE) * (WAVE / lp) + lane / lp;
+    const bool live = id < N * G;
+    const int64_t n = live ? id / G : 0, g = live ? id % G : 0;
     const float* v = w + n * K + g * block;
-    float mn = v[0], mx = v[0];
-    for (int64_t i = 0; i < block; i += 4) {
-        const f32x4 t = *reinterpret_cast<const f32x4*>(v + i);
+    float mn = INFINITY, mx = -INFINITY;
+    if (live)
+        for (int c = li; c < ch; c += lp) {
+            const f32x4 t = *reinterpret_cast<const f32x4*>(v + 4 * c);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            mn = fminf(mn, t[j]);
-            mx = fmaxf(mx, t[j]);
+            for (int j = 0; j < 4; ++j) {
+                mn = fminf(mn, t[j]);
+                mx = fmaxf(mx, t[j]);
+            }
         }
+    for (int o = lp / 2; o > 0; o >>= 1) {
+        mn = fminf(mn, __shfl_xor(mn, o, WAVE));
+        mx = fmaxf(mx, __shfl_xor(mx, o, WAVE));
     }
+    if (!live)
+        return;
     float s = (mx - mn) / 255.0f;
     s = fmaxf(s, 1e-8f);
     const float zf = fminf(fmaxf(rintf(-mn / s), 0.0f), 255.0f);
     const int z = (int)zf;
     uint8_t* qo = q + n * K + g * block;
-    for (int64_t i = 0; i < block; i += 4) {
-        const f32x4 t = *reinterpret_cast<const f32x4*>(v + i);
+    for (int c = li; c < ch; c += lp) {
+        const f32x4 t = *reinterpret_cast<const f32x4*>(v + 4 * c);
         uint32_t b = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            int c = (int)rintf(t[j] / s) + z;
-            c = c < 0 ? 0 : (c > 255 ? 255 : c);
-            b |= (uint32_t)c << (8 * j);
+            int cq = (int)rintf(t[j] / s) + z;
+            cq = cq < 0 ? 0 : (cq > 255 ? 255 : cq);
+            b |= (uint32_t)cq << (8 * j);
         }
-        *reinterpret_cast<uint32_t*>(qo + i) = b;
+        *reinterpret_cast<uint32_t*>(qo + 4 * c) = b;
     }
-    scale[id] = s;
-    zp[id] = (uint8_t)z;
+    if (li == 0) {
+        scale[id] = s;
+        zp[id] = (uint8_t)z;
+    }
 }
 
 // Per-group symmetric int4 (xdnf.cn INT4/FP16 mixed GEMM on CANN TBE, §5.1: scale =
 // absmax / 7, stored fp16 per §3.1): s16 = fp16(max(absmax, 7 * 2^-24) / 7) (round to
 // nearest even); q = clamp(round(w / s16), -8, 7), packed eight per int32 along K with
-// element k % 8 = j in bits [4j, 4j+3]. One thread per (column, group).
+// element k % 8 = j in bits [4j, 4j+3]. A chunk is 8 weights (32 bytes in, one word out).
 __global__ __launch_bounds__(256) void quant_int4_group_kernel(
     const float* __restrict__ w, int64_t K, int64_t N, int64_t group, int32_t* __restrict__ packed,
     _Float16* __restrict__ scales) {
     const int64_t G = K / group;
-    const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (id >= N * G)
-        return;
-    const int64_t n = id / G, g = id % G;
+    const int ch = (int)(group / 8);
+    const int lp = producer_lanes(ch);
+    const int lane = threadIdx.x & (WAVE - 1), li = lane & (lp - 1);
+    const int64_t id = ((int64_t)blockIdx.x * (blockDim.x / WAVE) + threadIdx.x / WAVE) * (WAVE / lp) + lane / lp;
+    const bool live = id < N * G;
+    const int64_t n = live ? id / G : 0, g = live ? id % G : 0;
     const float* v = w + n * K + g * group;
     float a = 0.0f;
-    for (int64_t i = 0; i < group; i += 4) {
-        const f32x4 t = *reinterpret_cast<const f32x4*>(v + i);
+    if (live)
+        for (int c = li; c < ch; c += lp) {
+            const f32x4 t0 = *reinterpret_cast<const f32x4*>(v + 8 * c);
+            const f32x4 t1 = *reinterpret_cast<const f32x4*>(v + 8 * c + 4);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            a = fmaxf(a, fabsf(t[j]));
-    }
+            for (int j = 0; j < 4; ++j)
+                a = fmaxf(a, fmaxf(fabsf(t0[j]), fabsf(t1[j])));
+        }
+    for (int o = lp / 2; o > 0; o >>= 1)
+        a = fmaxf(a, __shfl_xor(a, o, WAVE));
+    if (!live)
+        return;
     const float floor_a = 7.0f * 0x1p-24f;
     const _Float16 h = (_Float16)(fmaxf(a, floor_a) / 7.0f);
     const float s = (float)h;
     int32_t* po = packed + n * (K / 8) + g * (group / 8);
-    for (int64_t i = 0; i < group; i += 8) {
-        const f32x4 t0 = *reinterpret_cast<const f32x4*>(v + i);
-        const f32x4 t1 = *reinterpret_cast<const f32x4*>(v + i + 4);
+    for (int c = li; c < ch; c += lp) {
+        const f32x4 t0 = *reinterpret_cast<const f32x4*>(v + 8 * c);
+        const f32x4 t1 = *reinterpret_cast<const f32x4*>(v + 8 * c + 4);
         uint32_t word = 0;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -483,12 +514,21 @@ __global__ __launch_bounds__(256) void quant_int4_group_kernel(
             const float r = fminf(fmaxf(rintf(x / s), -8.0f), 7.0f);
             word |= ((uint32_t)(int)r & 0xFu) << (4 * j);
         }
-        po[i / 8] = (int32_t)word;
+        po[c] = (int32_t)word;
     }
-    scales[id] = h;
+    if (li == 0)
+        scales[id] = h;
 }
 
 }  // namespace
+
+// Lanes per (column, group) in the producers, as producer_lanes computes it on the device.
+inline int producer_lanes_host(int chunks) {
+    int lp = 1;
+    while (lp < chunks && lp < WAVE)
+        lp <<= 1;
+    return lp;
+}
 
 // The chunk count per thread for rows of K values: short rows keep the smaller count.
 inline bool long_rows(int64_t K, int x_is_f16) { return K / (x_is_f16 ? 8 : 4) > (int64_t)QT * QC_SHORT; }
@@ -588,7 +628,8 @@ ql_status launch_quant_block_asym_u8(const float* w, int64_t K, int64_t N, int64
     const int64_t total = N * (K / block);
     if (total == 0)
         return QL_OK;
-    const dim3 grid((unsigned)((total + 255) / 256)), blk(256);
+    const int64_t per_wg = (256 / WAVE) * (WAVE / producer_lanes_host((int)(block / 4)));
+    const dim3 grid((unsigned)((total + per_wg - 1) / per_wg)), blk(256);
     hipLaunchKernelGGL(quant_block_asym_u8_kernel, grid, blk, 0, stream, w, K, N, block, q, scale,
                        zp);
     return launch_status();
@@ -599,7 +640,8 @@ ql_status launch_quant_int4_group(const float* w, int64_t K, int64_t N, int64_t 
     const int64_t total = N * (K / group);
     if (total == 0)
         return QL_OK;
-    const dim3 grid((unsigned)((total + 255) / 256)), blk(256);
+    const int64_t per_wg = (256 / WAVE) * (WAVE / producer_lanes_host((int)(group / 8)));
+    const dim3 grid((unsigned)((total + per_wg - 1) / per_wg)), blk(256);
     hipLaunchKernelGGL(quant_int4_group_kernel, grid, blk, 0, stream, w, K, N, group, packed,
                        reinterpret_cast<_Float16*>(scales));
     return launch_status();
