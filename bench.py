@@ -526,6 +526,26 @@ def main():
                               "layer_us": us1["quant"] + us1["gemm"],
                               "note": "latency-bound: 16 quantizer workgroups (one per row), then one 128 x 256 GEMM tile; event-timed"}
     if args.act_steps > 0:
+        # W8A8 with few rows (decode-time batches) at the 4096 x 4096 decode shape, weights
+        # rotated like the decode kernels' so every launch reads W from HBM
+        nk = w2.N * w2.K
+        rot = max(2, math.ceil(ROTATE_BYTES / nk))
+        wsets = [torch.randint(-127, 128, (w2.N, w2.K), dtype=torch.int8, device=dev) for _ in range(rot)]
+        wsc = torch.rand(w2.N, device=dev) * 0.01
+        few = {}
+        for m in (1, 16):
+            xqm = torch.randint(-127, 128, (m, w2.K), dtype=torch.int8, device=dev)
+            xsm = torch.rand(m, device=dev) * 0.01
+            ym = torch.empty((m, w2.N), dtype=torch.float16, device=dev)
+            launches = [ql.prepare("gemm_w8a8_per_channel", xqm, xsm, wq_, wsc, None, ym, F16, m, w2.N, w2.K)
+                        for wq_ in wsets]
+            it = iter(range(10 ** 9))
+            us = _alternate(args.act_steps, {"run": lambda: launches[next(it) % rot]()})["run"]
+            few["m%d" % m] = {"us": us, "GB_per_s": nk / (us * 1e-6) / 1e9}
+        out["w8a8_few_rows"] = {"shape": "M x K4096 x N4096, fp16 out", "weight_sets_rotated": rot, **few,
+                                "note": "M <= 64 runs on the few-row kernel; GB/s counts W's bytes"}
+        del wsets
+    if args.act_steps > 0:
         s_out = torch.full((w3.N,), 0.02, dtype=torch.float32, device=dev)
         yq3 = torch.empty((w3.M, w3.N), dtype=torch.int8, device=dev)
         yqs = torch.empty((w3.M,), dtype=torch.float32, device=dev)

@@ -24,7 +24,7 @@ BUILD = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["capi.cpp", "quant.hip", "gemm_w8a8.hip", "wonly.hip"]
+SOURCES = ["capi.cpp", "quant.hip", "gemm_w8a8.hip", "gemm_w8a8_small.hip", "wonly.hip"]
 PROBE_SOURCES = ["probes.hip"]
 FLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",

@@ -1,0 +1,177 @@
+// gemm_w8a8_small.hip -- the W8A8 layer for a few rows of X (M <= 64: decode-time batches).
+//
+// The same operation as gemm_w8a8.hip (hotelren.com "量化算法的本质", "W8A8矩阵乘法":
+// Y = (x_scale * Xq) @ (w_scale * Wq) + bias; quant67.com ch.17 §四: exact int32 sums, scales,
+// bias and activation in the epilogue), laid out for the case where W's bytes dominate: with
+// few rows the tile kernel has only N / 256 workgroups, far too few to stream W at HBM rate.
+// Here a workgroup owns 16 output columns (N / 16 workgroups), its waves split K, and
+// every byte of W is read once, in 64-byte segments per lane quad:
+//   - lane l loads 16 bytes of line (l >> 2) (a column of W or a row of X) at byte 16 (l & 3)
+//     of a 64-deep k-step, so the four lanes of a quad read one 64-byte segment;
+//   - ds_bpermute moves the words to the matrix core's order, where lane l holds line
+//     (l & 15) and k-chunk (l >> 4) (the k order inside one step is the same for both operands,
+//     which is all the product needs);
+//   - v_mfma_i32_16x16x64_i8 accumulates exactly in int32 for up to four 16-row blocks;
+//   - the waves' sums meet in LDS (int32, exact) and the epilogue writes y.
+#include <stdint.h>
+
+#include "ql_internal.h"
+
+namespace ql {
+namespace {
+
+// SW waves per workgroup, each taking every SW-th group of SU 64-deep k-steps and loading a
+// group at once. With about one workgroup per CU, eight waves of 8-step groups keep the most
+// bytes in flight per CU; with several workgroups per CU, four waves of 16-step groups do
+// (measured: 6.3 against 6.8 us at N = 4096, 11.8 against 15.2 us at N = 11008, M = 16,
+// K = 4096).
+constexpr int SCOLS = 16;   // output columns per workgroup
+
+__device__ inline i32x4 to_mfma_order(i32x4 v, int src_byte) {
+    i32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        r[i] = __builtin_amdgcn_ds_bpermute(src_byte, v[i]);
+    return r;
+}
+
+template <int YMODE, int MB, int ACT, int SW, int SU>
+__global__ __launch_bounds__(64 * SW) void gemm_w8a8_small_kernel(
+    const int8_t* __restrict__ A, const float* __restrict__ xs, const int8_t* __restrict__ B,
+    const float* __restrict__ ws, const float* __restrict__ bias, void* __restrict__ Y, int M, int N,
+    int K) {
+    __shared__ i32x4 red[SW][MB][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n0 = blockIdx.x * SCOLS;
+    // load side: line lane >> 2 at byte (lane & 3) * 16 of each 64-byte step; lines past
+    // the end read the last one (their results are never stored)
+    const int ln = lane >> 2, kc = (lane & 3) * 16;
+    const int8_t* bp = B + (int64_t)min(n0 + ln, N - 1) * K + kc;
+    const int8_t* ap[MB];
+#pragma unroll
+    for (int b = 0; b < MB; ++b)
+        ap[b] = A + (int64_t)min(16 * b + ln, M - 1) * K + kc;
+    const int src = (((lane & 15) << 2) | (lane >> 4)) * 4;
+
+    i32x4 acc[MB];
+#pragma unroll
+    for (int b = 0; b < MB; ++b)
+        acc[b] = i32x4{0, 0, 0, 0};
+    const int S = K / 64;
+    for (int base = wave * SU; base < S; base += SW * SU) {
+        i32x4 wv[SU], xv[MB][SU];
+#pragma unroll
+        for (int u = 0; u < SU; ++u) {
+            if (base + u < S) {
+                wv[u] = *reinterpret_cast<const i32x4*>(bp + (int64_t)(base + u) * 64);
+#pragma unroll
+                for (int b = 0; b < MB; ++b)
+                    xv[b][u] = *reinterpret_cast<const i32x4*>(ap[b] + (int64_t)(base + u) * 64);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < SU; ++u) {
+            if (base + u < S) {   // uniform across the wave: every lane takes part in the permutes
+                const i32x4 bw = to_mfma_order(wv[u], src);
+#pragma unroll
+                for (int b = 0; b < MB; ++b)
+                    acc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(to_mfma_order(xv[b][u], src), bw, acc[b], 0, 0, 0);
+            }
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < MB; ++b)
+        red[wave][b][lane] = acc[b];
+    __syncthreads();
+    if (wave >= MB)
+        return;
+    // wave b finishes row block b: element i of lane l is C[4 (l >> 4) + i][l & 15]
+    const int b = wave;
+    i32x4 t = red[0][b][lane];
+#pragma unroll
+    for (int w = 1; w < SW; ++w)
+        t += red[w][b][lane];
+    const int n = n0 + (lane & 15);
+    if (n >= N)
+        return;
+    float wsn = 0.0f, bn = 0.0f;
+    if constexpr (YMODE != Y_I32) {
+        wsn = ws[n];
+        bn = bias != nullptr ? bias[n] : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int m = 16 * b + 4 * (lane >> 4) + i;
+        if (m >= M)
+            continue;
+        const int64_t o = (int64_t)m * N + n;
+        if constexpr (YMODE == Y_I32) {
+            reinterpret_cast<int32_t*>(Y)[o] = t[i];
+        } else {
+            const float v = activation<ACT>((float)t[i] * xs[m] * wsn + bn);
+            if constexpr (YMODE == Y_F16)
+                reinterpret_cast<_Float16*>(Y)[o] = (_Float16)v;
+            else
+                reinterpret_cast<float*>(Y)[o] = v;
+        }
+    }
+}
+
+template <int YMODE, int ACT, int SW, int SU>
+void launch_mb(const int8_t* xq, const float* xs, const int8_t* wq, const float* ws, const float* bias,
+               void* y, int M, int N, int K, hipStream_t stream) {
+    const dim3 grid((unsigned)((N + SCOLS - 1) / SCOLS)), block(64 * SW);
+    const int mb = (M + 15) / 16;
+#define QL_SMALL(MBV)                                                                                   \
+    hipLaunchKernelGGL((gemm_w8a8_small_kernel<YMODE, MBV, ACT, SW, SU>), grid, block, 0, stream, xq, xs, wq, \
+                       ws, bias, y, M, N, K)
+    if (mb == 1)
+        QL_SMALL(1);
+    else if (mb == 2)
+        QL_SMALL(2);
+    else if (mb == 3)
+        QL_SMALL(3);
+    else
+        QL_SMALL(4);
+#undef QL_SMALL
+}
+
+template <int YMODE, int ACT>
+void launch_shape(const int8_t* xq, const float* xs, const int8_t* wq, const float* ws, const float* bias,
+                  void* y, int M, int N, int K, hipStream_t stream) {
+    const int64_t wgs = (N + SCOLS - 1) / SCOLS;
+    if (wgs > 2 * (int64_t)cu_count())
+        launch_mb<YMODE, ACT, 4, 16>(xq, xs, wq, ws, bias, y, M, N, K, stream);
+    else
+        launch_mb<YMODE, ACT, 8, 8>(xq, xs, wq, ws, bias, y, M, N, K, stream);
+}
+
+template <int YMODE>
+void launch_act(const int8_t* xq, const float* xs, const int8_t* wq, const float* ws, const float* bias,
+                void* y, int act, int M, int N, int K, hipStream_t stream) {
+    if (act == ACT_GELU)
+        launch_shape<YMODE, ACT_GELU>(xq, xs, wq, ws, bias, y, M, N, K, stream);
+    else if (act == ACT_SILU)
+        launch_shape<YMODE, ACT_SILU>(xq, xs, wq, ws, bias, y, M, N, K, stream);
+    else
+        launch_shape<YMODE, ACT_NONE>(xq, xs, wq, ws, bias, y, M, N, K, stream);
+}
+
+}  // namespace
+
+ql_status launch_gemm_w8a8_small(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                                 const float* w_scale, const float* bias, void* y, int y_mode, int act,
+                                 int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+    if (M == 0 || N == 0)
+        return QL_OK;
+    const int m = (int)M, n = (int)N, k = (int)K;
+    if (y_mode == Y_I32)
+        launch_shape<Y_I32, ACT_NONE>(xq, x_scale, wq, w_scale, bias, y, m, n, k, stream);
+    else if (y_mode == Y_F16)
+        launch_act<Y_F16>(xq, x_scale, wq, w_scale, bias, y, act, m, n, k, stream);
+    else
+        launch_act<Y_F32>(xq, x_scale, wq, w_scale, bias, y, act, m, n, k, stream);
+    return launch_status();
+}
+
+}  // namespace ql

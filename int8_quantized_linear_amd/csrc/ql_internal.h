@@ -17,6 +17,21 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int WAVE = 64;
 
+// Compute units of the current device, read once per process (256 on MI355X; 256 if the
+// query fails). Launch shapes use it to size grids.
+inline int cu_count() {
+    static int n = 0;
+    if (n == 0) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            n = v;
+        else
+            n = 256;
+    }
+    return n;
+}
+
 // Launch helpers, one per kernel family. Arguments are already validated; each returns
 // QL_OK or QL_ERR_DEVICE (from hipGetLastError after the launch).
 ql_status launch_quant_rows_i8(const void* x, int x_is_f16, int64_t rows, int64_t K, int8_t* q,
@@ -42,6 +57,10 @@ ql_status launch_gemm_w8a8(const int8_t* xq, const float* x_scale, const int8_t*
                            const float* x_zero, const int32_t* colsum, int64_t M, int64_t N,
                            int64_t K, hipStream_t stream, bool e4m3 = false,
                            const float* out_scale = nullptr, int out_scale_n = 0);
+// The symmetric W8A8 layer for M <= 64 (y_mode F32, F16 or I32; int8 codes only).
+ql_status launch_gemm_w8a8_small(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                                 const float* w_scale, const float* bias, void* y, int y_mode, int act,
+                                 int64_t M, int64_t N, int64_t K, hipStream_t stream);
 ql_status launch_wonly(const void* x, const void* codes, int fmt, const void* scale,
                        const uint8_t* zp, int64_t group, const float* bias, void* y, int64_t M,
                        int64_t N, int64_t K, int act, hipStream_t stream);

@@ -533,19 +533,6 @@ __global__ __launch_bounds__(64 * nwaves<MT>()) void wonly_kernel(
         finish(std::integral_constant<int, ACT_NONE>{});
 }
 
-int cu_count() {
-    static int n = 0;
-    if (n == 0) {
-        int dev = 0, v = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-            n = v;
-        else
-            n = 256;
-    }
-    return n;
-}
-
 template <int FMT, int KS, int MT, int NT, int SCALES>
 ql_status launch_cfg(const void* x, const void* codes, const void* scale, const uint8_t* zp,
                      int64_t group, const float* bias, void* y, int64_t M, int64_t N, int64_t K,

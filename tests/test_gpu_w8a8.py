@@ -303,3 +303,44 @@ def test_requant_with_activation(ql, act, M, N, K):
     assert np.all(np.abs(got - q_ref) <= 1)
     assert np.all((got == q_ref) | near), "codes differ away from a rounding boundary"
     assert near.sum() < 0.01 * near.size
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 64), (1, 4096, 4096), (5, 17, 192), (16, 4096, 4096), (17, 300, 128),
+                                   (33, 1000, 640), (48, 16, 4096), (64, 11008, 4096), (64, 31, 64), (65, 300, 256)])
+def test_few_rows_int32(ql, M, N, K):
+    """M <= 64 runs on the few-row kernel (16 columns per workgroup, K split over four waves,
+    16x16x64 matrix-core steps after a lane permutation): accumulators bit for bit, with
+    codes at the extremes, ragged N, one to 64 k-steps (fewer than the four waves' groups, and
+    more), and M = 65 back on the tile kernel."""
+    rng = np.random.default_rng(M * 7919 + N + K)
+    a = _rand_codes(rng, (M, K), -128)
+    b = _rand_codes(rng, (N, K), -128)
+    a[0, :] = -128
+    b[-1, :] = -128
+    g = Guarded((M, N), torch.int32)
+    ql.gemm_w8a8_int32(dev(a), dev(b), acc=g.view)
+    g.check()
+    assert np.array_equal(host(g.view), oracle.gemm_i32(a, b))
+
+
+@pytest.mark.parametrize("act", ["none", "gelu", "silu"])
+@pytest.mark.parametrize("M,N,K,out", [(1, 4096, 4096, torch.float16), (16, 300, 256, torch.float32),
+                                       (40, 1000, 1024, torch.float16), (64, 257, 192, torch.float32)])
+def test_few_rows_layer(ql, act, M, N, K, out):
+    """The few-row kernel's epilogue (scales, bias, activation; fp32 and fp16) within the same
+    bounds as the tile kernel's."""
+    w = workloads.with_shape(workloads.W8A8_PREFILL, M, K, N)
+    inp, (xq, xs, wq, ws), (xq_r, xs_r, wq_r, ws_r) = _layer(ql, w)
+    g = Guarded((M, N), out)
+    ql.gemm_w8a8_per_channel_act(xq, xs, wq, ws, dev(inp.bias), act, out, y=g.view)
+    g.check()
+    acc = oracle.gemm_i32(xq_r, wq_r)
+    y64 = oracle.epilogue_w8a8(acc, xs_r, ws_r, inp.bias)[1]
+    mag = np.abs(acc.astype(np.float64) * xs_r[:, None] * ws_r[None, :]) + np.abs(inp.bias)[None, :]
+    code = {"none": 0, "gelu": 1, "silu": 2}[act]
+    ref = oracle.activation_f64(y64, code)
+    tol = (1.13 if code else 1.0) * 1e-5 * mag + (2e-6 * np.abs(ref) if code else 0.0)
+    if out == torch.float16:
+        tol = tol + f16_ulp(ref)
+    y = host(g.view).astype(np.float64)
+    assert np.all(np.abs(y - ref) <= tol)
