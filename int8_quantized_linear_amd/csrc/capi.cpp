@@ -12,7 +12,7 @@ constexpr int64_t kMaxKw8a8 = 131008;           // K * 128^2 < 2^31, K % 64 == 0
 constexpr int64_t kMaxNw8a8 = (int64_t)1 << 23; // 32 output rows of 4-byte values: 2^30 bytes
 constexpr int64_t kMaxKwonly = (int64_t)1 << 22; // 64 rows of fp16 X and 64 weight columns < 2^31 bytes
 
-// Up to this many rows of X the symmetric W8A8 layer runs on the few-row kernel
+// Up to this many rows of X the int8 W8A8 calls run on the few-row kernel
 // (gemm_w8a8_small.hip), whose grid grows with N alone.
 constexpr int64_t kSmallM = 64;
 
@@ -149,6 +149,10 @@ ql_status gemm_w8a8_asym(const int8_t* xq, const float* x_scale, const float* x_
     if (!aligned(x_scale, 4) || !aligned(x_zero, 4) || !aligned(w_scale, 4) || !aligned(w_colsum, 4) ||
         (bias && !aligned(bias, 4)))
         return QL_ERR_ALIGN;
+    if (M <= kSmallM)
+        return ql::launch_gemm_w8a8_small(xq, x_scale, wq, w_scale, bias, y,
+                                          y_dtype == QL_F32 ? ql::Y_F32 : ql::Y_F16, (int)act, x_zero,
+                                          w_colsum, nullptr, 0, M, N, K, as_stream(stream));
     return ql::launch_gemm_w8a8(xq, x_scale, wq, w_scale, bias, y,
                                 y_dtype == QL_F32 ? ql::Y_F32 : ql::Y_F16, (int)act, x_zero, w_colsum,
                                 M, N, K, as_stream(stream));
@@ -171,8 +175,8 @@ ql_status gemm_w8a8_per_channel_act(const int8_t* xq, const float* x_scale, cons
         return QL_ERR_ALIGN;
     if (M <= kSmallM)
         return ql::launch_gemm_w8a8_small(xq, x_scale, wq, w_scale, bias, y,
-                                          y_dtype == QL_F32 ? ql::Y_F32 : ql::Y_F16, (int)act, M, N, K,
-                                          as_stream(stream));
+                                          y_dtype == QL_F32 ? ql::Y_F32 : ql::Y_F16, (int)act, nullptr,
+                                          nullptr, nullptr, 0, M, N, K, as_stream(stream));
     return ql::launch_gemm_w8a8(xq, x_scale, wq, w_scale, bias, y,
                                 y_dtype == QL_F32 ? ql::Y_F32 : ql::Y_F16, (int)act, nullptr, nullptr, M, N, K,
                                 as_stream(stream));
@@ -245,6 +249,9 @@ ql_status gemm_w8a8_requant(const int8_t* xq, const float* x_scale, const int8_t
     if (!aligned(x_scale, 4) || !aligned(w_scale, 4) || !aligned(out_scale, 4) ||
         (bias && !aligned(bias, 4)))
         return QL_ERR_ALIGN;
+    if (M <= kSmallM)
+        return ql::launch_gemm_w8a8_small(xq, x_scale, wq, w_scale, bias, yq, ql::Y_I8, (int)act, nullptr,
+                                          nullptr, out_scale, (int)out_scale_n, M, N, K, as_stream(stream));
     return ql::launch_gemm_w8a8(xq, x_scale, wq, w_scale, bias, yq, ql::Y_I8, (int)act, nullptr,
                                 nullptr, M, N, K, as_stream(stream), false, out_scale,
                                 (int)out_scale_n);
@@ -263,8 +270,8 @@ ql_status gemm_w8a8_int32(const int8_t* xq, const int8_t* wq, int32_t* acc, int6
     if (st != QL_OK || M == 0 || N == 0)
         return st;
     if (M <= kSmallM)
-        return ql::launch_gemm_w8a8_small(xq, nullptr, wq, nullptr, nullptr, acc, ql::Y_I32, ql::ACT_NONE, M,
-                                          N, K, as_stream(stream));
+        return ql::launch_gemm_w8a8_small(xq, nullptr, wq, nullptr, nullptr, acc, ql::Y_I32, ql::ACT_NONE,
+                                          nullptr, nullptr, nullptr, 0, M, N, K, as_stream(stream));
     return ql::launch_gemm_w8a8(xq, nullptr, wq, nullptr, nullptr, acc, ql::Y_I32, ql::ACT_NONE, nullptr,
                                 nullptr, M, N, K, as_stream(stream));
 }

@@ -69,12 +69,6 @@ struct EpiArgs {
     int out_scale_n;
 };
 
-// y = ((t * xs) * ws) + b with every operation rounded on its own (no fused multiply-add),
-// the order in which the int8 output's codes are defined.
-__device__ inline float epilogue_unfused(float t, float xs, float ws, float b) {
-#pragma clang fp contract(off)
-    return (t * xs) * ws + b;
-}
 
 // Operand element type: int8 codes (v_mfma_i32_32x32x32_i8, exact int32 sums) or OCP E4M3
 // fp8 codes (v_mfma_f32_32x32x64_f8f6f4, fp32 sums). The bytes move the same way (copies,
@@ -258,10 +252,8 @@ __device__ __forceinline__ void store_tile(const ACC (&acc)[FM][FN], bool has_bi
                 if constexpr (YMODE == Y_I32) {
                     v = acc[i][j][e];
                 } else if constexpr (YMODE == Y_I8) {
-                    const float y = activation<ACT>(epilogue_unfused((float)acc[i][j][e], xsv[e], wsv[j], bv[j]));
-                    const float q0 = y * orv[j];
-                    const float qt = fmaf(fmaf(-q0, osv[j], y), orv[j], q0);
-                    v = (OutT)__builtin_amdgcn_fmed3f(rintf(qt), -127.0f, 127.0f);
+                    v = requant_code(activation<ACT>(epilogue_unfused((float)acc[i][j][e], xsv[e], wsv[j], bv[j])),
+                                     osv[j], orv[j]);
                 } else if constexpr (ASYM) {
                     // sum_k (q_x - z_x) q_w = acc - z_x colsum, with one rounding
                     const float t = fmaf(-zsv[e], csv[j], (float)acc[i][j][e]);

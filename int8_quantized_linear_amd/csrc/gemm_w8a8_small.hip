@@ -1,4 +1,6 @@
-// gemm_w8a8_small.hip -- the W8A8 layer for a few rows of X (M <= 64: decode-time batches).
+// gemm_w8a8_small.hip -- the W8A8 layer for a few rows of X (M <= 64: decode-time batches),
+// with the tile kernel's epilogues: scales and bias (fp32, fp16 or int32 output), zero-point
+// activations, int8 output with static scales, and the fused activations.
 //
 // The same operation as gemm_w8a8.hip (hotelren.com "量化算法的本质", "W8A8矩阵乘法":
 // Y = (x_scale * Xq) @ (w_scale * Wq) + bias; quant67.com ch.17 §四: exact int32 sums, scales,
@@ -35,11 +37,20 @@ __device__ inline i32x4 to_mfma_order(i32x4 v, int src_byte) {
     return r;
 }
 
-template <int YMODE, int MB, int ACT, int SW, int SU>
+// The epilogue's optional terms, as in the tile kernel: the rows' zero points and W's column
+// code sums (asymmetric activations), or the output scales of int8 output.
+struct SmallEpi {
+    const float* x_zero;
+    const int32_t* colsum;
+    const float* out_scale;
+    int out_scale_n;
+};
+
+template <int YMODE, int MB, int ACT, bool ASYM, int SW, int SU>
 __global__ __launch_bounds__(64 * SW) void gemm_w8a8_small_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ xs, const int8_t* __restrict__ B,
     const float* __restrict__ ws, const float* __restrict__ bias, void* __restrict__ Y, int M, int N,
-    int K) {
+    int K, SmallEpi epi) {
     __shared__ i32x4 red[SW][MB][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n0 = blockIdx.x * SCOLS;
@@ -94,10 +105,16 @@ __global__ __launch_bounds__(64 * SW) void gemm_w8a8_small_kernel(
     const int n = n0 + (lane & 15);
     if (n >= N)
         return;
-    float wsn = 0.0f, bn = 0.0f;
+    float wsn = 0.0f, bn = 0.0f, csn = 0.0f, son = 0.0f, orn = 0.0f;
     if constexpr (YMODE != Y_I32) {
         wsn = ws[n];
         bn = bias != nullptr ? bias[n] : 0.0f;
+    }
+    if constexpr (ASYM)
+        csn = (float)epi.colsum[n];   // exact: |sum| <= 128 K < 2^24
+    if constexpr (YMODE == Y_I8) {
+        son = epi.out_scale[epi.out_scale_n == 1 ? 0 : n];
+        orn = 1.0f / son;
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -107,6 +124,17 @@ __global__ __launch_bounds__(64 * SW) void gemm_w8a8_small_kernel(
         const int64_t o = (int64_t)m * N + n;
         if constexpr (YMODE == Y_I32) {
             reinterpret_cast<int32_t*>(Y)[o] = t[i];
+        } else if constexpr (YMODE == Y_I8) {
+            reinterpret_cast<int8_t*>(Y)[o] =
+                requant_code(activation<ACT>(epilogue_unfused((float)t[i], xs[m], wsn, bn)), son, orn);
+        } else if constexpr (ASYM) {
+            // sum_k (q_x - z_x) q_w = acc - z_x colsum, with one rounding
+            const float ta = fmaf(-epi.x_zero[m], csn, (float)t[i]);
+            const float v = activation<ACT>(ta * xs[m] * wsn + bn);
+            if constexpr (YMODE == Y_F16)
+                reinterpret_cast<_Float16*>(Y)[o] = (_Float16)v;
+            else
+                reinterpret_cast<float*>(Y)[o] = v;
         } else {
             const float v = activation<ACT>((float)t[i] * xs[m] * wsn + bn);
             if constexpr (YMODE == Y_F16)
@@ -117,14 +145,14 @@ __global__ __launch_bounds__(64 * SW) void gemm_w8a8_small_kernel(
     }
 }
 
-template <int YMODE, int ACT, int SW, int SU>
+template <int YMODE, int ACT, bool ASYM, int SW, int SU>
 void launch_mb(const int8_t* xq, const float* xs, const int8_t* wq, const float* ws, const float* bias,
-               void* y, int M, int N, int K, hipStream_t stream) {
+               void* y, int M, int N, int K, SmallEpi epi, hipStream_t stream) {
     const dim3 grid((unsigned)((N + SCOLS - 1) / SCOLS)), block(64 * SW);
     const int mb = (M + 15) / 16;
-#define QL_SMALL(MBV)                                                                                   \
-    hipLaunchKernelGGL((gemm_w8a8_small_kernel<YMODE, MBV, ACT, SW, SU>), grid, block, 0, stream, xq, xs, wq, \
-                       ws, bias, y, M, N, K)
+#define QL_SMALL(MBV)                                                                                         \
+    hipLaunchKernelGGL((gemm_w8a8_small_kernel<YMODE, MBV, ACT, ASYM, SW, SU>), grid, block, 0, stream, xq, xs, \
+                       wq, ws, bias, y, M, N, K, epi)
     if (mb == 1)
         QL_SMALL(1);
     else if (mb == 2)
@@ -136,41 +164,47 @@ void launch_mb(const int8_t* xq, const float* xs, const int8_t* wq, const float*
 #undef QL_SMALL
 }
 
-template <int YMODE, int ACT>
+template <int YMODE, int ACT, bool ASYM>
 void launch_shape(const int8_t* xq, const float* xs, const int8_t* wq, const float* ws, const float* bias,
-                  void* y, int M, int N, int K, hipStream_t stream) {
+                  void* y, int M, int N, int K, SmallEpi epi, hipStream_t stream) {
     const int64_t wgs = (N + SCOLS - 1) / SCOLS;
     if (wgs > 2 * (int64_t)cu_count())
-        launch_mb<YMODE, ACT, 4, 16>(xq, xs, wq, ws, bias, y, M, N, K, stream);
+        launch_mb<YMODE, ACT, ASYM, 4, 16>(xq, xs, wq, ws, bias, y, M, N, K, epi, stream);
     else
-        launch_mb<YMODE, ACT, 8, 8>(xq, xs, wq, ws, bias, y, M, N, K, stream);
+        launch_mb<YMODE, ACT, ASYM, 8, 8>(xq, xs, wq, ws, bias, y, M, N, K, epi, stream);
 }
 
-template <int YMODE>
+template <int YMODE, bool ASYM>
 void launch_act(const int8_t* xq, const float* xs, const int8_t* wq, const float* ws, const float* bias,
-                void* y, int act, int M, int N, int K, hipStream_t stream) {
+                void* y, int act, int M, int N, int K, SmallEpi epi, hipStream_t stream) {
     if (act == ACT_GELU)
-        launch_shape<YMODE, ACT_GELU>(xq, xs, wq, ws, bias, y, M, N, K, stream);
+        launch_shape<YMODE, ACT_GELU, ASYM>(xq, xs, wq, ws, bias, y, M, N, K, epi, stream);
     else if (act == ACT_SILU)
-        launch_shape<YMODE, ACT_SILU>(xq, xs, wq, ws, bias, y, M, N, K, stream);
+        launch_shape<YMODE, ACT_SILU, ASYM>(xq, xs, wq, ws, bias, y, M, N, K, epi, stream);
     else
-        launch_shape<YMODE, ACT_NONE>(xq, xs, wq, ws, bias, y, M, N, K, stream);
+        launch_shape<YMODE, ACT_NONE, ASYM>(xq, xs, wq, ws, bias, y, M, N, K, epi, stream);
 }
 
 }  // namespace
 
 ql_status launch_gemm_w8a8_small(const int8_t* xq, const float* x_scale, const int8_t* wq,
                                  const float* w_scale, const float* bias, void* y, int y_mode, int act,
-                                 int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+                                 const float* x_zero, const int32_t* colsum, const float* out_scale,
+                                 int out_scale_n, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
     if (M == 0 || N == 0)
         return QL_OK;
     const int m = (int)M, n = (int)N, k = (int)K;
+    const SmallEpi epi{x_zero, colsum, out_scale, out_scale_n};
     if (y_mode == Y_I32)
-        launch_shape<Y_I32, ACT_NONE>(xq, x_scale, wq, w_scale, bias, y, m, n, k, stream);
-    else if (y_mode == Y_F16)
-        launch_act<Y_F16>(xq, x_scale, wq, w_scale, bias, y, act, m, n, k, stream);
+        launch_shape<Y_I32, ACT_NONE, false>(xq, x_scale, wq, w_scale, bias, y, m, n, k, epi, stream);
+    else if (y_mode == Y_I8)
+        launch_act<Y_I8, false>(xq, x_scale, wq, w_scale, bias, y, act, m, n, k, epi, stream);
+    else if (x_zero != nullptr)
+        (y_mode == Y_F16 ? launch_act<Y_F16, true> : launch_act<Y_F32, true>)(xq, x_scale, wq, w_scale, bias, y,
+                                                                             act, m, n, k, epi, stream);
     else
-        launch_act<Y_F32>(xq, x_scale, wq, w_scale, bias, y, act, m, n, k, stream);
+        (y_mode == Y_F16 ? launch_act<Y_F16, false> : launch_act<Y_F32, false>)(xq, x_scale, wq, w_scale, bias,
+                                                                               y, act, m, n, k, epi, stream);
     return launch_status();
 }
 

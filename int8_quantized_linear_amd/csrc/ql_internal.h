@@ -17,6 +17,21 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int WAVE = 64;
 
+// y = ((t * xs) * ws) + b with every operation rounded on its own (no fused multiply-add),
+// the order in which the int8 output's codes are defined.
+__device__ inline float epilogue_unfused(float t, float xs, float ws, float b) {
+#pragma clang fp contract(off)
+    return (t * xs) * ws + b;
+}
+
+// int8 code of y with output scale s and r = RN(1 / s): the correctly rounded quotient y / s
+// as q0 = RN(y r), RN(q0 + fma(-q0, s, y) r), then RNE and the [-127, 127] clamp.
+__device__ inline int8_t requant_code(float y, float s, float r) {
+    const float q0 = y * r;
+    const float qt = fmaf(fmaf(-q0, s, y), r, q0);
+    return (int8_t)__builtin_amdgcn_fmed3f(rintf(qt), -127.0f, 127.0f);
+}
+
 // Compute units of the current device, read once per process (256 on MI355X; 256 if the
 // query fails). Launch shapes use it to size grids.
 inline int cu_count() {
@@ -57,10 +72,12 @@ ql_status launch_gemm_w8a8(const int8_t* xq, const float* x_scale, const int8_t*
                            const float* x_zero, const int32_t* colsum, int64_t M, int64_t N,
                            int64_t K, hipStream_t stream, bool e4m3 = false,
                            const float* out_scale = nullptr, int out_scale_n = 0);
-// The symmetric W8A8 layer for M <= 64 (y_mode F32, F16 or I32; int8 codes only).
+// The W8A8 layer for M <= 64 (int8 codes): y_mode F32, F16 (with zero points when x_zero
+// and colsum are given), I32, or I8 (out_scale_n = 1 or N output scales).
 ql_status launch_gemm_w8a8_small(const int8_t* xq, const float* x_scale, const int8_t* wq,
                                  const float* w_scale, const float* bias, void* y, int y_mode, int act,
-                                 int64_t M, int64_t N, int64_t K, hipStream_t stream);
+                                 const float* x_zero, const int32_t* colsum, const float* out_scale,
+                                 int out_scale_n, int64_t M, int64_t N, int64_t K, hipStream_t stream);
 ql_status launch_wonly(const void* x, const void* codes, int fmt, const void* scale,
                        const uint8_t* zp, int64_t group, const float* bias, void* y, int64_t M,
                        int64_t N, int64_t K, int act, hipStream_t stream);

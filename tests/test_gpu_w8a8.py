@@ -196,7 +196,7 @@ def test_fused_activation_none_is_plain(ql):
     assert np.array_equal(y0.view(np.uint16), y1.view(np.uint16))
 
 
-@pytest.mark.parametrize("M,N,K,out,act", [(16, 256, 256, torch.float32, "none"), (300, 520, 384, torch.float16, "none"),
+@pytest.mark.parametrize("M,N,K,out,act", [(1, 4096, 4096, torch.float16, "none"), (33, 520, 384, torch.float32, "gelu"), (16, 256, 256, torch.float32, "none"), (300, 520, 384, torch.float16, "none"),
                                            (257, 129, 192, torch.float32, "gelu"), (2000, 8300, 64, torch.float16, "silu"),
                                            (2048, 11008, 4096, torch.float16, "none")])
 def test_asymmetric_layer(ql, M, N, K, out, act):
@@ -266,7 +266,8 @@ def _requant_case(ql, M, N, K, per_tensor, seed_shift=0):
     return inp, rows, xq, xs, wq, ws, s_out, y32
 
 
-@pytest.mark.parametrize("M,N,K,per_tensor", [(16, 256, 256, False), (16, 256, 256, True), (300, 520, 384, False),
+@pytest.mark.parametrize("M,N,K,per_tensor", [(1, 4096, 4096, False), (40, 1000, 640, True), (64, 257, 192, False),
+                                              (16, 256, 256, False), (16, 256, 256, True), (300, 520, 384, False),
                                               (257, 129, 192, True), (128, 1000, 128, False),
                                               (2000, 8300, 256, False), (2048, 11008, 4096, True)])
 def test_requant_bit_exact(ql, M, N, K, per_tensor):
