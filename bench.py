@@ -524,7 +524,8 @@ def main():
             "gemm": ql.prepare("gemm_w8a8_per_channel", xq1, xs1, wq1, ws1, b1, y1, 0, w1.M, w1.N, w1.K)})
         out["small_layer"] = {"workload": w1.name, "quant_us": us1["quant"], "gemm_us": us1["gemm"],
                               "layer_us": us1["quant"] + us1["gemm"],
-                              "note": "latency-bound: 16 quantizer workgroups (one per row), then one 128 x 256 GEMM tile; event-timed"}
+                              "note": "latency-bound: 16 quantizer workgroups (one per row), then the few-row GEMM kernel "
+                                      "(16 workgroups of 16 columns); event-timed"}
     if args.act_steps > 0:
         # W8A8 with few rows (decode-time batches) at the 4096 x 4096 decode shape, weights
         # rotated like the decode kernels' so every launch reads W from HBM
@@ -543,7 +544,8 @@ def main():
             us = _alternate(args.act_steps, {"run": lambda: launches[next(it) % rot]()})["run"]
             few["m%d" % m] = {"us": us, "GB_per_s": nk / (us * 1e-6) / 1e9}
         out["w8a8_few_rows"] = {"shape": "M x K4096 x N4096, fp16 out", "weight_sets_rotated": rot, **few,
-                                "note": "M <= 64 runs on the few-row kernel; GB/s counts W's bytes"}
+                                "note": "M <= 64 runs on the few-row kernel; GB/s counts W's bytes; timed after "
+                                        "the GEMM runs above, whose power draw can leave the clock lower"}
         del wsets
     if args.act_steps > 0:
         s_out = torch.full((w3.N,), 0.02, dtype=torch.float32, device=dev)
