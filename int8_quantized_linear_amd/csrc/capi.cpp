@@ -14,7 +14,7 @@ constexpr int64_t kMaxKwonly = (int64_t)1 << 22; // 64 rows of fp16 X and 64 wei
 
 // Up to this many rows of X the int8 W8A8 calls run on the few-row kernel
 // (gemm_w8a8_small.hip), whose grid grows with N alone.
-constexpr int64_t kSmallM = 64;
+constexpr int64_t kSmallM = 128;
 
 inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 

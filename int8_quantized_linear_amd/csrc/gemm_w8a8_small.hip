@@ -1,4 +1,4 @@
-// gemm_w8a8_small.hip -- the W8A8 layer for a few rows of X (M <= 64: decode-time batches),
+// gemm_w8a8_small.hip -- the W8A8 layer for a few rows of X (M <= 128: decode-time batches),
 // with the tile kernel's epilogues: scales and bias (fp32, fp16 or int32 output), zero-point
 // activations, int8 output with static scales, and the fused activations.
 //
@@ -13,7 +13,7 @@
 //   - ds_bpermute moves the words to the matrix core's order, where lane l holds line
 //     (l & 15) and k-chunk (l >> 4) (the k order inside one step is the same for both operands,
 //     which is all the product needs);
-//   - v_mfma_i32_16x16x64_i8 accumulates exactly in int32 for up to four 16-row blocks;
+//   - v_mfma_i32_16x16x64_i8 accumulates exactly in int32 for up to eight 16-row blocks;
 //   - the waves' sums meet in LDS (int32, exact) and the epilogue writes y.
 #include <stdint.h>
 
@@ -94,14 +94,6 @@ __global__ __launch_bounds__(64 * SW) void gemm_w8a8_small_kernel(
     for (int b = 0; b < MB; ++b)
         red[wave][b][lane] = acc[b];
     __syncthreads();
-    if (wave >= MB)
-        return;
-    // wave b finishes row block b: element i of lane l is C[4 (l >> 4) + i][l & 15]
-    const int b = wave;
-    i32x4 t = red[0][b][lane];
-#pragma unroll
-    for (int w = 1; w < SW; ++w)
-        t += red[w][b][lane];
     const int n = n0 + (lane & 15);
     if (n >= N)
         return;
@@ -116,6 +108,12 @@ __global__ __launch_bounds__(64 * SW) void gemm_w8a8_small_kernel(
         son = epi.out_scale[epi.out_scale_n == 1 ? 0 : n];
         orn = 1.0f / son;
     }
+    // wave w finishes row blocks w, w + SW, ...: element i of lane l is C[4 (l >> 4) + i][l & 15]
+    for (int b = wave; b < MB; b += SW) {
+    i32x4 t = red[0][b][lane];
+#pragma unroll
+    for (int w = 1; w < SW; ++w)
+        t += red[w][b][lane];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int m = 16 * b + 4 * (lane >> 4) + i;
@@ -143,6 +141,7 @@ __global__ __launch_bounds__(64 * SW) void gemm_w8a8_small_kernel(
                 reinterpret_cast<float*>(Y)[o] = v;
         }
     }
+    }
 }
 
 template <int YMODE, int ACT, bool ASYM, int SW, int SU>
@@ -164,11 +163,30 @@ void launch_mb(const int8_t* xq, const float* xs, const int8_t* wq, const float*
 #undef QL_SMALL
 }
 
+// 65 to 128 rows: eight row blocks, with four waves of 4-step groups (X's registers and the
+// LDS reduction stay within limits).
+template <int YMODE, int ACT, bool ASYM>
+void launch_mb8(const int8_t* xq, const float* xs, const int8_t* wq, const float* ws, const float* bias,
+                void* y, int M, int N, int K, SmallEpi epi, hipStream_t stream) {
+    const dim3 grid((unsigned)((N + SCOLS - 1) / SCOLS)), block(64 * 4);
+    const int mb = (M + 15) / 16;
+#define QL_SMALL8(MBV)                                                                                    \
+    hipLaunchKernelGGL((gemm_w8a8_small_kernel<YMODE, MBV, ACT, ASYM, 4, 4>), grid, block, 0, stream, xq, xs, \
+                       wq, ws, bias, y, M, N, K, epi)
+    if (mb <= 6)
+        QL_SMALL8(6);
+    else
+        QL_SMALL8(8);
+#undef QL_SMALL8
+}
+
 template <int YMODE, int ACT, bool ASYM>
 void launch_shape(const int8_t* xq, const float* xs, const int8_t* wq, const float* ws, const float* bias,
                   void* y, int M, int N, int K, SmallEpi epi, hipStream_t stream) {
     const int64_t wgs = (N + SCOLS - 1) / SCOLS;
-    if (wgs > 2 * (int64_t)cu_count())
+    if (M > 64)
+        launch_mb8<YMODE, ACT, ASYM>(xq, xs, wq, ws, bias, y, M, N, K, epi, stream);
+    else if (wgs > 2 * (int64_t)cu_count())
         launch_mb<YMODE, ACT, ASYM, 4, 16>(xq, xs, wq, ws, bias, y, M, N, K, epi, stream);
     else
         launch_mb<YMODE, ACT, ASYM, 8, 8>(xq, xs, wq, ws, bias, y, M, N, K, epi, stream);

@@ -307,12 +307,13 @@ def test_requant_with_activation(ql, act, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 64), (1, 4096, 4096), (5, 17, 192), (16, 4096, 4096), (17, 300, 128),
-                                   (33, 1000, 640), (48, 16, 4096), (64, 11008, 4096), (64, 31, 64), (65, 300, 256)])
+                                   (33, 1000, 640), (48, 16, 4096), (64, 11008, 4096), (64, 31, 64), (65, 300, 256),
+                                   (96, 1000, 640), (100, 17, 64), (128, 4096, 4096), (129, 300, 256)])
 def test_few_rows_int32(ql, M, N, K):
-    """M <= 64 runs on the few-row kernel (16 columns per workgroup, K split over four waves,
-    16x16x64 matrix-core steps after a lane permutation): accumulators bit for bit, with
-    codes at the extremes, ragged N, one to 64 k-steps (fewer than the four waves' groups, and
-    more), and M = 65 back on the tile kernel."""
+    """M <= 128 runs on the few-row kernel (16 columns per workgroup, K split over the waves,
+    16x16x64 matrix-core steps after a lane permutation; up to four row blocks with two wave
+    shapes, five to eight with a third): accumulators bit for bit, with codes at the extremes,
+    ragged N, one to 64 k-steps, and M = 129 back on the tile kernel."""
     rng = np.random.default_rng(M * 7919 + N + K)
     a = _rand_codes(rng, (M, K), -128)
     b = _rand_codes(rng, (N, K), -128)
@@ -326,7 +327,8 @@ def test_few_rows_int32(ql, M, N, K):
 
 @pytest.mark.parametrize("act", ["none", "gelu", "silu"])
 @pytest.mark.parametrize("M,N,K,out", [(1, 4096, 4096, torch.float16), (16, 300, 256, torch.float32),
-                                       (40, 1000, 1024, torch.float16), (64, 257, 192, torch.float32)])
+                                       (40, 1000, 1024, torch.float16), (64, 257, 192, torch.float32),
+                                       (128, 600, 256, torch.float16)])
 def test_few_rows_layer(ql, act, M, N, K, out):
     """The few-row kernel's epilogue (scales, bias, activation; fp32 and fp16) within the same
     bounds as the tile kernel's."""
