@@ -109,38 +109,36 @@ __global__ __launch_bounds__(64 * SW) void gemm_w8a8_small_kernel(
         orn = 1.0f / son;
     }
     // wave w finishes row blocks w, w + SW, ...: element i of lane l is C[4 (l >> 4) + i][l & 15]
+    auto put_float = [&](int64_t o, float v) {
+        if constexpr (YMODE == Y_F16)
+            reinterpret_cast<_Float16*>(Y)[o] = (_Float16)v;
+        else
+            reinterpret_cast<float*>(Y)[o] = v;
+    };
     for (int b = wave; b < MB; b += SW) {
-    i32x4 t = red[0][b][lane];
+        i32x4 t = red[0][b][lane];
 #pragma unroll
-    for (int w = 1; w < SW; ++w)
-        t += red[w][b][lane];
+        for (int w = 1; w < SW; ++w)
+            t += red[w][b][lane];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int m = 16 * b + 4 * (lane >> 4) + i;
-        if (m >= M)
-            continue;
-        const int64_t o = (int64_t)m * N + n;
-        if constexpr (YMODE == Y_I32) {
-            reinterpret_cast<int32_t*>(Y)[o] = t[i];
-        } else if constexpr (YMODE == Y_I8) {
-            reinterpret_cast<int8_t*>(Y)[o] =
-                requant_code(activation<ACT>(epilogue_unfused((float)t[i], xs[m], wsn, bn)), son, orn);
-        } else if constexpr (ASYM) {
-            // sum_k (q_x - z_x) q_w = acc - z_x colsum, with one rounding
-            const float ta = fmaf(-epi.x_zero[m], csn, (float)t[i]);
-            const float v = activation<ACT>(ta * xs[m] * wsn + bn);
-            if constexpr (YMODE == Y_F16)
-                reinterpret_cast<_Float16*>(Y)[o] = (_Float16)v;
-            else
-                reinterpret_cast<float*>(Y)[o] = v;
-        } else {
-            const float v = activation<ACT>((float)t[i] * xs[m] * wsn + bn);
-            if constexpr (YMODE == Y_F16)
-                reinterpret_cast<_Float16*>(Y)[o] = (_Float16)v;
-            else
-                reinterpret_cast<float*>(Y)[o] = v;
+        for (int i = 0; i < 4; ++i) {
+            const int m = 16 * b + 4 * (lane >> 4) + i;
+            if (m >= M)
+                continue;
+            const int64_t o = (int64_t)m * N + n;
+            if constexpr (YMODE == Y_I32) {
+                reinterpret_cast<int32_t*>(Y)[o] = t[i];
+            } else if constexpr (YMODE == Y_I8) {
+                reinterpret_cast<int8_t*>(Y)[o] =
+                    requant_code(activation<ACT>(epilogue_unfused((float)t[i], xs[m], wsn, bn)), son, orn);
+            } else if constexpr (ASYM) {
+                // sum_k (q_x - z_x) q_w = acc - z_x colsum, with one rounding
+                const float ta = fmaf(-epi.x_zero[m], csn, (float)t[i]);
+                put_float(o, activation<ACT>(ta * xs[m] * wsn + bn));
+            } else {
+                put_float(o, activation<ACT>((float)t[i] * xs[m] * wsn + bn));
+            }
         }
-    }
     }
 }
 
