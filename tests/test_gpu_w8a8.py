@@ -33,8 +33,8 @@ def _rand_codes(rng, shape, lo=-127):
                                    (100, 1000, 384), (128, 300, 128), (64, 256, 640), (127, 513, 256)])
 def test_int32_bit_exact(ql, M, N, K):
     """Several tiles in M and N, ragged tails, K with a half k-tile tail, codes including -128.
-    M <= 128 runs every tile at half height (K split between the workgroup's two wave
-    groups), with 1, 2, 3 and 5 128-deep stages."""
+    M <= 128 runs on the few-row kernel, larger M on the tile kernel (whose half-height
+    tiles appear in the mixed plans below), with 1, 2, 3 and 5 128-deep stages."""
     rng = np.random.default_rng(M * 1000 + N + K)
     a = _rand_codes(rng, (M, K), -128)
     b = _rand_codes(rng, (N, K), -128)
