@@ -834,8 +834,10 @@ TilePlan plan_tiles(int64_t M, int64_t N) {
     const int tm = (int)((M + 255) / 256), tn = (int)((N + 255) / 256);
     const int total = tm * tn, cus = cu_count();
     int small_panels = 0;
-    if (M <= 128) {
-        small_panels = tn;                      // every tile is half height
+    if (M <= 128 || 2 * total <= cus) {
+        // every tile is half height: with at most half the CUs' worth of big tiles, half
+        // tiles (K split between the two wave groups) put twice as many CUs to work
+        small_panels = tn;
     } else if (total > cus) {
         const int left = total % cus;           // tiles of the last, partial round
         if (left > 0 && left <= cus / 2)
