@@ -226,6 +226,10 @@ ql_status gemm_e4m3_per_channel(const uint8_t* xq, const float* x_scale, const u
         return QL_ERR_NULL;
     if (!aligned(x_scale, 4) || !aligned(w_scale, 4) || (bias && !aligned(bias, 4)))
         return QL_ERR_ALIGN;
+    if (M <= kSmallM)
+        return ql::launch_gemm_w8a8_small(xc, x_scale, wc, w_scale, bias, y,
+                                          y_dtype == QL_F32 ? ql::Y_F32 : ql::Y_F16, (int)act, nullptr,
+                                          nullptr, nullptr, 0, M, N, K, as_stream(stream), true);
     return ql::launch_gemm_w8a8(xc, x_scale, wc, w_scale, bias, y,
                                 y_dtype == QL_F32 ? ql::Y_F32 : ql::Y_F16, (int)act, nullptr, nullptr, M, N, K,
                                 as_stream(stream), true);

@@ -1,6 +1,7 @@
 // gemm_w8a8_small.hip -- the W8A8 layer for a few rows of X (M <= 128: decode-time batches),
 // with the tile kernel's epilogues: scales and bias (fp32, fp16 or int32 output), zero-point
-// activations, int8 output with static scales, and the fused activations.
+// activations, int8 output with static scales, and the fused activations; and the same layer
+// with OCP E4M3 fp8 codes.
 //
 // The same operation as gemm_w8a8.hip (hotelren.com "量化算法的本质", "W8A8矩阵乘法":
 // Y = (x_scale * Xq) @ (w_scale * Wq) + bias; quant67.com ch.17 §四: exact int32 sums, scales,
@@ -29,6 +30,17 @@ namespace {
 // K = 4096).
 constexpr int SCOLS = 16;   // output columns per workgroup
 
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4s __attribute__((ext_vector_type(4)));
+
+// Operand codes: int8 (exact int32 sums) or OCP E4M3 fp8 (fp32 sums; one 16x16x128 fp8 step
+// takes the permuted fragments of two consecutive 64-deep steps, a missing second step being
+// zero codes, and E4M3 code 0 is +0).
+template <bool FP8>
+using SmallAcc = typename std::conditional<FP8, f32x4s, i32x4>::type;
+
+__device__ inline i32x8 cat8s(i32x4 lo, i32x4 hi) { return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7); }
+
 __device__ inline i32x4 to_mfma_order(i32x4 v, int src_byte) {
     i32x4 r;
 #pragma unroll
@@ -46,12 +58,13 @@ struct SmallEpi {
     int out_scale_n;
 };
 
-template <int YMODE, int MB, int ACT, bool ASYM, int SW, int SU>
+template <int YMODE, int MB, int ACT, bool ASYM, int SW, int SU, bool FP8>
 __global__ __launch_bounds__(64 * SW) void gemm_w8a8_small_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ xs, const int8_t* __restrict__ B,
     const float* __restrict__ ws, const float* __restrict__ bias, void* __restrict__ Y, int M, int N,
     int K, SmallEpi epi) {
-    __shared__ i32x4 red[SW][MB][64];
+    using Acc = SmallAcc<FP8>;
+    __shared__ Acc red[SW][MB][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n0 = blockIdx.x * SCOLS;
     // load side: line lane >> 2 at byte (lane & 3) * 16 of each 64-byte step; lines past
@@ -64,10 +77,10 @@ __global__ __launch_bounds__(64 * SW) void gemm_w8a8_small_kernel(
         ap[b] = A + (int64_t)min(16 * b + ln, M - 1) * K + kc;
     const int src = (((lane & 15) << 2) | (lane >> 4)) * 4;
 
-    i32x4 acc[MB];
+    Acc acc[MB];
 #pragma unroll
     for (int b = 0; b < MB; ++b)
-        acc[b] = i32x4{0, 0, 0, 0};
+        acc[b] = Acc{0, 0, 0, 0};
     const int S = K / 64;
     for (int base = wave * SU; base < S; base += SW * SU) {
         i32x4 wv[SU], xv[MB][SU];
@@ -80,13 +93,31 @@ __global__ __launch_bounds__(64 * SW) void gemm_w8a8_small_kernel(
                     xv[b][u] = *reinterpret_cast<const i32x4*>(ap[b] + (int64_t)(base + u) * 64);
             }
         }
+        // the conditions below are uniform across the wave: every lane takes part in the permutes
+        if constexpr (FP8) {
+            const i32x4 zero{0, 0, 0, 0};
 #pragma unroll
-        for (int u = 0; u < SU; ++u) {
-            if (base + u < S) {   // uniform across the wave: every lane takes part in the permutes
-                const i32x4 bw = to_mfma_order(wv[u], src);
+            for (int u = 0; u < SU; u += 2) {
+                if (base + u < S) {
+                    const bool two = base + u + 1 < S;
+                    const i32x8 bw = cat8s(to_mfma_order(wv[u], src), two ? to_mfma_order(wv[u + 1], src) : zero);
 #pragma unroll
-                for (int b = 0; b < MB; ++b)
-                    acc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(to_mfma_order(xv[b][u], src), bw, acc[b], 0, 0, 0);
+                    for (int b = 0; b < MB; ++b) {
+                        const i32x8 aw = cat8s(to_mfma_order(xv[b][u], src),
+                                               two ? to_mfma_order(xv[b][u + 1], src) : zero);
+                        acc[b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aw, bw, acc[b], 0, 0, 0, 0, 0, 0);
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < SU; ++u) {
+                if (base + u < S) {
+                    const i32x4 bw = to_mfma_order(wv[u], src);
+#pragma unroll
+                    for (int b = 0; b < MB; ++b)
+                        acc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(to_mfma_order(xv[b][u], src), bw, acc[b], 0, 0, 0);
+                }
             }
         }
     }
@@ -116,7 +147,7 @@ __global__ __launch_bounds__(64 * SW) void gemm_w8a8_small_kernel(
             reinterpret_cast<float*>(Y)[o] = v;
     };
     for (int b = wave; b < MB; b += SW) {
-        i32x4 t = red[0][b][lane];
+        Acc t = red[0][b][lane];
 #pragma unroll
         for (int w = 1; w < SW; ++w)
             t += red[w][b][lane];
@@ -142,14 +173,14 @@ __global__ __launch_bounds__(64 * SW) void gemm_w8a8_small_kernel(
     }
 }
 
-template <int YMODE, int ACT, bool ASYM, int SW, int SU>
+template <int YMODE, int ACT, bool ASYM, int SW, int SU, bool FP8>
 void launch_mb(const int8_t* xq, const float* xs, const int8_t* wq, const float* ws, const float* bias,
                void* y, int M, int N, int K, SmallEpi epi, hipStream_t stream) {
     const dim3 grid((unsigned)((N + SCOLS - 1) / SCOLS)), block(64 * SW);
     const int mb = (M + 15) / 16;
 #define QL_SMALL(MBV)                                                                                         \
-    hipLaunchKernelGGL((gemm_w8a8_small_kernel<YMODE, MBV, ACT, ASYM, SW, SU>), grid, block, 0, stream, xq, xs, \
-                       wq, ws, bias, y, M, N, K, epi)
+    hipLaunchKernelGGL((gemm_w8a8_small_kernel<YMODE, MBV, ACT, ASYM, SW, SU, FP8>), grid, block, 0, stream, xq, \
+                       xs, wq, ws, bias, y, M, N, K, epi)
     if (mb == 1)
         QL_SMALL(1);
     else if (mb == 2)
@@ -163,13 +194,13 @@ void launch_mb(const int8_t* xq, const float* xs, const int8_t* wq, const float*
 
 // 65 to 128 rows: eight row blocks, with four waves of 4-step groups (X's registers and the
 // LDS reduction stay within limits).
-template <int YMODE, int ACT, bool ASYM>
+template <int YMODE, int ACT, bool ASYM, bool FP8>
 void launch_mb8(const int8_t* xq, const float* xs, const int8_t* wq, const float* ws, const float* bias,
                 void* y, int M, int N, int K, SmallEpi epi, hipStream_t stream) {
     const dim3 grid((unsigned)((N + SCOLS - 1) / SCOLS)), block(64 * 4);
     const int mb = (M + 15) / 16;
 #define QL_SMALL8(MBV)                                                                                    \
-    hipLaunchKernelGGL((gemm_w8a8_small_kernel<YMODE, MBV, ACT, ASYM, 4, 4>), grid, block, 0, stream, xq, xs, \
+    hipLaunchKernelGGL((gemm_w8a8_small_kernel<YMODE, MBV, ACT, ASYM, 4, 4, FP8>), grid, block, 0, stream, xq, xs, \
                        wq, ws, bias, y, M, N, K, epi)
     if (mb <= 6)
         QL_SMALL8(6);
@@ -178,27 +209,27 @@ void launch_mb8(const int8_t* xq, const float* xs, const int8_t* wq, const float
 #undef QL_SMALL8
 }
 
-template <int YMODE, int ACT, bool ASYM>
+template <int YMODE, int ACT, bool ASYM, bool FP8>
 void launch_shape(const int8_t* xq, const float* xs, const int8_t* wq, const float* ws, const float* bias,
                   void* y, int M, int N, int K, SmallEpi epi, hipStream_t stream) {
     const int64_t wgs = (N + SCOLS - 1) / SCOLS;
     if (M > 64)
-        launch_mb8<YMODE, ACT, ASYM>(xq, xs, wq, ws, bias, y, M, N, K, epi, stream);
+        launch_mb8<YMODE, ACT, ASYM, FP8>(xq, xs, wq, ws, bias, y, M, N, K, epi, stream);
     else if (wgs > 2 * (int64_t)cu_count())
-        launch_mb<YMODE, ACT, ASYM, 4, 16>(xq, xs, wq, ws, bias, y, M, N, K, epi, stream);
+        launch_mb<YMODE, ACT, ASYM, 4, 16, FP8>(xq, xs, wq, ws, bias, y, M, N, K, epi, stream);
     else
-        launch_mb<YMODE, ACT, ASYM, 8, 8>(xq, xs, wq, ws, bias, y, M, N, K, epi, stream);
+        launch_mb<YMODE, ACT, ASYM, 8, 8, FP8>(xq, xs, wq, ws, bias, y, M, N, K, epi, stream);
 }
 
-template <int YMODE, bool ASYM>
+template <int YMODE, bool ASYM, bool FP8 = false>
 void launch_act(const int8_t* xq, const float* xs, const int8_t* wq, const float* ws, const float* bias,
                 void* y, int act, int M, int N, int K, SmallEpi epi, hipStream_t stream) {
     if (act == ACT_GELU)
-        launch_shape<YMODE, ACT_GELU, ASYM>(xq, xs, wq, ws, bias, y, M, N, K, epi, stream);
+        launch_shape<YMODE, ACT_GELU, ASYM, FP8>(xq, xs, wq, ws, bias, y, M, N, K, epi, stream);
     else if (act == ACT_SILU)
-        launch_shape<YMODE, ACT_SILU, ASYM>(xq, xs, wq, ws, bias, y, M, N, K, epi, stream);
+        launch_shape<YMODE, ACT_SILU, ASYM, FP8>(xq, xs, wq, ws, bias, y, M, N, K, epi, stream);
     else
-        launch_shape<YMODE, ACT_NONE, ASYM>(xq, xs, wq, ws, bias, y, M, N, K, epi, stream);
+        launch_shape<YMODE, ACT_NONE, ASYM, FP8>(xq, xs, wq, ws, bias, y, M, N, K, epi, stream);
 }
 
 }  // namespace
@@ -206,13 +237,19 @@ void launch_act(const int8_t* xq, const float* xs, const int8_t* wq, const float
 ql_status launch_gemm_w8a8_small(const int8_t* xq, const float* x_scale, const int8_t* wq,
                                  const float* w_scale, const float* bias, void* y, int y_mode, int act,
                                  const float* x_zero, const int32_t* colsum, const float* out_scale,
-                                 int out_scale_n, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+                                 int out_scale_n, int64_t M, int64_t N, int64_t K, hipStream_t stream,
+                                 bool e4m3) {
     if (M == 0 || N == 0)
         return QL_OK;
     const int m = (int)M, n = (int)N, k = (int)K;
     const SmallEpi epi{x_zero, colsum, out_scale, out_scale_n};
+    if (e4m3) {
+        (y_mode == Y_F16 ? launch_act<Y_F16, false, true> : launch_act<Y_F32, false, true>)(
+            xq, x_scale, wq, w_scale, bias, y, act, m, n, k, epi, stream);
+        return launch_status();
+    }
     if (y_mode == Y_I32)
-        launch_shape<Y_I32, ACT_NONE, false>(xq, x_scale, wq, w_scale, bias, y, m, n, k, epi, stream);
+        launch_shape<Y_I32, ACT_NONE, false, false>(xq, x_scale, wq, w_scale, bias, y, m, n, k, epi, stream);
     else if (y_mode == Y_I8)
         launch_act<Y_I8, false>(xq, x_scale, wq, w_scale, bias, y, act, m, n, k, epi, stream);
     else if (x_zero != nullptr)

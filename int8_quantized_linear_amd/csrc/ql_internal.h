@@ -72,12 +72,13 @@ ql_status launch_gemm_w8a8(const int8_t* xq, const float* x_scale, const int8_t*
                            const float* x_zero, const int32_t* colsum, int64_t M, int64_t N,
                            int64_t K, hipStream_t stream, bool e4m3 = false,
                            const float* out_scale = nullptr, int out_scale_n = 0);
-// The W8A8 layer for M <= 128 (int8 codes): y_mode F32, F16 (with zero points when x_zero
-// and colsum are given), I32, or I8 (out_scale_n = 1 or N output scales).
+// The W8A8 layer for M <= 128: y_mode F32, F16 (with zero points when x_zero and colsum are
+// given), I32, or I8 (out_scale_n = 1 or N output scales); e4m3: E4M3 codes, F32 or F16 only.
 ql_status launch_gemm_w8a8_small(const int8_t* xq, const float* x_scale, const int8_t* wq,
                                  const float* w_scale, const float* bias, void* y, int y_mode, int act,
                                  const float* x_zero, const int32_t* colsum, const float* out_scale,
-                                 int out_scale_n, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+                                 int out_scale_n, int64_t M, int64_t N, int64_t K, hipStream_t stream,
+                                 bool e4m3 = false);
 ql_status launch_wonly(const void* x, const void* codes, int fmt, const void* scale,
                        const uint8_t* zp, int64_t group, const float* bias, void* y, int64_t M,
                        int64_t N, int64_t K, int act, hipStream_t stream);
