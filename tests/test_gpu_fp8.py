@@ -190,8 +190,12 @@ def test_layer(ql, M, N, K, out, act):
     assert np.all(err <= tol), "max err/tol %.3g" % float((err / tol).max())
 
 
-def test_matrix_core_groups(ql):
-    """The premises of the bound above, one output each (unit scales, K = 64, fp32 out): a
+@pytest.mark.parametrize("rows", ["few", "tiles"])
+def test_matrix_core_groups(ql, rows):
+    """The premises of the bound above, on both kernels: up to 128 rows run the few-row kernel
+    (16x16x128 fp8 steps), more rows the tile kernel (32x32x64 steps); the cases are padded
+    with zero rows to more than 128 for the latter. One output each (unit scales, K = 64,
+    fp32 out): a
     product of 4 beside 2^16 (2^-14 of it) vanishes when both lie in one group of 8
     consecutive k and survives in another group; a product of +-28 beside 2^16 keeps
     +-24 (truncation toward zero to multiples of 2^(16 - 13)); 2^16 + 2^-7 across groups
@@ -209,7 +213,8 @@ def test_matrix_core_groups(ql):
     cases.append(({3: 2.0 ** -9}, {3: 2.0 ** -9}, 2.0 ** -18))
     cases.append(({9: 3 * 2.0 ** -9}, {9: 5 * 2.0 ** -9}, 15 * 2.0 ** -18))
     R = len(cases)
-    M = (R + 31) // 32 * 32
+    M = (R + 31) // 32 * 32 if rows == "few" else 160
+    assert (M <= 128) == (rows == "few")
     A = np.zeros((M, 64), np.uint8)
     B = np.zeros((M, 64), np.uint8)
     for r, (a, b, _) in enumerate(cases):
