@@ -12,9 +12,14 @@ constexpr int64_t kMaxKw8a8 = 131008;           // K * 128^2 < 2^31, K % 64 == 0
 constexpr int64_t kMaxNw8a8 = (int64_t)1 << 23; // 32 output rows of 4-byte values: 2^30 bytes
 constexpr int64_t kMaxKwonly = (int64_t)1 << 22; // 64 rows of fp16 X and 64 weight columns < 2^31 bytes
 
-// Up to this many rows of X the int8 W8A8 calls run on the few-row kernel
-// (gemm_w8a8_small.hip), whose grid grows with N alone.
+// The few-row kernel (gemm_w8a8_small.hip) has N/16 workgroups, each reading all of X, so its
+// time grows with M*N while the tile kernel's stays flat until its tiles fill the chip.
+// Measured at K = 4096, the few-row kernel wins up to M*N of about 640K (M = 32, N = 11008:
+// 17.5 against 33.1 us; M = 128, N = 4096: 19 against 25 us) and loses past it (M = 64,
+// N = 11008: 36.0 against 34.3 us).
 constexpr int64_t kSmallM = 128;
+constexpr int64_t kSmallMN = 640 * 1024;
+inline bool few_rows(int64_t M, int64_t N) { return M <= kSmallM && M * N <= kSmallMN; }
 
 inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
@@ -149,7 +154,7 @@ ql_status gemm_w8a8_asym(const int8_t* xq, const float* x_scale, const float* x_
     if (!aligned(x_scale, 4) || !aligned(x_zero, 4) || !aligned(w_scale, 4) || !aligned(w_colsum, 4) ||
         (bias && !aligned(bias, 4)))
         return QL_ERR_ALIGN;
-    if (M <= kSmallM)
+    if (few_rows(M, N))
         return ql::launch_gemm_w8a8_small(xq, x_scale, wq, w_scale, bias, y,
                                           y_dtype == QL_F32 ? ql::Y_F32 : ql::Y_F16, (int)act, x_zero,
                                           w_colsum, nullptr, 0, M, N, K, as_stream(stream));
@@ -173,7 +178,7 @@ ql_status gemm_w8a8_per_channel_act(const int8_t* xq, const float* x_scale, cons
         return QL_ERR_NULL;
     if (!aligned(x_scale, 4) || !aligned(w_scale, 4) || (bias && !aligned(bias, 4)))
         return QL_ERR_ALIGN;
-    if (M <= kSmallM)
+    if (few_rows(M, N))
         return ql::launch_gemm_w8a8_small(xq, x_scale, wq, w_scale, bias, y,
                                           y_dtype == QL_F32 ? ql::Y_F32 : ql::Y_F16, (int)act, nullptr,
                                           nullptr, nullptr, 0, M, N, K, as_stream(stream));
@@ -226,7 +231,7 @@ ql_status gemm_e4m3_per_channel(const uint8_t* xq, const float* x_scale, const u
         return QL_ERR_NULL;
     if (!aligned(x_scale, 4) || !aligned(w_scale, 4) || (bias && !aligned(bias, 4)))
         return QL_ERR_ALIGN;
-    if (M <= kSmallM)
+    if (few_rows(M, N))
         return ql::launch_gemm_w8a8_small(xc, x_scale, wc, w_scale, bias, y,
                                           y_dtype == QL_F32 ? ql::Y_F32 : ql::Y_F16, (int)act, nullptr,
                                           nullptr, nullptr, 0, M, N, K, as_stream(stream), true);
@@ -253,7 +258,7 @@ ql_status gemm_w8a8_requant(const int8_t* xq, const float* x_scale, const int8_t
     if (!aligned(x_scale, 4) || !aligned(w_scale, 4) || !aligned(out_scale, 4) ||
         (bias && !aligned(bias, 4)))
         return QL_ERR_ALIGN;
-    if (M <= kSmallM)
+    if (few_rows(M, N))
         return ql::launch_gemm_w8a8_small(xq, x_scale, wq, w_scale, bias, yq, ql::Y_I8, (int)act, nullptr,
                                           nullptr, out_scale, (int)out_scale_n, M, N, K, as_stream(stream));
     return ql::launch_gemm_w8a8(xq, x_scale, wq, w_scale, bias, yq, ql::Y_I8, (int)act, nullptr,
@@ -273,7 +278,7 @@ ql_status gemm_w8a8_int32(const int8_t* xq, const int8_t* wq, int32_t* acc, int6
     ql_status st = check_w8a8(xq, wq, acc, M, N, K);
     if (st != QL_OK || M == 0 || N == 0)
         return st;
-    if (M <= kSmallM)
+    if (few_rows(M, N))
         return ql::launch_gemm_w8a8_small(xq, nullptr, wq, nullptr, nullptr, acc, ql::Y_I32, ql::ACT_NONE,
                                           nullptr, nullptr, nullptr, 0, M, N, K, as_stream(stream));
     return ql::launch_gemm_w8a8(xq, nullptr, wq, nullptr, nullptr, acc, ql::Y_I32, ql::ACT_NONE, nullptr,

@@ -310,7 +310,7 @@ def test_requant_with_activation(ql, act, M, N, K):
                                    (33, 1000, 640), (48, 16, 4096), (64, 11008, 4096), (64, 31, 64), (65, 300, 256),
                                    (96, 1000, 640), (100, 17, 64), (128, 4096, 4096), (129, 300, 256)])
 def test_few_rows_int32(ql, M, N, K):
-    """M <= 128 runs on the few-row kernel (16 columns per workgroup, K split over the waves,
+    """M <= 128 with M * N <= 640K runs on the few-row kernel (16 columns per workgroup, K split over the waves,
     16x16x64 matrix-core steps after a lane permutation; up to four row blocks with two wave
     shapes, five to eight with a third): accumulators bit for bit, with codes at the extremes,
     ragged N, one to 64 k-steps, and M = 129 back on the tile kernel."""
