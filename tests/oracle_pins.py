@@ -688,4 +688,208 @@ def pin_channel_scales(orc):
     assert np.all(err <= s[None, :].astype(np.float64) * (0.5 + SLOP))
 
 
+# ------------------------------------- quotient reading x / s in every quantizer
+#
+# The codes of every quantizer are round(x / s) with x / s the correctly rounded fp32
+# quotient. The multiply by a rounded reciprocal, x * round_f32(1 / s), agrees with it
+# except near ties, so these pins put many exact ties x = (j + 1/2) s at scales that are
+# not powers of two (where round_f32(1 / s) is inexact) and check every code.
+
+# Odd-significand scales (not powers of two) and power-of-two multiples of them.
+TIE_SCALES = (0.875, 0.9375, 0.8125, 0.875 * 2.0 ** -6, 0.9375 * 2.0 ** 5, 0.8125 * 2.0 ** -11)
+
+
+def _f32(fr) -> Fraction:
+    return Fraction(round_to_f32(Fraction(fr)))
+
+
+def pin_asym_golden_ties(orc):
+    """Hand-derived asymmetric codes at scale 0.875 with integer zero points
+    (tests/golden/asym_ties.txt)."""
+    for s_txt, z_txt, x_txt, q_txt in _rows("asym_ties.txt"):
+        x = np.array([float(v) for v in x_txt.split()], np.float32)[None, :]
+        q, s, z = orc.quant_rows_i8_asym(x)
+        assert float(s[0]) == float(s_txt) and float(z[0]) == float(z_txt), (s, z)
+        assert q[0].tolist() == [int(v) for v in q_txt.split()], (q[0], q_txt)
+
+
+def _asym_ref_row(row):
+    """Exact-rational evaluation of the asymmetric reading on one fp32 row: (codes, s, z)."""
+    lo, hi = Fraction(float(min(row))), Fraction(float(max(row)))
+    s = _f32(_f32(hi - lo) / 255)
+    if s < Fraction(float(np.float32(1e-8))):
+        s = Fraction(float(np.float32(1e-8)))
+    z = _f32(_f32(-lo / s) - 128)
+    q = [max(-128, min(127, rne_int(_f32(_f32(Fraction(float(v)) / s) + z)))) for v in row]
+    return q, float(s), float(z)
+
+
+def pin_asym_exact_rational(orc):
+    """Asymmetric per-row codes, scales and zero points against exact rational arithmetic
+    of the reading: s = fl(fl(hi - lo) / 255) (floor 1e-8), z = fl(fl(-lo / s) - 128),
+    q = clamp(rne(fl(fl(x / s) + z)), -128, 127). Every code of rows built from exact ties
+    (j + 1/2) s, with the row minimum at -j0 s so that the zero point is j0 - 128, and
+    sampled codes of random rows."""
+    rows = []
+    for s in TIE_SCALES:
+        for j0 in (0, 128, 250, 37):
+            j = np.arange(-j0, 255 - j0)
+            rows.append(np.concatenate([[-j0 * s, (255 - j0) * s], (j[:-1] + 0.5) * s]))
+    width = max(len(r) for r in rows)
+    x = np.array([np.resize(r, width) for r in rows], np.float32)
+    q, s, z = orc.quant_rows_i8_asym(x)
+    for i, r in enumerate(x):
+        qr, sr, zr = _asym_ref_row(r)
+        assert float(s[i]) == sr and float(z[i]) == zr, (i, float(s[i]), sr, float(z[i]), zr)
+        assert q[i].tolist() == qr, i
+    rng = np.random.default_rng(84)
+    x = (rng.standard_normal((8, 200)) * np.exp2(rng.integers(-9, 9, (8, 1)))
+         + rng.uniform(-2, 2, (8, 1))).astype(np.float32)
+    q, s, z = orc.quant_rows_i8_asym(x)
+    for i, r in enumerate(x):
+        qr, sr, zr = _asym_ref_row(r)
+        assert float(s[i]) == sr and float(z[i]) == zr, i
+        assert q[i].tolist() == qr, i
+
+
+def pin_block_asym_golden_ties(orc):
+    """Hand-derived block-64 uint8 codes at scale 0.875, including a zero point that is a
+    tie (tests/golden/block_asym_ties.txt)."""
+    for s_txt, z_txt, w_txt, q_txt in _rows("block_asym_ties.txt"):
+        wv = [float(v) for v in w_txt.split()]
+        w = np.full((1, 64), wv[0], np.float32)
+        w[0, :len(wv)] = wv
+        q, s, z = orc.quant_block_asym_u8(w, 64)
+        assert float(s[0, 0]) == float(s_txt) and int(z[0, 0]) == int(z_txt), (s, z)
+        assert q[0, :len(wv)].tolist() == [int(v) for v in q_txt.split()], (q[0, :len(wv)], q_txt)
+
+
+def _block_ref(block):
+    """Exact-rational evaluation of the block-asymmetric reading on one block: (codes, s, zp)."""
+    mn, mx = Fraction(float(min(block))), Fraction(float(max(block)))
+    s = _f32(_f32(mx - mn) / 255)
+    if s < Fraction(float(np.float32(1e-8))):
+        s = Fraction(float(np.float32(1e-8)))
+    zp = max(0, min(255, rne_int(_f32(-mn / s))))
+    q = [max(0, min(255, rne_int(_f32(Fraction(float(v)) / s)) + zp)) for v in block]
+    return q, float(s), zp
+
+
+def pin_block_asym_exact_rational(orc):
+    """Block-64 uint8 codes, scales and zero points against exact rational arithmetic of
+    the reading: s = fl(fl(max - min) / 255) (floor 1e-8), zp = clamp(rne(fl(-min / s)),
+    0, 255), q = clamp(rne(fl(w / s)) + zp, 0, 255). Every code of blocks of exact ties
+    (j + 1/2) s (the minimum at -m0 s, with m0 an integer or itself a tie) and of blocks
+    of a workload's weights."""
+    rng = np.random.default_rng(85)
+    blocks = []
+    for s in TIE_SCALES:
+        for m0 in (96, 96.5, 200, 200.5, 250):
+            lo, hi = -m0 * s, (255 - m0) * s
+            j = rng.choice(np.arange(-int(m0), int(254 - m0)), 62, replace=False)
+            blocks.append(np.concatenate([[lo, hi], (j + 0.5) * s]))
+    w = np.array(blocks, np.float32).reshape(-1, 128)     # two blocks per row
+    inp = workloads.draw(workloads.with_shape(workloads.W8A16_BLOCK, 1, 128, 4))
+    w = np.concatenate([w, inp.w_nk], 0)
+    q, s, z = orc.quant_block_asym_u8(w, 64)
+    for n in range(w.shape[0]):
+        for b in range(2):
+            qr, sr, zr = _block_ref(w[n, 64 * b:64 * b + 64])
+            assert float(s[n, b]) == sr and int(z[n, b]) == zr, (n, b)
+            assert q[n, 64 * b:64 * b + 64].tolist() == qr, (n, b)
+
+
+def pin_int4_exact_rational(orc):
+    """int4 group codes against exact rational arithmetic of the reading:
+    s16 = fp16(fl(max(a, 7 * 2^-24) / 7)), q = clamp(rne(fl(w / s16)), -8, 7). Every code of
+    groups of exact ties (j + 1/2) s16 with absmax 7 s16 at scales that are not powers of
+    two, and of a workload's groups."""
+    rng = np.random.default_rng(86)
+    groups = []
+    for s in TIE_SCALES:
+        for _ in range(2):
+            j = rng.integers(-7, 7, 127)          # |(j + 1/2) s| <= 6.5 s < 7 s
+            groups.append(rng.permutation(np.concatenate([[7 * s * rng.choice([-1, 1])], (j + 0.5) * s])))
+    w = np.array(groups, np.float32)
+    w = np.concatenate([w, workloads.draw(workloads.with_shape(workloads.W4A16_GROUP, 1, 128, 6)).w_nk], 0)
+    packed, s16 = orc.quant_int4_group(w, 128)
+    q = orc.unpack_int4(packed, 128)
+    floor_a = Fraction(7) * Fraction(1, 2 ** 24)
+    for n in range(w.shape[0]):
+        a = max(Fraction(abs(float(v))) for v in w[n])
+        sr = Fraction(round_to_f16(_f32(max(a, floor_a) / 7)))
+        assert Fraction(float(s16[n, 0])) == sr, n
+        qr = [max(-8, min(7, rne_int(_f32(Fraction(float(v)) / sr)))) for v in w[n]]
+        assert q[n].tolist() == qr, n
+
+
+def pin_e4m3_golden_ties(orc):
+    """Hand-derived E4M3 codes at scale 0.875, on midpoints between E4M3 values
+    (tests/golden/e4m3_ties.txt)."""
+    for s_txt, x_txt, q_txt in _rows("e4m3_ties.txt"):
+        x = np.array([float(v) for v in x_txt.split()], np.float32)[None, :]
+        q, s = orc.quant_rows_e4m3(x)
+        assert float(s[0]) == float(s_txt), s
+        assert q[0].tolist() == [int(v, 16) for v in q_txt.split()], ([hex(v) for v in q[0]], q_txt)
+
+
+def _e4m3_code_exact(t: Fraction, negative: bool) -> int:
+    """The E4M3 code of the value nearest to t (|t| <= 448), ties to the even mantissa,
+    from the format's definition: spacing 2^-9 below 2^-6, else 2^(E-3) in [2^E, 2^(E+1))."""
+    a = abs(t)
+    if a < Fraction(1, 64):
+        quantum = Fraction(1, 512)
+    else:
+        E = 0
+        while Fraction(2) ** E > a:
+            E -= 1
+        while Fraction(2) ** (E + 1) <= a:
+            E += 1
+        quantum = Fraction(2) ** (E - 3)
+    n = rne_int(a / quantum)
+    v = n * quantum
+    sign = 0x80 if negative else 0
+    if v < Fraction(1, 64):
+        return sign | int(v * 512)                      # exponent field 0: m / 8 * 2^-6
+    E = 0
+    while Fraction(2) ** E > v:
+        E -= 1
+    while Fraction(2) ** (E + 1) <= v:
+        E += 1
+    m = int((v / Fraction(2) ** E - 1) * 8)
+    return sign | ((E + 7) << 3) | m
+
+
+def pin_e4m3_exact_rational(orc):
+    """Per-row E4M3 codes against exact rational arithmetic of the reading:
+    s = fl(max(a, 1e-10) / 448), t = clamp(fl(x / s), -448, 448), code = the nearest E4M3
+    value with ties to the even mantissa (a negative t keeps the sign bit). Every code of
+    rows whose quotients are midpoints and values of E4M3 in every binade, at scales that
+    are not powers of two, and of random rows."""
+    pos = [Fraction(m, 512) for m in range(8)] + \
+          [Fraction(2) ** (e - 7) * (1 + Fraction(m, 8)) for e in range(1, 16) for m in range(8)][:-1]
+    mids = [(a + b) / 2 for a, b in zip(pos[:-1], pos[1:])]
+    rows = []
+    for s in TIE_SCALES:
+        vals = [448 * s] + [float(v) * s for v in mids] + [-float(v) * s for v in mids[::3]] + \
+               [float(v) * s for v in pos[1::5]]
+        rows.append(vals)
+    width = max(len(r) for r in rows)
+    x = np.array([np.resize(r, width) for r in rows], np.float32)
+    rng = np.random.default_rng(87)
+    xr = (rng.standard_normal((6, width)) * np.exp2(rng.integers(-10, 10, (6, 1)))).astype(np.float32)
+    xr[:, :40] *= np.float32(2.0 ** -9)          # subnormal E4M3 quotients
+    x = np.concatenate([x, xr], 0)
+    q, s = orc.quant_rows_e4m3(x)
+    f1e10 = Fraction(float(np.float32(1e-10)))
+    for i, r in enumerate(x):
+        a = max(Fraction(abs(float(v))) for v in r)
+        sr = _f32(max(a, f1e10) / 448)
+        assert Fraction(float(s[i])) == sr, i
+        for c, v in enumerate(r):
+            t = _f32(Fraction(float(v)) / sr)
+            t = max(Fraction(-448), min(Fraction(448), t))
+            assert int(q[i, c]) == _e4m3_code_exact(t, bool(np.signbit(v))), (i, c, float(v))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

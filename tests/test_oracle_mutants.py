@@ -68,6 +68,14 @@ MUTANTS = [
      "            if (r < -128.0f)\n                r = -128.0f;\n            q[m * N + n]"),
     ("channel_scales_row_axis", "const float t = fabsf(y[m * N + n]);", "const float t = fabsf(y[(n * M + m) % (M * N)]);"),
     ("channel_scales_no_floor", "s[n] = (a > 1e-10f ? a : 1e-10f) / 127.0f;", "s[n] = a / 127.0f;"),
+    ("asym_reciprocal", "const float t = v[i] / s + z;", "const float t = v[i] * (1.0f / s) + z;"),
+    ("asym_zero_reciprocal", "const float z = -lo / s - 128.0f;", "const float z = -lo * (1.0f / s) - 128.0f;"),
+    ("block_reciprocal", "int c = (int)nearbyintf(v[i] / s) + z;", "int c = (int)nearbyintf(v[i] * (1.0f / s)) + z;"),
+    ("block_zero_reciprocal", "float zf = nearbyintf(-mn / s);", "float zf = nearbyintf(-mn * (1.0f / s));"),
+    ("int4_reciprocal", "float r = nearbyintf(v[i] / s);\n                if (r > 7.0f)",
+     "float r = nearbyintf(v[i] * (1.0f / s));\n                if (r > 7.0f)"),
+    ("e4m3_reciprocal_448", "float t = v[i] / s;", "float t = v[i] * (448.0f / (a > 1e-10f ? a : 1e-10f));"),
+    ("e4m3_reciprocal", "float t = v[i] / s;", "float t = v[i] * (1.0f / s);"),
     ("act_codes_swapped", "if (act == 1)\n            y[i] = v * (0.5", "if (act == 2)\n            y[i] = v * (0.5"),
 ]
 
