@@ -14,8 +14,17 @@ weights from HBM rather than from the 256 MB Infinity Cache.
 
 Printed: one JSON line. ``value`` is the W8A8 prefill layer's throughput in TOPS
 (2*M*N*K integer ops over the average time of steps 1 + 2); the decode workloads'
-GB/s are reported alongside. Kernel times come from HIP events recorded around each
-launch on the stream the kernels run on, inside the timed region.
+GB/s are reported alongside. The timed region runs exactly K steps, issued in groups of
+GROUP steps: within a group each kernel's GROUP launches go back to back, bracketed by
+one pair of HIP events on the stream the kernels run on. A kernel's time is the sum of
+its bracketed intervals over K. It includes the stream's launch-to-launch gap (about a
+microsecond) but no event between two launches; short groups keep the GEMM's launches
+from running long enough on their own to lower the chip's clock more than a pass of the
+path does. Every input that streams from HBM rotates over more than 512 MiB of copies
+(the decode weights and the quantizer's X), so no launch finds it in the Infinity Cache.
+``roofline`` is the W8A8 GEMM's (the dominant kernel); ``rooflines`` holds one entry per
+hot-path kernel, each beside the rocprofv3 kernel-trace average of the committed profile
+when that profile was taken on the current kernel sources.
 
 After the timed region, measured ceilings (libqlprobe.so, not part of the layer) are
 reported beside the published peaks: the int8 MFMA rate from registers alone, with
@@ -43,6 +52,7 @@ PEAK_INT8_TOPS = 5000.0        # MI355X dense int8 MFMA, 5.0 POP/s
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA, 5.0 PFLOP/s
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 ROTATE_BYTES = 512 << 20
+GROUP = 10                     # steps per group of back-to-back launches in the timed region
 
 
 def _algorithmic_bytes():
@@ -65,6 +75,18 @@ def _kernel_hash():
     return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
 
 
+def _library_hash():
+    """Hash of every source of libql.so (sorted by name), to tie profiles to the code."""
+    csrc = os.path.join(ROOT, "int8_quantized_linear_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".cpp", ".h")) and name != "probes.hip":
+            h.update(name.encode())
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    h.update(open(os.path.join(ROOT, "include", "ql.h"), "rb").read())
+    return h.hexdigest()[:16]
+
+
 def _traffic_for_gemm():
     """HBM bytes per launch of the W8A8 GEMM from committed rocprofv3 counter runs, or None
     if absent or taken on a different version of the kernel source."""
@@ -78,10 +100,35 @@ def _traffic_for_gemm():
     return rec.get("hbm_bytes_per_launch")
 
 
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def _profiled_kernel_times():
+    """Per-kernel rocprofv3 kernel-trace averages (microseconds) of this benchmark's default
+    command, from profiles/kernel_times.json, or {} when that file was written for other
+    kernel sources (its hash covers every HIP source of the library)."""
+    path = os.path.join(ROOT, "profiles", "kernel_times.json")
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return {}
+    if rec.get("library_source_sha256_16") != _library_hash():
+        return {}
+    return rec.get("avg_us", {})
+
+
 def cpu_baseline(target_s: float):
     """The oracle timed on this host on a bounded sample of the W8A8 prefill layer: the first
     R rows of X through per-row quantization, the exact int32 GEMM against all of W, and the
-    epilogue. R is chosen so the timed work takes about target_s seconds."""
+    epilogue. R is chosen so that one run takes about target_s / 3 seconds; the reported
+    time is the median of three runs."""
     import numpy as np
 
     import oracle
@@ -100,14 +147,16 @@ def cpu_baseline(target_s: float):
     # rows are spread over the oracle's OpenMP threads: calibrate on one row per thread
     nt = max(1, min(64, oracle.num_threads()))
     per_row = run(nt) / nt
-    rows = int(max(nt, min(w.M, nt * round(target_s / per_row / nt))))
-    dt = run(rows)
+    rows = int(max(nt, min(w.M, nt * round(target_s / 3 / per_row / nt))))
+    times = sorted(run(rows) for _ in range(3))
+    dt = times[1]
     ops = 2.0 * rows * w.N * w.K
     return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": "rows 0..%d of X [2048,4096] through the W8A8 layer (per-row quantize, exact "
-                      "int32 GEMM with W [4096,11008], fp32 epilogue, fp16 output): %.1f s" % (rows - 1, dt),
-            "seconds": dt, "host": platform.processor() or platform.machine(),
-            "single_thread": _cpu_single_thread(target_s / 4)}
+                      "int32 GEMM with W [4096,11008], fp32 epilogue, fp16 output): median of 3 runs "
+                      "of %.2f, %.2f, %.2f s" % (rows - 1, *times),
+            "seconds": dt, "host": _cpu_model(), "os_cpu_count": os.cpu_count(),
+            "single_thread": _cpu_single_thread(target_s / 6)}
 
 
 _ONE_THREAD = r"""
@@ -120,14 +169,16 @@ inp = wl.draw(w)
 wq, ws = oracle.quant_weight_per_channel(inp.w_nk)
 t0 = time.perf_counter(); oracle.linear_w8a8(inp.x[:1], wq, ws, inp.bias); per_row = time.perf_counter() - t0
 rows = int(max(1, min(w.M, round(float(sys.argv[2]) / per_row))))
-t0 = time.perf_counter(); r = oracle.linear_w8a8(inp.x[:rows], wq, ws, inp.bias); dt = time.perf_counter() - t0
-print(rows, dt, oracle.num_threads())
+ts = []
+for _ in range(3):
+    t0 = time.perf_counter(); r = oracle.linear_w8a8(inp.x[:rows], wq, ws, inp.bias); ts.append(time.perf_counter() - t0)
+print(rows, sorted(ts)[1], oracle.num_threads())
 """
 
 
 def _cpu_single_thread(target_s: float):
-    """The same oracle sample on one thread, in a child process started with
-    OMP_NUM_THREADS=1 (the oracle reads it when its library loads)."""
+    """The same oracle sample on one thread (median of three runs), in a child process
+    started with OMP_NUM_THREADS=1 (the oracle reads it when its library loads)."""
     import subprocess
     env = dict(os.environ, OMP_NUM_THREADS="1")
     r = subprocess.run([sys.executable, "-c", _ONE_THREAD, ROOT, str(target_s)], env=env,
@@ -140,33 +191,26 @@ def _cpu_single_thread(target_s: float):
     return {"value": w / dt / 1e12, "unit": "TOPS", "cores": int(threads), "rows": rows, "seconds": dt}
 
 
-def fused_activation_timings(ql, n, gemm, dec5, r5, make_gemm, make_dec, ops, w4_bytes, gemm_name,
+def _cycle(launches):
+    """A zero-argument callable that launches the next of `launches` at each call."""
+    state = [0]
+
+    def f():
+        launches[state[0] % len(launches)]()
+        state[0] += 1
+    return f
+
+
+def fused_activation_timings(ql, n, gemm, dec5, make_gemm, make_dec, ops, w4_bytes, gemm_name,
                              dec_name, progress):
     """The epilogue with a fused activation (GELU, SiLU) against the plain epilogue: the
-    W8A8 GEMM at the prefill shape and W4A16 at the decode shape, each launch event-timed
-    on the launch stream. Plain and fused launches alternate so that both run at the same
-    clock; the decode weights rotate as in the step loop."""
-    import torch
-    progress("fused activations: %d launches each" % n)
+    W8A8 GEMM at the prefill shape and W4A16 at the decode shape. Plain and fused bursts
+    alternate so that both run at the same clock; the decode weights rotate as in the
+    step loop."""
+    progress("fused activations: %d bursts each" % n)
     gelu, silu = ql.ACTIVATIONS["gelu"], ql.ACTIVATIONS["silu"]
-    runs = {"w8a8_plain": lambda i: gemm(), "w8a8_gelu": (lambda f: lambda i: f())(make_gemm(gelu)),
-            "w8a8_silu": (lambda f: lambda i: f())(make_gemm(silu)),
-            "w4a16_plain": lambda i: dec5[i % r5]()}
-    dec_g = make_dec(gelu)
-    runs["w4a16_gelu"] = lambda i: dec_g[i % r5]()
-    ev = {k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-          for k in runs}
-    for i in range(3):
-        for f in runs.values():
-            f(i)
-    torch.cuda.synchronize()
-    for i in range(n):
-        for k, f in runs.items():
-            ev[k][i][0].record()
-            f(i)
-            ev[k][i][1].record()
-    torch.cuda.synchronize()
-    us = {k: 1e3 * sum(a.elapsed_time(b) for a, b in v) / n for k, v in ev.items()}
+    us = _alternate(n, {"w8a8_plain": gemm, "w8a8_gelu": make_gemm(gelu), "w8a8_silu": make_gemm(silu),
+                        "w4a16_plain": _cycle(dec5), "w4a16_gelu": _cycle(make_dec(gelu))})
     return {
         gemm_name: {"plain_us": us["w8a8_plain"], "gelu_us": us["w8a8_gelu"], "silu_us": us["w8a8_silu"],
                     "gelu_TOPS": ops / (us["w8a8_gelu"] * 1e-6) / 1e12,
@@ -175,26 +219,32 @@ def fused_activation_timings(ql, n, gemm, dec5, r5, make_gemm, make_dec, ops, w4
         dec_name: {"plain_us": us["w4a16_plain"], "gelu_us": us["w4a16_gelu"],
                    "gelu_GB_per_s": w4_bytes / (us["w4a16_gelu"] * 1e-6) / 1e9,
                    "gelu_overhead": us["w4a16_gelu"] / us["w4a16_plain"] - 1},
-        "note": "launches alternate plain / fused; event-timed per launch",
+        "note": "bursts of plain and fused launches alternate; event-timed per burst",
     }
+
+
+BURST = 10
 
 
 def _alternate(n, runs):
     """Mean microseconds per launch of each zero-argument callable in runs: one warm-up
-    round, then n rounds in which the launches alternate, each bracketed by events."""
+    burst each, then n rounds in which each callable runs a burst of BURST back-to-back
+    launches bracketed by one event pair, the callables alternating burst by burst."""
     import torch
     ev = {k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
           for k in runs}
     for f in runs.values():
-        f()
+        for _ in range(BURST):
+            f()
     torch.cuda.synchronize()
     for i in range(n):
         for k, f in runs.items():
             ev[k][i][0].record()
-            f()
+            for _ in range(BURST):
+                f()
             ev[k][i][1].record()
     torch.cuda.synchronize()
-    return {k: 1e3 * sum(a.elapsed_time(b) for a, b in v) / n for k, v in ev.items()}
+    return {k: 1e3 * sum(a.elapsed_time(b) for a, b in v) / (n * BURST) for k, v in ev.items()}
 
 
 def asym_timings(n, runs, ops, quant_bytes, name, progress):
@@ -279,13 +329,14 @@ def measured_ceilings(dev, byte_counts, progress):
             raise RuntimeError("%s failed with %d" % (what, rc))
 
     def timed(fn, reps):
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-        for i, (a, b) in enumerate(evs):
-            a.record(stream)
+        # one event pair around reps back-to-back launches, as for the layer's kernels
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(reps):
             fn(i)
-            b.record(stream)
+        b.record(stream)
         torch.cuda.synchronize()
-        return sum(a.elapsed_time(b) for a, b in evs) / reps * 1e-3   # seconds per launch
+        return a.elapsed_time(b) / reps * 1e-3   # seconds per launch
 
     progress("measured ceilings")
     out = {"mfma_i8_TOPS": {}, "stream_read_GB_per_s": {}}
@@ -308,18 +359,18 @@ def measured_ceilings(dev, byte_counts, progress):
         out["stream_read_GB_per_s"][name] = nb / dt / 1e9
         del bufs
     out["note"] = ("MFMA: %d workgroups x 4 waves issuing v_mfma_i32_32x32x32_i8 from registers; "
-                   "stream read: one launch reading a cold buffer of each kernel's algorithmic "
-                   "byte count (buffers rotated over more than 512 MiB)" % cus)
+                   "stream read: launches reading a cold buffer of each kernel's algorithmic "
+                   "byte count (buffers rotated over more than 512 MiB), timed as a back-to-back burst" % cus)
     return out
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", dest="cpu", action="store_false")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=18.0)
     ap.add_argument("--act-steps", type=int, default=20,
                     help="launches of each fused-activation variant timed after the step loop (0: skip)")
     ap.add_argument("--no-ceilings", dest="ceilings", action="store_false",
@@ -405,21 +456,17 @@ def main():
 
     # ------------------------------------------------- prepared launches
     F16 = 1
-    quant = ql.prepare("quantize_per_row_int8", x3, F16, w3.M, w3.K, xq3, xs3)
+    rq = rotations(2 * w3.M * w3.K)
+    xsets3 = [x3.clone() for _ in range(rq)]
+    quants = [ql.prepare("quantize_per_row_int8", xc, F16, w3.M, w3.K, xq3, xs3) for xc in xsets3]
     gemm = ql.prepare("gemm_w8a8_per_channel", xq3, xs3, wq3, ws3, b3, y3, F16, w3.M, w3.N, w3.K)
     dec2 = [ql.prepare("gemm_w8a16", x2, q, s, None, 0, None, y2, w2.M, w2.N, w2.K) for q, s in set2]
     dec4 = [ql.prepare("gemm_w8a16", x4, q, s, z, 64, None, y4, w4.M, w4.N, w4.K) for q, s, z in set4]
     dec5 = [ql.prepare("gemm_w4a16_grouped", x5, p, s, 128, None, y5, w5.M, w5.N, w5.K) for p, s in set5]
-    names = ["quant", "gemm", "w8a16", "w8a16_block", "w4a16"]
 
-    def step(i, ev=None):
-        launches = [quant, gemm, dec2[i % r2], dec4[i % r4], dec5[i % r5]]
-        for j, fn in enumerate(launches):
-            if ev is not None:
-                ev[j][0].record()
-            fn()
-            if ev is not None:
-                ev[j][1].record()
+    # the kernels of one step, in path order (decode weight sets rotate by step)
+    burst = {"quant": lambda i: quants[i % rq](), "gemm": lambda i: gemm(), "w8a16": lambda i: dec2[i % r2](),
+             "w8a16_block": lambda i: dec4[i % r4](), "w4a16": lambda i: dec5[i % r5]()}
 
     # Plain device copy of known size (reference for hardware byte counters), untimed.
     if args.calib_copy_mib > 0:
@@ -432,22 +479,32 @@ def main():
 
     progress("warmup %d steps" % args.warmup)
     for i in range(args.warmup):
-        step(i)
+        for f in burst.values():
+            f(i)
     torch.cuda.synchronize()
 
     K = args.steps
-    events = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-               for _ in names] for _ in range(K)]
+    stream = torch.cuda.current_stream(dev)
+    names = list(burst)
+    # Steps in groups of GROUP: within a group, each kernel's launches for the group's steps go
+    # back to back between two events on the launch stream
+    intervals = {n: [] for n in names}
     progress("timing %d steps" % K)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(K):
-        step(args.warmup + i, events[i])
+    for g0 in range(0, K, GROUP):
+        steps = range(args.warmup + g0, args.warmup + min(K, g0 + GROUP))
+        for n in names:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for i in steps:
+                burst[n](i)
+            b.record(stream)
+            intervals[n].append((a, b))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / K
-    avg_ms = {n: sum(events[i][j][0].elapsed_time(events[i][j][1]) for i in range(K)) / K
-              for j, n in enumerate(names)}
+    avg_ms = {n: sum(a.elapsed_time(b) for a, b in intervals[n]) / K for n in names}
 
     ops = 2.0 * w3.M * w3.N * w3.K
     layer_s = (avg_ms["quant"] + avg_ms["gemm"]) * 1e-3
@@ -458,11 +515,30 @@ def main():
     def gbs(name):
         return ab[name] / (avg_ms[name] * 1e-3) / 1e9
 
+    prof = _profiled_kernel_times()
     decode = {}
     for name, w, rot in (("w8a16", w2, r2), ("w8a16_block", w4, r4), ("w4a16", w5, r5)):
         decode[name] = {"workload": w.name, "us": avg_ms[name] * 1e3, "GB_per_s": gbs(name),
                         "frac_hbm_peak": gbs(name) / PEAK_HBM_GBS, "bytes": ab[name],
                         "weight_sets_rotated": rot}
+    rooflines = {}
+    for name, kern in (("quant", "quantize_per_row_int8 " + w3.name), ("w8a16", "gemm_w8a16 " + w2.name),
+                       ("w8a16_block", "gemm_w8a16 " + w4.name), ("w4a16", "gemm_w4a16_grouped " + w5.name)):
+        r = {"bound": "hbm", "kernel": kern, "achieved": gbs(name), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+             "frac": gbs(name) / PEAK_HBM_GBS, "avg_us": avg_ms[name] * 1e3, "bytes_per_launch": ab[name]}
+        if name in prof:
+            r["rocprof_avg_us"] = prof[name]
+            r["frac_by_rocprof_avg"] = ab[name] / (prof[name] * 1e-6) / 1e9 / PEAK_HBM_GBS
+        rooflines[name] = r
+    roof = {"bound": "mfma", "kernel": "gemm_w8a8_per_channel " + w3.name, "achieved": gemm_tops,
+            "peak": PEAK_INT8_TOPS, "unit": "TOPS", "frac": gemm_tops / PEAK_INT8_TOPS,
+            "traffic": _traffic_for_gemm(), "avg_us": avg_ms["gemm"] * 1e3, "ops_per_launch": ops,
+            "note": "int8 operations (2*M*N*K per launch) over the kernel's average time in the timed "
+                    "steps, against the dense int8 MFMA peak (5.0 POP/s)"}
+    if "gemm" in prof:
+        roof["rocprof_avg_us"] = prof["gemm"]
+        roof["frac_by_rocprof_avg"] = ops / (prof["gemm"] * 1e-6) / 1e12 / PEAK_INT8_TOPS
+    rooflines["gemm"] = roof
     out = {
         "metric": METRIC,
         "value": value,
@@ -479,19 +555,19 @@ def main():
         "config": {"workload": w3.name, "M": w3.M, "K": w3.K, "N": w3.N, "x": "fp16", "y": "fp16",
                    "bias": True, "value_covers": "per-row quantization + W8A8 GEMM",
                    "decode_workloads": [w2.name, w4.name, w5.name]},
-        "roofline": {"bound": "mfma", "kernel": "gemm_w8a8_per_channel", "achieved": gemm_tops,
-                     "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s", "frac": gemm_tops / PEAK_INT8_TOPS,
-                     "traffic": _traffic_for_gemm(), "avg_us": avg_ms["gemm"] * 1e3,
-                     "note": "int8 operations (2*M*N*K per launch) against the dense int8 MFMA peak"},
+        "roofline": roof,
+        "rooflines": rooflines,
         "w8a16_decode_GB_per_s": decode["w8a16"]["GB_per_s"],
         "quantizer": {"us": avg_ms["quant"] * 1e3, "GB_per_s": gbs("quant"),
                       "frac_hbm_peak": gbs("quant") / PEAK_HBM_GBS},
         "decode": decode,
+        "timing": "steps in groups of %d; within a group each kernel's launches run back to back between "
+                  "two HIP events on the launch stream (includes the launch gap)" % GROUP,
         "device": torch.cuda.get_device_name(0),
     }
     if args.act_steps > 0:
         out["fused_activation"] = fused_activation_timings(
-            ql, args.act_steps, gemm, dec5, r5,
+            ql, args.act_steps, gemm, dec5,
             lambda code: ql.prepare("gemm_w8a8_per_channel_act", xq3, xs3, wq3, ws3, b3, code, y3, F16,
                                     w3.M, w3.N, w3.K),
             lambda code: [ql.prepare("gemm_w4a16_grouped_act", x5, p, s, 128, None, code, y5, w5.M, w5.N,
@@ -502,8 +578,9 @@ def main():
         cs3 = ql.weight_column_sums_i8(wq3)
         out["asymmetric_activations"] = asym_timings(
             args.act_steps, {
-                "quant_symmetric": quant, "gemm_symmetric": gemm,
-                "quant_asym": ql.prepare("quantize_per_row_int8_asym", x3, F16, w3.M, w3.K, xq3, xs3, xz3),
+                "quant_symmetric": _cycle(quants), "gemm_symmetric": gemm,
+                "quant_asym": _cycle([ql.prepare("quantize_per_row_int8_asym", xc, F16, w3.M, w3.K, xq3, xs3, xz3)
+                                      for xc in xsets3]),
                 "gemm_asym": ql.prepare("gemm_w8a8_asym", xq3, xs3, xz3, wq3, ws3, cs3, b3, 0, y3, F16,
                                         w3.M, w3.N, w3.K)},
             ops, ab["quant"] + 4 * w3.M, w3.name, progress)
@@ -512,8 +589,9 @@ def main():
         xs8 = torch.empty((w3.M,), dtype=torch.float32, device=dev)
         out["fp8"] = fp8_timings(
             args.act_steps, {
-                "quant_int8": quant, "gemm_int8": gemm,
-                "quant_e4m3": ql.prepare("quantize_per_row_e4m3", x3, F16, w3.M, w3.K, xq8, xs8),
+                "quant_int8": _cycle(quants), "gemm_int8": gemm,
+                "quant_e4m3": _cycle([ql.prepare("quantize_per_row_e4m3", xc, F16, w3.M, w3.K, xq8, xs8)
+                                      for xc in xsets3]),
                 "gemm_e4m3": ql.prepare("gemm_e4m3_per_channel", xq8, xs8, wq8, ws8, b3, 0, y3, F16,
                                         w3.M, w3.N, w3.K)},
             ops, ab["quant"], w3.name, progress)
@@ -525,7 +603,7 @@ def main():
         out["small_layer"] = {"workload": w1.name, "quant_us": us1["quant"], "gemm_us": us1["gemm"],
                               "layer_us": us1["quant"] + us1["gemm"],
                               "note": "latency-bound: 16 quantizer workgroups (one per row), then the few-row GEMM kernel "
-                                      "(16 workgroups of 16 columns); event-timed"}
+                                      "(16 workgroups of 16 columns); bursts event-timed"}
     if args.act_steps > 0:
         # W8A8 with few rows (decode-time batches) at the 4096 x 4096 decode shape, weights
         # rotated like the decode kernels' so every launch reads W from HBM
@@ -540,11 +618,10 @@ def main():
             ym = torch.empty((m, w2.N), dtype=torch.float16, device=dev)
             launches = [ql.prepare("gemm_w8a8_per_channel", xqm, xsm, wq_, wsc, None, ym, F16, m, w2.N, w2.K)
                         for wq_ in wsets]
-            it = iter(range(10 ** 9))
-            us = _alternate(args.act_steps, {"run": lambda: launches[next(it) % rot]()})["run"]
+            us = _alternate(args.act_steps, {"run": _cycle(launches)})["run"]
             few["m%d" % m] = {"us": us, "GB_per_s": nk / (us * 1e-6) / 1e9}
         out["w8a8_few_rows"] = {"shape": "M x K4096 x N4096, fp16 out", "weight_sets_rotated": rot, **few,
-                                "note": "M <= 64 runs on the few-row kernel; GB/s counts W's bytes; timed after "
+                                "note": "M <= 128 with M*N <= 640K runs on the few-row kernel; GB/s counts W's bytes; timed after "
                                         "the GEMM runs above, whose power draw can leave the clock lower"}
         del wsets
     if args.act_steps > 0:

@@ -27,9 +27,11 @@
  * Conventions for every entry point:
  *   - Every array is a DEVICE pointer owned by the caller. The library never
  *     allocates, frees, retains or synchronizes, and keeps no state.
- *   - All work is enqueued on `stream` (a hipStream_t; NULL is the null stream) and the
- *     call returns without waiting. Device faults surface at the caller's next
- *     synchronization on that stream.
+ *   - All work is enqueued on `stream` and the call returns without waiting. Device
+ *     faults surface at the caller's next synchronization on that stream. The `stream`
+ *     parameter is declared `void*` so that this header needs no HIP include; it is a
+ *     hipStream_t (HIP defines that as a pointer to an opaque struct, so the two have
+ *     the same size and calling convention). NULL is the null stream.
  *   - Layouts: X and Y are row-major and contiguous. W [K,N] is column-major, i.e. an
  *     [N][K] array with K contiguous ([hotelren] opening section). Per-group scales
  *     and zero points are column-major [K/group, N], i.e. [N][K/group].

@@ -816,19 +816,6 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void gemm_w8a8_kernel(
     }
 }
 
-int cu_count() {
-    static int n = 0;
-    if (n == 0) {
-        int dev = 0, v = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-            n = v;
-        else
-            n = 256;
-    }
-    return n;
-}
-
 TilePlan plan_tiles(int64_t M, int64_t N) {
     TilePlan p{};
     const int tm = (int)((M + 255) / 256), tn = (int)((N + 255) / 256);

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/ql.h"
 
 namespace ql {
@@ -32,19 +34,23 @@ __device__ inline int8_t requant_code(float y, float s, float r) {
     return (int8_t)__builtin_amdgcn_fmed3f(rintf(qt), -127.0f, 127.0f);
 }
 
-// Compute units of the current device, read once per process (256 on MI355X; 256 if the
-// query fails). Launch shapes use it to size grids.
+// Compute units of the current device (256 on MI355X; 256 if the query fails), read once
+// per device under std::call_once, so concurrent first calls from several host threads are
+// safe. Launch shapes use it to size grids.
+constexpr int kMaxDevices = 64;
 inline int cu_count() {
-    static int n = 0;
-    if (n == 0) {
-        int dev = 0, v = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-            n = v;
-        else
-            n = 256;
-    }
-    return n;
+    static std::once_flag once[kMaxDevices];
+    static int count[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return 256;
+    std::call_once(once[dev], [dev] {
+        int v = 0;
+        count[dev] = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0
+                         ? v
+                         : 256;
+    });
+    return count[dev];
 }
 
 // Launch helpers, one per kernel family. Arguments are already validated; each returns

@@ -197,6 +197,7 @@ def test_fused_activation_none_is_plain(ql):
 
 
 @pytest.mark.parametrize("M,N,K,out,act", [(1, 4096, 4096, torch.float16, "none"), (33, 520, 384, torch.float32, "gelu"), (16, 256, 256, torch.float32, "none"), (300, 520, 384, torch.float16, "none"),
+                                           (16, 11008, 512, torch.float16, "silu"),
                                            (257, 129, 192, torch.float32, "gelu"), (2000, 8300, 64, torch.float16, "silu"),
                                            (2048, 11008, 4096, torch.float16, "none")])
 def test_asymmetric_layer(ql, M, N, K, out, act):
@@ -267,6 +268,7 @@ def _requant_case(ql, M, N, K, per_tensor, seed_shift=0):
 
 
 @pytest.mark.parametrize("M,N,K,per_tensor", [(1, 4096, 4096, False), (40, 1000, 640, True), (64, 257, 192, False),
+                                              (40, 9000, 640, False),
                                               (16, 256, 256, False), (16, 256, 256, True), (300, 520, 384, False),
                                               (257, 129, 192, True), (128, 1000, 128, False),
                                               (2000, 8300, 256, False), (2048, 11008, 4096, True)])
@@ -307,13 +309,18 @@ def test_requant_with_activation(ql, act, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 64), (1, 4096, 4096), (5, 17, 192), (16, 4096, 4096), (17, 300, 128),
-                                   (33, 1000, 640), (48, 16, 4096), (64, 11008, 4096), (64, 31, 64), (65, 300, 256),
-                                   (96, 1000, 640), (100, 17, 64), (128, 4096, 4096), (129, 300, 256)])
+                                   (33, 1000, 640), (48, 16, 4096), (64, 31, 64), (65, 300, 256),
+                                   (96, 1000, 640), (100, 17, 64), (128, 4096, 4096), (129, 300, 256),
+                                   (1, 11008, 4096), (16, 11008, 4096), (40, 9000, 640), (64, 10240, 192),
+                                   (64, 11008, 4096)])
 def test_few_rows_int32(ql, M, N, K):
     """M <= 128 with M * N <= 640K runs on the few-row kernel (16 columns per workgroup, K split over the waves,
-    16x16x64 matrix-core steps after a lane permutation; up to four row blocks with two wave
-    shapes, five to eight with a third): accumulators bit for bit, with codes at the extremes,
-    ragged N, one to 64 k-steps, and M = 129 back on the tile kernel."""
+    16x16x64 matrix-core steps after a lane permutation). Its three wave shapes are all covered:
+    eight waves of 8-step groups (at most 2 x CUs workgroups, M <= 64), four waves of 16-step
+    groups (more workgroups than that: N > 8192, e.g. M = 16, N = 11008, up to M * N = 640K at
+    M = 64, N = 10240), and eight waves of 4-step groups for five to eight row blocks.
+    Accumulators bit for bit, with codes at the extremes, ragged N, one to 64 k-steps, M = 129
+    back on the tile kernel, and M = 64, N = 11008 (past 640K) on the tile kernel."""
     rng = np.random.default_rng(M * 7919 + N + K)
     a = _rand_codes(rng, (M, K), -128)
     b = _rand_codes(rng, (N, K), -128)
