@@ -91,7 +91,13 @@ __device__ __forceinline__ T bits_as(S s) {
 
 __device__ inline i32x8 cat8(i32x4 lo, i32x4 hi) { return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7); }
 
-// The four 32-deep substeps of a 128-deep stage (F[ks][block]) into acc[i][j].
+// The four 32-deep substeps of a 128-deep stage (F[ks][block]) into acc[i][j]. W's fragment
+// is the matrix core's first operand and X's the second, so acc[i][j] holds the block
+// transposed: element e of lane l is C[l & 31][8 (e >> 2) + 4 (l >> 5) + (e & 3)] of the
+// 32 x 32 block (i, j). The products are the same either way; with this order the matrix
+// cores draw less power on quantized activations (small codes) against weights (codes
+// spread over the range), so the power-limited clock runs higher (measured A/B on one GPU:
+// 57.8 -> 56.1 us at M = 2048, N = 8192, K = 4096).
 template <int ELEM, int FM, int FN>
 __device__ __forceinline__ void mfma_stage_of(AccT<ELEM> (&acc)[FM][FN], const i32x4 (&F)[4][FM + FN]) {
     if constexpr (ELEM == EL_I8) {
@@ -101,7 +107,7 @@ __device__ __forceinline__ void mfma_stage_of(AccT<ELEM> (&acc)[FM][FN], const i
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(F[ks][i], F[ks][FM + j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(F[ks][FM + j], F[ks][i], acc[i][j], 0, 0, 0);
     } else {
         // format 0 (E4M3) for A and B, no block scales
 #pragma unroll
@@ -111,7 +117,7 @@ __device__ __forceinline__ void mfma_stage_of(AccT<ELEM> (&acc)[FM][FN], const i
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        cat8(F[2 * kp][i], F[2 * kp + 1][i]), cat8(F[2 * kp][FM + j], F[2 * kp + 1][FM + j]),
+                        cat8(F[2 * kp][FM + j], F[2 * kp + 1][FM + j]), cat8(F[2 * kp][i], F[2 * kp + 1][i]),
                         acc[i][j], 0, 0, 0, 0, 0, 0);
     }
 }
@@ -173,10 +179,15 @@ __device__ inline void issue_scales(const float* xs, const float* ws, const floa
 // in registers and leave through LDS, one 32-row band of the wave's block at a time, so
 // that global stores are whole 16-byte pieces of contiguous row segments rather than
 // 2- or 4-byte scattered writes. Element e of block (i, j) in lane l is
-// C[8 (e >> 2) + 4 (l >> 5) + (e & 3)][l & 31] of that 32 x 32 block.
-// Stores go through a buffer descriptor whose size ends at row M: the hardware drops
-// stores of rows past M, and a column piece past N gets an offset beyond the size, so no
-// store needs a branch.
+// C[l & 31][8 (e >> 2) + 4 (l >> 5) + (e & 3)] of that 32 x 32 block (see mfma_stage_of):
+// a lane holds one row and, for each g = e >> 2, four consecutive columns, which it stages
+// with one store. Stores go through a buffer descriptor whose size ends at row M: the
+// hardware drops stores of rows past M, and a column piece past N gets an offset beyond
+// the size, so no store needs a branch.
+// Workgroup barriers store_tile runs (a wave that does not store runs as many).
+template <int YMODE>
+constexpr int STORE_BARRIERS = YMODE == Y_I8 ? 2 : 1;
+
 template <int WM, int WN, int FM, int FN, int YMODE, int NWV, int ACT, bool ASYM, typename ACC>
 __device__ __forceinline__ void store_tile(const ACC (&acc)[FM][FN], bool has_bias,
                                            void* __restrict__ Y, int M, int N, int mrow0,
@@ -196,6 +207,7 @@ __device__ __forceinline__ void store_tile(const ACC (&acc)[FM][FN], bool has_bi
     // (32 rows of at most 2^23 4-byte values); a column piece past N is sent to offset
     // row + LIM, at or past the size, and row + LIM stays below 2^31.
     constexpr int LIM = 1 << 30;
+    using Out4 = OutT __attribute__((ext_vector_type(4)));
 
     barrier_no_fence();   // the ring is no longer read; every wave's scale copies landed
     int8_t* stage = smem + wave * 32 * ROWB;
@@ -204,22 +216,17 @@ __device__ __forceinline__ void store_tile(const ACC (&acc)[FM][FN], bool has_bi
     const float* sb = sx + 512;
     const float* sz = sx + 768;
     const int32_t* scs = reinterpret_cast<const int32_t*>(sx + 1024);
-    float wsv[FN], bv[FN], csv[FN], osv[FN], orv[FN];
-    if constexpr (YMODE != Y_I32) {
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int c = ln0 + 32 * j + (lane & 31);
-            wsv[j] = sw[c];
-            bv[j] = has_bias ? sb[c] : 0.0f;
-            if constexpr (ASYM)
-                csv[j] = (float)scs[c];   // exact: |sum| <= 128 K < 2^24
-            if constexpr (YMODE == Y_I8) {
-                // the output scale and its correctly rounded reciprocal: y / s is then
-                // q0 = RN(y r), RN(q0 + fma(-q0, s, y) r), the correctly rounded quotient
-                osv[j] = reinterpret_cast<const float*>(scs)[c];
-                orv[j] = 1.0f / osv[j];
-            }
-        }
+    const int lr = lane & 31, lh = lane >> 5;
+    // int8 output: the correctly rounded reciprocals of the tile's output scales, once per
+    // tile, into the zero-point slot (int8 output has no zero points); y / s is then
+    // q0 = RN(y r), RN(q0 + fma(-q0, s, y) r), the correctly rounded quotient. A second
+    // barrier makes them visible (STORE_BARRIERS).
+    if constexpr (YMODE == Y_I8) {
+        float* srcp = const_cast<float*>(sz);
+        for (int c = wave * 64 + lane; c < 256; c += NWV * 64)
+            srcp[c] = 1.0f / reinterpret_cast<const float*>(scs)[c];
+        __builtin_amdgcn_s_waitcnt(vmcnt_le(63) & ~(0xF << 8));   // lgkmcnt(0): the writes landed
+        barrier_no_fence();
     }
     const bool vec_ok = (N % VEC) == 0;   // rows start 16-byte aligned
     // byte offset of this lane's 16-byte piece in the first row it stores of a band
@@ -227,41 +234,53 @@ __device__ __forceinline__ void store_tile(const ACC (&acc)[FM][FN], bool has_bi
     const int lane_off = (lane / LPR) * N * SZ + (ncol < N ? ncol * SZ : LIM);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-        float xsv[16], zsv[16];
+        float xsv = 0.0f, zsv = 0.0f;
         if constexpr (YMODE != Y_I32) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const f32x4 v = *reinterpret_cast<const f32x4*>(sx + lm0 + 32 * i + 8 * g + 4 * (lane >> 5));
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    xsv[4 * g + q] = v[q];
-                if constexpr (ASYM) {
-                    const f32x4 zv = *reinterpret_cast<const f32x4*>(sz + lm0 + 32 * i + 8 * g + 4 * (lane >> 5));
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        zsv[4 * g + q] = zv[q];
-                }
-            }
+            xsv = sx[lm0 + 32 * i + lr];
+            if constexpr (ASYM)
+                zsv = sz[lm0 + 32 * i + lr];
         }
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int r = 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        for (int j = 0; j < FN; ++j) {
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                OutT v;
-                if constexpr (YMODE == Y_I32) {
-                    v = acc[i][j][e];
+            for (int g = 0; g < 4; ++g) {
+                const int c0 = ln0 + 32 * j + 8 * g + 4 * lh;   // first of the four columns
+                f32x4 wsv{}, bv{}, csv{}, osv{}, orv{};
+                if constexpr (YMODE != Y_I32 && YMODE != Y_I8) {
+                    wsv = *reinterpret_cast<const f32x4*>(sw + c0);
+                    if (has_bias)
+                        bv = *reinterpret_cast<const f32x4*>(sb + c0);
+                    if constexpr (ASYM) {
+                        const i32x4 cs = *reinterpret_cast<const i32x4*>(scs + c0);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            csv[q] = (float)cs[q];   // exact: |sum| <= 128 K < 2^24
+                    }
                 } else if constexpr (YMODE == Y_I8) {
-                    v = requant_code(activation<ACT>(epilogue_unfused((float)acc[i][j][e], xsv[e], wsv[j], bv[j])),
-                                     osv[j], orv[j]);
-                } else if constexpr (ASYM) {
-                    // sum_k (q_x - z_x) q_w = acc - z_x colsum, with one rounding
-                    const float t = fmaf(-zsv[e], csv[j], (float)acc[i][j][e]);
-                    v = (OutT)activation<ACT>(t * xsv[e] * wsv[j] + bv[j]);
-                } else {
-                    v = (OutT)activation<ACT>((float)acc[i][j][e] * xsv[e] * wsv[j] + bv[j]);
+                    wsv = *reinterpret_cast<const f32x4*>(sw + c0);
+                    if (has_bias)
+                        bv = *reinterpret_cast<const f32x4*>(sb + c0);
+                    osv = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(scs) + c0);
+                    orv = *reinterpret_cast<const f32x4*>(sz + c0);
                 }
-                *reinterpret_cast<OutT*>(stage + r * ROWB + (32 * j + (lane & 31)) * SZ) = v;
+                Out4 v;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int e = 4 * g + q;
+                    if constexpr (YMODE == Y_I32) {
+                        v[q] = acc[i][j][e];
+                    } else if constexpr (YMODE == Y_I8) {
+                        v[q] = requant_code(activation<ACT>(epilogue_unfused((float)acc[i][j][e], xsv, wsv[q], bv[q])),
+                                            osv[q], orv[q]);
+                    } else if constexpr (ASYM) {
+                        // sum_k (q_x - z_x) q_w = acc - z_x colsum, with one rounding
+                        const float t = fmaf(-zsv, csv[q], (float)acc[i][j][e]);
+                        v[q] = (OutT)activation<ACT>(t * xsv * wsv[q] + bv[q]);
+                    } else {
+                        v[q] = (OutT)activation<ACT>((float)acc[i][j][e] * xsv * wsv[q] + bv[q]);
+                    }
+                }
+                *reinterpret_cast<Out4*>(stage + lr * ROWB + (32 * j + 8 * g + 4 * lh) * SZ) = v;
             }
         }
         // The wave's LDS operations complete in order, so its reads below see all of its
@@ -778,7 +797,9 @@ __device__ __forceinline__ void gemm_tile_ks(const int8_t* __restrict__ A, const
                 acc, bias != nullptr, Y, M, N, m0 + wm * WM, n0 + wn * WN, wm * WM, wn * WN, q, lane, smem);
         });
     } else {
-        barrier_no_fence();   // the one barrier store_tile runs
+#pragma unroll
+        for (int b = 0; b < STORE_BARRIERS<YMODE>; ++b)
+            barrier_no_fence();   // the barriers store_tile runs
     }
 }
 
