@@ -12,14 +12,19 @@ constexpr int64_t kMaxKw8a8 = 131008;           // K * 128^2 < 2^31, K % 64 == 0
 constexpr int64_t kMaxNw8a8 = (int64_t)1 << 23; // 32 output rows of 4-byte values: 2^30 bytes
 constexpr int64_t kMaxKwonly = (int64_t)1 << 22; // 64 rows of fp16 X and 64 weight columns < 2^31 bytes
 
-// The few-row kernel (gemm_w8a8_small.hip) has N/16 workgroups, each reading all of X, so its
-// time grows with M*N while the tile kernel's stays flat until its tiles fill the chip.
-// Measured at K = 4096, the few-row kernel wins up to M*N of about 640K (M = 32, N = 11008:
-// 17.5 against 33.1 us; M = 128, N = 4096: 19 against 25 us) and loses past it (M = 64,
-// N = 11008: 36.0 against 34.3 us).
+// Three W8A8 kernels share the calls: the few-row kernel (gemm_w8a8_small.hip, N / 16
+// workgroups each reading all of X), the 64 x 64 tile kernel (gemm_w8a8_mid.hip) and the
+// 256 x 256 / 128 x 256 tile kernel (gemm_w8a8.hip); launch_gemm_w8a8 chooses between the
+// last two. The few-row kernel's time grows with M * N, the 64 x 64 kernel's stays flat while
+// its tiles make one round (M <= 64 up to N = 16384). Measured (us, few-row / 64 x 64) at
+// K = 4096: N = 4096 M = 64 11.6 / 12.8, M = 96 14.9 / 13.2; N = 11008 M = 16 14.5 / 16.5,
+// M = 32 21.2 / 16.7; N = 14336 M = 1 13.1 / 17.0, M = 16 17.7 / 17.1. The crossover moves
+// with N, hardly with K (K = 11008 and 14336 give the same choices within 5%, except
+// N = 4096, M = 96 at K = 14336: 41.7 / 43.8).
 constexpr int64_t kSmallM = 128;
-constexpr int64_t kSmallMN = 640 * 1024;
-inline bool few_rows(int64_t M, int64_t N) { return M <= kSmallM && M * N <= kSmallMN; }
+inline bool few_rows(int64_t M, int64_t N) {
+    return M <= kSmallM && (M <= 8 || (M * N <= 256 * 1024 && N <= 12288));
+}
 
 inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 

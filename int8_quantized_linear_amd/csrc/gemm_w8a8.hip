@@ -859,6 +859,17 @@ TilePlan plan_tiles(int64_t M, int64_t N) {
     return p;
 }
 
+// The 64 x 64 kernel (gemm_w8a8_mid.hip) takes the shapes where the tile plan puts at most
+// half of the CUs to work and its own tiles make at most two rounds. Measured at K = 4096
+// (us, tile plan against 64 x 64 tiles): N = 4096: M = 256 24.3 / 13.5, M = 512 25.5 / 17.2,
+// M = 768 27.3 / 28.4; N = 11008: M = 129 26.7 / 27.0, M = 256 27.6 / 29.1; at M = 256,
+// N = 4096 also K = 11008 53.7 / 30.6 and K = 14336 66.4 / 38.4.
+bool use_mid_tiles(const TilePlan& p, int64_t M, int64_t N) {
+    const int wgs = p.nbig > p.nsmall ? p.nbig : p.nsmall;
+    const int64_t mid = ((M + 63) / 64) * ((N + 63) / 64);
+    return 2 * wgs <= cu_count() && mid <= 2 * (int64_t)cu_count();
+}
+
 }  // namespace
 
 ql_status launch_gemm_w8a8(const int8_t* xq, const float* x_scale, const int8_t* wq,
@@ -869,6 +880,11 @@ ql_status launch_gemm_w8a8(const int8_t* xq, const float* x_scale, const int8_t*
     if (M == 0 || N == 0)
         return QL_OK;
     const TilePlan plan = plan_tiles(M, N);
+    if (use_mid_tiles(plan, M, N)) {
+        // the tile plan would leave most CUs idle: 64 x 64 tiles instead
+        return launch_gemm_w8a8_mid(xq, x_scale, wq, w_scale, bias, y, y_mode, act, x_zero, colsum, out_scale,
+                                    out_scale_n, M, N, K, stream, e4m3);
+    }
     // Workgroup b runs big tile b (b < nbig) and then half tile b (b < nsmall), so the
     // half tiles start on the first CUs to finish a big tile without a new dispatch and
     // their first copies overlap the big tile's last stores.

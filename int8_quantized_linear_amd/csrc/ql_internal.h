@@ -85,6 +85,13 @@ ql_status launch_gemm_w8a8_small(const int8_t* xq, const float* x_scale, const i
                                  const float* x_zero, const int32_t* colsum, const float* out_scale,
                                  int out_scale_n, int64_t M, int64_t N, int64_t K, hipStream_t stream,
                                  bool e4m3 = false);
+// The W8A8 layer on 64 x 64 tiles (row counts between the few-row kernel's and where the tile
+// kernel fills the chip), with the same epilogue modes as launch_gemm_w8a8_small.
+ql_status launch_gemm_w8a8_mid(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                               const float* w_scale, const float* bias, void* y, int y_mode, int act,
+                               const float* x_zero, const int32_t* colsum, const float* out_scale,
+                               int out_scale_n, int64_t M, int64_t N, int64_t K, hipStream_t stream,
+                               bool e4m3 = false);
 ql_status launch_wonly(const void* x, const void* codes, int fmt, const void* scale,
                        const uint8_t* zp, int64_t group, const float* bias, void* y, int64_t M,
                        int64_t N, int64_t K, int act, hipStream_t stream);

@@ -110,12 +110,12 @@ def _half_integer_codes(rng, shape) -> np.ndarray:
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 64), (16, 256, 256), (300, 520, 384), (257, 129, 192),
                                    (128, 300, 128), (2000, 8300, 256), (64, 256, 4096), (16, 11008, 1024),
-                                   (64, 10240, 192)])
+                                   (24, 10240, 192), (200, 3001, 576)])
 def test_exact_sums(ql, M, N, K):
     """With unit scales, no bias and fp32 output, y is the exact sum of products: any
     dropped, repeated or misplaced product shows. Covers several tiles, ragged M and N,
-    half-height tiles, the mixed big/half tile plan, a long K, and the few-row kernel's
-    four-wave shape (more than 2 x CUs workgroups of 16 columns, M * N <= 640K)."""
+    the 64 x 64 kernel (with a half-deep last stage), the mixed big/half tile plan, a long K,
+    and the few-row kernel's four-wave shape (more than 2 x CUs workgroups of 16 columns)."""
     rng = np.random.default_rng(M + 3 * N + 7 * K)
     a = _half_integer_codes(rng, (M, K))
     b = _half_integer_codes(rng, (N, K))

@@ -32,9 +32,9 @@ def _rand_codes(rng, shape, lo=-127):
                                    (512, 768, 1024), (33, 1000, 192), (256, 256, 64),
                                    (100, 1000, 384), (128, 300, 128), (64, 256, 640), (127, 513, 256)])
 def test_int32_bit_exact(ql, M, N, K):
-    """Several tiles in M and N, ragged tails, K with a half k-tile tail, codes including -128.
-    M <= 128 runs on the few-row kernel, larger M on the tile kernel (whose half-height
-    tiles appear in the mixed plans below), with 1, 2, 3 and 5 128-deep stages."""
+    """Several tiles in M and N, ragged tails, K with a half k-tile tail, codes including -128,
+    with 1, 2, 3 and 5 128-deep stages: small M on the few-row kernel, the others on the 64 x 64
+    kernel (the 256 x 256 / 128 x 256 tile kernel's plans are covered below)."""
     rng = np.random.default_rng(M * 1000 + N + K)
     a = _rand_codes(rng, (M, K), -128)
     b = _rand_codes(rng, (N, K), -128)
@@ -268,7 +268,7 @@ def _requant_case(ql, M, N, K, per_tensor, seed_shift=0):
 
 
 @pytest.mark.parametrize("M,N,K,per_tensor", [(1, 4096, 4096, False), (40, 1000, 640, True), (64, 257, 192, False),
-                                              (40, 9000, 640, False),
+                                              (20, 9000, 640, False),
                                               (16, 256, 256, False), (16, 256, 256, True), (300, 520, 384, False),
                                               (257, 129, 192, True), (128, 1000, 128, False),
                                               (2000, 8300, 256, False), (2048, 11008, 4096, True)])
@@ -310,17 +310,18 @@ def test_requant_with_activation(ql, act, M, N, K):
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 64), (1, 4096, 4096), (5, 17, 192), (16, 4096, 4096), (17, 300, 128),
                                    (33, 1000, 640), (48, 16, 4096), (64, 31, 64), (65, 300, 256),
-                                   (96, 1000, 640), (100, 17, 64), (128, 4096, 4096), (129, 300, 256),
-                                   (1, 11008, 4096), (16, 11008, 4096), (40, 9000, 640), (64, 10240, 192),
+                                   (96, 1000, 640), (100, 17, 64), (128, 2048, 4096), (129, 300, 256),
+                                   (1, 11008, 4096), (16, 11008, 4096), (24, 10240, 640), (8, 16384, 192),
                                    (64, 11008, 4096)])
 def test_few_rows_int32(ql, M, N, K):
-    """M <= 128 with M * N <= 640K runs on the few-row kernel (16 columns per workgroup, K split over the waves,
-    16x16x64 matrix-core steps after a lane permutation). Its three wave shapes are all covered:
-    eight waves of 8-step groups (at most 2 x CUs workgroups, M <= 64), four waves of 16-step
-    groups (more workgroups than that: N > 8192, e.g. M = 16, N = 11008, up to M * N = 640K at
-    M = 64, N = 10240), and eight waves of 4-step groups for five to eight row blocks.
-    Accumulators bit for bit, with codes at the extremes, ragged N, one to 64 k-steps, M = 129
-    back on the tile kernel, and M = 64, N = 11008 (past 640K) on the tile kernel."""
+    """The few-row kernel takes M <= 8, or M <= 128 with M * N <= 256K and N <= 12288 (16
+    columns per workgroup, K split over the waves, 16x16x64 matrix-core steps after a lane
+    permutation). Its three wave shapes are all covered: eight waves of 8-step groups (at most
+    2 x CUs workgroups, M <= 64), four waves of 16-step groups (more workgroups than that:
+    N > 8192, e.g. M = 16, N = 11008; M = 24, N = 10240; M = 8, N = 16384), and eight waves of
+    4-step groups for five to eight row blocks (M = 65 .. 128). Accumulators bit for bit, with
+    codes at the extremes, ragged N, one to 64 k-steps; M = 129 and M = 64, N = 11008 (past
+    256K) run on the 64 x 64 kernel."""
     rng = np.random.default_rng(M * 7919 + N + K)
     a = _rand_codes(rng, (M, K), -128)
     b = _rand_codes(rng, (N, K), -128)
@@ -354,3 +355,56 @@ def test_few_rows_layer(ql, act, M, N, K, out):
         tol = tol + f16_ulp(ref)
     y = host(g.view).astype(np.float64)
     assert np.all(np.abs(y - ref) <= tol)
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 4096, 256), (65, 4096, 256), (8, 14336, 192), (9, 14336, 192),
+                                   (16, 11008, 128), (24, 11008, 128), (512, 4096, 256), (513, 4096, 256),
+                                   (128, 11008, 320), (129, 11008, 320), (200, 3001, 576), (1024, 4096, 192),
+                                   (600, 9000, 192)])
+def test_kernel_switches_int32(ql, M, N, K):
+    """Shapes on both sides of each switch between the three W8A8 kernels: few-row against
+    64 x 64 tiles (M * N = 256K at N = 4096; M = 8 against 9 at N = 14336 > 12288; 16 against
+    24 rows at N = 11008), 64 x 64 tiles against the tile kernel (M = 512 against 513 at
+    N = 4096, where 64 x 64 tiles pass two rounds; M = 128 against 129 at N = 11008), a ragged
+    64 x 64 case with a half-deep last stage, and the tile kernel's half-height-only plan
+    (M = 1024, N = 4096; ragged at M = 600, N = 9000). Accumulators bit for bit on rows
+    sampled from every 64-row band."""
+    rng = np.random.default_rng(M * 7 + N * 3 + K)
+    a = _rand_codes(rng, (M, K), -128)
+    b = _rand_codes(rng, (N, K), -128)
+    acc = host(ql.gemm_w8a8_int32(dev(a), dev(b)))
+    rows = np.unique(np.concatenate([np.arange(0, M, 13), np.arange(max(0, M - 3), M)]))
+    assert np.array_equal(acc[rows], oracle.gemm_i32(a[rows], b))
+
+
+@pytest.mark.parametrize("act", ["none", "gelu"])
+@pytest.mark.parametrize("M,N,K,out", [(200, 3001, 576, torch.float16), (300, 1000, 256, torch.float32),
+                                       (40, 11008, 512, torch.float16)])
+def test_mid_tile_layer(ql, act, M, N, K, out):
+    """The 64 x 64 kernel's epilogue (ragged N with scalar stores, fp16 and fp32 output, a fused
+    activation): within the tile kernel's tolerances, and with act = none bit for bit the value
+    the plain call gives."""
+    w = workloads.with_shape(workloads.W8A8_PREFILL, M, K, N, seed=M + N)
+    inp, (xq, xs, wq, ws), (xq_r, xs_r, wq_r, ws_r) = _layer(ql, w)
+    g = Guarded((M, N), out)
+    ql.gemm_w8a8_per_channel_act(xq, xs, wq, ws, dev(inp.bias), act, out, y=g.view)
+    g.check()
+    acc_ref = oracle.gemm_i32(xq_r, wq_r)
+    y32, y64 = oracle.epilogue_w8a8(acc_ref, xs_r, ws_r, inp.bias)
+    y = host(g.view).astype(np.float64)
+    mag = np.abs(acc_ref.astype(np.float64) * xs_r[:, None] * ws_r[None, :]) + np.abs(inp.bias)[None, :]
+    if act == "none":
+        if out == torch.float32:
+            assert np.all(np.abs(y - y64) <= 1e-5 * mag)
+        else:
+            ref16 = y32.astype(np.float16).astype(np.float64)
+            assert np.all(np.abs(y - ref16) <= f16_ulp(ref16))
+        plain = host(ql.gemm_w8a8_per_channel(xq, xs, wq, ws, dev(inp.bias), out))
+        assert np.array_equal(plain.view(np.uint8), host(g.view).view(np.uint8))
+    else:
+        a64 = oracle.activation_f64(y64, ACT[act])
+        if out == torch.float32:
+            assert np.all(np.abs(y - a64) <= 1.2e-5 * mag + 2e-6 * np.abs(a64))
+        else:
+            ref16 = a64.astype(np.float16).astype(np.float64)
+            assert np.all(np.abs(y - ref16) <= f16_ulp(ref16))
