@@ -147,13 +147,15 @@ struct Geo {
     static_assert(WB == 8 || WB == 16, "a lane loads 8 or 16 bytes of a column per step");
 };
 
-// Activation ring in LDS. A slot holds one k-step of the launch's 16 MT rows: RB bytes per
+// Activation ring in LDS. A slot holds one k-step of the launch's XR rows (16 MT, or 8 for a
+// launch of at most 8 rows, which then copies half as many bytes per step: W8A16 at M = 1
+// 5.59 -> 5.30 us, block-asymmetric at M = 8 7.65 -> 7.35 us, measured A/B): RB bytes per
 // row, filled by NXC copies of 1 KiB (RPC rows each). Chunk c (16 bytes) of row r sits at
 // position c ^ (r & XM) of its row, so that the 16 lanes of an MFMA-layout read (16 rows,
 // one chunk) fall on 16 different bank groups, while the 4 lanes of a copy quad still read
 // one aligned 64-byte piece. With 8 rows per copy (128-byte rows) a 16-byte pad after each
 // copy moves rows 8..15 to the other bank groups.
-template <int KS, int MT>
+template <int KS, int XR>
 struct XRing {
     static constexpr int RB = KS * 2;
     static constexpr int CPR = RB / 16;               // chunks per row
@@ -161,7 +163,7 @@ struct XRing {
     static constexpr int XM = CPR - 1;                // swizzle mask
     static constexpr int PAD = RPC == 8 ? 16 : 0;
     static constexpr int CSTRIDE = 1024 + PAD;        // bytes per copy in LDS
-    static constexpr int NXC = MT * 16 / RPC;         // copies per slot
+    static constexpr int NXC = XR / RPC;              // copies per slot
     static constexpr int SLOT = NXC * CSTRIDE;
     static constexpr int ISTRIDE = (16 / RPC) * CSTRIDE;   // bytes between 16-row blocks
     static constexpr int QV = CPR / RPC > 1 ? CPR / RPC : 1;   // copies before the swizzle repeats
@@ -183,13 +185,17 @@ constexpr int SL_WORDS = 4096;   // 16 KB
 // ring allow, as a power of two (at most 16) so that it divides a wave's step count when
 // K is a multiple of 4 * KS * D (the loop is padded to whole rings with zero-filled steps).
 // The waves' partial sums share the first ring slot when they fit in it.
-template <int KS, int MT, int NT>
+// Rows of the activation ring: 16 per block, or 8 when the launch has at most 8 rows (HX).
+template <int MT, bool HX>
+constexpr int xrows() { return HX ? 8 : 16 * MT; }
+
+template <int KS, int MT, int NT, bool HX>
 constexpr int red_extra() {
-    constexpr int red = nwaves<MT>() * MT * NT * 64 * 16, slot = nwaves<MT>() * XRing<KS, MT>::SLOT;
+    constexpr int red = nwaves<MT>() * MT * NT * 64 * 16, slot = nwaves<MT>() * XRing<KS, xrows<MT, HX>()>::SLOT;
     return red > slot ? red : 0;
 }
 
-template <int FMT, int KS, int MT, int NT, bool GLOAD>
+template <int FMT, int KS, int MT, int NT, bool GLOAD, bool HX>
 constexpr int ring_depth() {
     using G = Geo<FMT, KS>;
     constexpr int per_step = NT * (G::WB / 4) + (GLOAD ? NT * (FMT == W_UINT8_ZP ? 2 : 1) : 0);
@@ -197,7 +203,8 @@ constexpr int ring_depth() {
     // one wave per SIMD may use about 280 registers (VGPRs and AGPRs); two share the file
     // and get about 200 each
     constexpr int dr = ((nwaves<MT>() == 4 ? 280 : 200) - fixed) / per_step;
-    constexpr int dl = (LDS_BUDGET - SL_WORDS * 4 - red_extra<KS, MT, NT>()) / (nwaves<MT>() * XRing<KS, MT>::SLOT);
+    constexpr int dl = (LDS_BUDGET - SL_WORDS * 4 - red_extra<KS, MT, NT, HX>()) /
+                       (nwaves<MT>() * XRing<KS, xrows<MT, HX>()>::SLOT);
     constexpr int d = dr < dl ? dr : dl;
     // at most 8: each slot is its own LDS array (see the kernel)
     return d >= 8 ? 8 : d >= 4 ? 4 : 2;
@@ -208,13 +215,13 @@ constexpr int ring_depth() {
 // column col0 + 16 j + ln of block j. SCALES: 0 = one scale per column (applied at the
 // end), 1 = per group, staged in LDS, 2 = per group, loaded from global memory each step
 // (blocks too large for LDS).
-template <int FMT, int KS, int MT, int NT, int SCALES, int D>
+template <int FMT, int KS, int MT, int NT, int SCALES, int D, bool HX>
 __global__ __launch_bounds__(64 * nwaves<MT>()) void wonly_kernel(
     const _Float16* __restrict__ X, const uint8_t* __restrict__ Wc, const void* __restrict__ scale,
     const uint8_t* __restrict__ zp, int group, const float* __restrict__ bias,
     _Float16* __restrict__ Y, int M, int N, int K, int cols, int act) {
     using G = Geo<FMT, KS>;
-    using XG = XRing<KS, MT>;
+    using XG = XRing<KS, xrows<MT, HX>()>;
     using WR = typename G::WR;
     constexpr int NW = nwaves<MT>();
     constexpr int HN = G::HN;
@@ -226,7 +233,7 @@ __global__ __launch_bounds__(64 * nwaves<MT>()) void wonly_kernel(
     // copies), not every copy in flight. After the K loop the waves' partial sums go to
     // slot 0, or to an array of their own when larger.
     static_assert(D <= 8, "one LDS array per ring slot");
-    constexpr int SLOTB = NW * XG::SLOT, REDX = red_extra<KS, MT, NT>();
+    constexpr int SLOTB = NW * XG::SLOT, REDX = red_extra<KS, MT, NT, HX>();
     __shared__ __attribute__((aligned(16))) char xs0[SLOTB];
     __shared__ __attribute__((aligned(16))) char xs1[D > 1 ? SLOTB : 16];
     __shared__ __attribute__((aligned(16))) char xs2[D > 2 ? SLOTB : 16];
@@ -308,7 +315,10 @@ __global__ __launch_bounds__(64 * nwaves<MT>()) void wonly_kernel(
     // Fragment reads: row 16 i + ln, chunk HN lg + h, in this wave's ring.
     int xfo[HN];
     {
-        const int row = (ln / XG::RPC) * XG::CSTRIDE + (ln % XG::RPC) * XG::RB;
+        // with an 8-row ring (HX), lanes of rows 8..15 read rows 0..7 again: those output rows
+        // are past M and never stored, and an MFMA output row depends on its own input row only
+        const int rr = HX ? (ln & 7) : ln;
+        const int row = (rr / XG::RPC) * XG::CSTRIDE + (rr % XG::RPC) * XG::RB;
 #pragma unroll
         for (int h = 0; h < HN; ++h)
             xfo[h] = wave * XG::SLOT + row + (((HN * lg + h) ^ (ln & XG::XM)) * 16);
@@ -533,31 +543,31 @@ __global__ __launch_bounds__(64 * nwaves<MT>()) void wonly_kernel(
         finish(std::integral_constant<int, ACT_NONE>{});
 }
 
-template <int FMT, int KS, int MT, int NT, int SCALES>
+template <int FMT, int KS, int MT, int NT, int SCALES, bool HX>
 ql_status launch_cfg(const void* x, const void* codes, const void* scale, const uint8_t* zp,
                      int64_t group, const float* bias, void* y, int64_t M, int64_t N, int64_t K,
                      int cols, int act, hipStream_t stream) {
-    constexpr int D = ring_depth<FMT, KS, MT, NT, SCALES == 2>();
+    constexpr int D = ring_depth<FMT, KS, MT, NT, SCALES == 2, HX>();
     const dim3 grid((unsigned)((N + cols - 1) / cols)), block(64 * nwaves<MT>());
-    hipLaunchKernelGGL((wonly_kernel<FMT, KS, MT, NT, SCALES, D>), grid, block, 0, stream,
+    hipLaunchKernelGGL((wonly_kernel<FMT, KS, MT, NT, SCALES, D, HX>), grid, block, 0, stream,
                        reinterpret_cast<const _Float16*>(x), reinterpret_cast<const uint8_t*>(codes),
                        scale, zp, (int)group, bias, reinterpret_cast<_Float16*>(y), (int)M, (int)N,
                        (int)K, cols, act);
     return launch_status();
 }
 
-template <int FMT, int KS, int MT, int SCALES>
+template <int FMT, int KS, int MT, int SCALES, bool HX>
 ql_status launch_nt(const void* x, const void* codes, const void* scale, const uint8_t* zp,
                     int64_t group, const float* bias, void* y, int64_t M, int64_t N, int64_t K,
                     int cols, int act, hipStream_t stream) {
     if (cols <= 16)
-        return launch_cfg<FMT, KS, MT, 1, SCALES>(x, codes, scale, zp, group, bias, y, M, N, K, cols, act, stream);
+        return launch_cfg<FMT, KS, MT, 1, SCALES, HX>(x, codes, scale, zp, group, bias, y, M, N, K, cols, act, stream);
     if (cols <= 32)
-        return launch_cfg<FMT, KS, MT, 2, SCALES>(x, codes, scale, zp, group, bias, y, M, N, K, cols, act, stream);
-    return launch_cfg<FMT, KS, MT, 4, SCALES>(x, codes, scale, zp, group, bias, y, M, N, K, cols, act, stream);
+        return launch_cfg<FMT, KS, MT, 2, SCALES, HX>(x, codes, scale, zp, group, bias, y, M, N, K, cols, act, stream);
+    return launch_cfg<FMT, KS, MT, 4, SCALES, HX>(x, codes, scale, zp, group, bias, y, M, N, K, cols, act, stream);
 }
 
-template <int FMT, int KS, int MT>
+template <int FMT, int KS, int MT, bool HX = false>
 ql_status launch_mt(const void* x, const void* codes, const void* scale, const uint8_t* zp,
                     int64_t group, const float* bias, void* y, int64_t M, int64_t N, int64_t K,
                     bool grouped, int act, hipStream_t stream) {
@@ -567,13 +577,13 @@ ql_status launch_mt(const void* x, const void* codes, const void* scale, const u
     if (cols > 64)
         cols = 64;
     if (!grouped)
-        return launch_nt<FMT, KS, MT, 0>(x, codes, scale, zp, group, bias, y, M, N, K, (int)cols, act, stream);
+        return launch_nt<FMT, KS, MT, 0, HX>(x, codes, scale, zp, group, bias, y, M, N, K, (int)cols, act, stream);
     // The scale block (and zero-point block after it, at a 64-word boundary) must fit in LDS.
     const int64_t ng = K / group, sb = FMT == W_INT4_SYM ? 2 : 4;
     const int64_t words = ((cols * ng * sb + 3) / 4 + 63) / 64 * 64 + (FMT == W_UINT8_ZP ? (cols * ng + 3) / 4 : 0);
     if (words + 63 <= SL_WORDS)
-        return launch_nt<FMT, KS, MT, 1>(x, codes, scale, zp, group, bias, y, M, N, K, (int)cols, act, stream);
-    return launch_nt<FMT, KS, MT, 2>(x, codes, scale, zp, group, bias, y, M, N, K, (int)cols, act, stream);
+        return launch_nt<FMT, KS, MT, 1, HX>(x, codes, scale, zp, group, bias, y, M, N, K, (int)cols, act, stream);
+    return launch_nt<FMT, KS, MT, 2, HX>(x, codes, scale, zp, group, bias, y, M, N, K, (int)cols, act, stream);
 }
 
 template <int FMT, int KS>
@@ -586,7 +596,9 @@ ql_status launch_rows(const void* x, const void* codes, const void* scale, const
         const void* xs = reinterpret_cast<const _Float16*>(x) + m0 * K;
         void* ys = reinterpret_cast<_Float16*>(y) + m0 * N;
         ql_status st;
-        if (mc <= 16)
+        if (mc <= 8)
+            st = launch_mt<FMT, KS, 1, true>(xs, codes, scale, zp, group, bias, ys, mc, N, K, grouped, act, stream);
+        else if (mc <= 16)
             st = launch_mt<FMT, KS, 1>(xs, codes, scale, zp, group, bias, ys, mc, N, K, grouped, act, stream);
         else if (mc <= 32)
             st = launch_mt<FMT, KS, 2>(xs, codes, scale, zp, group, bias, ys, mc, N, K, grouped, act, stream);
