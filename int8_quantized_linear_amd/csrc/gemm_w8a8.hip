@@ -198,7 +198,12 @@ __device__ __forceinline__ void store_tile(const ACC (&acc)[FM][FN], bool has_bi
                  typename std::conditional<YMODE == Y_I8, int8_t, int32_t>::type>::type>::type;
     constexpr int SZ = sizeof(OutT);
     constexpr int VEC = 16 / SZ;                    // elements per 16-byte store
-    constexpr int ROWB = WN * SZ + 32;              // staged row, padded: rows r, r + 4 differ in bank half
+    // Staged row pitch: a row plus 16 bytes. A lane stages 4 * SZ bytes of its own row per
+    // store, so the lanes served together sit in rows ROWB / 4 words apart: with the 16-byte
+    // pad 16-byte stores (fp32, int32) hit distinct banks and 8-byte stores (fp16) at most two
+    // to a bank (a 32-byte pad put four fp16 stores on one bank). Rows stay 16-byte aligned
+    // for the 16-byte reads below.
+    constexpr int ROWB = WN * SZ + 16;
     constexpr int LPR = WN * SZ / 16;               // lanes per staged row
     constexpr int RPI = 64 / LPR;                   // rows per read / store instruction
     constexpr int NRD = 32 / RPI;                   // reads (and stores) per band
