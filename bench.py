@@ -322,7 +322,7 @@ def measured_ceilings(dev, byte_counts, progress):
         raise RuntimeError("qlp_cu_count failed")
     stream = torch.cuda.current_stream(dev)
     sh = ctypes.c_void_p(stream.cuda_stream)
-    sink = torch.empty(cus * 256, dtype=torch.int32, device=dev)
+    sink = torch.empty(cus * 512, dtype=torch.int32, device=dev)
 
     def check(rc, what):
         if rc != 0:
@@ -364,6 +364,46 @@ def measured_ceilings(dev, byte_counts, progress):
     return out
 
 
+def read_sweep(dev, progress):
+    """Cold streaming reads of 16 MiB to 1 GiB with the probe of libqlprobe.so (buffers rotated
+    over at least 1.5 GiB, two for the largest), each size timed as a burst of back-to-back
+    launches between two events; under rocprofv3 --kernel-trace the same command gives each
+    launch's duration. Returns {MiB: {"us": per launch, "GB_per_s": ...}}."""
+    import ctypes
+
+    import torch
+
+    P = ctypes.CDLL(os.path.join(ROOT, "int8_quantized_linear_amd", "libqlprobe.so"))
+    P.qlp_cu_count.restype = ctypes.c_int
+    P.qlp_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    P.qlp_stream_read.restype = ctypes.c_int
+    cus = P.qlp_cu_count()
+    stream = torch.cuda.current_stream(dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    sink = torch.empty(cus * 512, dtype=torch.int32, device=dev)
+    out = {}
+    for mib in (16, 32, 64, 128, 256, 512, 1024):
+        nb = mib << 20
+        nbuf = 2 if mib >= 1024 else max(2, (1536 << 20) // nb)
+        bufs = [torch.ones(nb, dtype=torch.uint8, device=dev) for _ in range(nbuf)]
+        reps = max(8, min(2 * nbuf, 96))
+        for i in range(nbuf):
+            P.qlp_stream_read(ctypes.c_void_p(bufs[i].data_ptr()), nb, ctypes.c_void_p(sink.data_ptr()), sh)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(reps):
+            rc = P.qlp_stream_read(ctypes.c_void_p(bufs[i % nbuf].data_ptr()), nb, ctypes.c_void_p(sink.data_ptr()), sh)
+            if rc != 0:
+                raise RuntimeError("qlp_stream_read failed with %d" % rc)
+        b.record(stream)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / reps
+        out[mib] = {"us": us, "GB_per_s": nb / us / 1e3, "launches": reps, "buffers": nbuf}
+        progress("read %d MiB: %.2f us per launch (%.0f GB/s)" % (mib, us, nb / us / 1e3))
+        del bufs
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -375,6 +415,8 @@ def main():
                     help="launches of each fused-activation variant timed after the step loop (0: skip)")
     ap.add_argument("--no-ceilings", dest="ceilings", action="store_false",
                     help="skip the measured ceilings (MFMA-only and streaming-read probes)")
+    ap.add_argument("--read-sweep", action="store_true",
+                    help="only measure cold streaming reads of 16 MiB .. 1 GiB with the probe and print them")
     ap.add_argument("--calib-copy-mib", type=int, default=256,
                     help="size of the plain device copy run once before the timed region "
                          "(reference point for hardware byte counters)")
@@ -394,6 +436,10 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.read_sweep:
+        res = read_sweep(dev, lambda m: print("[bench] " + m, file=sys.stderr, flush=True))
+        print(json.dumps({"read_sweep_MiB": res, "device": torch.cuda.get_device_name(0)}), flush=True)
+        return
 
     def up(a):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)

@@ -32,8 +32,8 @@ int qlp_cu_count(void);
 int qlp_mfma_i8(int64_t iters, int random_operands, int32_t* sink, void* stream);
 
 /*
- * Reads `bytes` bytes at `src` once (bytes % 16 == 0, src 16-byte aligned). sink: uint32
- * [CUs * 256], written once per thread.
+ * Reads `bytes` bytes at `src` once (bytes % 16 == 0, src 16-byte aligned), one workgroup of
+ * 8 waves per CU. sink: uint32 [CUs * 512], written once per thread.
  */
 int qlp_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream);
 
