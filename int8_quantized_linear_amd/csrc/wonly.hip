@@ -180,11 +180,20 @@ constexpr int LDS_BUDGET = 150 * 1024;  // activation rings + partial sums + sca
 // Scales (and zero points) of the workgroup's columns, staged in LDS when they fit.
 constexpr int SL_WORDS = 4096;   // 16 KB
 
-// Ring depth: as many k-steps in flight as the weight registers (about 280 per lane beside
-// the accumulators and the operands of the step being computed) and the LDS activation
-// ring allow, as a power of two (at most 16) so that it divides a wave's step count when
-// K is a multiple of 4 * KS * D (the loop is padded to whole rings with zero-filled steps).
+// Ring depth: k-steps in flight per wave, as a power of two (at most 8) so that it divides a
+// wave's step count when K is a multiple of 4 * KS * D (the loop is padded to whole rings
+// with zero-filled steps). Bounded by the weight registers (about 280 per lane beside the
+// accumulators and the operands of the step being computed), by the LDS activation ring,
+// and by a budget of about 32K weights in flight per CU. More than that is slower: with a
+// whole K range issued at once (a CU's 56 columns of 4096 int4 weights, say), the requests
+// of every CU queue together, a wave's first step completes about when its last does, and
+// none of the dequantization overlaps the transfer. Measured on MI355X, K = 4096, one row
+// (event-timed bursts over cold weights), against depths set by registers and LDS alone:
+// N = 14336 int4 12.9 -> 9.7 us, int8 15.0 -> 13.4 us; N = 28672 int4 24.6 -> 16.1 us;
+// block-asymmetric N = 11008 19.1 -> 16.0 us; N = 4096 int4 at 16 rows 6.6 -> 5.9 us. From
+// 17 rows on the LDS ring already held the depth at 2 (no change).
 // The waves' partial sums share the first ring slot when they fit in it.
+constexpr int INFLIGHT_WEIGHTS = 32768;   // per CU
 // Rows of the activation ring: 16 per block, or 8 when the launch has at most 8 rows (HX).
 template <int MT, bool HX>
 constexpr int xrows() { return HX ? 8 : 16 * MT; }
@@ -205,7 +214,9 @@ constexpr int ring_depth() {
     constexpr int dr = ((nwaves<MT>() == 4 ? 280 : 200) - fixed) / per_step;
     constexpr int dl = (LDS_BUDGET - SL_WORDS * 4 - red_extra<KS, MT, NT, HX>()) /
                        (nwaves<MT>() * XRing<KS, xrows<MT, HX>()>::SLOT);
-    constexpr int d = dr < dl ? dr : dl;
+    constexpr int db = INFLIGHT_WEIGHTS / (nwaves<MT>() * NT * 16 * KS);
+    constexpr int d0 = dr < dl ? dr : dl;
+    constexpr int d = d0 < db ? d0 : db;
     // at most 8: each slot is its own LDS array (see the kernel)
     return d >= 8 ? 8 : d >= 4 ? 4 : 2;
 }
