@@ -182,7 +182,10 @@ constexpr int SL_WORDS = 4096;   // 16 KB
 
 // Ring depth: k-steps in flight per wave, as a power of two (at most 8) so that it divides a
 // wave's step count when K is a multiple of 4 * KS * D (the loop is padded to whole rings
-// with zero-filled steps). Bounded by the weight registers (about 280 per lane beside the
+// with zero-filled steps), and at least 2, or 1 for group scales with two waves per SIMD
+// (where the other wave runs while one waits: int4 at 32 rows, N = 14336, 13.9 -> 13.1 us,
+// N = 28672 26.6 -> 24.0 us, block-asymmetric 57.5 -> 55.4 us against a floor of 2; per-
+// channel int8 there, and anything with one wave per SIMD, is slower with a single step). Bounded by the weight registers (about 280 per lane beside the
 // accumulators and the operands of the step being computed), by the LDS activation ring,
 // and by a budget of about 32K weights in flight per CU. More than that is slower: with a
 // whole K range issued at once (a CU's 56 columns of 4096 int4 weights, say), the requests
@@ -204,8 +207,9 @@ constexpr int red_extra() {
     return red > slot ? red : 0;
 }
 
-template <int FMT, int KS, int MT, int NT, bool GLOAD, bool HX>
+template <int FMT, int KS, int MT, int NT, int SCALES, bool HX>
 constexpr int ring_depth() {
+    constexpr bool GLOAD = SCALES == 2;
     using G = Geo<FMT, KS>;
     constexpr int per_step = NT * (G::WB / 4) + (GLOAD ? NT * (FMT == W_UINT8_ZP ? 2 : 1) : 0);
     constexpr int fixed = MT * NT * 4 + 2 * MT * G::HN * 4 + 12 + NT * 2 + MT + 24 + G::HN;
@@ -218,7 +222,7 @@ constexpr int ring_depth() {
     constexpr int d0 = dr < dl ? dr : dl;
     constexpr int d = d0 < db ? d0 : db;
     // at most 8: each slot is its own LDS array (see the kernel)
-    return d >= 8 ? 8 : d >= 4 ? 4 : 2;
+    return d >= 8 ? 8 : d >= 4 ? 4 : d >= 2 || nwaves<MT>() == 4 || SCALES == 0 ? 2 : 1;
 }
 
 // One workgroup of NW waves: `cols` (<= 16 NT) consecutive columns from col0, all M
@@ -414,8 +418,8 @@ __global__ __launch_bounds__(64 * nwaves<MT>()) void wonly_kernel(
         __builtin_amdgcn_s_waitcnt(vmcnt_le(pending < 63 ? pending : 63));
         __builtin_amdgcn_sched_barrier(0);
         // the next step's scales are read from LDS one step ahead, so that their latency
-        // hides behind this step's work
-        if constexpr (SCALES == 1)
+        // hides behind this step's work (with a single slot, after this step's products)
+        if constexpr (SCALES == 1 && D > 1)
             lds_scales((u + 1) % D);
         f16x8 xa[MT][HN];
         const char* xs = xslot[u];
@@ -457,6 +461,8 @@ __global__ __launch_bounds__(64 * nwaves<MT>()) void wonly_kernel(
                 }
             }
         }
+        if constexpr (SCALES == 1 && D == 1)
+            lds_scales(0);
     };
 
 #pragma unroll
@@ -558,7 +564,7 @@ template <int FMT, int KS, int MT, int NT, int SCALES, bool HX>
 ql_status launch_cfg(const void* x, const void* codes, const void* scale, const uint8_t* zp,
                      int64_t group, const float* bias, void* y, int64_t M, int64_t N, int64_t K,
                      int cols, int act, hipStream_t stream) {
-    constexpr int D = ring_depth<FMT, KS, MT, NT, SCALES == 2, HX>();
+    constexpr int D = ring_depth<FMT, KS, MT, NT, SCALES, HX>();
     const dim3 grid((unsigned)((N + cols - 1) / cols)), block(64 * nwaves<MT>());
     hipLaunchKernelGGL((wonly_kernel<FMT, KS, MT, NT, SCALES, D, HX>), grid, block, 0, stream,
                        reinterpret_cast<const _Float16*>(x), reinterpret_cast<const uint8_t*>(codes),
