@@ -278,19 +278,38 @@ __global__ __launch_bounds__(64 * nwaves<MT>()) void wonly_kernel(
     // The block of scales (and zero points) of this workgroup's columns is contiguous:
     // [ncols][ngroups]. With SCALES == 1 it is copied into LDS by direct copies issued
     // before anything else, so the wait for them below does not wait for the weights.
+    // A step reads one group of 16 consecutive columns, words a column's length apart: with
+    // 64 fp32 scales per column, all on one bank. When a column is a power-of-two number of
+    // words, word i of column c is stored at position i ^ (c & mask) of the column (mask =
+    // min(words, 32) - 1), which puts the 16 reads on 16 banks. A copy writes lane l's word
+    // to slot l, but each lane may fetch any word, so the permutation costs the copies
+    // nothing: lane l fetches the word that belongs in its slot (the swizzle is its own
+    // inverse), from the same cache lines.
     const int sbytes = ncols * ngroups * SB, zbytes = ZP ? ncols * ngroups : 0;
     const int swords = (sbytes + 3) >> 2, zwords = (zbytes + 3) >> 2;
+    auto col_swizzle = [](int col_bytes, int& shift) {
+        const int w = col_bytes >> 2;   // words per column
+        shift = __builtin_ctz(w | 0x40000000);
+        return col_bytes % 4 == 0 && (w & (w - 1)) == 0 ? (w < 32 ? w : 32) - 1 : 0;
+    };
+    int s_shift, z_shift;
+    const int smask = col_swizzle(ngroups * SB, s_shift);
+    const int zmask = ZP ? col_swizzle(ngroups, z_shift) : 0;
     if constexpr (SCALES == 1) {
         // Words past the block's last are copies of its last word (never read); the last
         // word may hold up to 3 bytes past the array's end, inside the same aligned word.
         const uint8_t* sg = reinterpret_cast<const uint8_t*>(scale) + (int64_t)col0 * ngroups * SB;
-        for (int q0 = wave * 64; q0 < swords; q0 += 64 * NW)
-            lds_copy4(sg + 4 * min(q0 + lane, swords - 1), sl + q0);
+        for (int q0 = wave * 64; q0 < swords; q0 += 64 * NW) {
+            const int w = min(q0 + lane, swords - 1);
+            lds_copy4(sg + 4 * (w ^ ((w >> s_shift) & smask)), sl + q0);
+        }
         if constexpr (ZP) {
             const uint8_t* zg = zp + (int64_t)col0 * ngroups;
             const int zw0 = (swords + 63) & ~63;
-            for (int q0 = wave * 64; q0 < zwords; q0 += 64 * NW)
-                lds_copy4(zg + 4 * min(q0 + lane, zwords - 1), sl + zw0 + q0);
+            for (int q0 = wave * 64; q0 < zwords; q0 += 64 * NW) {
+                const int w = min(q0 + lane, zwords - 1);
+                lds_copy4(zg + 4 * (w ^ ((w >> z_shift) & zmask)), sl + zw0 + q0);
+            }
         }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -310,12 +329,15 @@ __global__ __launch_bounds__(64 * nwaves<MT>()) void wonly_kernel(
     // the L1 serves a quad in one request, against one request per lane when the four lanes
     // of a quad sit on four columns as in the MFMA layout (3x the load rate per CU). A lane
     // permute then moves chunk lg of column ln to MFMA lane (ln, lg).
-    int woff[NT], soff[NT];
+    int woff[NT], soff[NT], sxe[NT], zxe[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
         const int cq = 16 * j + (lane >> 2);
         woff[j] = cq < ncols ? cq * wrow + s0 * G::WSTEP + (lane & 3) * G::WB : OOB;
-        soff[j] = min(16 * j + ln, ncols - 1) * ngroups;   // clamped column: scale and zero index
+        const int c = min(16 * j + ln, ncols - 1);   // clamped column
+        soff[j] = c * ngroups;                       // its scale and zero index
+        sxe[j] = (c & smask) << (SB == 2 ? 1 : 0);   // staged-scale swizzle, in elements
+        zxe[j] = (c & zmask) << 2;                   // staged zero-point swizzle, in bytes
     }
     const int wperm = (4 * ln + lg) * 4;   // ds_bpermute byte address of the source lane
     // Activation copies: lane l of copy q takes row q RPC + l / CPR and chunk (l % CPR) ^
@@ -392,11 +414,11 @@ __global__ __launch_bounds__(64 * nwaves<MT>()) void wonly_kernel(
         for (int j = 0; j < NT; ++j) {
             const int e = soff[j] + g;
             if constexpr (FMT == W_INT4_SYM)
-                sc[u][j] = (float)reinterpret_cast<const _Float16*>(sl)[e];
+                sc[u][j] = (float)reinterpret_cast<const _Float16*>(sl)[e ^ sxe[j]];
             else
-                sc[u][j] = reinterpret_cast<const float*>(sl)[e];
+                sc[u][j] = reinterpret_cast<const float*>(sl)[e ^ sxe[j]];
             if constexpr (ZP)
-                zq[u][j] = reinterpret_cast<const uint8_t*>(sl + zw0)[e];
+                zq[u][j] = reinterpret_cast<const uint8_t*>(sl + zw0)[e ^ zxe[j]];
         }
     };
 
