@@ -177,8 +177,16 @@ template <int MT>
 constexpr int nwaves() { return MT == 2 ? 8 : 4; }
 constexpr int LDS_BUDGET = 150 * 1024;  // activation rings + partial sums + scales
 
-// Scales (and zero points) of the workgroup's columns, staged in LDS when they fit.
-constexpr int SL_WORDS = 4096;   // 16 KB
+// Scales (and zero points) of the workgroup's columns, staged in LDS when they fit: 32 KB
+// where the activation ring leaves room (one block of 16 rows, or two with 64-column tiles,
+// which keep a single step in flight), else 16 KB. With 32 KB, 56 columns of 64 fp32
+// scales and 64 zero points (N = 14336 over 256 CUs, K = 4096) fit: block-asymmetric at
+// one row 24.4 -> 15.7 us, at 32 rows 27.3 -> 19.6 us, N = 28672 47.9 -> 27.6 us, against
+// loading them from global memory every step. int4 at 17..32 rows keeps 16 KB (its fp16
+// scales fit there, and the larger area measured 2% slower).
+constexpr int sl_words(int fmt, int mt, int nt) {
+    return mt == 1 || (mt == 2 && nt == 4 && fmt != W_INT4_SYM) ? 8192 : 4096;
+}
 
 // Ring depth: k-steps in flight per wave, as a power of two (at most 8) so that it divides a
 // wave's step count when K is a multiple of 4 * KS * D (the loop is padded to whole rings
@@ -216,7 +224,7 @@ constexpr int ring_depth() {
     // one wave per SIMD may use about 280 registers (VGPRs and AGPRs); two share the file
     // and get about 200 each
     constexpr int dr = ((nwaves<MT>() == 4 ? 280 : 200) - fixed) / per_step;
-    constexpr int dl = (LDS_BUDGET - SL_WORDS * 4 - red_extra<KS, MT, NT, HX>()) /
+    constexpr int dl = (LDS_BUDGET - sl_words(FMT, MT, NT) * 4 - red_extra<KS, MT, NT, HX>()) /
                        (nwaves<MT>() * XRing<KS, xrows<MT, HX>()>::SLOT);
     constexpr int db = INFLIGHT_WEIGHTS / (nwaves<MT>() * NT * 16 * KS);
     constexpr int d0 = dr < dl ? dr : dl;
@@ -258,7 +266,7 @@ __global__ __launch_bounds__(64 * nwaves<MT>()) void wonly_kernel(
     __shared__ __attribute__((aligned(16))) char xs6[D > 6 ? SLOTB : 16];
     __shared__ __attribute__((aligned(16))) char xs7[D > 7 ? SLOTB : 16];
     __shared__ __attribute__((aligned(16))) char redx[REDX ? REDX : 16];
-    __shared__ uint32_t sl[SCALES == 1 ? SL_WORDS : 1];
+    __shared__ uint32_t sl[SCALES == 1 ? sl_words(FMT, MT, NT) : 1];
     char* const xslot[8] = {xs0, xs1, xs2, xs3, xs4, xs5, xs6, xs7};
     f32x4* red = reinterpret_cast<f32x4*>(REDX ? redx : xs0);
 
@@ -620,7 +628,8 @@ ql_status launch_mt(const void* x, const void* codes, const void* scale, const u
     // The scale block (and zero-point block after it, at a 64-word boundary) must fit in LDS.
     const int64_t ng = K / group, sb = FMT == W_INT4_SYM ? 2 : 4;
     const int64_t words = ((cols * ng * sb + 3) / 4 + 63) / 64 * 64 + (FMT == W_UINT8_ZP ? (cols * ng + 3) / 4 : 0);
-    if (words + 63 <= SL_WORDS)
+    const int nt = cols <= 16 ? 1 : cols <= 32 ? 2 : 4;   // as launch_nt picks it
+    if (words + 63 <= sl_words(FMT, MT, nt))
         return launch_nt<FMT, KS, MT, 1, HX>(x, codes, scale, zp, group, bias, y, M, N, K, (int)cols, act, stream);
     return launch_nt<FMT, KS, MT, 2, HX>(x, codes, scale, zp, group, bias, y, M, N, K, (int)cols, act, stream);
 }
