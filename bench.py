@@ -22,6 +22,8 @@ microsecond) but no event between two launches; short groups keep the GEMM's lau
 from running long enough on their own to lower the chip's clock more than a pass of the
 path does. Every input that streams from HBM rotates over more than 512 MiB of copies
 (the decode weights and the quantizer's X), so no launch finds it in the Infinity Cache.
+The warm-up steps (200 by default) bring the chip out of its idle state first: after only 10,
+every kernel of the timed region ran slower for its first several groups (the GEMM up to 15%).
 ``roofline`` is the W8A8 GEMM's (the dominant kernel); ``rooflines`` holds one entry per
 hot-path kernel, each beside the rocprofv3 kernel-trace average of the committed profile
 when that profile was taken on the current kernel sources.
@@ -407,8 +409,10 @@ def read_sweep(dev, progress):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    # The chip ramps up from idle: with 10 warm-up steps the GEMM's groups of the timed region ran
+    # 91.6, 99.1, 100.3, 96.2, ..., 85.6 us; after 100 they hold at 85-86 us from the first group.
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", dest="cpu", action="store_false")
     ap.add_argument("--cpu-seconds", type=float, default=18.0)
     ap.add_argument("--act-steps", type=int, default=20,
@@ -609,6 +613,8 @@ def main():
         "decode": decode,
         "timing": "steps in groups of %d; within a group each kernel's launches run back to back between "
                   "two HIP events on the launch stream (includes the launch gap)" % GROUP,
+        "gemm_us_by_group": [round(a.elapsed_time(b) * 1e3 / (min(K, g0 + GROUP) - g0), 2)
+                             for g0, (a, b) in zip(range(0, K, GROUP), intervals["gemm"])],
         "device": torch.cuda.get_device_name(0),
     }
     if args.act_steps > 0:
