@@ -431,11 +431,24 @@ __global__ __launch_bounds__(64 * nwaves<MT>()) void wonly_kernel(
     };
 
     f32x4 acc[MT][NT];
+    // With group scales and one block of 16 rows (one wave per SIMD, nothing else to run while
+    // a step's products finish), a step's scaled add is deferred to the next step: its products
+    // (pp) and scale (sp) wait in registers, so the add does not wait for the step's last MFMA
+    // (block-asymmetric at 8 rows 6.97 -> 6.52 us; with more row blocks, two waves per SIMD
+    // already hide the wait and the extra registers made it slower).
+    constexpr bool DEFER = GROUPED && MT == 1;
+    f32x4 pp[MT][NT];
+    float sp[NT];
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int j = 0; j < NT; ++j)
+        for (int j = 0; j < NT; ++j) {
             acc[i][j] = f32x4{0, 0, 0, 0};
+            pp[i][j] = f32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+        sp[j] = 0.0f;
 
     // Vector-memory operations of one step, in issue order: the activation copies, the
     // weight loads, the scale (and zero-point) loads.
@@ -483,7 +496,14 @@ __global__ __launch_bounds__(64 * nwaves<MT>()) void wonly_kernel(
 #pragma unroll
                     for (int h = 1; h < HN; ++h)
                         p = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[i][h], wb[h], p, 0, 0, 0);
-                    acc[i][j] += sc[u][j] * p;
+                    if constexpr (DEFER) {
+                        acc[i][j] += sp[j] * pp[i][j];
+                        pp[i][j] = p;
+                        if (i == MT - 1)
+                            sp[j] = sc[u][j];
+                    } else {
+                        acc[i][j] += sc[u][j] * p;
+                    }
                 } else {
 #pragma unroll
                     for (int h = 0; h < HN; ++h)
@@ -524,6 +544,13 @@ __global__ __launch_bounds__(64 * nwaves<MT>()) void wonly_kernel(
         __builtin_amdgcn_sched_barrier(0);
     });
 
+    if constexpr (DEFER) {
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+                acc[i][j] += sp[j] * pp[i][j];
+    }
     // The waves' partial sums meet in LDS (over the rings: every wave must be done with
     // its ring first); wave w then finishes blocks b = w (mod NW). Their per-column
     // factors are loaded first, before any store: a vector-memory wait also waits for the
