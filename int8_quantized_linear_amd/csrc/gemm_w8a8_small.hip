@@ -23,11 +23,17 @@
 namespace ql {
 namespace {
 
-// SW waves per workgroup, each taking every SW-th group of SU 64-deep k-steps and loading a
-// group at once. With about one workgroup per CU, eight waves of 8-step groups keep the most
-// bytes in flight per CU; with several workgroups per CU, four waves of 16-step groups do
-// (measured: 6.3 against 6.8 us at N = 4096, 11.8 against 15.2 us at N = 11008, M = 16,
-// K = 4096).
+// SW waves per workgroup. In group mode each wave takes every SW-th group of SU 64-deep
+// k-steps and loads a group at once; in ring mode (RING) each wave takes a contiguous range of
+// k-steps and keeps SU of them in flight, loading step t + SU as soon as step t is computed.
+// With several workgroups per CU (N > 16 x 2 x CUs), four waves of 16-step groups are fastest
+// (the resident workgroups overlap one another; a ring measured 7% slower at N = 14336, one
+// row). With about one workgroup per CU, eight waves on a ring: with 8-step groups each wave
+// issued its whole K range at once (64 KB per CU at K = 4096), and the requests of all CUs came
+// back in no useful order. Measured at N = K = 4096 against 8-step groups: one row 6.64 ->
+// 5.98 us, 8 rows 7.56 -> 6.62 us (4 steps in flight); 16 rows 7.85 -> 6.93 us, 32 rows 9.04
+// -> 8.20 us, 64 rows 13.46 -> 12.02 us (2 steps in flight: from 16 rows X adds as many bytes
+// per step as W).
 constexpr int SCOLS = 16;   // output columns per workgroup
 
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
@@ -58,7 +64,7 @@ struct SmallEpi {
     int out_scale_n;
 };
 
-template <int YMODE, int MB, int ACT, bool ASYM, int SW, int SU, bool FP8>
+template <int YMODE, int MB, int ACT, bool ASYM, int SW, int SU, bool FP8, bool RING>
 __global__ __launch_bounds__(64 * SW) void gemm_w8a8_small_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ xs, const int8_t* __restrict__ B,
     const float* __restrict__ ws, const float* __restrict__ bias, void* __restrict__ Y, int M, int N,
@@ -82,6 +88,37 @@ __global__ __launch_bounds__(64 * SW) void gemm_w8a8_small_kernel(
     for (int b = 0; b < MB; ++b)
         acc[b] = Acc{0, 0, 0, 0};
     const int S = K / 64;
+    if constexpr (RING) {
+        static_assert(!FP8, "the ring serves int8 codes");
+        const int s0 = wave * S / SW, s1 = (wave + 1) * S / SW, T = s1 - s0;
+        i32x4 wv[SU], xv[MB][SU];
+        auto load = [&](int u, int t) {
+            if (t < T) {
+                const int64_t off = (int64_t)(s0 + t) * 64;
+                wv[u] = *reinterpret_cast<const i32x4*>(bp + off);
+#pragma unroll
+                for (int b = 0; b < MB; ++b)
+                    xv[b][u] = *reinterpret_cast<const i32x4*>(ap[b] + off);
+            }
+        };
+#pragma unroll
+        for (int u = 0; u < SU; ++u)
+            load(u, u);
+        // t < T is uniform across the wave: every lane takes part in the permutes
+        for (int tb = 0; tb < T; tb += SU) {
+#pragma unroll
+            for (int u = 0; u < SU; ++u) {
+                const int t = tb + u;
+                if (t < T) {
+                    const i32x4 bw = to_mfma_order(wv[u], src);
+#pragma unroll
+                    for (int b = 0; b < MB; ++b)
+                        acc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(to_mfma_order(xv[b][u], src), bw, acc[b], 0, 0, 0);
+                    load(u, t + SU);
+                }
+            }
+        }
+    } else
     for (int base = wave * SU; base < S; base += SW * SU) {
         i32x4 wv[SU], xv[MB][SU];
 #pragma unroll
@@ -173,14 +210,14 @@ __global__ __launch_bounds__(64 * SW) void gemm_w8a8_small_kernel(
     }
 }
 
-template <int YMODE, int ACT, bool ASYM, int SW, int SU, bool FP8>
+template <int YMODE, int ACT, bool ASYM, int SW, int SU, bool FP8, bool RING = false>
 void launch_mb(const int8_t* xq, const float* xs, const int8_t* wq, const float* ws, const float* bias,
                void* y, int M, int N, int K, SmallEpi epi, hipStream_t stream) {
     const dim3 grid((unsigned)((N + SCOLS - 1) / SCOLS)), block(64 * SW);
     const int mb = (M + 15) / 16;
 #define QL_SMALL(MBV)                                                                                         \
-    hipLaunchKernelGGL((gemm_w8a8_small_kernel<YMODE, MBV, ACT, ASYM, SW, SU, FP8>), grid, block, 0, stream, xq, \
-                       xs, wq, ws, bias, y, M, N, K, epi)
+    hipLaunchKernelGGL((gemm_w8a8_small_kernel<YMODE, MBV, ACT, ASYM, SW, SU, FP8, RING>), grid, block, 0, stream, \
+                       xq, xs, wq, ws, bias, y, M, N, K, epi)
     if (mb == 1)
         QL_SMALL(1);
     else if (mb == 2)
@@ -200,8 +237,8 @@ void launch_mb8(const int8_t* xq, const float* xs, const int8_t* wq, const float
     const dim3 grid((unsigned)((N + SCOLS - 1) / SCOLS)), block(64 * 8);
     const int mb = (M + 15) / 16;
 #define QL_SMALL8(MBV)                                                                                    \
-    hipLaunchKernelGGL((gemm_w8a8_small_kernel<YMODE, MBV, ACT, ASYM, 8, 4, FP8>), grid, block, 0, stream, xq, xs, \
-                       wq, ws, bias, y, M, N, K, epi)
+    hipLaunchKernelGGL((gemm_w8a8_small_kernel<YMODE, MBV, ACT, ASYM, 8, 4, FP8, false>), grid, block, 0, stream, \
+                       xq, xs, wq, ws, bias, y, M, N, K, epi)
     if (mb <= 6)
         QL_SMALL8(6);
     else
@@ -217,8 +254,12 @@ void launch_shape(const int8_t* xq, const float* xs, const int8_t* wq, const flo
         launch_mb8<YMODE, ACT, ASYM, FP8>(xq, xs, wq, ws, bias, y, M, N, K, epi, stream);
     else if (wgs > 2 * (int64_t)cu_count())
         launch_mb<YMODE, ACT, ASYM, 4, 16, FP8>(xq, xs, wq, ws, bias, y, M, N, K, epi, stream);
-    else
+    else if (FP8)
         launch_mb<YMODE, ACT, ASYM, 8, 8, FP8>(xq, xs, wq, ws, bias, y, M, N, K, epi, stream);
+    else if (M <= 8)
+        launch_mb<YMODE, ACT, ASYM, 8, 4, false, true>(xq, xs, wq, ws, bias, y, M, N, K, epi, stream);
+    else
+        launch_mb<YMODE, ACT, ASYM, 8, 2, false, true>(xq, xs, wq, ws, bias, y, M, N, K, epi, stream);
 }
 
 template <int YMODE, bool ASYM, bool FP8 = false>

@@ -312,16 +312,17 @@ def test_requant_with_activation(ql, act, M, N, K):
                                    (33, 1000, 640), (48, 16, 4096), (64, 31, 64), (65, 300, 256),
                                    (96, 1000, 640), (100, 17, 64), (128, 2048, 4096), (129, 300, 256),
                                    (1, 11008, 4096), (16, 11008, 4096), (24, 10240, 640), (8, 16384, 192),
-                                   (64, 11008, 4096)])
+                                   (64, 11008, 4096), (8, 2000, 2880), (12, 4096, 1600), (20, 1000, 1472)])
 def test_few_rows_int32(ql, M, N, K):
     """The few-row kernel takes M <= 8, or M <= 128 with M * N <= 256K and N <= 12288 (16
     columns per workgroup, K split over the waves, 16x16x64 matrix-core steps after a lane
-    permutation). Its three wave shapes are all covered: eight waves of 8-step groups (at most
-    2 x CUs workgroups, M <= 64), four waves of 16-step groups (more workgroups than that:
-    N > 8192, e.g. M = 16, N = 11008; M = 24, N = 10240; M = 8, N = 16384), and eight waves of
-    4-step groups for five to eight row blocks (M = 65 .. 128). Accumulators bit for bit, with
-    codes at the extremes, ragged N, one to 64 k-steps; M = 129 and M = 64, N = 11008 (past
-    256K) run on the 64 x 64 kernel."""
+    permutation). Its four wave shapes are all covered: eight waves on a ring of 4 steps (at most
+    2 x CUs workgroups, M <= 8) or 2 steps (9 <= M <= 64), with wave step counts below, at and
+    past the ring's depth (e.g. M = 8, K = 2880: 5 or 6 steps per wave; M = 20, K = 1472: 2 or 3);
+    four waves of 16-step groups (more workgroups than that: N > 8192, e.g. M = 16, N = 11008;
+    M = 24, N = 10240; M = 8, N = 16384); and eight waves of 4-step groups for five to eight row
+    blocks (M = 65 .. 128). Accumulators bit for bit, with codes at the extremes, ragged N, one
+    to 64 k-steps; M = 129 and M = 64, N = 11008 (past 256K) run on the 64 x 64 kernel."""
     rng = np.random.default_rng(M * 7919 + N + K)
     a = _rand_codes(rng, (M, K), -128)
     b = _rand_codes(rng, (N, K), -128)
