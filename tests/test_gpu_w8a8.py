@@ -93,20 +93,20 @@ def test_small_layer_fp32(ql):
 
 
 def test_prefill_full_size(ql):
-    """M=2048 K=4096 N=11008 in the benchmark's launch configuration: quantized tensors
-    bit-exact everywhere; accumulators and fp16 outputs on rows sampled from every M tile."""
+    """M=2048 K=4096 N=11008 in the benchmark's launch configuration: quantized tensors,
+    all 22.5 M int32 accumulators bit for bit, and every fp16 output within one fp16 step of
+    the oracle's fp32 epilogue (the oracle's whole GEMM takes a few seconds on the host)."""
     inp, (xq, xs, wq, ws), (xq_r, xs_r, wq_r, ws_r) = _layer(ql, workloads.W8A8_PREFILL)
     y = ql.gemm_w8a8_per_channel(xq, xs, wq, ws, dev(inp.bias), torch.float16)
     acc = ql.gemm_w8a8_int32(xq, wq)
-    rows = np.unique(np.concatenate([np.arange(0, 2048, 97), [255, 256, 2047]]))
-    acc_ref = oracle.gemm_i32(xq_r[rows], wq_r)
-    assert np.array_equal(host(acc)[rows], acc_ref)
-    y32, y64 = oracle.epilogue_w8a8(acc_ref, xs_r[rows], ws_r, inp.bias)
+    acc_ref = oracle.gemm_i32(xq_r, wq_r)
+    assert np.array_equal(host(acc), acc_ref)
+    y32, y64 = oracle.epilogue_w8a8(acc_ref, xs_r, ws_r, inp.bias)
     yg = host(y)
     assert np.all(np.isfinite(yg))
     ref16 = y32.astype(np.float16).astype(np.float64)
-    assert np.all(np.abs(yg[rows].astype(np.float64) - ref16) <= f16_ulp(ref16))
-    same = np.mean(yg[rows] == y32.astype(np.float16))
+    assert np.all(np.abs(yg.astype(np.float64) - ref16) <= f16_ulp(ref16))
+    same = np.mean(yg == y32.astype(np.float16))
     assert same > 0.99, same
 
 
