@@ -673,7 +673,7 @@ def main():
             us = _alternate(args.act_steps, {"run": _cycle(launches)})["run"]
             few["m%d" % m] = {"us": us, "GB_per_s": nk / (us * 1e-6) / 1e9}
         out["w8a8_few_rows"] = {"shape": "M x K4096 x N4096, fp16 out", "weight_sets_rotated": rot, **few,
-                                "note": "M <= 128 with M*N <= 640K runs on the few-row kernel; GB/s counts W's bytes; timed after "
+                                "note": "M <= 8, or M <= 128 with M*N <= 256K and N <= 12288, runs on the few-row kernel; GB/s counts W's bytes; timed after "
                                         "the GEMM runs above, whose power draw can leave the clock lower"}
         del wsets
     if args.act_steps > 0:
