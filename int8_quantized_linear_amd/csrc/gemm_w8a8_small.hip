@@ -33,7 +33,9 @@ namespace {
 // back in no useful order. Measured at N = K = 4096 against 8-step groups: one row 6.64 ->
 // 5.98 us, 8 rows 7.56 -> 6.62 us (4 steps in flight); 16 rows 7.85 -> 6.93 us, 32 rows 9.04
 // -> 8.20 us, 64 rows 13.46 -> 12.02 us (2 steps in flight: from 16 rows X adds as many bytes
-// per step as W).
+// per step as W). The fp8 codes use the same ring over pairs of steps (2 pairs in flight up to
+// 8 rows, 1 beyond): 6.85 -> 6.40 us at one row, 9.17 -> 7.94 us at 32 rows, 13.49 -> 11.69 us
+// at 64 rows.
 constexpr int SCOLS = 16;   // output columns per workgroup
 
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
@@ -88,8 +90,48 @@ __global__ __launch_bounds__(64 * SW) void gemm_w8a8_small_kernel(
     for (int b = 0; b < MB; ++b)
         acc[b] = Acc{0, 0, 0, 0};
     const int S = K / 64;
-    if constexpr (RING) {
-        static_assert(!FP8, "the ring serves int8 codes");
+    if constexpr (RING && FP8) {
+        // fp8: a slot holds a pair of steps (s0 + 2p, s0 + 2p + 1) for one 16x16x128 step, a
+        // missing second step being zero codes; SU pairs in flight. The hardware's groups of
+        // 8 consecutive k lie within one 64-deep step, so the pairing changes only the order
+        // in which fp32 group sums are added.
+        const int s0 = wave * S / SW, s1 = (wave + 1) * S / SW, T = s1 - s0, P = (T + 1) / 2;
+        i32x4 wv[SU][2], xv[MB][SU][2];
+        const i32x4 zero{0, 0, 0, 0};
+        auto load = [&](int u, int p) {
+            if (p < P) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    if (2 * p + h < T) {
+                        const int64_t off = (int64_t)(s0 + 2 * p + h) * 64;
+                        wv[u][h] = *reinterpret_cast<const i32x4*>(bp + off);
+#pragma unroll
+                        for (int b = 0; b < MB; ++b)
+                            xv[b][u][h] = *reinterpret_cast<const i32x4*>(ap[b] + off);
+                    }
+                }
+            }
+        };
+#pragma unroll
+        for (int u = 0; u < SU; ++u)
+            load(u, u);
+        for (int pb = 0; pb < P; pb += SU) {
+#pragma unroll
+            for (int u = 0; u < SU; ++u) {
+                const int p = pb + u;
+                if (p < P) {
+                    const bool two = 2 * p + 1 < T;
+                    const i32x8 bw = cat8s(to_mfma_order(wv[u][0], src), two ? to_mfma_order(wv[u][1], src) : zero);
+#pragma unroll
+                    for (int b = 0; b < MB; ++b) {
+                        const i32x8 aw = cat8s(to_mfma_order(xv[b][u][0], src), two ? to_mfma_order(xv[b][u][1], src) : zero);
+                        acc[b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aw, bw, acc[b], 0, 0, 0, 0, 0, 0);
+                    }
+                    load(u, p + SU);
+                }
+            }
+        }
+    } else if constexpr (RING) {
         const int s0 = wave * S / SW, s1 = (wave + 1) * S / SW, T = s1 - s0;
         i32x4 wv[SU], xv[MB][SU];
         auto load = [&](int u, int t) {
@@ -254,8 +296,10 @@ void launch_shape(const int8_t* xq, const float* xs, const int8_t* wq, const flo
         launch_mb8<YMODE, ACT, ASYM, FP8>(xq, xs, wq, ws, bias, y, M, N, K, epi, stream);
     else if (wgs > 2 * (int64_t)cu_count())
         launch_mb<YMODE, ACT, ASYM, 4, 16, FP8>(xq, xs, wq, ws, bias, y, M, N, K, epi, stream);
+    else if (FP8 && M <= 8)
+        launch_mb<YMODE, ACT, ASYM, 8, 2, true, true>(xq, xs, wq, ws, bias, y, M, N, K, epi, stream);
     else if (FP8)
-        launch_mb<YMODE, ACT, ASYM, 8, 8, FP8>(xq, xs, wq, ws, bias, y, M, N, K, epi, stream);
+        launch_mb<YMODE, ACT, ASYM, 8, 1, true, true>(xq, xs, wq, ws, bias, y, M, N, K, epi, stream);
     else if (M <= 8)
         launch_mb<YMODE, ACT, ASYM, 8, 4, false, true>(xq, xs, wq, ws, bias, y, M, N, K, epi, stream);
     else

@@ -110,12 +110,15 @@ def _half_integer_codes(rng, shape) -> np.ndarray:
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 64), (16, 256, 256), (300, 520, 384), (257, 129, 192),
                                    (128, 300, 128), (2000, 8300, 256), (64, 256, 4096), (16, 11008, 1024),
-                                   (24, 10240, 192), (200, 3001, 576)])
+                                   (24, 10240, 192), (200, 3001, 576), (1, 4096, 4096), (8, 1000, 1344),
+                                   (40, 2000, 704), (20, 4096, 1472)])
 def test_exact_sums(ql, M, N, K):
     """With unit scales, no bias and fp32 output, y is the exact sum of products: any
     dropped, repeated or misplaced product shows. Covers several tiles, ragged M and N,
     the 64 x 64 kernel (with a half-deep last stage), the mixed big/half tile plan, a long K,
-    and the few-row kernel's four-wave shape (more than 2 x CUs workgroups of 16 columns)."""
+    the few-row kernel's four-wave shape (more than 2 x CUs workgroups of 16 columns), and its
+    eight-wave ring over pairs of steps (2 pairs in flight up to 8 rows, 1 beyond), with odd
+    step counts per wave and odd first steps (K = 1344: 21 steps over 8 waves; K = 704, 1472)."""
     rng = np.random.default_rng(M + 3 * N + 7 * K)
     a = _half_integer_codes(rng, (M, K))
     b = _half_integer_codes(rng, (N, K))
@@ -192,11 +195,12 @@ def test_layer(ql, M, N, K, out, act):
     assert np.all(err <= tol), "max err/tol %.3g" % float((err / tol).max())
 
 
-@pytest.mark.parametrize("rows", ["few", "tiles"])
+@pytest.mark.parametrize("rows", ["few", "mid", "tiles"])
 def test_matrix_core_groups(ql, rows):
-    """The premises of the bound above, on both kernels: up to 128 rows run the few-row kernel
-    (16x16x128 fp8 steps), more rows the tile kernel (32x32x64 steps); the cases are padded
-    with zero rows to more than 128 for the latter. One output each (unit scales, K = 64,
+    """The premises of the bound above, on all three kernels: up to 128 rows the few-row kernel
+    (16x16x128 fp8 steps); 160 rows against 160 columns the 64 x 64 kernel, and against 33024
+    columns (more tiles than the 64 x 64 kernel takes) the tile kernel, both on 32x32x64 steps.
+    The cases are padded with zero rows and columns. One output each (unit scales, K = 64,
     fp32 out): a
     product of 4 beside 2^16 (2^-14 of it) vanishes when both lie in one group of 8
     consecutive k and survives in another group; a product of +-28 beside 2^16 keeps
@@ -216,16 +220,17 @@ def test_matrix_core_groups(ql, rows):
     cases.append(({9: 3 * 2.0 ** -9}, {9: 5 * 2.0 ** -9}, 15 * 2.0 ** -18))
     R = len(cases)
     M = (R + 31) // 32 * 32 if rows == "few" else 160
+    N = 33024 if rows == "tiles" else M
     assert (M <= 128) == (rows == "few")
     A = np.zeros((M, 64), np.uint8)
-    B = np.zeros((M, 64), np.uint8)
+    B = np.zeros((N, 64), np.uint8)
     for r, (a, b, _) in enumerate(cases):
         for k, v in a.items():
             A[r, k] = enc(v)
         for k, v in b.items():
             B[r, k] = enc(v)
-    ones = np.ones(M, np.float32)
-    y = host(ql.gemm_e4m3_per_channel(dev(A), dev(ones), dev(B), dev(ones), out_dtype=torch.float32))
+    y = host(ql.gemm_e4m3_per_channel(dev(A), dev(np.ones(M, np.float32)), dev(B), dev(np.ones(N, np.float32)),
+                                      out_dtype=torch.float32))
     got = np.array([y[r, r] for r in range(R)], np.float64)
     want = np.array([c[2] for c in cases])
     assert np.array_equal(got, want), [(r, got[r], want[r]) for r in range(R) if got[r] != want[r]][:6]
