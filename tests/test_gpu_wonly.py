@@ -70,7 +70,8 @@ def test_w8a16_block_full(ql):
 
 @pytest.mark.parametrize("M,N,K,block", [(1, 50, 128, 64), (8, 333, 512, 128), (20, 100, 384, 192),
                                          (40, 9000, 128, 64), (3, 64, 256, 256),
-                                         (24, 9000, 256, 64)])   # one step in flight
+                                         (24, 9000, 256, 64),    # one step in flight
+                                         (56, 300, 256, 64)])    # four row blocks
 def test_w8a16_block_ragged(ql, M, N, K, block):
     _w8a16_block(ql, workloads.with_shape(workloads.W8A16_BLOCK, M, K, N), block, with_bias=True)
 
@@ -109,7 +110,8 @@ def test_w4a16_ragged(ql, M, N, K, group):
 @pytest.mark.parametrize("fmt,M,N,K,group", [
     ("u8", 8, 16384, 4096, 64),     # 64 columns x 64 blocks (20 KB): staged, one row block
     ("u8", 20, 16384, 4096, 64),    # the same, staged at 17..32 rows
-    ("u8", 40, 16384, 4096, 64),    # the same over the 16 KB staging of 33..64 rows
+    ("u8", 40, 16384, 4096, 64),    # the same, staged at 33..48 rows (three row blocks)
+    ("u8", 56, 16384, 4096, 64),    # the same over the 16 KB staging of 49..64 rows
     ("u8", 8, 16384, 8192, 64),     # 64 columns x 128 blocks (40 KB): over LDS at one row block
     ("i8", 20, 16384, 8192, 64),    # int8 with group scales, 64 x 128 fp32 scales: over LDS
     ("int4", 40, 3000, 1024, 64),   # 33..64 rows with 64-deep int4 steps
