@@ -18,8 +18,9 @@
 // multiply-adds. The two 4-wave groups alternate between MFMA phases (with the copies
 // spread between the MFMAs) and phases of LDS fragment reads, so a SIMD's MFMA stream
 // never waits behind its own LDS reads. When the last round of 256 x 256 tiles would leave CUs idle, its N
-// panels run as 128 x 256 tiles whose K is split between the two groups. K % 128 == 64
-// runs a last stage whose upper half reads zeros.
+// panels run as 128 x 256 tiles whose K is split between the two groups; when no round of
+// big tiles fills the chip either, every tile is small, as 128 x 128 tiles where those make
+// at most one round. K % 128 == 64 runs a last stage whose upper half reads zeros.
 #include <type_traits>
 
 #include "ql_internal.h"
@@ -583,14 +584,15 @@ __device__ __forceinline__ void gemm_tile_pp(const int8_t* __restrict__ A, const
 // j + 3 spread between them, while the other group reads stage j + 1's fragments from
 // LDS. Three LDS buffers give the copies a phase to land before their stage is read. At the end group 1's int32 sums are added
 // to group 0's through LDS (exact) and group 0 writes the tile.
-template <int YMODE, int ELEM>
+template <int BN, int YMODE, int ELEM>
 __device__ __forceinline__ void gemm_tile_ks(const int8_t* __restrict__ A, const float* __restrict__ xs,
                                              const int8_t* __restrict__ B, const float* __restrict__ ws,
                                              const float* __restrict__ bias, void* __restrict__ Y,
                                              int M, int N, int K, int m0, int n0, int act, EpiArgs epi,
                                              int8_t* smem) {
-    constexpr int BM = 128, BN = 256, BKL = 128;
-    constexpr int WM = 64, WN = 128, FM = WM / 32, FN = WN / 32;
+    constexpr int BM = 128, BKL = 128;
+    constexpr int WM = 64, WN = BN / 2, FM = WM / 32, FN = WN / 32;
+    static_assert(BN == 256 || BN == 128, "128 x 256 or 128 x 128 tiles");
     constexpr int STAGE_A = BM * BKL, STAGE = (BM + BN) * BKL;
     constexpr int CA = BM / 32, CB = BN / 32;   // copies of A and B per wave of a group (8 rows each)
     static_assert(3 * STAGE <= RING_BYTES, "three stages fit the LDS allocation");
@@ -809,15 +811,16 @@ __device__ __forceinline__ void gemm_tile_ks(const int8_t* __restrict__ A, const
 }
 
 // Tiles: `nbig` 256 x 256 tiles cover the first `nbig / tiles_m` N-panels and `nsmall`
-// 128 x 256 tiles the remaining panels; workgroup b takes big tile b, then half tile b.
+// 128 x BNS tiles (BNS = 256, or 128 when every tile is small) the remaining panels;
+// workgroup b takes big tile b, then small tile b.
 // With 256 CUs, whole rounds of big tiles keep every CU busy and the leftover panels run
 // as half-height tiles in a shorter final round. Within each kind, tiles are dealt to
 // XCDs so that an XCD's tiles are consecutive and share W panels (column-major order).
 struct TilePlan {
-    int tiles_m_big, nbig, tiles_m_small, nsmall, n_small0;
+    int tiles_m_big, nbig, tiles_m_small, nsmall, n_small0, bn_small;
 };
 
-template <int YMODE, int ELEM>
+template <int YMODE, int ELEM, int BNS>
 __global__ __launch_bounds__(64 * NWAVES, 1) void gemm_w8a8_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ xs, const int8_t* __restrict__ B,
     const float* __restrict__ ws, const float* __restrict__ bias, void* __restrict__ Y, int M,
@@ -838,7 +841,8 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void gemm_w8a8_kernel(
     if (bid < plan.nsmall) {
         const int tile = xcd_remap(bid, plan.nsmall);
         const int tn = tile / plan.tiles_m_small, tm = tile - tn * plan.tiles_m_small;
-        gemm_tile_ks<YMODE, ELEM>(A, xs, B, ws, bias, Y, M, N, K, tm * 128, plan.n_small0 + tn * 256, act, epi, smem);
+        gemm_tile_ks<BNS, YMODE, ELEM>(A, xs, B, ws, bias, Y, M, N, K, tm * 128, plan.n_small0 + tn * BNS, act, epi,
+                                      smem);
     }
 }
 
@@ -861,6 +865,7 @@ TilePlan plan_tiles(int64_t M, int64_t N) {
     p.tiles_m_small = (int)((M + 127) / 128);
     p.nsmall = small_panels * p.tiles_m_small;
     p.n_small0 = (tn - small_panels) * 256;
+    p.bn_small = 256;
     return p;
 }
 
@@ -869,6 +874,23 @@ TilePlan plan_tiles(int64_t M, int64_t N) {
 // (us, tile plan against 64 x 64 tiles): N = 4096: M = 256 24.3 / 13.5, M = 512 25.5 / 17.2,
 // M = 768 27.3 / 28.4; N = 11008: M = 129 26.7 / 27.0, M = 256 27.6 / 29.1; at M = 256,
 // N = 4096 also K = 11008 53.7 / 30.6 and K = 14336 66.4 / 38.4.
+// 128 x 128 small tiles instead of 128 x 256 when every tile is small and the 128 x 128 tiles
+// make at most one round: twice the workgroups on the same two-group split-K schedule.
+// Measured at K = 4096 (us, 128 x 256 / 128 x 128): N = 4096: M = 600 30.4 / 21.9, M = 768
+// 31.5 / 23.0, M = 1024 31.2 / 23.1; N = 11008: M = 129 29.4 / 21.5, M = 256 34.0 / 24.1;
+// N = 14336, M = 256 35.1 / 25.6; N = 4096, M = 1024, K = 11008 74.1 / 53.4; M = 768,
+// K = 14336 92.7 / 65.9. Past one round it loses (M = 1536, N = 4096: 32.4 / 43.3; M = 384,
+// N = 11008, 258 tiles: 32.6 / 34.6).
+bool use_quarter_tiles(const TilePlan& p, int64_t N) {
+    return p.nbig == 0 && (int64_t)p.tiles_m_small * ((N + 127) / 128) <= cu_count();
+}
+
+TilePlan quarter_plan(TilePlan p, int64_t N) {
+    p.nsmall = p.tiles_m_small * (int)((N + 127) / 128);
+    p.bn_small = 128;
+    return p;
+}
+
 bool use_mid_tiles(const TilePlan& p, int64_t M, int64_t N) {
     const int wgs = p.nbig > p.nsmall ? p.nbig : p.nsmall;
     const int64_t mid = ((M + 63) / 64) * ((N + 63) / 64);
@@ -884,20 +906,30 @@ ql_status launch_gemm_w8a8(const int8_t* xq, const float* x_scale, const int8_t*
                            int out_scale_n) {
     if (M == 0 || N == 0)
         return QL_OK;
-    const TilePlan plan = plan_tiles(M, N);
+    TilePlan plan = plan_tiles(M, N);
     if (use_mid_tiles(plan, M, N)) {
         // the tile plan would leave most CUs idle: 64 x 64 tiles instead
         return launch_gemm_w8a8_mid(xq, x_scale, wq, w_scale, bias, y, y_mode, act, x_zero, colsum, out_scale,
                                     out_scale_n, M, N, K, stream, e4m3);
     }
+    if (use_quarter_tiles(plan, N))
+        plan = quarter_plan(plan, N);
     // Workgroup b runs big tile b (b < nbig) and then half tile b (b < nsmall), so the
     // half tiles start on the first CUs to finish a big tile without a new dispatch and
     // their first copies overlap the big tile's last stores.
     const dim3 grid((unsigned)(plan.nbig > plan.nsmall ? plan.nbig : plan.nsmall)), block(64 * NWAVES);
     const int m = (int)M, n = (int)N, k = (int)K;
-#define QL_LAUNCH(MODE, EL)                                                                         \
-    hipLaunchKernelGGL((gemm_w8a8_kernel<MODE, EL>), grid, block, 0, stream, xq, x_scale, wq, w_scale, \
-                       bias, y, m, n, k, act, (EpiArgs{x_zero, colsum, out_scale, out_scale_n}), plan)
+#define QL_LAUNCH(MODE, EL)                                                                              \
+    do {                                                                                                 \
+        if (plan.bn_small == 128)                                                                        \
+            hipLaunchKernelGGL((gemm_w8a8_kernel<MODE, EL, 128>), grid, block, 0, stream, xq, x_scale, wq, \
+                               w_scale, bias, y, m, n, k, act, (EpiArgs{x_zero, colsum, out_scale, out_scale_n}), \
+                               plan);                                                                    \
+        else                                                                                             \
+            hipLaunchKernelGGL((gemm_w8a8_kernel<MODE, EL, 256>), grid, block, 0, stream, xq, x_scale, wq, \
+                               w_scale, bias, y, m, n, k, act, (EpiArgs{x_zero, colsum, out_scale, out_scale_n}), \
+                               plan);                                                                    \
+    } while (0)
     if (e4m3) {
         if (y_mode == Y_F32)
             QL_LAUNCH(Y_F32, EL_E4M3);

@@ -111,13 +111,14 @@ def _half_integer_codes(rng, shape) -> np.ndarray:
 @pytest.mark.parametrize("M,N,K", [(1, 1, 64), (16, 256, 256), (300, 520, 384), (257, 129, 192),
                                    (128, 300, 128), (2000, 8300, 256), (64, 256, 4096), (16, 11008, 1024),
                                    (24, 10240, 192), (200, 3001, 576), (1, 4096, 4096), (8, 1000, 1344),
-                                   (40, 2000, 704), (20, 4096, 1472)])
+                                   (40, 2000, 704), (20, 4096, 1472), (1000, 4096, 192), (300, 7000, 320)])
 def test_exact_sums(ql, M, N, K):
     """With unit scales, no bias and fp32 output, y is the exact sum of products: any
     dropped, repeated or misplaced product shows. Covers several tiles, ragged M and N,
     the 64 x 64 kernel (with a half-deep last stage), the mixed big/half tile plan, a long K,
-    the few-row kernel's four-wave shape (more than 2 x CUs workgroups of 16 columns), and its
-    eight-wave ring over pairs of steps (2 pairs in flight up to 8 rows, 1 beyond), with odd
+    the tile kernel on 128 x 128 tiles (M = 1000, N = 4096; ragged with a half-deep last stage at
+    300 x 7000 x 320), the few-row kernel's four-wave shape (more than 2 x CUs workgroups of 16
+    columns), and its eight-wave ring over pairs of steps (2 pairs in flight up to 8 rows, 1 beyond), with odd
     step counts per wave and odd first steps (K = 1344: 21 steps over 8 waves; K = 704, 1472)."""
     rng = np.random.default_rng(M + 3 * N + 7 * K)
     a = _half_integer_codes(rng, (M, K))

@@ -199,7 +199,8 @@ def test_fused_activation_none_is_plain(ql):
 @pytest.mark.parametrize("M,N,K,out,act", [(1, 4096, 4096, torch.float16, "none"), (33, 520, 384, torch.float32, "gelu"), (16, 256, 256, torch.float32, "none"), (300, 520, 384, torch.float16, "none"),
                                            (16, 11008, 512, torch.float16, "silu"),
                                            (257, 129, 192, torch.float32, "gelu"), (2000, 8300, 64, torch.float16, "silu"),
-                                           (2048, 11008, 4096, torch.float16, "none")])
+                                           (2048, 11008, 4096, torch.float16, "none"),
+                                           (768, 4096, 256, torch.float16, "gelu")])   # 128 x 128 tiles
 def test_asymmetric_layer(ql, M, N, K, out, act):
     """Asymmetric activations end to end on the GPU (quantizer bit-exact, column sums exact)
     against the oracle's layer from its definition, sum_k s_x (q_x - z_x) s_w q_w + b.
@@ -271,7 +272,8 @@ def _requant_case(ql, M, N, K, per_tensor, seed_shift=0):
                                               (20, 9000, 640, False),
                                               (16, 256, 256, False), (16, 256, 256, True), (300, 520, 384, False),
                                               (257, 129, 192, True), (128, 1000, 128, False),
-                                              (2000, 8300, 256, False), (2048, 11008, 4096, True)])
+                                              (2000, 8300, 256, False), (2048, 11008, 4096, True),
+                                              (1000, 4096, 256, False)])   # 128 x 128 tiles
 def test_requant_bit_exact(ql, M, N, K, per_tensor):
     """int8 output codes bit for bit: the kernel takes ((acc * xs) * ws) + b with separate
     roundings, then the correctly rounded y / s, RNE and the clamp, exactly the oracle's
@@ -361,15 +363,17 @@ def test_few_rows_layer(ql, act, M, N, K, out):
 @pytest.mark.parametrize("M,N,K", [(64, 4096, 256), (65, 4096, 256), (8, 14336, 192), (9, 14336, 192),
                                    (16, 11008, 128), (24, 11008, 128), (512, 4096, 256), (513, 4096, 256),
                                    (128, 11008, 320), (129, 11008, 320), (200, 3001, 576), (1024, 4096, 192),
-                                   (600, 9000, 192)])
+                                   (1025, 4096, 192), (300, 7000, 320), (600, 9000, 192)])
 def test_kernel_switches_int32(ql, M, N, K):
     """Shapes on both sides of each switch between the three W8A8 kernels: few-row against
     64 x 64 tiles (M * N = 256K at N = 4096; M = 8 against 9 at N = 14336 > 12288; 16 against
     24 rows at N = 11008), 64 x 64 tiles against the tile kernel (M = 512 against 513 at
-    N = 4096, where 64 x 64 tiles pass two rounds; M = 128 against 129 at N = 11008), a ragged
-    64 x 64 case with a half-deep last stage, and the tile kernel's half-height-only plan
-    (M = 1024, N = 4096; ragged at M = 600, N = 9000). Accumulators bit for bit on rows
-    sampled from every 64-row band."""
+    N = 4096, where 64 x 64 tiles pass two rounds; M = 128 against 129 at N = 11008, the latter
+    on 128 x 128 tiles), a ragged 64 x 64 case with a half-deep last stage, and the tile
+    kernel's plans without big tiles on both sides of the switch from 128 x 128 to 128 x 256
+    tiles (M = 1024 against 1025 at N = 4096: 256 tiles of 128 x 128 against 288; ragged at
+    M = 300, N = 7000 with a half-deep last stage; 128 x 256 at M = 600, N = 9000). Accumulators
+    bit for bit on rows sampled from every 64-row band."""
     rng = np.random.default_rng(M * 7 + N * 3 + K)
     a = _rand_codes(rng, (M, K), -128)
     b = _rand_codes(rng, (N, K), -128)
@@ -380,10 +384,12 @@ def test_kernel_switches_int32(ql, M, N, K):
 
 @pytest.mark.parametrize("act", ["none", "gelu"])
 @pytest.mark.parametrize("M,N,K,out", [(200, 3001, 576, torch.float16), (300, 1000, 256, torch.float32),
-                                       (40, 11008, 512, torch.float16)])
+                                       (40, 11008, 512, torch.float16), (600, 4096, 256, torch.float16),
+                                       (300, 7000, 320, torch.float32)])
 def test_mid_tile_layer(ql, act, M, N, K, out):
     """The 64 x 64 kernel's epilogue (ragged N with scalar stores, fp16 and fp32 output, a fused
-    activation): within the tile kernel's tolerances, and with act = none bit for bit the value
+    activation), and the tile kernel's on 128 x 128 tiles (M = 600, N = 4096; ragged M and N at
+    300 x 7000): within the tile kernel's tolerances, and with act = none bit for bit the value
     the plain call gives."""
     w = workloads.with_shape(workloads.W8A8_PREFILL, M, K, N, seed=M + N)
     inp, (xq, xs, wq, ws), (xq_r, xs_r, wq_r, ws_r) = _layer(ql, w)
