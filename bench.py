@@ -303,9 +303,10 @@ def producer_timings(n, runs, nbytes, progress):
     return {k: {"us": us[k], "GB_per_s": nbytes[k] / (us[k] * 1e-6) / 1e9} for k in runs}
 
 
-def measured_ceilings(dev, byte_counts, progress):
+def measured_ceilings(dev, byte_counts, progress, layer_codes=None):
     """Ceilings measured with libqlprobe.so: int8 MFMA TOPS from registers (random and
-    constant operands) and the GB/s of one cold streaming read of each byte count."""
+    constant operands, and the layer's own W and X codes when `layer_codes` = (wq, xq) is
+    given) and the GB/s of one cold streaming read of each byte count."""
     import ctypes
 
     import torch
@@ -319,6 +320,9 @@ def measured_ceilings(dev, byte_counts, progress):
     P.qlp_mfma_i8.restype = ctypes.c_int
     P.qlp_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
     P.qlp_stream_read.restype = ctypes.c_int
+    P.qlp_mfma_i8_data.argtypes = [ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                   ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    P.qlp_mfma_i8_data.restype = ctypes.c_int
     cus = P.qlp_cu_count()
     if cus <= 0:
         raise RuntimeError("qlp_cu_count failed")
@@ -349,6 +353,16 @@ def measured_ceilings(dev, byte_counts, progress):
         dt = timed(lambda i: check(P.qlp_mfma_i8(iters, rnd, ctypes.c_void_p(sink.data_ptr()), sh),
                                    "qlp_mfma_i8"), 5)
         out["mfma_i8_TOPS"][name] = ops / dt / 1e12
+    if layer_codes is not None:
+        wq, xq = layer_codes
+        wb, xb = wq.numel() // 16 * 16, xq.numel() // 16 * 16
+
+        def data_launch(n):
+            check(P.qlp_mfma_i8_data(n, ctypes.c_void_p(wq.data_ptr()), wb, ctypes.c_void_p(xq.data_ptr()), xb,
+                                     ctypes.c_void_p(sink.data_ptr()), sh), "qlp_mfma_i8_data")
+        data_launch(100)
+        dt = timed(lambda i: data_launch(iters), 5)
+        out["mfma_i8_TOPS"]["layer_operands"] = ops / dt / 1e12
     for name, nbytes in byte_counts.items():
         nb = (nbytes + 15) // 16 * 16
         nbuf = max(2, math.ceil(ROTATE_BYTES / nb))
@@ -360,7 +374,8 @@ def measured_ceilings(dev, byte_counts, progress):
                                    "qlp_stream_read"), reps)
         out["stream_read_GB_per_s"][name] = nb / dt / 1e9
         del bufs
-    out["note"] = ("MFMA: %d workgroups x 4 waves issuing v_mfma_i32_32x32x32_i8 from registers; "
+    out["note"] = ("MFMA: %d workgroups x 4 waves issuing v_mfma_i32_32x32x32_i8 from registers (layer_operands: "
+                   "fragments loaded once from the W8A8 layer's own W and X codes, W first as in the GEMM); "
                    "stream read: launches reading a cold buffer of each kernel's algorithmic "
                    "byte count (buffers rotated over more than 512 MiB), timed as a back-to-back burst" % cus)
     return out
@@ -716,11 +731,13 @@ def main():
     if args.ceilings:
         del set2, set4, set5, dec2, dec4, dec5
         ceil = measured_ceilings(dev, {"quant": ab["quant"], "w8a16": ab["w8a16"],
-                                       "w8a16_block": ab["w8a16_block"], "w4a16": ab["w4a16"]}, progress)
+                                       "w8a16_block": ab["w8a16_block"], "w4a16": ab["w4a16"]}, progress,
+                                 layer_codes=(wq3, xq3))
         out["ceilings"] = ceil
         mc = ceil["mfma_i8_TOPS"]["random_operands"]
         out["roofline"]["measured_ceiling"] = mc
         out["roofline"]["frac_of_measured_ceiling"] = gemm_tops / mc
+        out["roofline"]["frac_of_layer_operand_ceiling"] = gemm_tops / ceil["mfma_i8_TOPS"]["layer_operands"]
         rd = ceil["stream_read_GB_per_s"]
         out["quantizer"]["frac_of_stream_read"] = gbs("quant") / rd["quant"]
         for name in decode:

@@ -32,6 +32,15 @@ int qlp_cu_count(void);
 int qlp_mfma_i8(int64_t iters, int random_operands, int32_t* sink, void* stream);
 
 /*
+ * The same loop with operands loaded once from two code arrays of w_bytes and x_bytes bytes
+ * (device pointers, 16-byte aligned, sizes multiples of 16, at least 16): lane t's four
+ * 16-byte fragments are the array's 16-byte pieces 4 t .. 4 t + 3 (wrapping around), W's the
+ * matrix core's first operand. Returns -1 on a bad argument. Same sink and operation count.
+ */
+int qlp_mfma_i8_data(int64_t iters, const int8_t* w, int64_t w_bytes, const int8_t* x, int64_t x_bytes,
+                     int32_t* sink, void* stream);
+
+/*
  * Reads `bytes` bytes at `src` once (bytes % 16 == 0, src 16-byte aligned), one workgroup of
  * 8 waves per CU. sink: uint32 [CUs * 512], written once per thread.
  */

@@ -6,6 +6,10 @@
 // operands are random bytes or one constant pattern: the chip lowers its clock to stay
 // within its power limit, and MFMA power depends on the operand bits.
 //
+// qlp_mfma_i8_data: the same loop on operands loaded once from two code arrays (a layer's
+// own quantized W and X), W's as the first operand as in the GEMM: the matrix cores'
+// ceiling for that data.
+//
 // qlp_stream_read: reads a buffer once, 16 bytes a lane with 4 loads in flight per lane on
 // one workgroup of 8 waves per CU, and folds the words so that the loads stay live: the rate
 // one launch can pull a buffer of a given size out of HBM. That shape was the fastest or
@@ -63,6 +67,36 @@ __global__ __launch_bounds__(THREADS) void mfma_i8_kernel(int64_t iters, int ran
     sink[id] = s;
 }
 
+// Lane t of the grid takes its four 16-byte fragments of each operand from consecutive
+// 16-byte pieces at piece 4 t of the array (wrapping around its end): 16 consecutive codes
+// of a row, as a fragment holds them.
+__global__ __launch_bounds__(THREADS) void mfma_i8_data_kernel(int64_t iters, const i32x4* __restrict__ w,
+                                                                int64_t nw16, const i32x4* __restrict__ x,
+                                                                int64_t nx16, int32_t* __restrict__ sink) {
+    const uint32_t id = blockIdx.x * THREADS + threadIdx.x;
+    i32x4 a[4], b[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        a[q] = w[(4 * (int64_t)id + q) % nw16];
+        b[q] = x[(4 * (int64_t)id + q) % nx16];
+    }
+    i32x16 acc[4] = {};
+    for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                acc[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[q], b[(q + j) & 3], acc[j], 0, 0, 0);
+    }
+    int32_t s = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            s += acc[j][e];
+    sink[id] = s;
+}
+
 constexpr int READ_THREADS = 512;   // threads per stream-read workgroup (one per CU)
 constexpr int READ_DEPTH = 4;       // loads in flight per lane
 
@@ -101,6 +135,19 @@ extern "C" int qlp_mfma_i8(int64_t iters, int random_operands, int32_t* sink, vo
         return -1;
     hipLaunchKernelGGL(mfma_i8_kernel, dim3((unsigned)cus), dim3(THREADS), 0,
                        reinterpret_cast<hipStream_t>(stream), iters, random_operands, sink);
+    return (int)hipGetLastError();
+}
+
+extern "C" int qlp_mfma_i8_data(int64_t iters, const int8_t* w, int64_t w_bytes, const int8_t* x,
+                                int64_t x_bytes, int32_t* sink, void* stream) {
+    const int cus = qlp_cu_count();
+    if (cus <= 0 || sink == nullptr || iters < 0 || w == nullptr || x == nullptr || w_bytes < 16 ||
+        x_bytes < 16 || w_bytes % 16 != 0 || x_bytes % 16 != 0 || reinterpret_cast<uintptr_t>(w) % 16 != 0 ||
+        reinterpret_cast<uintptr_t>(x) % 16 != 0)
+        return -1;
+    hipLaunchKernelGGL(mfma_i8_data_kernel, dim3((unsigned)cus), dim3(THREADS), 0,
+                       reinterpret_cast<hipStream_t>(stream), iters, reinterpret_cast<const i32x4*>(w),
+                       w_bytes / 16, reinterpret_cast<const i32x4*>(x), x_bytes / 16, sink);
     return (int)hipGetLastError();
 }
 

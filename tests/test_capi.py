@@ -287,12 +287,16 @@ def test_probe_library_exports_its_header():
         pytest.skip("libqlprobe.so not built")
     text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
     names = set(re.findall(r"^\s*int\s+([a-z_0-9]+)\s*\(", text, re.M))
-    assert names == {"qlp_cu_count", "qlp_mfma_i8", "qlp_stream_read"}
+    assert names == {"qlp_cu_count", "qlp_mfma_i8", "qlp_mfma_i8_data", "qlp_stream_read"}
     out = subprocess.run(["nm", "-D", "--defined-only", PROBE_LIB], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
     assert names <= exported
     L = ctypes.CDLL(PROBE_LIB)
     L.qlp_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
     L.qlp_stream_read.restype = ctypes.c_int
+    L.qlp_mfma_i8_data.argtypes = [ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                   ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    L.qlp_mfma_i8_data.restype = ctypes.c_int
     # no GPU here: the device query fails first and nothing is launched
     assert L.qlp_stream_read(A, 16, A, None) == -1
+    assert L.qlp_mfma_i8_data(1, A, 16, A, 16, A, None) == -1
