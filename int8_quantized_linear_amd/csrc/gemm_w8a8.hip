@@ -18,9 +18,9 @@
 // multiply-adds. The two 4-wave groups alternate between MFMA phases (with the copies
 // spread between the MFMAs) and phases of LDS fragment reads, so a SIMD's MFMA stream
 // never waits behind its own LDS reads. When the last round of 256 x 256 tiles would leave CUs idle, its N
-// panels run as 128 x 256 tiles whose K is split between the two groups; when no round of
-// big tiles fills the chip either, every tile is small, as 128 x 128 tiles where those make
-// at most one round. K % 128 == 64 runs a last stage whose upper half reads zeros.
+// panels run as 128 x 256 or 128 x 192 tiles whose K is split between the two groups; when no
+// round of big tiles fills the chip either, every tile is small, as 128 x 128 tiles where those
+// make at most one round. K % 128 == 64 runs a last stage whose upper half reads zeros.
 #include <type_traits>
 
 #include "ql_internal.h"
@@ -205,9 +205,14 @@ __device__ __forceinline__ void store_tile(const ACC (&acc)[FM][FN], bool has_bi
     // to a bank (a 32-byte pad put four fp16 stores on one bank). Rows stay 16-byte aligned
     // for the 16-byte reads below.
     constexpr int ROWB = WN * SZ + 16;
-    constexpr int LPR = WN * SZ / 16;               // lanes per staged row
+    // The band is read back in segments of SEGW columns, whose 16-byte pieces divide a wave's
+    // 64 lanes evenly: the whole row, or 32 columns when the row's pieces do not (WN = 96).
+    constexpr int SEGW = 64 % (WN * SZ / 16) == 0 ? WN : 32;
+    constexpr int NSEG = WN / SEGW;
+    constexpr int LPR = SEGW * SZ / 16;             // lanes per staged row segment
     constexpr int RPI = 64 / LPR;                   // rows per read / store instruction
-    constexpr int NRD = 32 / RPI;                   // reads (and stores) per band
+    constexpr int NRD = 32 / RPI;                   // reads (and stores) per band segment
+    static_assert(WN % SEGW == 0 && 64 % LPR == 0, "segments tile the band");
     static_assert(NWV * 32 * ROWB <= RING_BYTES, "output staging fits the LDS ring");
     // Descriptor sizes are capped at LIM = 2^30 bytes, which no in-range offset reaches
     // (32 rows of at most 2^23 4-byte values); a column piece past N is sent to offset
@@ -235,9 +240,6 @@ __device__ __forceinline__ void store_tile(const ACC (&acc)[FM][FN], bool has_bi
         barrier_no_fence();
     }
     const bool vec_ok = (N % VEC) == 0;   // rows start 16-byte aligned
-    // byte offset of this lane's 16-byte piece in the first row it stores of a band
-    const int ncol = ncol0 + (lane % LPR) * VEC;
-    const int lane_off = (lane / LPR) * N * SZ + (ncol < N ? ncol * SZ : LIM);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
         float xsv = 0.0f, zsv = 0.0f;
@@ -301,36 +303,43 @@ __device__ __forceinline__ void store_tile(const ACC (&acc)[FM][FN], bool has_bi
         // keeps the band's registers few beside the accumulators.
         constexpr int PB = NRD < 4 ? NRD : 4;
 #pragma unroll
-        for (int p0 = 0; p0 < NRD; p0 += PB) {
-            u32x4 rv[PB];
+        for (int sg = 0; sg < NSEG; ++sg) {
+            // this lane's column in the segment, and the byte offset of its 16-byte piece in
+            // the first row it stores
+            const int cseg = sg * SEGW + (lane % LPR) * VEC;
+            const int n = ncol0 + cseg;
+            const int lane_off = (lane / LPR) * N * SZ + (n < N ? n * SZ : LIM);
 #pragma unroll
-            for (int b = 0; b < PB; ++b) {
-                const int r = (p0 + b) * RPI + lane / LPR, c = (lane % LPR) * VEC;
-                rv[b] = *reinterpret_cast<const u32x4*>(stage + r * ROWB + c * SZ);
-            }
-            if (vec_ok) {
-#pragma unroll
-                for (int b = 0; b < PB; ++b)
-                    __builtin_amdgcn_raw_buffer_store_b128(rv[b], rs, lane_off + (p0 + b) * RPI * N * SZ, 0, 0);
-            } else {
-                const int n = ncol0 + (lane % LPR) * VEC;
+            for (int p0 = 0; p0 < NRD; p0 += PB) {
+                u32x4 rv[PB];
 #pragma unroll
                 for (int b = 0; b < PB; ++b) {
-                    const int roff = ((p0 + b) * RPI + lane / LPR) * N * SZ;
-                    const OutT* pv = reinterpret_cast<const OutT*>(&rv[b]);
+                    const int r = (p0 + b) * RPI + lane / LPR;
+                    rv[b] = *reinterpret_cast<const u32x4*>(stage + r * ROWB + cseg * SZ);
+                }
+                if (vec_ok) {
 #pragma unroll
-                    for (int q = 0; q < VEC; ++q) {
-                        const int off = roff + (n + q < N ? (n + q) * SZ : LIM);
-                        if constexpr (SZ == 1)
-                            __builtin_amdgcn_raw_buffer_store_b8(__builtin_bit_cast(uint8_t, pv[q]), rs, off, 0, 0);
-                        else if constexpr (SZ == 2)
-                            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, pv[q]), rs, off, 0, 0);
-                        else
-                            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, pv[q]), rs, off, 0, 0);
+                    for (int b = 0; b < PB; ++b)
+                        __builtin_amdgcn_raw_buffer_store_b128(rv[b], rs, lane_off + (p0 + b) * RPI * N * SZ, 0, 0);
+                } else {
+#pragma unroll
+                    for (int b = 0; b < PB; ++b) {
+                        const int roff = ((p0 + b) * RPI + lane / LPR) * N * SZ;
+                        const OutT* pv = reinterpret_cast<const OutT*>(&rv[b]);
+#pragma unroll
+                        for (int q = 0; q < VEC; ++q) {
+                            const int off = roff + (n + q < N ? (n + q) * SZ : LIM);
+                            if constexpr (SZ == 1)
+                                __builtin_amdgcn_raw_buffer_store_b8(__builtin_bit_cast(uint8_t, pv[q]), rs, off, 0, 0);
+                            else if constexpr (SZ == 2)
+                                __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, pv[q]), rs, off, 0, 0);
+                            else
+                                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, pv[q]), rs, off, 0, 0);
+                        }
                     }
                 }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
         }
         asm volatile("" ::: "memory");   // the next band's writes follow these reads
     }
@@ -592,7 +601,7 @@ __device__ __forceinline__ void gemm_tile_ks(const int8_t* __restrict__ A, const
                                              int8_t* smem) {
     constexpr int BM = 128, BKL = 128;
     constexpr int WM = 64, WN = BN / 2, FM = WM / 32, FN = WN / 32;
-    static_assert(BN == 256 || BN == 128, "128 x 256 or 128 x 128 tiles");
+    static_assert(BN == 256 || BN == 192 || BN == 128, "128 x 256, 128 x 192 or 128 x 128 tiles");
     constexpr int STAGE_A = BM * BKL, STAGE = (BM + BN) * BKL;
     constexpr int CA = BM / 32, CB = BN / 32;   // copies of A and B per wave of a group (8 rows each)
     static_assert(3 * STAGE <= RING_BYTES, "three stages fit the LDS allocation");
@@ -811,7 +820,7 @@ __device__ __forceinline__ void gemm_tile_ks(const int8_t* __restrict__ A, const
 }
 
 // Tiles: `nbig` 256 x 256 tiles cover the first `nbig / tiles_m` N-panels and `nsmall`
-// 128 x BNS tiles (BNS = 256, or 128 when every tile is small) the remaining panels;
+// 128 x BNS tiles (BNS = 256, 192, or 128 when every tile is small) the remaining columns;
 // workgroup b takes big tile b, then small tile b.
 // With 256 CUs, whole rounds of big tiles keep every CU busy and the leftover panels run
 // as half-height tiles in a shorter final round. Within each kind, tiles are dealt to
@@ -891,6 +900,29 @@ TilePlan quarter_plan(TilePlan p, int64_t N) {
     return p;
 }
 
+// Small tiles 192 columns wide where they make more workgroups than 256-wide ones and still
+// at most one round: the small tiles run together, so the widest sets their time, and a CU's
+// operand bytes per tile fall by a sixth. Measured at K = 4096 (us, 128 x 256 / 128 x 192; the
+// same int32 sums and outputs): M = 2048, N = 11008 (256 big tiles, then 176 / 240 small)
+// 86.6 / 84.0; M = 384, N = 11008 27.9 / 24.3; M = 512, N = 11008 30.6 / 27.4; M = 384,
+// N = 14336 31.2 / 27.2; M = 600, N = 9000 30.8 / 27.6; M = 1025, N = 4096 28.6 / 24.7;
+// M = 1536, N = 11008 78.6 / 74.4; M = 3072, N = 11008 132.9 / 128.2; M = 512, N = 11008,
+// K = 11008 66.2 / 60.2.
+int small_tiles_192(const TilePlan& p, int64_t N) {
+    return p.tiles_m_small * (int)((N - p.n_small0 + 191) / 192);
+}
+
+bool use_192_tiles(const TilePlan& p, int64_t N) {
+    const int n = small_tiles_192(p, N);
+    return p.nsmall > 0 && n > p.nsmall && n <= cu_count();
+}
+
+TilePlan plan_192(TilePlan p, int64_t N) {
+    p.nsmall = small_tiles_192(p, N);
+    p.bn_small = 192;
+    return p;
+}
+
 bool use_mid_tiles(const TilePlan& p, int64_t M, int64_t N) {
     const int wgs = p.nbig > p.nsmall ? p.nbig : p.nsmall;
     const int64_t mid = ((M + 63) / 64) * ((N + 63) / 64);
@@ -914,6 +946,8 @@ ql_status launch_gemm_w8a8(const int8_t* xq, const float* x_scale, const int8_t*
     }
     if (use_quarter_tiles(plan, N))
         plan = quarter_plan(plan, N);
+    else if (use_192_tiles(plan, N))
+        plan = plan_192(plan, N);
     // Workgroup b runs big tile b (b < nbig) and then half tile b (b < nsmall), so the
     // half tiles start on the first CUs to finish a big tile without a new dispatch and
     // their first copies overlap the big tile's last stores.
@@ -923,6 +957,10 @@ ql_status launch_gemm_w8a8(const int8_t* xq, const float* x_scale, const int8_t*
     do {                                                                                                 \
         if (plan.bn_small == 128)                                                                        \
             hipLaunchKernelGGL((gemm_w8a8_kernel<MODE, EL, 128>), grid, block, 0, stream, xq, x_scale, wq, \
+                               w_scale, bias, y, m, n, k, act, (EpiArgs{x_zero, colsum, out_scale, out_scale_n}), \
+                               plan);                                                                    \
+        else if (plan.bn_small == 192)                                                                   \
+            hipLaunchKernelGGL((gemm_w8a8_kernel<MODE, EL, 192>), grid, block, 0, stream, xq, x_scale, wq, \
                                w_scale, bias, y, m, n, k, act, (EpiArgs{x_zero, colsum, out_scale, out_scale_n}), \
                                plan);                                                                    \
         else                                                                                             \

@@ -40,6 +40,20 @@ typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 // bits 3:0 and 15:14; expcnt and lgkmcnt left at their maxima).
 constexpr int vmcnt_le(int n) { return (n & 0xF) | (0x7 << 4) | (0xF << 8) | (((n >> 4) & 3) << 14); }
 
+// Waits until this wave's copies of a stage have landed, when min(C, n) later stages (CPS
+// copies each) were issued after it: the waitcnt immediate for the wave-uniform n.
+template <int CPS, int C>
+__device__ inline void wait_stages(int n) {
+    if constexpr (C <= 0) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
+    } else {
+        if (n >= C)
+            __builtin_amdgcn_s_waitcnt(vmcnt_le(C * CPS));
+        else
+            wait_stages<CPS, C - 1>(n);
+    }
+}
+
 __device__ inline int hsw(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 // 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at l * 16 past the
@@ -144,35 +158,22 @@ __global__ __launch_bounds__(256) void gemm_w8a8_mid_kernel(
     for (int s = 0; s < MID_NS - 1; ++s)
         if (s < KT)
             copies(s);
-    {
-        const int after = min(MID_NS - 2, KT - 1);   // stages issued after stage 0
-        if (after >= 2)
-            __builtin_amdgcn_s_waitcnt(vmcnt_le(2 * CPS));
-        else if (after == 1)
-            __builtin_amdgcn_s_waitcnt(vmcnt_le(CPS));
-        else
-            __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
-    }
+    wait_stages<CPS, MID_NS - 2>(KT - 1);   // stages issued after stage 0
     asm volatile("s_barrier" ::: "memory");
     read(0, 0);
     // Stage kt: its fragments are in fa/fb[kt & 1]. Wait for this wave's copies of stage
     // kt + 1, barrier (every wave's copies of kt + 1 landed; every wave is past its reads of
-    // stage kt - 1, whose buffer (kt + 3) % 4 is refilled next), issue the copies of stage
-    // kt + 3, read stage kt + 1, run stage kt's MFMAs. The loop runs two stages per trip so
-    // that the fragment parity is a constant.
+    // stage kt - 1, whose buffer (kt + NS - 1) % NS is refilled next), issue the copies of
+    // stage kt + NS - 1, read stage kt + 1, run stage kt's MFMAs. The loop runs two stages
+    // per trip so that the fragment parity is a constant.
     auto stage = [&](int kt, auto par) {
         constexpr int P = decltype(par)::value;
-        if (kt + 1 < KT) {
-            // stages issued after kt + 1: kt + 2, if it exists
-            if (kt + 2 < KT)
-                __builtin_amdgcn_s_waitcnt(vmcnt_le(CPS));
-            else
-                __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
-        }
+        if (kt + 1 < KT)
+            wait_stages<CPS, MID_NS - 3>(KT - 2 - kt);   // stages issued after kt + 1
         asm volatile("s_barrier" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
-        if (kt + 3 < KT)
-            copies(kt + 3);
+        if (kt + MID_NS - 1 < KT)
+            copies(kt + MID_NS - 1);
         if (kt + 1 < KT)
             read(kt + 1, 1 - P);
         mfma(P);

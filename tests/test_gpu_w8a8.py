@@ -113,7 +113,9 @@ def test_prefill_full_size(ql):
 @pytest.mark.parametrize("M,N,K,with_bias,out", [(300, 520, 384, True, torch.float16),
                                                  (300, 520, 384, False, torch.float16),
                                                  (1, 77, 64, True, torch.float32),
-                                                 (513, 300, 640, True, torch.float32)])
+                                                 (513, 300, 640, True, torch.float32),
+                                                 (600, 9001, 256, True, torch.float32),    # 128 x 192 tiles,
+                                                 (1025, 4100, 192, False, torch.float16)])  # scalar stores
 def test_ragged_layer(ql, M, N, K, with_bias, out):
     w = workloads.with_shape(workloads.W8A8_PREFILL, M, K, N)
     inp, (xq, xs, wq, ws), (xq_r, xs_r, wq_r, ws_r) = _layer(ql, w)
@@ -151,7 +153,8 @@ ACT = {"gelu": 1, "silu": 2}
 
 @pytest.mark.parametrize("act", ["gelu", "silu"])
 @pytest.mark.parametrize("M,N,K,out", [(16, 256, 256, torch.float32), (300, 520, 384, torch.float16),
-                                       (300, 520, 384, torch.float32), (2000, 8300, 64, torch.float16)])
+                                       (300, 520, 384, torch.float32), (2000, 8300, 64, torch.float16),
+                                       (600, 9001, 256, torch.float32)])   # 128 x 192 tiles
 def test_fused_activation(ql, act, M, N, K, out):
     """act(acc * x_scale * w_scale + bias) from the epilogue, against the oracle's fp64
     activation of its fp64 epilogue; half-height-only, mixed and big-tile plans.
@@ -200,7 +203,8 @@ def test_fused_activation_none_is_plain(ql):
                                            (16, 11008, 512, torch.float16, "silu"),
                                            (257, 129, 192, torch.float32, "gelu"), (2000, 8300, 64, torch.float16, "silu"),
                                            (2048, 11008, 4096, torch.float16, "none"),
-                                           (768, 4096, 256, torch.float16, "gelu")])   # 128 x 128 tiles
+                                           (768, 4096, 256, torch.float16, "gelu"),    # 128 x 128 tiles
+                                           (600, 9001, 256, torch.float32, "silu")])   # 128 x 192 tiles
 def test_asymmetric_layer(ql, M, N, K, out, act):
     """Asymmetric activations end to end on the GPU (quantizer bit-exact, column sums exact)
     against the oracle's layer from its definition, sum_k s_x (q_x - z_x) s_w q_w + b.
@@ -273,7 +277,8 @@ def _requant_case(ql, M, N, K, per_tensor, seed_shift=0):
                                               (16, 256, 256, False), (16, 256, 256, True), (300, 520, 384, False),
                                               (257, 129, 192, True), (128, 1000, 128, False),
                                               (2000, 8300, 256, False), (2048, 11008, 4096, True),
-                                              (1000, 4096, 256, False)])   # 128 x 128 tiles
+                                              (1000, 4096, 256, False),    # 128 x 128 tiles
+                                              (600, 9000, 256, False), (1025, 4100, 192, True)])   # 128 x 192
 def test_requant_bit_exact(ql, M, N, K, per_tensor):
     """int8 output codes bit for bit: the kernel takes ((acc * xs) * ws) + b with separate
     roundings, then the correctly rounded y / s, RNE and the clamp, exactly the oracle's
@@ -363,17 +368,20 @@ def test_few_rows_layer(ql, act, M, N, K, out):
 @pytest.mark.parametrize("M,N,K", [(64, 4096, 256), (65, 4096, 256), (8, 14336, 192), (9, 14336, 192),
                                    (16, 11008, 128), (24, 11008, 128), (512, 4096, 256), (513, 4096, 256),
                                    (128, 11008, 320), (129, 11008, 320), (200, 3001, 576), (1024, 4096, 192),
-                                   (1025, 4096, 192), (300, 7000, 320), (600, 9000, 192)])
+                                   (1025, 4096, 192), (300, 7000, 320), (600, 9000, 192), (384, 14336, 128),
+                                   (1536, 11008, 128)])
 def test_kernel_switches_int32(ql, M, N, K):
     """Shapes on both sides of each switch between the three W8A8 kernels: few-row against
     64 x 64 tiles (M * N = 256K at N = 4096; M = 8 against 9 at N = 14336 > 12288; 16 against
     24 rows at N = 11008), 64 x 64 tiles against the tile kernel (M = 512 against 513 at
     N = 4096, where 64 x 64 tiles pass two rounds; M = 128 against 129 at N = 11008, the latter
     on 128 x 128 tiles), a ragged 64 x 64 case with a half-deep last stage, and the tile
-    kernel's plans without big tiles on both sides of the switch from 128 x 128 to 128 x 256
-    tiles (M = 1024 against 1025 at N = 4096: 256 tiles of 128 x 128 against 288; ragged at
-    M = 300, N = 7000 with a half-deep last stage; 128 x 256 at M = 600, N = 9000). Accumulators
-    bit for bit on rows sampled from every 64-row band."""
+    kernel's plans without big tiles on both sides of the switch from 128 x 128 to 128 x 192
+    tiles (M = 1024 against 1025 at N = 4096: 256 tiles of 128 x 128 against 198 of 128 x 192,
+    where 128 x 128 would make 288; ragged at M = 300, N = 7000 with a half-deep last stage;
+    128 x 192 at M = 600, N = 9000 and M = 384, N = 14336), and big tiles followed by 128 x 192
+    tiles (M = 1536, N = 11008: 252 big tiles, then 24 small ones over the last 256 columns).
+    Accumulators bit for bit on rows sampled from every 64-row band."""
     rng = np.random.default_rng(M * 7 + N * 3 + K)
     a = _rand_codes(rng, (M, K), -128)
     b = _rand_codes(rng, (N, K), -128)
