@@ -18,8 +18,9 @@
 // multiply-adds. The two 4-wave groups alternate between MFMA phases (with the copies
 // spread between the MFMAs) and phases of LDS fragment reads, so a SIMD's MFMA stream
 // never waits behind its own LDS reads. When the last round of 256 x 256 tiles would leave CUs idle, its N
-// panels run as 128 x 256 or 128 x 192 tiles whose K is split between the two groups; when no
-// round of big tiles fills the chip either, every tile is small, as 128 x 128 tiles where those
+// panels run as 128 x 256 or 128 x 192 tiles whose K is split between the two groups; a single
+// partial round of big tiles runs as 256 x 192 tiles where those put more CUs to work; when
+// no round of big tiles fills the chip, every tile is small, as 128 x 128 tiles where those
 // make at most one round. K % 128 == 64 runs a last stage whose upper half reads zeros.
 #include <type_traits>
 
@@ -385,9 +386,10 @@ __device__ inline int stage_soff(int v) {
 // read or a copy of its own wave, and the copies' address work in the texture unit (16
 // bytes a lane, one copy every ~16 clocks per CU) is split evenly between the two phases.
 // Wave w owns the (BM / 2) x (BN / 4) block at rows (BM / 2) (w & 1), columns (BN / 4)
-// (w >> 1): group 0 reads all of A and the low half of B's columns, group 1 all of A and
-// the high half, so the three parts of a stage buffer (A, B low, B high) fall free at
-// different times.
+// (w >> 1); with BN = 192 (whose quarters are not whole 32-column blocks) the (BM / 4) x
+// (BN / 2) block at rows (BM / 4) (w & 3), columns (BN / 2) (w >> 2). Either way group 0
+// reads all of A and the low half of B's columns, group 1 all of A and the high half, so
+// the three parts of a stage buffer (A, B low, B high) fall free at different times.
 //
 // Phase 2j (A_j):    group 0 runs stage j's MFMAs; group 1 reads stage j, then copies B
 //                    high of stage j + 1 and B low of stage j + 2.
@@ -403,16 +405,18 @@ __device__ __forceinline__ void gemm_tile_pp(const int8_t* __restrict__ A, const
                                              int M, int N, int K, int m0, int n0, int act, EpiArgs epi,
                                              int8_t* smem) {
     constexpr int BKL = 128;
-    constexpr int WM = BM / 2, WN = BN / 4, FM = WM / 32, FN = WN / 32;
+    constexpr bool ROWS4 = BN % 128 != 0;   // four row blocks per group, two column halves
+    constexpr int WM = ROWS4 ? BM / 4 : BM / 2, WN = ROWS4 ? BN / 2 : BN / 4, FM = WM / 32, FN = WN / 32;
     constexpr int STAGE_A = BM * BKL, STAGE = (BM + BN) * BKL;
     constexpr int CA = BM / 32, CH = BN / 64;   // per wave: copies of A, and of each half of B (8 rows each)
     static_assert(2 * STAGE <= RING_BYTES, "two stages fit the LDS allocation");
-    static_assert(FM >= 1 && FN >= 1 && CA % 2 == 0 && CH % 2 == 0, "tile shape");
+    static_assert(FM >= 1 && FN >= 1 && WM % 32 == 0 && WN % 32 == 0 && CA % 2 == 0 && BN % 64 == 0,
+                  "tile shape");
 
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int grp = wave >> 2, q = wave & 3;
-    const int wm = wave & 1, wn = wave >> 1;
+    const int wm = ROWS4 ? wave & 3 : wave & 1, wn = ROWS4 ? wave >> 2 : wave >> 1;
     const int KT = (K + BKL - 1) / BKL;   // the last stage may be half deep (K % 128 == 64)
 
     // Wave q copies rows (BM / 4) q .. of A, and rows (BN / 8) q .. of each half of B: copy
@@ -424,13 +428,17 @@ __device__ __forceinline__ void gemm_tile_pp(const int8_t* __restrict__ A, const
         const_cast<int8_t*>(A) + (int64_t)m0 * K, 0, rows_a * K, 0x00020000);
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<int8_t*>(B) + (int64_t)n0 * K, 0, rows_b * K, 0x00020000);
-    // Row R + 8 c + (l >> 3) (R a multiple of 16) has h128 = ((l >> 3) & 7) ^ (c & 1), so
-    // a lane's offset is one of two values plus 8 c rows and the k-step.
+    // Row R + 8 c + (l >> 3) (R a multiple of 8) has h128 = ((l >> 3) & 7) ^ ((R / 8 + c) & 1),
+    // so a lane's offset is one of two values plus 8 c rows and the k-step. R / 8 is even for
+    // A's rows and for B's when each wave's share of a half (BN / 8 rows) is a multiple of 16;
+    // with BN = 192 (24 rows a wave) it has the wave's parity, q & 1 (the half's base, 96 h
+    // rows, is a multiple of 16).
     const int cra = (BM / 4) * q + (lane >> 3), crb = (BN / 8) * q + (lane >> 3);
+    const int bpar = (BN / 64) % 2 == 0 ? 0 : q & 1;
     const int cx = (lane & 7) ^ ((lane >> 3) & 7);
     const int va0 = cra * K + (cx << 4), va1 = cra * K + ((cx ^ 1) << 4);
     const int vb0 = crb * K + (cx << 4), vb1 = crb * K + ((cx ^ 1) << 4);
-    // The lane's logical chunk is cx ^ (c & 1): in the upper half (k 64..127 of the stage)
+    // The lane's logical chunk is cx or cx ^ 1: in the upper half (k 64..127 of the stage)
     // exactly when cx >= 4. A half-deep last stage reads zeros there.
     const int hi = (K & (BKL - 1)) != 0 && cx >= 4 ? 0x40000000 : 0;
     // Copy c of A's rows, or of B's half h, of stage kt into buffer buf; see copy_voff.
@@ -441,7 +449,7 @@ __device__ __forceinline__ void gemm_tile_pp(const int8_t* __restrict__ A, const
     };
     auto copy_b = [&](int kt, int buf, int h, int c) {
         const int so = stage_soff(kt * BKL + (h * (BN / 2) + 8 * c) * K);
-        lds_copy16_buf(rb, copy_voff((c & 1) ? vb1 : vb0, so, hi, kt == KT - 1 ? -1 : 0), 0,
+        lds_copy16_buf(rb, copy_voff(((c ^ bpar) & 1) ? vb1 : vb0, so, hi, kt == KT - 1 ? -1 : 0), 0,
                        smem + buf * STAGE + STAGE_A + (h * (BN / 2) + (BN / 8) * q + 8 * c) * BKL);
     };
 
@@ -819,17 +827,18 @@ __device__ __forceinline__ void gemm_tile_ks(const int8_t* __restrict__ A, const
     }
 }
 
-// Tiles: `nbig` 256 x 256 tiles cover the first `nbig / tiles_m` N-panels and `nsmall`
-// 128 x BNS tiles (BNS = 256, 192, or 128 when every tile is small) the remaining columns;
-// workgroup b takes big tile b, then small tile b.
+// Tiles: `nbig` 256 x BNB tiles (BNB = 256, or 192 when the big tiles make one partial round
+// and nothing else) cover the first `nbig / tiles_m` N-panels and `nsmall` 128 x BNS tiles
+// (BNS = 256, 192, or 128 when every tile is small) the remaining columns; workgroup b takes
+// big tile b, then small tile b.
 // With 256 CUs, whole rounds of big tiles keep every CU busy and the leftover panels run
 // as half-height tiles in a shorter final round. Within each kind, tiles are dealt to
 // XCDs so that an XCD's tiles are consecutive and share W panels (column-major order).
 struct TilePlan {
-    int tiles_m_big, nbig, tiles_m_small, nsmall, n_small0, bn_small;
+    int tiles_m_big, nbig, tiles_m_small, nsmall, n_small0, bn_small, bn_big;
 };
 
-template <int YMODE, int ELEM, int BNS>
+template <int YMODE, int ELEM, int BNS, int BNB>
 __global__ __launch_bounds__(64 * NWAVES, 1) void gemm_w8a8_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ xs, const int8_t* __restrict__ B,
     const float* __restrict__ ws, const float* __restrict__ bias, void* __restrict__ Y, int M,
@@ -839,7 +848,7 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void gemm_w8a8_kernel(
     if (bid < plan.nbig) {
         const int tile = xcd_remap(bid, plan.nbig);
         const int tn = tile / plan.tiles_m_big, tm = tile - tn * plan.tiles_m_big;
-        gemm_tile_pp<256, 256, YMODE, ELEM>(A, xs, B, ws, bias, Y, M, N, K, tm * 256, tn * 256, act, epi, smem);
+        gemm_tile_pp<256, BNB, YMODE, ELEM>(A, xs, B, ws, bias, Y, M, N, K, tm * 256, tn * BNB, act, epi, smem);
         if (bid >= plan.nsmall)
             return;
         // The big tile's epilogue has read all it needs from LDS (its stores may still be in
@@ -875,6 +884,26 @@ TilePlan plan_tiles(int64_t M, int64_t N) {
     p.nsmall = small_panels * p.tiles_m_small;
     p.n_small0 = (tn - small_panels) * 256;
     p.bn_small = 256;
+    p.bn_big = 256;
+    return p;
+}
+
+// 256 x 192 big tiles when the 256 x 256 ones make one partial round and no small tiles follow
+// (between half and all of the CUs), and the narrower tiles put more CUs to work, still in one
+// round: each does three quarters of a big tile's work. Measured at K = 4096 (us, 256 x 256 /
+// 256 x 192; the same int32 sums and outputs): M = 768, N = 11008 (129 / 174 tiles) 43.5 /
+// 36.9; M = 1024, N = 11008 46.0 / 43.1; M = 768, N = 14336 44.9 / 42.1; M = 1280, N = 8192
+// 43.8 / 40.4; M = 768, N = 11008, K = 11008 95.9 / 85.4.
+int big_tiles_192(const TilePlan& p, int64_t N) { return p.tiles_m_big * (int)((N + 191) / 192); }
+
+bool use_big_192(const TilePlan& p, int64_t N) {
+    const int n = big_tiles_192(p, N);
+    return p.nsmall == 0 && p.nbig > 0 && p.nbig < cu_count() && n > p.nbig && n <= cu_count();
+}
+
+TilePlan plan_big_192(TilePlan p, int64_t N) {
+    p.nbig = big_tiles_192(p, N);
+    p.bn_big = 192;
     return p;
 }
 
@@ -948,25 +977,26 @@ ql_status launch_gemm_w8a8(const int8_t* xq, const float* x_scale, const int8_t*
         plan = quarter_plan(plan, N);
     else if (use_192_tiles(plan, N))
         plan = plan_192(plan, N);
+    else if (use_big_192(plan, N))
+        plan = plan_big_192(plan, N);
     // Workgroup b runs big tile b (b < nbig) and then half tile b (b < nsmall), so the
     // half tiles start on the first CUs to finish a big tile without a new dispatch and
     // their first copies overlap the big tile's last stores.
     const dim3 grid((unsigned)(plan.nbig > plan.nsmall ? plan.nbig : plan.nsmall)), block(64 * NWAVES);
     const int m = (int)M, n = (int)N, k = (int)K;
+#define QL_LAUNCH_ONE(MODE, EL, BNS, BNB)                                                                \
+    hipLaunchKernelGGL((gemm_w8a8_kernel<MODE, EL, BNS, BNB>), grid, block, 0, stream, xq, x_scale, wq, w_scale, \
+                       bias, y, m, n, k, act, (EpiArgs{x_zero, colsum, out_scale, out_scale_n}), plan)
 #define QL_LAUNCH(MODE, EL)                                                                              \
     do {                                                                                                 \
-        if (plan.bn_small == 128)                                                                        \
-            hipLaunchKernelGGL((gemm_w8a8_kernel<MODE, EL, 128>), grid, block, 0, stream, xq, x_scale, wq, \
-                               w_scale, bias, y, m, n, k, act, (EpiArgs{x_zero, colsum, out_scale, out_scale_n}), \
-                               plan);                                                                    \
+        if (plan.bn_big == 192)                                                                          \
+            QL_LAUNCH_ONE(MODE, EL, 256, 192);                                                           \
+        else if (plan.bn_small == 128)                                                                   \
+            QL_LAUNCH_ONE(MODE, EL, 128, 256);                                                           \
         else if (plan.bn_small == 192)                                                                   \
-            hipLaunchKernelGGL((gemm_w8a8_kernel<MODE, EL, 192>), grid, block, 0, stream, xq, x_scale, wq, \
-                               w_scale, bias, y, m, n, k, act, (EpiArgs{x_zero, colsum, out_scale, out_scale_n}), \
-                               plan);                                                                    \
+            QL_LAUNCH_ONE(MODE, EL, 192, 256);                                                           \
         else                                                                                             \
-            hipLaunchKernelGGL((gemm_w8a8_kernel<MODE, EL, 256>), grid, block, 0, stream, xq, x_scale, wq, \
-                               w_scale, bias, y, m, n, k, act, (EpiArgs{x_zero, colsum, out_scale, out_scale_n}), \
-                               plan);                                                                    \
+            QL_LAUNCH_ONE(MODE, EL, 256, 256);                                                           \
     } while (0)
     if (e4m3) {
         if (y_mode == Y_F32)
@@ -990,6 +1020,7 @@ ql_status launch_gemm_w8a8(const int8_t* xq, const float* x_scale, const int8_t*
         break;
     }
 #undef QL_LAUNCH
+#undef QL_LAUNCH_ONE
     return launch_status();
 }
 

@@ -112,7 +112,8 @@ def _half_integer_codes(rng, shape) -> np.ndarray:
                                    (128, 300, 128), (2000, 8300, 256), (64, 256, 4096), (16, 11008, 1024),
                                    (24, 10240, 192), (200, 3001, 576), (1, 4096, 4096), (8, 1000, 1344),
                                    (40, 2000, 704), (20, 4096, 1472), (1000, 4096, 192), (300, 7000, 320),
-                                   (600, 9001, 192), (1025, 4100, 192)])   # 128 x 192 tiles
+                                   (600, 9001, 192), (1025, 4100, 192),    # 128 x 192 tiles
+                                   (1000, 9001, 192), (768, 11008, 128)])  # 256 x 192 tiles
 def test_exact_sums(ql, M, N, K):
     """With unit scales, no bias and fp32 output, y is the exact sum of products: any
     dropped, repeated or misplaced product shows. Covers several tiles, ragged M and N,
@@ -167,7 +168,8 @@ def _layer_tol(y64, mag, trunc, K, code, out):
                                            (257, 129, 192, torch.float32, "gelu"),
                                            (100, 1000, 384, torch.float16, "silu"),
                                            (2048, 11008, 4096, torch.float16, "none"),
-                                           (600, 9001, 256, torch.float32, "gelu")])   # 128 x 192 tiles
+                                           (600, 9001, 256, torch.float32, "gelu"),    # 128 x 192 tiles
+                                           (1000, 9001, 256, torch.float16, "none")])  # 256 x 192 tiles
 def test_layer(ql, M, N, K, out, act):
     """The whole fp8 layer (both quantizers on the GPU) against the oracle's fp8 layer in
     fp64 on the oracle's own codes. Quantization is per row of X and per column of W, so

@@ -43,13 +43,15 @@ def test_int32_bit_exact(ql, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(2000, 8300, 64), (2048, 11008, 192), (2048, 11008, 384),
-                                   (2000, 8300, 256), (4096, 8400, 128), (8192, 2100, 64)])
+                                   (2000, 8300, 256), (4096, 8400, 128), (8192, 2100, 64),
+                                   (768, 11008, 256), (1000, 9001, 192), (1280, 8192, 320)])
 def test_int32_mixed_tile_plan(ql, M, N, K):
     """Shapes with more 256 x 256 tiles than CUs, where the last N panels run as 128-row
     tiles in the same launch, each after a big tile in the same workgroup (ragged M and N
     in the first case; two rounds of big tiles before the half tiles in the fifth; a ragged
-    half-tile panel in the last); rows sampled from every 128-row band are checked
-    bit-exactly."""
+    half-tile panel in the last); and shapes whose 256 x 256 tiles would make one partial
+    round, run as 256 x 192 tiles (ragged M and N, a half-deep last stage); rows sampled from
+    every 128-row band are checked bit-exactly."""
     rng = np.random.default_rng(M + N + K)
     a = _rand_codes(rng, (M, K), -128)
     b = _rand_codes(rng, (N, K), -128)
@@ -115,7 +117,9 @@ def test_prefill_full_size(ql):
                                                  (1, 77, 64, True, torch.float32),
                                                  (513, 300, 640, True, torch.float32),
                                                  (600, 9001, 256, True, torch.float32),    # 128 x 192 tiles,
-                                                 (1025, 4100, 192, False, torch.float16)])  # scalar stores
+                                                 (1025, 4100, 192, False, torch.float16),   # scalar stores
+                                                 (1000, 9001, 256, True, torch.float32),   # 256 x 192 tiles
+                                                 (768, 11008, 256, True, torch.float16)])
 def test_ragged_layer(ql, M, N, K, with_bias, out):
     w = workloads.with_shape(workloads.W8A8_PREFILL, M, K, N)
     inp, (xq, xs, wq, ws), (xq_r, xs_r, wq_r, ws_r) = _layer(ql, w)
@@ -154,7 +158,8 @@ ACT = {"gelu": 1, "silu": 2}
 @pytest.mark.parametrize("act", ["gelu", "silu"])
 @pytest.mark.parametrize("M,N,K,out", [(16, 256, 256, torch.float32), (300, 520, 384, torch.float16),
                                        (300, 520, 384, torch.float32), (2000, 8300, 64, torch.float16),
-                                       (600, 9001, 256, torch.float32)])   # 128 x 192 tiles
+                                       (600, 9001, 256, torch.float32),    # 128 x 192 tiles
+                                       (1000, 9001, 256, torch.float16)])  # 256 x 192 tiles
 def test_fused_activation(ql, act, M, N, K, out):
     """act(acc * x_scale * w_scale + bias) from the epilogue, against the oracle's fp64
     activation of its fp64 epilogue; half-height-only, mixed and big-tile plans.
@@ -204,7 +209,8 @@ def test_fused_activation_none_is_plain(ql):
                                            (257, 129, 192, torch.float32, "gelu"), (2000, 8300, 64, torch.float16, "silu"),
                                            (2048, 11008, 4096, torch.float16, "none"),
                                            (768, 4096, 256, torch.float16, "gelu"),    # 128 x 128 tiles
-                                           (600, 9001, 256, torch.float32, "silu")])   # 128 x 192 tiles
+                                           (600, 9001, 256, torch.float32, "silu"),    # 128 x 192 tiles
+                                           (768, 11008, 256, torch.float16, "gelu")])  # 256 x 192 tiles
 def test_asymmetric_layer(ql, M, N, K, out, act):
     """Asymmetric activations end to end on the GPU (quantizer bit-exact, column sums exact)
     against the oracle's layer from its definition, sum_k s_x (q_x - z_x) s_w q_w + b.
@@ -278,7 +284,8 @@ def _requant_case(ql, M, N, K, per_tensor, seed_shift=0):
                                               (257, 129, 192, True), (128, 1000, 128, False),
                                               (2000, 8300, 256, False), (2048, 11008, 4096, True),
                                               (1000, 4096, 256, False),    # 128 x 128 tiles
-                                              (600, 9000, 256, False), (1025, 4100, 192, True)])   # 128 x 192
+                                              (600, 9000, 256, False), (1025, 4100, 192, True),    # 128 x 192
+                                              (1000, 9001, 192, False), (1280, 8192, 256, True)])  # 256 x 192
 def test_requant_bit_exact(ql, M, N, K, per_tensor):
     """int8 output codes bit for bit: the kernel takes ((acc * xs) * ws) + b with separate
     roundings, then the correctly rounded y / s, RNE and the clamp, exactly the oracle's
