@@ -43,6 +43,50 @@ def test_w8a8_int32_random(ql, seed):
     assert np.array_equal(host(g.view), oracle.gemm_i32(a, b)), (M, N, K)
 
 
+def _large_shape(seed):
+    rng = np.random.default_rng(seed)
+    M = int(rng.integers(129, 4097))
+    N = int(rng.integers(256, 16385))
+    K = 64 * int(rng.integers(1, 9))
+    return rng, M, N, K
+
+
+def _sampled_rows(M):
+    return np.unique(np.concatenate([np.arange(0, M, 97), np.arange(M - 3, M)]))
+
+
+@pytest.mark.parametrize("seed", range(1100, 1124))
+def test_w8a8_int32_random_tile_plans(ql, seed):
+    """Large random shapes (M 129..4096, N 256..16384), where the routing takes every tile
+    plan across the draws: 64 x 64 tiles, 128 x 128, 128 x 192 and 128 x 256 split-K tiles
+    alone, big tiles alone (256 x 256 in one or several rounds, 256 x 192), and big tiles
+    followed by 128 x 192 or 128 x 256 tiles. Accumulators bit for bit on rows sampled from
+    every band of 97."""
+    rng, M, N, K = _large_shape(seed)
+    a = rng.integers(-128, 128, (M, K), dtype=np.int8)
+    b = rng.integers(-128, 128, (N, K), dtype=np.int8)
+    g = Guarded((M, N), torch.int32)
+    ql.gemm_w8a8_int32(dev(a), dev(b), acc=g.view)
+    g.check()
+    rows = _sampled_rows(M)
+    assert np.array_equal(host(g.view)[rows], oracle.gemm_i32(a[rows], b)), (M, N, K)
+
+
+@pytest.mark.parametrize("seed", range(3100, 3106))
+def test_e4m3_exact_random_tile_plans(ql, seed):
+    """The fp8 layer on large random shapes (the same draws' plans), exact on half-integer
+    codes, rows sampled from every band of 97."""
+    rng, M, N, K = _large_shape(seed)
+    table = oracle.e4m3_encode((np.arange(-15, 16) / 2).astype(np.float32))
+    a = table[rng.integers(0, 31, (M, K))]
+    b = table[rng.integers(0, 31, (N, K))]
+    ones_m, ones_n = np.ones(M, np.float32), np.ones(N, np.float32)
+    y = ql.gemm_e4m3_per_channel(dev(a), dev(ones_m), dev(b), dev(ones_n), out_dtype=torch.float32)
+    rows = _sampled_rows(M)
+    y64, _ = oracle.gemm_e4m3_f64(a[rows], ones_m[rows], b, ones_n)
+    assert np.array_equal(host(y)[rows].astype(np.float64), y64), (M, N, K)
+
+
 @pytest.mark.parametrize("seed", range(2000, 2010))
 def test_w8a8_requant_random(ql, seed):
     """Quantizers, GEMM and int8 output on random shapes, per-column or per-tensor scales."""
