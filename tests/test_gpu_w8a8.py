@@ -44,7 +44,8 @@ def test_int32_bit_exact(ql, M, N, K):
 
 @pytest.mark.parametrize("M,N,K", [(2000, 8300, 64), (2048, 11008, 192), (2048, 11008, 384),
                                    (2000, 8300, 256), (4096, 8400, 128), (8192, 2100, 64),
-                                   (768, 11008, 256), (1000, 9001, 192), (1280, 8192, 320)])
+                                   (768, 11008, 256), (1000, 9001, 192), (1280, 8192, 320),
+                                   (768, 11008, 64), (2048, 11008, 64)])   # one half-deep stage
 def test_int32_mixed_tile_plan(ql, M, N, K):
     """Shapes with more 256 x 256 tiles than CUs, where the last N panels run as 128-row
     tiles in the same launch, each after a big tile in the same workgroup (ragged M and N
