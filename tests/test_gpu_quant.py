@@ -33,7 +33,8 @@ def test_per_row_prefill_full(ql):
 
 @pytest.mark.parametrize("M,K,dtype", [(1, 16, np.float16), (37, 4096, np.float16),
                                        (5, 8256, np.float16), (3, 4112, np.float32),
-                                       (64, 48, np.float32), (130, 1024, np.float16), (4, 11008, np.float16), (2, 14336, np.float16), (3, 16400, np.float16), (2, 8208, np.float32)])
+                                       (64, 48, np.float32), (130, 1024, np.float16), (4, 11008, np.float16), (2, 14336, np.float16), (3, 16400, np.float16), (2, 8208, np.float32),
+                                       (2, 1 << 20, np.float16), (1, 1 << 19, np.float32)])
 def test_per_row_shapes(ql, M, K, dtype):
     """Ragged M, the shortest K, and rows too long to keep in registers."""
     rng = np.random.default_rng(M * 7 + K)
@@ -131,7 +132,8 @@ def _check_asym(ql, x):
 
 
 @pytest.mark.parametrize("M,K,dtype", [(1, 16, np.float32), (37, 4096, np.float16), (5, 8256, np.float16),
-                                       (3, 4112, np.float32), (130, 1024, np.float16), (64, 48, np.float32), (4, 11008, np.float16), (2, 14336, np.float16), (3, 16400, np.float16), (2, 8208, np.float32)])
+                                       (3, 4112, np.float32), (130, 1024, np.float16), (64, 48, np.float32), (4, 11008, np.float16), (2, 14336, np.float16), (3, 16400, np.float16), (2, 8208, np.float32),
+                                       (2, 1 << 20, np.float16)])
 def test_asym_rows_bit_exact(ql, M, K, dtype):
     """Codes, scales and float zero points bit for bit: offset and scaled normal rows,
     rows longer than the registers hold (re-read), fp16 and fp32 inputs."""

@@ -45,7 +45,8 @@ def test_w8a16_decode_full(ql):
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 64), (3, 77, 192), (17, 1000, 640), (33, 130, 256),
                                    (70, 64, 128), (1, 9000, 256), (5, 8200, 128),
-                                   (24, 9000, 512)])   # 17..32 rows, 64-column tiles
+                                   (24, 9000, 512),    # 17..32 rows, 64-column tiles
+                                   (3, 70, 1 << 20), (2, 17, 1 << 22)])   # long K, up to the largest allowed
 def test_w8a16_ragged(ql, M, N, K):
     _w8a16_sym(ql, workloads.with_shape(workloads.W8A16_DECODE, M, K, N), with_bias=(M % 2 == 1))
 
@@ -71,7 +72,8 @@ def test_w8a16_block_full(ql):
 @pytest.mark.parametrize("M,N,K,block", [(1, 50, 128, 64), (8, 333, 512, 128), (20, 100, 384, 192),
                                          (40, 9000, 128, 64), (3, 64, 256, 256),
                                          (24, 9000, 256, 64),    # one step in flight
-                                         (56, 300, 256, 64)])    # four row blocks
+                                         (56, 300, 256, 64),     # four row blocks
+                                         (8, 40, 1 << 19, 64)])  # 8192 blocks a column: scales from global memory
 def test_w8a16_block_ragged(ql, M, N, K, block):
     _w8a16_block(ql, workloads.with_shape(workloads.W8A16_BLOCK, M, K, N), block, with_bias=True)
 
@@ -102,7 +104,8 @@ def test_w4a16_full(ql):
 
 @pytest.mark.parametrize("M,N,K,group", [(1, 1, 128, 128), (3, 77, 256, 128), (32, 1000, 512, 64),
                                          (17, 9000, 256, 256), (65, 96, 384, 128), (8, 70, 128, 64),
-                                         (24, 9000, 512, 64)])   # 64-deep steps, one in flight
+                                         (24, 9000, 512, 64),    # 64-deep steps, one in flight
+                                         (33, 50, 1 << 20, 128)])  # long K
 def test_w4a16_ragged(ql, M, N, K, group):
     _w4a16(ql, workloads.with_shape(workloads.W4A16_GROUP, M, K, N), group, with_bias=True)
 
