@@ -70,6 +70,23 @@ def test_int32_extremes(ql):
     assert np.all(acc == np.int64(127) * -128 * K)
 
 
+@pytest.mark.parametrize("M", [1, 9, 40])
+def test_int32_largest_n(ql, M):
+    """N = 2^23, the largest the boundary accepts: the few-row kernel at one row, the tile
+    kernel's small tiles at 9 and 40 rows (32,768 workgroups), where a band of 32 output rows
+    of int32 spans 2^30 bytes less the last piece. Columns sampled across the whole width and
+    at its end, bit for bit."""
+    N, K = 1 << 23, 64
+    rng = np.random.default_rng(M + 23)
+    a = rng.integers(-128, 128, (M, K), dtype=np.int8)
+    b = rng.integers(-128, 128, (N, K), dtype=np.int8)
+    g = Guarded((M, N), torch.int32)
+    ql.gemm_w8a8_int32(dev(a), dev(b), acc=g.view)
+    g.check()
+    cols = np.unique(np.concatenate([np.arange(0, N, 4093), np.arange(N - 300, N)]))
+    assert np.array_equal(host(g.view)[:, cols], oracle.gemm_i32(a, b[cols]))
+
+
 def _layer(ql, w: workloads.Workload, rows=None):
     inp = workloads.draw(w, x_rows=rows)
     wq_ref, ws_ref = oracle.quant_weight_per_channel(inp.w_nk)
