@@ -98,7 +98,8 @@ def test_weight_per_channel_full(ql, w):
     assert np.array_equal(host(wq), q_ref)
 
 
-@pytest.mark.parametrize("N,K,block", [(4096, 4096, 64), (77, 192, 64), (5, 256, 128), (3, 64, 16)])
+@pytest.mark.parametrize("N,K,block", [(4096, 4096, 64), (77, 192, 64), (5, 256, 128), (3, 64, 16),
+                                     (3, 1 << 20, 64)])
 def test_block_asym_producer(ql, N, K, block):
     w = workloads.with_shape(workloads.W8A16_BLOCK, 1, K, N)
     inp = workloads.draw(w, x_rows=slice(0, 1))
@@ -109,7 +110,8 @@ def test_block_asym_producer(ql, N, K, block):
     assert np.array_equal(host(q), q_ref)
 
 
-@pytest.mark.parametrize("N,K,group", [(14336, 4096, 128), (77, 384, 128), (9, 256, 64), (4, 64, 32)])
+@pytest.mark.parametrize("N,K,group", [(14336, 4096, 128), (77, 384, 128), (9, 256, 64), (4, 64, 32),
+                                     (2, 1 << 20, 128)])
 def test_int4_producer(ql, N, K, group):
     w = workloads.with_shape(workloads.W4A16_GROUP, 1, K, N)
     inp = workloads.draw(w, x_rows=slice(0, 1))
