@@ -101,41 +101,40 @@ enum { Y_F32 = 0, Y_F16 = 1, Y_I32 = 2, Y_I8 = 3 };
 // activation applied by an epilogue (values of ql_activation)
 enum { ACT_NONE = 0, ACT_GELU = 1, ACT_SILU = 2 };
 
-// erfc(x) for all x from the Chebyshev fit of Numerical Recipes (Press et al., 2nd ed.,
-// §6.2, "erfcc"): with z = |x| and t = 1 / (1 + z / 2),
-//   erfc(z) ~ t exp(-z^2 - 1.26551223 + t P(t)),   P a degree-8 polynomial,
-// fractional error below 1.2e-7 for every z >= 0; erfc(-z) = 2 - erfc(z). One
-// reciprocal, nine fused multiply-adds and one exponential, with no range branches (the
-// library's erfc branches by range, and lanes of a wave then run several ranges).
-__device__ inline float erfc_fit(float x) {
-    const float z = fabsf(x);
-    const float t = __builtin_amdgcn_rcpf(fmaf(0.5f, z, 1.0f));
-    float p = 0.17087277f;
-    p = fmaf(p, t, -0.82215223f);
-    p = fmaf(p, t, 1.48851587f);
-    p = fmaf(p, t, -1.13520398f);
-    p = fmaf(p, t, 0.27886807f);
-    p = fmaf(p, t, -0.18628806f);
-    p = fmaf(p, t, 0.09678418f);
-    p = fmaf(p, t, 0.37409196f);
-    p = fmaf(p, t, 1.00002368f);
-    const float r = t * __expf(fmaf(-z, z, fmaf(t, p, -1.26551223f)));
-    return x >= 0.0f ? r : 2.0f - r;
+// The standard normal tail Phi(-z) for z >= 0, as 2^P(u) with u = min(z / 8, 1): log2 of the
+// tail is smooth on [0, 8] (it falls from -1 to about -50), and P is a degree-11 polynomial
+// fitted to it with the error allowed at z the smaller of 1e-5 relative and 1e-7 absolute
+// (int8_quantized_linear_amd/gelu_tail_fit.py, which also prints this table). In this fp32
+// order the GELU below is within 9e-8 |y| of y Phi(y) for every y, within 5e-6 relative for
+// y in (-6, 0), and rounds to the correctly rounded fp16 value for all but 3 of the 63,488
+// finite fp16 inputs (one fp16 step away for those). Past z = 8 the tail stays at
+// Phi(-8) ~ 6.2e-16. Eleven fused multiply-adds and one exp2, no reciprocal and no branch.
+__device__ inline float normal_tail(float z) {
+    constexpr float c[12] = {7.989465714e+00f, -4.585392761e+01f, 1.142428360e+02f, -1.604418030e+02f,
+                             1.351405334e+02f, -6.053829956e+01f, -3.572053194e+00f, 2.901321411e+01f,
+                             -2.689651489e+01f, -2.938829422e+01f, -9.208859444e+00f, -9.999999404e-01f};
+    const float u = fminf(z * 0.125f, 1.0f);
+    float p = c[0];
+#pragma unroll
+    for (int i = 1; i < 12; ++i)
+        p = fmaf(p, u, c[i]);
+    return __builtin_amdgcn_exp2f(p);
 }
 
 // The epilogue's activation of an fp32 value: GELU in its exact form y * Phi(y), or SiLU
-// y * sigmoid(y). Phi(y) = erfc(-y / sqrt 2) / 2, the same function as
-// (1 + erf(y / sqrt 2)) / 2 without its cancellation for negative y (near -5 the sum
-// keeps only a few bits of Phi in fp32). Relative error a few 1e-6 at most: below the
-// fp32 epilogue's own for the values that matter, and far below an fp16 step.
+// y * sigmoid(y). GELU is evaluated as max(y, 0) - |y| Phi(-|y|) (equal for every y, since
+// y Phi(y) = y - y Phi(-y)), which needs the normal tail only and has no cancellation for
+// negative y. Its error is well below the fp32 epilogue's own and far below an fp16 step.
 template <int ACT>
 __device__ inline float activation(float y) {
-    if constexpr (ACT == ACT_GELU)
-        return 0.5f * y * erfc_fit(-y * 0.70710678118654752f);
-    else if constexpr (ACT == ACT_SILU)
+    if constexpr (ACT == ACT_GELU) {
+        const float z = fabsf(y);
+        return fmaf(-z, normal_tail(z), fmaxf(y, 0.0f));
+    } else if constexpr (ACT == ACT_SILU) {
         return y * __builtin_amdgcn_rcpf(1.0f + __expf(-y));
-    else
+    } else {
         return y;
+    }
 }
 // fmt of launch_wonly
 enum { W_INT8_SYM = 0, W_UINT8_ZP = 1, W_INT4_SYM = 2 };
