@@ -641,6 +641,24 @@ def main():
                                      w5.K) for p, s in set5],
             ops, ab["w4a16"], w3.name, w5.name, progress)
     if args.act_steps > 0:
+        # The decode kernels with one weight set launched over and over (its bytes stay in the
+        # 256 MB Infinity Cache) against the rotated cold sets, bursts alternating: how much of a
+        # launch the HBM accounts for, and how much the kernel's own on-chip work does.
+        progress("decode with warm weights: %d bursts each" % args.act_steps)
+        dsets = {"w8a16": dec2, "w8a16_block": dec4, "w4a16": dec5}
+        runs = {}
+        for name, decs in dsets.items():
+            runs[name + "_cold"] = _cycle(decs)
+            runs[name + "_warm"] = decs[0]
+        us = _alternate(args.act_steps, runs)
+        out["decode_warm_weights"] = {
+            name: {"cold_us": us[name + "_cold"], "warm_us": us[name + "_warm"],
+                   "warm_GB_per_s": ab[name] / (us[name + "_warm"] * 1e-6) / 1e9}
+            for name in dsets}
+        out["decode_warm_weights"]["note"] = (
+            "bursts alternate between rotated weight sets (read from HBM) and one set launched "
+            "repeatedly (served from the Infinity Cache); event-timed per burst")
+    if args.act_steps > 0:
         xz3 = torch.empty((w3.M,), dtype=torch.float32, device=dev)
         cs3 = ql.weight_column_sums_i8(wq3)
         out["asymmetric_activations"] = asym_timings(
