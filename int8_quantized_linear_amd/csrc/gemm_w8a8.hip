@@ -830,12 +830,14 @@ __device__ __forceinline__ void gemm_tile_ks(const int8_t* __restrict__ A, const
 // Tiles: `nbig` 256 x BNB tiles (BNB = 256, or 192 when the big tiles make one partial round
 // and nothing else) cover the first `nbig / tiles_m` N-panels and `nsmall` 128 x BNS tiles
 // (BNS = 256, 192, or 128 when every tile is small) the remaining columns; workgroup b takes
-// big tile b, then small tile b.
+// big tile b, then small tile b (or the small tile first, when staggered).
 // With 256 CUs, whole rounds of big tiles keep every CU busy and the leftover panels run
 // as half-height tiles in a shorter final round. Within each kind, tiles are dealt to
 // XCDs so that an XCD's tiles are consecutive and share W panels (column-major order).
+// `stagger` != 0: the workgroups b < nsmall with (b & stagger) != 0 run their half tile first
+// and their big tile after it (below).
 struct TilePlan {
-    int tiles_m_big, nbig, tiles_m_small, nsmall, n_small0, bn_small, bn_big;
+    int tiles_m_big, nbig, tiles_m_small, nsmall, n_small0, bn_small, bn_big, stagger;
 };
 
 template <int YMODE, int ELEM, int BNS, int BNB>
@@ -845,6 +847,27 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void gemm_w8a8_kernel(
     int N, int K, int act, EpiArgs epi, TilePlan plan) {
     __shared__ __attribute__((aligned(1024))) int8_t smem[RING_BYTES + SCALE_BYTES];
     const int bid = blockIdx.x;
+    // Staggered order: when every CU runs one big tile and then a half tile, all big tiles
+    // finish together and their epilogues store the whole big-tile output (32 MiB at the
+    // 2048 x 11008 layer) at once, with the matrix cores idle everywhere. Half of each XCD's
+    // workgroups (bit 3 of b: workgroups are dealt to the XCDs round-robin) instead run the
+    // half tile first, so half of that burst overlaps the other workgroups' K loops. The
+    // tiles and their sums are unchanged.
+    if ((bid & plan.stagger) != 0 && bid < plan.nsmall && bid < plan.nbig) {
+        {
+            const int tile = xcd_remap(bid, plan.nsmall);
+            const int tn = tile / plan.tiles_m_small, tm = tile - tn * plan.tiles_m_small;
+            gemm_tile_ks<BNS, YMODE, ELEM>(A, xs, B, ws, bias, Y, M, N, K, tm * 128, plan.n_small0 + tn * BNS, act,
+                                          epi, smem);
+        }
+        // the half tile's epilogue has read all it needs from LDS
+        __builtin_amdgcn_s_waitcnt(vmcnt_le(63) & ~(0xF << 8));   // lgkmcnt(0)
+        barrier_no_fence();
+        const int tile = xcd_remap(bid, plan.nbig);
+        const int tn = tile / plan.tiles_m_big, tm = tile - tn * plan.tiles_m_big;
+        gemm_tile_pp<256, BNB, YMODE, ELEM>(A, xs, B, ws, bias, Y, M, N, K, tm * 256, tn * BNB, act, epi, smem);
+        return;
+    }
     if (bid < plan.nbig) {
         const int tile = xcd_remap(bid, plan.nbig);
         const int tn = tile / plan.tiles_m_big, tm = tile - tn * plan.tiles_m_big;
@@ -979,9 +1002,16 @@ ql_status launch_gemm_w8a8(const int8_t* xq, const float* x_scale, const int8_t*
         plan = plan_192(plan, N);
     else if (use_big_192(plan, N))
         plan = plan_big_192(plan, N);
-    // Workgroup b runs big tile b (b < nbig) and then half tile b (b < nsmall), so the
-    // half tiles start on the first CUs to finish a big tile without a new dispatch and
-    // their first copies overlap the big tile's last stores.
+    // One round of big tiles followed by half tiles on the same workgroups: stagger the order
+    // on half of them. Measured at K = 4096 (us, all big-first / staggered; the same outputs):
+    // M = 2048, N = 11008 83.1 / 80.6 and 82.9 / 80.3; N = 10000 82.4 / 81.4; N = 8704 76.7 /
+    // 74.7; M = 1792, N = 11008 81.6 / 81.1; M = 2048, N = 9000 77.2 / 77.5; at K = 11008
+    // 192.5 / 191.0. With two rounds of big tiles (M = 3072, N = 11008) staggering delayed the
+    // first round (123.8 / 124.9), so it is not used there.
+    plan.stagger = plan.nsmall > 0 && plan.nbig <= cu_count() ? 8 : 0;
+    // Workgroup b runs big tile b (b < nbig) and then half tile b (b < nsmall), or the two the
+    // other way round when staggered, so the half tiles need no dispatch of their own and
+    // each tile's first copies overlap the previous tile's last stores.
     const dim3 grid((unsigned)(plan.nbig > plan.nsmall ? plan.nbig : plan.nsmall)), block(64 * NWAVES);
     const int m = (int)M, n = (int)N, k = (int)K;
 #define QL_LAUNCH_ONE(MODE, EL, BNS, BNB)                                                                \

@@ -48,7 +48,8 @@ def test_int32_bit_exact(ql, M, N, K):
                                    (768, 11008, 64), (2048, 11008, 64)])   # one half-deep stage
 def test_int32_mixed_tile_plan(ql, M, N, K):
     """Shapes with more 256 x 256 tiles than CUs, where the last N panels run as 128-row
-    tiles in the same launch, each after a big tile in the same workgroup (ragged M and N
+    tiles in the same launch, each after a big tile in the same workgroup or, with one round
+    of big tiles, before it on half of the workgroups (the staggered order; ragged M and N
     in the first case; two rounds of big tiles before the half tiles in the fifth; a ragged
     half-tile panel in the last); and shapes whose 256 x 256 tiles would make one partial
     round, run as 256 x 192 tiles (ragged M and N, a half-deep last stage); rows sampled from
