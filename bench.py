@@ -249,6 +249,37 @@ def _alternate(n, runs):
     return {k: 1e3 * sum(a.elapsed_time(b) for a, b in v) / (n * BURST) for k, v in ev.items()}
 
 
+def small_layer_graph_us(ql, x, xq, xs, wq, ws, b, y, w, layers=20, replays=20):
+    """Microseconds per layer (per-row quantizer + GEMM) of a small layer whose launches are
+    captured in a HIP graph (`layers` layers per graph) and replayed: the device-side latency,
+    without the host's launch cost that bursts of launches from Python include."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # warm-up outside the capture
+        ql.prepare("quantize_per_row_int8", x, 0, w.M, w.K, xq, xs)()
+        ql.prepare("gemm_w8a8_per_channel", xq, xs, wq, ws, b, y, 0, w.M, w.N, w.K)()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        # prepared inside the capture, so that they launch on the capturing stream
+        q = ql.prepare("quantize_per_row_int8", x, 0, w.M, w.K, xq, xs)
+        m = ql.prepare("gemm_w8a8_per_channel", xq, xs, wq, ws, b, y, 0, w.M, w.N, w.K)
+        for _ in range(layers):
+            q()
+            m()
+    g.replay()
+    torch.cuda.synchronize()
+    a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(replays):
+        g.replay()
+    e.record()
+    torch.cuda.synchronize()
+    return 1e3 * a.elapsed_time(e) / (replays * layers)
+
+
 def asym_timings(n, runs, ops, quant_bytes, name, progress):
     """The layer with asymmetric per-row activations (quantizer with a float zero point, GEMM
     with the zero-point correction in the epilogue) against the symmetric one at the same
@@ -687,8 +718,10 @@ def main():
             "gemm": ql.prepare("gemm_w8a8_per_channel", xq1, xs1, wq1, ws1, b1, y1, 0, w1.M, w1.N, w1.K)})
         out["small_layer"] = {"workload": w1.name, "quant_us": us1["quant"], "gemm_us": us1["gemm"],
                               "layer_us": us1["quant"] + us1["gemm"],
+                              "graph_layer_us": small_layer_graph_us(ql, x1, xq1, xs1, wq1, ws1, b1, y1, w1),
                               "note": "latency-bound: 16 quantizer workgroups (one per row), then the few-row GEMM kernel "
-                                      "(16 workgroups of 16 columns); bursts event-timed"}
+                                      "(16 workgroups of 16 columns); bursts event-timed (host launch rate included); "
+                                      "graph_layer_us: the two launches replayed from a HIP graph, no host launch cost"}
     if args.act_steps > 0:
         # W8A8 with few rows (decode-time batches) at the 4096 x 4096 decode shape, weights
         # rotated like the decode kernels' so every launch reads W from HBM
