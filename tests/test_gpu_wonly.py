@@ -173,29 +173,38 @@ def test_w4a16_fused_activation(ql, act, M, N, K, group):
     assert np.all(np.abs(y - ref) <= 1.13 * 2e-3 * (np.abs(y64) + rms))
 
 
-def test_one_hot_exact(ql):
-    """x = e_k: y[n] is fp16((q[k,n] - z) * s) exactly for all three formats."""
-    N, K = 40, 256
+@pytest.mark.parametrize("N", [40, 10240])   # 8-column and 40-column workgroups (one and four column blocks)
+def test_one_hot_exact(ql, N):
+    """x = e_k: the group sums are exact (one product of an exact integer weight and 1.0), so
+    y[n] is fp16(fp32((q[k,n] - z) * s)) exactly for all three formats: the scale multiplies the
+    sum once in fp32 and the result is rounded once more to fp16. (For int8 codes the fp32
+    product is not always exact, and rounding twice differs from rounding fp64 (q - z) * s
+    straight to fp16 in a few elements of 70,000.)"""
+    K = 256
     rng = np.random.default_rng(17)
     ks = [0, 7, 8, 63, 64, 130, 255]
     x = np.zeros((len(ks), K), np.float16)
     x[np.arange(len(ks)), ks] = 1.0
     w = rng.standard_normal((N, K)).astype(np.float32)
+
+    def f32_then_f16(q, s):
+        return (np.asarray(q, np.float32) * np.asarray(s, np.float32)).astype(np.float16)
+
     q_ref, s_ref = oracle.quant_weight_per_channel(w)
     wq, ws = ql.quantize_weight_per_channel(dev(w))
     y = host(ql.gemm_w8a16(dev(x), wq, ws))
-    assert np.array_equal(y, (q_ref[:, ks].T.astype(np.float64) * s_ref[None, :]).astype(np.float16))
+    assert np.array_equal(y, f32_then_f16(q_ref[:, ks].T, s_ref[None, :]))
     qb, sb, zb = oracle.quant_block_asym_u8(w, 64)
     q, s, z = ql.quantize_weight_block_asym_u8(dev(w), 64)
     y = host(ql.gemm_w8a16(dev(x), q, s, z, 64))
-    ref = np.stack([(qb[:, k].astype(np.float64) - zb[:, k // 64]) * sb[:, k // 64] for k in ks])
-    assert np.array_equal(y, ref.astype(np.float16))
+    ref = np.stack([f32_then_f16(qb[:, k].astype(np.int32) - zb[:, k // 64], sb[:, k // 64]) for k in ks])
+    assert np.array_equal(y, ref)
     p_ref, s16 = oracle.quant_int4_group(w, 128)
     p, s = ql.quantize_weight_int4_grouped(dev(w), 128)
     y = host(ql.gemm_w4a16_grouped(dev(x), p, s, 128))
     qi = oracle.unpack_int4(p_ref, K)
-    ref = np.stack([qi[:, k].astype(np.float64) * s16[:, k // 128].astype(np.float64) for k in ks])
-    assert np.array_equal(y, ref.astype(np.float16))
+    ref = np.stack([f32_then_f16(qi[:, k], s16[:, k // 128].astype(np.float32)) for k in ks])
+    assert np.array_equal(y, ref)
 
 
 def test_empty(ql):
