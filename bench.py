@@ -21,7 +21,9 @@ its bracketed intervals over K. It includes the stream's launch-to-launch gap (a
 microsecond) but no event between two launches; short groups keep the GEMM's launches
 from running long enough on their own to lower the chip's clock more than a pass of the
 path does. Every input that streams from HBM rotates over more than 512 MiB of copies
-(the decode weights and the quantizer's X), so no launch finds it in the Infinity Cache.
+(the decode weights and the quantizer's X), so no launch finds it in the Infinity Cache. The
+GEMM, compute-bound, runs as a GEMM benchmark does, on the same W at every launch (45 MB, kept
+by the 256 MB Infinity Cache); ``gemm_cold_weights`` gives it with W read from HBM as well.
 The warm-up steps (200 by default) bring the chip out of its idle state first: after only 10,
 every kernel of the timed region ran slower for its first several groups (the GEMM up to 15%).
 ``roofline`` is the W8A8 GEMM's (the dominant kernel); ``rooflines`` holds one entry per
@@ -689,6 +691,24 @@ def main():
         out["decode_warm_weights"]["note"] = (
             "bursts alternate between rotated weight sets (read from HBM) and one set launched "
             "repeatedly (served from the Infinity Cache); event-timed per burst")
+    if args.act_steps > 0:
+        # The timed step's GEMM, like a GEMM benchmark, launches on the same W each time (45 MB,
+        # which the 256 MB Infinity Cache keeps between launches); here it also runs over copies of
+        # W rotated through more than 512 MiB, so that every launch reads W from HBM, bursts
+        # alternating with the resident W.
+        progress("W8A8 GEMM with cold weights: %d bursts each" % args.act_steps)
+        rw = rotations(w3.N * w3.K)
+        wsets3 = [wq3.clone() for _ in range(rw)]
+        gemms_cold = [ql.prepare("gemm_w8a8_per_channel", xq3, xs3, wq_, ws3, b3, y3, F16, w3.M, w3.N, w3.K)
+                      for wq_ in wsets3]
+        usg = _alternate(args.act_steps, {"resident": gemm, "cold": _cycle(gemms_cold)})
+        out["gemm_cold_weights"] = {
+            w3.name: {"resident_us": usg["resident"], "cold_us": usg["cold"], "weight_sets_rotated": rw,
+                      "cold_TOPS": ops / (usg["cold"] * 1e-6) / 1e12,
+                      "cold_frac_int8_peak": ops / (usg["cold"] * 1e-6) / 1e12 / PEAK_INT8_TOPS},
+            "note": "bursts alternate between the timed step's W (resident) and copies of W rotated over "
+                    "more than 512 MiB (read from HBM at every launch); event-timed per burst"}
+        del wsets3, gemms_cold
     if args.act_steps > 0:
         xz3 = torch.empty((w3.M,), dtype=torch.float32, device=dev)
         cs3 = ql.weight_column_sums_i8(wq3)
