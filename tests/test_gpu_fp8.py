@@ -11,7 +11,8 @@ multiple of 2^(E - 13); the exact group sum then enters the fp32 accumulator. So
     |y - y64| <= x_scale w_scale sum_g 8 * 2^(E_g - 13)            (truncation)
                + (K/8 + 8) * 2^-24 * (mag + |bias|)                (fp32 sums, epilogue)
 with mag = x_scale w_scale sum_k |products| from the oracle; times max |act'| = 1.13
-after an activation, plus 2e-6 |ref| for the activation's own error; fp16 outputs add
+after an activation, plus 6e-6 |ref| for the activation's own error (the
+GELU evaluation pinned in test_gelu_tail: within 6e-6 relative for y in (-6, 0)); fp16 outputs add
 one fp16 step.
 """
 import numpy as np
@@ -157,7 +158,7 @@ def _trunc_bound(xq: np.ndarray, wq: np.ndarray) -> np.ndarray:
 
 def _layer_tol(y64, mag, trunc, K, code, out):
     ref = oracle.activation_f64(y64, code)
-    tol = (1.13 if code else 1.0) * (trunc + (K / 8 + 8) * 2.0 ** -24 * mag) + 2e-6 * np.abs(ref)
+    tol = (1.13 if code else 1.0) * (trunc + (K / 8 + 8) * 2.0 ** -24 * mag) + 6e-6 * np.abs(ref)
     if out == torch.float16:
         tol = tol + f16_ulp(ref)
     return ref, tol

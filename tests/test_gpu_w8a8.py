@@ -183,8 +183,9 @@ def test_fused_activation(ql, act, M, N, K, out):
     """act(acc * x_scale * w_scale + bias) from the epilogue, against the oracle's fp64
     activation of its fp64 epilogue; half-height-only, mixed and big-tile plans.
     Scales put the pre-activation values at a few units, where both activations bend.
-    fp32: |y - act(y64)| <= 1.2e-5 * (|acc xs ws| + |bias|) + 2e-6 |act(y64)| (the
-    epilogue's error times |act'| <= 1.13, plus the activation's own fp32 evaluation);
+    fp32: |y - act(y64)| <= 1.2e-5 * (|acc xs ws| + |bias|) + 6e-6 |act(y64)| (the
+    epilogue's error times |act'| <= 1.13, plus the activation's own fp32 evaluation, which
+    test_gelu_tail pins within 6e-6 relative for GELU on y in (-6, 0));
     fp16: within one fp16 step of fp16(act(y64))."""
     rng = np.random.default_rng(M + 7 * N + K)
     a = _rand_codes(rng, (M, K))
@@ -203,7 +204,7 @@ def test_fused_activation(ql, act, M, N, K, out):
     assert np.all(np.isfinite(y))
     if out == torch.float32:
         mag = np.abs(acc_ref.astype(np.float64) * xs[rows][:, None] * ws[None, :]) + np.abs(bias)[None, :]
-        assert np.all(np.abs(y - ref) <= 1.2e-5 * mag + 2e-6 * np.abs(ref))
+        assert np.all(np.abs(y - ref) <= 1.2e-5 * mag + 6e-6 * np.abs(ref))
     else:
         ref16 = ref.astype(np.float16).astype(np.float64)
         assert np.all(np.abs(y - ref16) <= f16_ulp(ref16))
@@ -235,7 +236,7 @@ def test_asymmetric_layer(ql, M, N, K, out, act):
     against the oracle's layer from its definition, sum_k s_x (q_x - z_x) s_w q_w + b.
     The kernel takes acc - z_x colsum with one rounding: fp32 outputs within
     1e-5 (s_x s_w (|acc| + |z_x colsum|) + |b|), times max |act'| = 1.13 when an activation
-    follows, plus 2e-6 |act(y64)|; fp16 outputs additionally one fp16 step. Activations
+    follows, plus 6e-6 |act(y64)|; fp16 outputs additionally one fp16 step. Activations
     are ReLU-like on half the rows (non-negative, zero point -128)."""
     w = workloads.with_shape(workloads.W8A8_PREFILL, M, K, N)
     inp = workloads.draw(w)
@@ -261,7 +262,7 @@ def test_asymmetric_layer(ql, M, N, K, out, act):
            + np.abs(inp.bias.astype(np.float64))[None, :])
     code = {"none": 0, "gelu": 1, "silu": 2}[act]
     ref = oracle.activation_f64(y64, code)
-    tol = (1.13 if code else 1.0) * 1e-5 * mag + 2e-6 * np.abs(ref)
+    tol = (1.13 if code else 1.0) * 1e-5 * mag + 6e-6 * np.abs(ref)
     y = host(g.view)[rows].astype(np.float64)
     if out == torch.float16:
         tol = tol + f16_ulp(ref)
@@ -384,7 +385,7 @@ def test_few_rows_layer(ql, act, M, N, K, out):
     mag = np.abs(acc.astype(np.float64) * xs_r[:, None] * ws_r[None, :]) + np.abs(inp.bias)[None, :]
     code = {"none": 0, "gelu": 1, "silu": 2}[act]
     ref = oracle.activation_f64(y64, code)
-    tol = (1.13 if code else 1.0) * 1e-5 * mag + (2e-6 * np.abs(ref) if code else 0.0)
+    tol = (1.13 if code else 1.0) * 1e-5 * mag + (6e-6 * np.abs(ref) if code else 0.0)
     if out == torch.float16:
         tol = tol + f16_ulp(ref)
     y = host(g.view).astype(np.float64)
@@ -445,7 +446,7 @@ def test_mid_tile_layer(ql, act, M, N, K, out):
     else:
         a64 = oracle.activation_f64(y64, ACT[act])
         if out == torch.float32:
-            assert np.all(np.abs(y - a64) <= 1.2e-5 * mag + 2e-6 * np.abs(a64))
+            assert np.all(np.abs(y - a64) <= 1.2e-5 * mag + 6e-6 * np.abs(a64))
         else:
             ref16 = a64.astype(np.float16).astype(np.float64)
             assert np.all(np.abs(y - ref16) <= f16_ulp(ref16))
