@@ -246,10 +246,11 @@ __global__ __launch_bounds__(QT) void quant_rows_i8_kernel(const void* __restric
 
 // Per-tensor symmetric int8 (hotelren.com "量化算法的本质", per_tensor_quant_int8: one scale
 // for the whole array, s = max(absmax, 1e-10) / 127, codes as the per-row quantizer's). The
-// caller's one-float scale output is the only accumulator, so four small launches run in
-// order on the stream: zero it; fold every workgroup's absmax into it with one atomic max
-// on the float's bits (non-negative floats order like their bit patterns); write the codes,
-// each workgroup deriving s from the absmax; replace the absmax by s.
+// caller's one-float scale output is the only accumulator, so three launches run in order on
+// the stream: zero it; fold every workgroup's scale s_wg = max(absmax_wg, 1e-10) / 127 into it
+// with one atomic max on the float's bits (non-negative floats order like their bit patterns,
+// and a -> max(a, 1e-10) / 127, a correctly rounded division, never decreases, so the largest
+// s_wg is exactly the s of the whole array's absmax); write the codes with that s.
 constexpr int TCH = 4;   // 16-byte chunks per thread per step of the grid-stride loops
 
 __global__ __launch_bounds__(64) void tensor_slot_zero_kernel(float* __restrict__ slot) {
@@ -278,11 +279,11 @@ __global__ __launch_bounds__(QT) void tensor_absmax_kernel(const void* __restric
     }
     amax = block_max(amax, red);
     // Device-scope atomics on one address serialize at the memory side, so most workgroups
-    // skip theirs: the slot only grows, and a workgroup whose maximum does not exceed the
+    // skip theirs: the slot only grows, and a workgroup whose scale does not exceed the
     // value it reads (never more than the final one) cannot change the result.
     if (threadIdx.x == 0) {
         unsigned int* p = reinterpret_cast<unsigned int*>(slot);
-        const unsigned int mine = __float_as_uint(amax);
+        const unsigned int mine = __float_as_uint(fmaxf(amax, 1e-10f) / 127.0f);
         if (mine > __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
             atomicMax(p, mine);
     }
@@ -294,7 +295,7 @@ __global__ __launch_bounds__(QT) void tensor_codes_kernel(const void* __restrict
                                                           int8_t* __restrict__ q) {
     using C = Chunk<F16>;
     const char* xb = reinterpret_cast<const char*>(x);
-    const float s = fmaxf(*slot, 1e-10f) / 127.0f;
+    const float s = *slot;
     const float y = 1.0f / s;
     const int64_t stride = (int64_t)gridDim.x * QT * TCH;
     for (int64_t base = (int64_t)blockIdx.x * QT * TCH + threadIdx.x; base < nch; base += stride) {
@@ -308,11 +309,6 @@ __global__ __launch_bounds__(QT) void tensor_codes_kernel(const void* __restrict
             if (base + i * QT < nch)
                 c[i].store_codes(q + (base + i * QT) * C::E, s, y);
     }
-}
-
-__global__ __launch_bounds__(64) void tensor_slot_scale_kernel(float* __restrict__ slot) {
-    if (threadIdx.x == 0)
-        *slot = fmaxf(*slot, 1e-10f) / 127.0f;
 }
 
 // Asymmetric per-row int8 (hotelren.com "量化算法的本质", per_channel_quant_int8, the
@@ -570,7 +566,6 @@ ql_status launch_quant_tensor_i8(const void* x, int x_is_f16, int64_t n, int8_t*
         hipLaunchKernelGGL(tensor_absmax_kernel<false>, grid_max, block, 0, stream, x, nch, scale);
         hipLaunchKernelGGL(tensor_codes_kernel<false>, grid, block, 0, stream, x, nch, scale, q);
     }
-    hipLaunchKernelGGL(tensor_slot_scale_kernel, one, w64, 0, stream, scale);
     return launch_status();
 }
 

@@ -33,7 +33,7 @@ def _inputs(rng, M, K, N, Md, Nd, M4, N4):
 
 def test_path_replayed_in_a_graph(ql):
     """Per-row quantizer + W8A8 GEMM (600 x 1024 x 2000: 128 x 128 split-K tiles), per-tensor
-    quantizer (four launches), W8A16 decode (1 row) and W4A16 (32 rows, groups of 128)."""
+    quantizer (three launches), W8A16 decode (1 row) and W4A16 (32 rows, groups of 128)."""
     rng = np.random.default_rng(21)
     M, K, N, Md, Nd, M4, N4 = 600, 1024, 2000, 1, 3000, 32, 2500
     x, w, xd, wd, x4, w4 = _inputs(rng, M, K, N, Md, Nd, M4, N4)
