@@ -450,13 +450,18 @@ __global__ __launch_bounds__(256) void quant_block_asym_u8_kernel(
     s = fmaxf(s, 1e-8f);
     const float zf = fminf(fmaxf(rintf(-mn / s), 0.0f), 255.0f);
     const int z = (int)zf;
+    // w / s through the block's correctly rounded reciprocal and an exact remainder, as in
+    // code_u8_biased: the correctly rounded quotient at three operations
+    // (tests/quotient_identity.c checks this over the producer's domain of blocks)
+    const float y = 1.0f / s;
     uint8_t* qo = q + n * K + g * block;
     for (int c = li; c < ch; c += lp) {
         const f32x4 t = *reinterpret_cast<const f32x4*>(v + 4 * c);
         uint32_t b = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            int cq = (int)rintf(t[j] / s) + z;
+            const float q0 = __fmul_rn(t[j], y);
+            int cq = (int)rintf(fmaf(fmaf(-q0, s, t[j]), y, q0)) + z;
             cq = cq < 0 ? 0 : (cq > 255 ? 255 : cq);
             b |= (uint32_t)cq << (8 * j);
         }
@@ -499,6 +504,10 @@ __global__ __launch_bounds__(256) void quant_int4_group_kernel(
     const float floor_a = 7.0f * 0x1p-24f;
     const _Float16 h = (_Float16)(fmaxf(a, floor_a) / 7.0f);
     const float s = (float)h;
+    // x / s through the correctly rounded reciprocal and an exact remainder (the correctly
+    // rounded quotient; tests/quotient_identity.c checks scales of any binary32 exponent in
+    // [-100, 100] with |x / s| <= 128, which holds the fp16 scales here)
+    const float y = 1.0f / s;
     int32_t* po = packed + n * (K / 8) + g * (group / 8);
     for (int c = li; c < ch; c += lp) {
         const f32x4 t0 = *reinterpret_cast<const f32x4*>(v + 8 * c);
@@ -507,7 +516,8 @@ __global__ __launch_bounds__(256) void quant_int4_group_kernel(
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const float x = j < 4 ? t0[j] : t1[j - 4];
-            const float r = fminf(fmaxf(rintf(x / s), -8.0f), 7.0f);
+            const float q0 = __fmul_rn(x, y);
+            const float r = fminf(fmaxf(rintf(fmaf(fmaf(-q0, s, x), y, q0)), -8.0f), 7.0f);
             word |= ((uint32_t)(int)r & 0xFu) << (4 * j);
         }
         po[c] = (int32_t)word;

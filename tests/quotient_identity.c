@@ -14,6 +14,10 @@
  * s any binary32 with exponent in [-100, 100] (random significands, plus all-ones and
  * one-ulp-above-a-power significands), x = s * u with |u| <= 128, and x next to each
  * tie (k + 1/2) s.
+ * A third domain covers the block-asymmetric weight producer: a block's min and max drawn
+ * with a log-uniform spread in [1e-9, 1e3] around a centre log-uniform in [1e-6, 1e3] of
+ * either sign (so blocks of one sign, with quotients up to ~1e6, are included),
+ * s = max((max - min) / 255, 1e-8), and x uniform in [min, max] plus min and max themselves.
  * Usage: quotient_identity <trials>. Exit status 0 iff no mismatch.
  */
 #include <math.h>
@@ -103,6 +107,31 @@ int main(int argc, char** argv) {
             if (!same(q, q1)) {
                 if (bad < 5)
                     printf("mismatch: s %a x %a x/s %a identity %a\n", (float)s, x, (float)q, q1);
+                ++bad;
+            }
+        }
+    }
+    for (int t = 0; t < trials * 20; ++t) {
+        const double lc = log(1e-6) + (log(1e3) - log(1e-6)) * (next() / 4294967296.0);
+        const double lw = log(1e-9) + (log(1e3) - log(1e-9)) * (next() / 4294967296.0);
+        const float c = (float)exp(lc) * ((next() & 1) ? 1.0f : -1.0f);
+        const float half = (float)exp(lw) * 0.5f;
+        const float mn = c - half, mx = c + half;
+        if (!(mx > mn))
+            continue;
+        volatile float s = fmaxf((mx - mn) / 255.0f, 1e-8f);
+        volatile float y = 1.0f / s;
+        for (int i = 0; i < 2048 + 2; ++i) {
+            const float x = i == 2048 ? mn : i == 2049 ? mx
+                                       : mn + (mx - mn) * ((float)(next() >> 8) / 16777216.0f);
+            volatile float q = x / s;
+            volatile float q0 = x * y;
+            const float r = fmaf(-q0, s, x);
+            const float q1 = fmaf(r, y, q0);
+            ++checked;
+            if (!same(q, q1)) {
+                if (bad < 5)
+                    printf("mismatch: block [%a, %a] s %a x %a x/s %a identity %a\n", mn, mx, (float)s, x, (float)q, q1);
                 ++bad;
             }
         }
