@@ -284,9 +284,9 @@ __device__ __forceinline__ void store_tile(const ACC (&acc)[FM][FN], bool has_bi
                     } else if constexpr (ASYM) {
                         // sum_k (q_x - z_x) q_w = acc - z_x colsum, with one rounding
                         const float t = fmaf(-zsv, csv[q], (float)acc[i][j][e]);
-                        v[q] = (OutT)activation<ACT>(t * xsv * wsv[q] + bv[q]);
+                        v[q] = (OutT)activation<ACT, YMODE == Y_F16>(t * xsv * wsv[q] + bv[q]);
                     } else {
-                        v[q] = (OutT)activation<ACT>((float)acc[i][j][e] * xsv * wsv[q] + bv[q]);
+                        v[q] = (OutT)activation<ACT, YMODE == Y_F16>((float)acc[i][j][e] * xsv * wsv[q] + bv[q]);
                     }
                 }
                 *reinterpret_cast<Out4*>(stage + lr * ROWB + (32 * j + 8 * g + 4 * lh) * SZ) = v;

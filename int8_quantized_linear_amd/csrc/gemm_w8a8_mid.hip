@@ -219,9 +219,9 @@ __global__ __launch_bounds__(256) void gemm_w8a8_mid_kernel(
                 } else if constexpr (ASYM) {
                     // sum_k (q_x - z_x) q_w = acc - z_x colsum, with one rounding
                     const float t = fmaf(-zxm, (float)epi.colsum[n], (float)acc[e]);
-                    v[q] = (OutT)activation<ACT>(t * xsm * wsn + bn);
+                    v[q] = (OutT)activation<ACT, YMODE == Y_F16>(t * xsm * wsn + bn);
                 } else {
-                    v[q] = (OutT)activation<ACT>((float)acc[e] * xsm * wsn + bn);
+                    v[q] = (OutT)activation<ACT, YMODE == Y_F16>((float)acc[e] * xsm * wsn + bn);
                 }
             }
         }

@@ -244,9 +244,9 @@ __global__ __launch_bounds__(64 * SW) void gemm_w8a8_small_kernel(
             } else if constexpr (ASYM) {
                 // sum_k (q_x - z_x) q_w = acc - z_x colsum, with one rounding
                 const float ta = fmaf(-epi.x_zero[m], csn, (float)t[i]);
-                put_float(o, activation<ACT>(ta * xs[m] * wsn + bn));
+                put_float(o, activation<ACT, YMODE == Y_F16>(ta * xs[m] * wsn + bn));
             } else {
-                put_float(o, activation<ACT>((float)t[i] * xs[m] * wsn + bn));
+                put_float(o, activation<ACT, YMODE == Y_F16>((float)t[i] * xs[m] * wsn + bn));
             }
         }
     }

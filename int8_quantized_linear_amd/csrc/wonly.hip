@@ -626,7 +626,7 @@ __global__ __launch_bounds__(64 * nwaves<MT>()) void wonly_kernel(
             for (int r = 0; r < 4; ++r) {
                 const int m = 16 * i + 4 * lg + r;
                 if (m < M)
-                    Y[(int64_t)m * N + n] = (_Float16)activation<ACT>(v[r] + cbias[k]);
+                    Y[(int64_t)m * N + n] = (_Float16)activation<ACT, true>(v[r] + cbias[k]);
             }
         }
     };

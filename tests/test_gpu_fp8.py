@@ -11,9 +11,9 @@ multiple of 2^(E - 13); the exact group sum then enters the fp32 accumulator. So
     |y - y64| <= x_scale w_scale sum_g 8 * 2^(E_g - 13)            (truncation)
                + (K/8 + 8) * 2^-24 * (mag + |bias|)                (fp32 sums, epilogue)
 with mag = x_scale w_scale sum_k |products| from the oracle; times max |act'| = 1.13
-after an activation, plus 6e-6 |ref| for the activation's own error (the
-GELU evaluation pinned in test_gelu_tail: within 6e-6 relative for y in (-6, 0)); fp16 outputs add
-one fp16 step.
+after an activation, plus the activation's own error (the GELU evaluations pinned in
+test_gelu_tail: within 6e-6 relative for y in (-6, 0), 3.3e-5 with the shorter tail of fp16
+outputs); fp16 outputs add one fp16 step.
 """
 import numpy as np
 import pytest
@@ -158,7 +158,8 @@ def _trunc_bound(xq: np.ndarray, wq: np.ndarray) -> np.ndarray:
 
 def _layer_tol(y64, mag, trunc, K, code, out):
     ref = oracle.activation_f64(y64, code)
-    tol = (1.13 if code else 1.0) * (trunc + (K / 8 + 8) * 2.0 ** -24 * mag) + 6e-6 * np.abs(ref)
+    act_err = 3.3e-5 if out == torch.float16 else 6e-6
+    tol = (1.13 if code else 1.0) * (trunc + (K / 8 + 8) * 2.0 ** -24 * mag) + act_err * np.abs(ref)
     if out == torch.float16:
         tol = tol + f16_ulp(ref)
     return ref, tol
@@ -168,6 +169,7 @@ def _layer_tol(y64, mag, trunc, K, code, out):
                                            (300, 520, 384, torch.float16, "none"),
                                            (257, 129, 192, torch.float32, "gelu"),
                                            (100, 1000, 384, torch.float16, "silu"),
+                                           (100, 1000, 384, torch.float16, "gelu"),
                                            (2048, 11008, 4096, torch.float16, "none"),
                                            (600, 9001, 256, torch.float32, "gelu"),    # 128 x 192 tiles
                                            (1000, 9001, 256, torch.float16, "none")])  # 256 x 192 tiles
