@@ -113,7 +113,7 @@ __device__ inline float normal_tail(float z) {
     constexpr float c[12] = {7.989465714e+00f, -4.585392761e+01f, 1.142428360e+02f, -1.604418030e+02f,
                              1.351405334e+02f, -6.053829956e+01f, -3.572053194e+00f, 2.901321411e+01f,
                              -2.689651489e+01f, -2.938829422e+01f, -9.208859444e+00f, -9.999999404e-01f};
-    const float u = fminf(z * 0.125f, 1.0f);
+    const float u = fminf(fmaxf(z * 0.125f, 0.0f), 1.0f);   // one multiply with the clamp modifier
     float p = c[0];
 #pragma unroll
     for (int i = 1; i < 12; ++i)
@@ -130,7 +130,7 @@ __device__ inline float normal_tail(float z) {
 __device__ inline float normal_tail_f16out(float z) {
     constexpr float c16[8] = {-2.647568226e+00f, 1.263620567e+01f, -2.645191193e+01f, 3.254099274e+01f,
                               -2.694931412e+01f, -2.943723869e+01f, -9.204879761e+00f, -1.000043035e+00f};
-    const float u = fminf(z * 0.125f, 1.0f);
+    const float u = fminf(fmaxf(z * 0.125f, 0.0f), 1.0f);   // one multiply with the clamp modifier
     float p = c16[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i)
