@@ -454,3 +454,47 @@ def test_mid_tile_layer(ql, act, M, N, K, out):
         else:
             ref16 = a64.astype(np.float16).astype(np.float64)
             assert np.all(np.abs(y - ref16) <= f16_ulp(ref16))
+
+
+def _finite_fp16_values() -> np.ndarray:
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    return h[np.isfinite(h)].astype(np.float32)
+
+
+@pytest.mark.parametrize("M,N,out,act", [(1, 63488, torch.float16, "gelu"),     # few-row kernel
+                                         (100, 8192, torch.float16, "gelu"),    # mid-size M
+                                         (200, 63488, torch.float16, "gelu"),   # tile kernel
+                                         (1, 63488, torch.float16, "silu"),
+                                         (100, 8192, torch.float16, "silu"),
+                                         (200, 63488, torch.float16, "silu"),
+                                         (1, 63488, torch.float32, "gelu"),
+                                         (200, 63488, torch.float32, "gelu")])
+def test_activation_over_fp16_domain(ql, M, N, out, act):
+    """X = 0 with unit scales makes the epilogue's pre-activation value exactly the bias, so a
+    bias holding every finite fp16 value (N = 63,488; an evenly spread 8,192 of them, both ends
+    included, for the mid-size case) runs the kernels' activation over the whole fp16 domain on
+    the hardware, in every row. fp16 outputs: within one fp16 step of the correctly rounded
+    act(y), for GELU (the fp16-output tail) and SiLU. fp32 outputs (GELU only; SiLU's fp32
+    exponential underflows to an exact zero below y = -88, where act(y) is a denormal-sized
+    nonzero; test_fused_activation covers it): within 2e-7 |y| of y Phi(y), the 9e-8 |y| that test_gelu_tail pins for the
+    degree-11 tail in an exactly rounded emulation, plus v_exp_f32's own error of about one
+    ulp on a tail of at most 1/2."""
+    vals = _finite_fp16_values()
+    if N < vals.size:
+        vals = vals[np.unique(np.linspace(0, vals.size - 1, N).round().astype(np.int64))]
+    assert vals.size == N
+    K = 64
+    rng = np.random.default_rng(N + M)
+    a = np.zeros((M, K), np.int8)
+    b = _rand_codes(rng, (N, K))
+    g = Guarded((M, N), out)
+    ql.gemm_w8a8_per_channel_act(dev(a), dev(np.ones(M, np.float32)), dev(b), dev(np.ones(N, np.float32)),
+                                 dev(vals), act, out, y=g.view)
+    g.check()
+    y = host(g.view).astype(np.float64)
+    ref = oracle.activation_f64(vals.astype(np.float64), ACT[act])
+    if out == torch.float16:
+        ref16 = ref.astype(np.float16).astype(np.float64)
+        assert np.all(np.abs(y - ref16[None, :]) <= f16_ulp(ref16)[None, :])
+    else:
+        assert np.all(np.abs(y - ref[None, :]) <= 2e-7 * np.abs(vals.astype(np.float64))[None, :])

@@ -212,3 +212,26 @@ def test_empty(ql):
     wq = torch.zeros((8, 64), dtype=torch.int8, device=DEV)
     y = ql.gemm_w8a16(x, wq, torch.ones(8, device=DEV))
     assert y.shape == (0, 8)
+
+
+@pytest.mark.parametrize("act", ["gelu", "silu"])
+@pytest.mark.parametrize("M", [1, 32])
+def test_w4a16_activation_over_fp16_domain(ql, act, M):
+    """X = 0 makes the decode epilogue's pre-activation value exactly the bias, so a bias
+    holding every finite fp16 value (N = 63,488) runs the W4A16 epilogue's activation over the
+    whole fp16 domain on the hardware, in every row: within one fp16 step of the correctly
+    rounded act(y) (GELU through the fp16-output tail)."""
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    vals = h[np.isfinite(h)].astype(np.float32)
+    N, K, group = vals.size, 128, 128
+    rng = np.random.default_rng(M)
+    w_nk = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    p, s = ql.quantize_weight_int4_grouped(dev(w_nk), group)
+    g = Guarded((M, N), torch.float16)
+    ql.gemm_w4a16_grouped_act(dev(np.zeros((M, K), np.float16)), p, s, group, dev(vals), act, y=g.view)
+    g.check()
+    y = host(g.view).astype(np.float64)
+    ref = oracle.activation_f64(vals.astype(np.float64), {"gelu": 1, "silu": 2}[act])
+    ref16 = ref.astype(np.float16).astype(np.float64)
+    step = np.spacing(np.abs(ref.astype(np.float16))).astype(np.float64)
+    assert np.all(np.abs(y - ref16[None, :]) <= step[None, :])
